@@ -1,0 +1,587 @@
+/*
+ * cam_oracle.c -- plain, slow, obviously correct CPU oracle for the per-GPU hot
+ * path of sequence/context-parallel attention movement.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product library links, includes or
+ * calls this file; only the tests, the smoke check and the benchmark's CPU
+ * baseline leg load it.  It shares no code, header, table or helper with the
+ * HIP path.
+ *
+ * Sources (web pages, cited by title and section):
+ *  [FV]  FastVideo compare view "[perf] Probe H3 chunked all-to-all with direct
+ *        output slices": the Ulysses all_to_all_4D relayout (scatter dim 2 /
+ *        gather dim 1 and the inverse), benchmark_ulysses_a2a.py operand shapes.
+ *  [VA]  vllm-ascend PR "[Performance][Attention] Fuse local SFA LSE formation
+ *        into DCP pack": "What this PR does" (LSE = softmax_max +
+ *        log(softmax_sum), invalid statistics give -inf, stable combine) and
+ *        "How was this patch tested?" (special cases).
+ *  [CU]  cuLA PR "feat(distributed): add packed hybrid runtime and THD
+ *        planner": packed THD cu_seqlens, logical CP ranks in one process.
+ *
+ * Arithmetic: every floating-point result is computed in double and rounded
+ * once at the end (bf16 / fp16 round-to-nearest-even, fp32 by the C cast),
+ * since the pages do not fix the precision of the reduction.
+ *
+ * Readings of points the pages leave open are marked "reading:".
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------------ */
+/* Number formats (IEEE 754 binary16 and the bfloat16 truncation of binary32) */
+/* ------------------------------------------------------------------------ */
+
+/* Round a double to a binary format with `prec` significand bits (implicit bit
+ * included), smallest normal exponent `emin` and largest exponent `emax`,
+ * round-to-nearest, ties to even; returns the rounded value as a double
+ * (exactly representable in that format) or +-inf on overflow. */
+static double round_to_format(double x, int prec, int emin, int emax)
+{
+    if (isnan(x) || isinf(x) || x == 0.0)
+        return x;
+    int e;
+    frexp(fabs(x), &e);           /* |x| in [2^(e-1), 2^e) */
+    int ex = e - 1;
+    if (ex < emin)
+        ex = emin;                /* subnormal range: fixed spacing */
+    double spacing = ldexp(1.0, ex - (prec - 1));
+    double q = nearbyint(x / spacing); /* x / spacing is exact (power of two) */
+    double y = q * spacing;
+    double maxfinite = ldexp(2.0 - ldexp(1.0, -(prec - 1)), emax);
+    if (fabs(y) > maxfinite)
+        return copysign(INFINITY, x);
+    return y;
+}
+
+uint16_t orc_double_to_bf16(double x)
+{
+    if (isnan(x))
+        return (uint16_t)(signbit(x) ? 0xFFC0u : 0x7FC0u);
+    double y = round_to_format(x, 8, -126, 127);
+    float f = (float)y;           /* exact: y has at most 8 significant bits */
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    return (uint16_t)(u >> 16);
+}
+
+double orc_bf16_to_double(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return (double)f;
+}
+
+uint16_t orc_double_to_fp16(double x)
+{
+    if (isnan(x))
+        return (uint16_t)(signbit(x) ? 0xFE00u : 0x7E00u);
+    double y = round_to_format(x, 11, -14, 15);
+    uint16_t sign = signbit(y) ? 0x8000u : 0u;
+    double a = fabs(y);
+    if (isinf(a))
+        return sign | 0x7C00u;
+    if (a == 0.0)
+        return sign;
+    if (a < ldexp(1.0, -14))      /* subnormal: a = m * 2^-24 */
+        return sign | (uint16_t)(a / ldexp(1.0, -24));
+    int e;
+    frexp(a, &e);
+    int ex = e - 1;               /* a in [2^ex, 2^(ex+1)) */
+    double frac = a / ldexp(1.0, ex) - 1.0;
+    return sign | (uint16_t)((ex + 15) << 10) | (uint16_t)(frac * 1024.0);
+}
+
+double orc_fp16_to_double(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int ex = (h >> 10) & 0x1F;
+    int man = h & 0x3FF;
+    double v;
+    if (ex == 0)
+        v = ldexp((double)man, -24);
+    else if (ex == 31)
+        v = man ? NAN : INFINITY;
+    else
+        v = ldexp(1.0 + man / 1024.0, ex - 15);
+    return sign ? -v : v;
+}
+
+/* dtype codes: 0 = bf16, 1 = fp16 (16-bit storage, double arithmetic). */
+static double load_half(const void* base, int64_t elem_index, int dtype)
+{
+    uint16_t b;
+    memcpy(&b, (const char*)base + 2 * elem_index, 2);
+    return dtype == 0 ? orc_bf16_to_double(b) : orc_fp16_to_double(b);
+}
+
+static void store_half(void* base, int64_t elem_index, int dtype, double v)
+{
+    uint16_t b = dtype == 0 ? orc_double_to_bf16(v) : orc_double_to_fp16(v);
+    memcpy((char*)base + 2 * elem_index, &b, 2);
+}
+
+void orc_round_bf16_array(const double* x, uint16_t* y, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        y[i] = orc_double_to_bf16(x[i]);
+}
+
+void orc_round_fp16_array(const double* x, uint16_t* y, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        y[i] = orc_double_to_fp16(x[i]);
+}
+
+void orc_bf16_to_double_array(const uint16_t* x, double* y, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        y[i] = orc_bf16_to_double(x[i]);
+}
+
+void orc_fp16_to_double_array(const uint16_t* x, double* y, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        y[i] = orc_fp16_to_double(x[i]);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Dense Ulysses relayout  ([FV], ulysses_a2a.py and benchmark_ulysses_a2a.py) */
+/* ------------------------------------------------------------------------ */
+/*
+ * P logical ranks live in one buffer, rank outermost (reading: the stack order
+ * of the emulated ranks is [P] then the B batch planes, B = 3 carrying Q, K, V).
+ *
+ * Sequence-sharded side: in[j][b][s][h][d], rank j holds tokens
+ *   [j*S/P, (j+1)*S/P) of every plane, all H heads.
+ * Head-sharded side:     out[r][b][t][h'][d], rank r holds heads
+ *   [r*H/P, (r+1)*H/P) (reading: contiguous head blocks, sequence blocks
+ *   concatenated in source-rank order), all S tokens.
+ *
+ * seq->head (all_to_all_4D scatter dim 2, gather dim 1):
+ *   out[r][b][j*S/P + s][h][d] = in[j][b][s][r*H/P + h][d]
+ * head->seq (scatter dim 1, gather dim 2) is the inverse map.
+ * Elements are `esize` bytes and are copied as bits.
+ */
+void orc_seq_to_head(const void* in, void* out, int64_t P, int64_t B, int64_t S,
+                     int64_t H, int64_t D, int64_t esize)
+{
+    const char* src = (const char*)in;
+    char* dst = (char*)out;
+    int64_t Sp = S / P, Hp = H / P;
+    for (int64_t r = 0; r < P; ++r)
+        for (int64_t b = 0; b < B; ++b)
+            for (int64_t j = 0; j < P; ++j)
+                for (int64_t s = 0; s < Sp; ++s)
+                    for (int64_t h = 0; h < Hp; ++h) {
+                        int64_t o = (((r * B + b) * S + j * Sp + s) * Hp + h) * D;
+                        int64_t i = (((j * B + b) * Sp + s) * H + r * Hp + h) * D;
+                        memcpy(dst + o * esize, src + i * esize, (size_t)(D * esize));
+                    }
+}
+
+void orc_head_to_seq(const void* in, void* out, int64_t P, int64_t B, int64_t S,
+                     int64_t H, int64_t D, int64_t esize)
+{
+    const char* src = (const char*)in;
+    char* dst = (char*)out;
+    int64_t Sp = S / P, Hp = H / P;
+    for (int64_t j = 0; j < P; ++j)
+        for (int64_t b = 0; b < B; ++b)
+            for (int64_t s = 0; s < Sp; ++s)
+                for (int64_t r = 0; r < P; ++r)
+                    for (int64_t h = 0; h < Hp; ++h) {
+                        int64_t o = (((j * B + b) * Sp + s) * H + r * Hp + h) * D;
+                        int64_t i = (((r * B + b) * S + j * Sp + s) * Hp + h) * D;
+                        memcpy(dst + o * esize, src + i * esize, (size_t)(D * esize));
+                    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Varlen (packed THD, cu_seqlens) relayout  ([CU] description and review notes
+ * on cu_seqlens shard offsets; [FV] relayout per token)                     */
+/* ------------------------------------------------------------------------ */
+/*
+ * Reading: sequence i = tokens [cu[i], cu[i+1]) of length L is cut into P
+ * pieces, piece p = in-sequence positions [floor(p*L/P), floor((p+1)*L/P)),
+ * and piece p lives on logical rank p.  Rank p stores its pieces in sequence
+ * order: its token count is T_p = sum_i |piece_p(i)|, its slab [B][T_p][H][D]
+ * starts at token offset R_p = T_0 + ... + T_{p-1} of a [B]-planed rank-major
+ * buffer (element offset B*R_p*H*D).  With one sequence and P | T this is the
+ * dense layout above.
+ */
+static int64_t piece_start(int64_t p, int64_t L, int64_t P) { return (p * L) / P; }
+
+/* Host plan: rank_cu[p*(nseq+1) + i] = tokens of rank p that precede sequence
+ * i; rank_off[p] = R_p (rank_off[P] = total).  Written as plain counting. */
+void orc_varlen_plan(const int32_t* cu, int64_t nseq, int64_t P, int32_t* rank_cu,
+                     int64_t* rank_off)
+{
+    int64_t off = 0;
+    for (int64_t p = 0; p < P; ++p) {
+        rank_off[p] = off;
+        int64_t acc = 0;
+        for (int64_t i = 0; i < nseq; ++i) {
+            rank_cu[p * (nseq + 1) + i] = (int32_t)acc;
+            int64_t L = (int64_t)cu[i + 1] - cu[i];
+            acc += piece_start(p + 1, L, P) - piece_start(p, L, P);
+        }
+        rank_cu[p * (nseq + 1) + nseq] = (int32_t)acc;
+        off += acc;
+    }
+    rank_off[P] = off;
+}
+
+/* direction 0: seq->head (in rank-major ragged, out [P][B][T][H/P][D]);
+ * direction 1: head->seq (the inverse). */
+static void varlen_relayout(const void* in, void* out, const int32_t* cu, int64_t nseq,
+                            int64_t P, int64_t B, int64_t H, int64_t D, int64_t esize,
+                            int direction)
+{
+    const char* src = (const char*)in;
+    char* dst = (char*)out;
+    int64_t T = cu[nseq];
+    int64_t Hp = H / P;
+    int64_t R = 0; /* token offset of rank p's slab */
+    for (int64_t p = 0; p < P; ++p) {
+        int64_t Tp = 0;
+        for (int64_t i = 0; i < nseq; ++i) {
+            int64_t L = (int64_t)cu[i + 1] - cu[i];
+            Tp += piece_start(p + 1, L, P) - piece_start(p, L, P);
+        }
+        for (int64_t b = 0; b < B; ++b) {
+            int64_t l = 0; /* local row on rank p */
+            for (int64_t i = 0; i < nseq; ++i) {
+                int64_t L = (int64_t)cu[i + 1] - cu[i];
+                for (int64_t k = piece_start(p, L, P); k < piece_start(p + 1, L, P); ++k) {
+                    int64_t t = cu[i] + k;
+                    for (int64_t r = 0; r < P; ++r)
+                        for (int64_t h = 0; h < Hp; ++h) {
+                            int64_t seq_side = ((B * R + b * Tp + l) * H + r * Hp + h) * D;
+                            int64_t head_side = (((r * B + b) * T + t) * Hp + h) * D;
+                            if (direction == 0)
+                                memcpy(dst + head_side * esize, src + seq_side * esize,
+                                       (size_t)(D * esize));
+                            else
+                                memcpy(dst + seq_side * esize, src + head_side * esize,
+                                       (size_t)(D * esize));
+                        }
+                    ++l;
+                }
+            }
+        }
+        R += Tp;
+    }
+}
+
+void orc_varlen_seq_to_head(const void* in, void* out, const int32_t* cu, int64_t nseq,
+                            int64_t P, int64_t B, int64_t H, int64_t D, int64_t esize)
+{
+    varlen_relayout(in, out, cu, nseq, P, B, H, D, esize, 0);
+}
+
+void orc_varlen_head_to_seq(const void* in, void* out, const int32_t* cu, int64_t nseq,
+                            int64_t P, int64_t B, int64_t H, int64_t D, int64_t esize)
+{
+    varlen_relayout(in, out, cu, nseq, P, B, H, D, esize, 1);
+}
+
+/* ------------------------------------------------------------------------ */
+/* LSE formation and the max/sum-aware pack  ([VA] "What this PR does")       */
+/* ------------------------------------------------------------------------ */
+/* LSE = softmax_max + log(softmax_sum); a non-finite max, a non-finite sum or a
+ * sum <= 0 is an invalid contribution, written as -inf (natural log; -0.0 and
+ * NaN sums are invalid because they fail "> 0"). */
+double orc_lse_from_stats(float m, float s)
+{
+    if (isfinite(m) && isfinite(s) && s > 0.0f)
+        return (double)m + log((double)s);
+    return -INFINITY;
+}
+
+/* Packed exchange layout (reading: the pages keep "row/head/token mapping,
+ * packed payload semantics" but print no byte layout).  For source rank p and
+ * destination rank r, chunk (p, r) holds the rows rank r will combine:
+ *   scatter_dim = 1 (heads):  rows (t, h') for t < T, h' < H/P, source head
+ *                             r*H/P + h'; row index q = t*(H/P) + h'.
+ *   scatter_dim = 0 (tokens): rows (t', h) for t' < T/P, h < H, source token
+ *                             r*T/P + t'; row index q = t'*H + h.
+ * A chunk is the O-region [rows][Dv] in the payload dtype, padded to 16 bytes,
+ * then the L-region [rows] fp32, padded to 16 bytes.  Chunks are stored
+ * [P_src][P_dst].  Padding bytes carry no payload. */
+static int64_t round16(int64_t x) { return (x + 15) / 16 * 16; }
+
+int64_t orc_pack_rows(int64_t P, int64_t T, int64_t H, int scatter_dim)
+{
+    return scatter_dim == 1 ? T * (H / P) : (T / P) * H;
+}
+
+int64_t orc_pack_chunk_bytes(int64_t P, int64_t T, int64_t H, int64_t Dv, int scatter_dim,
+                             int64_t esize)
+{
+    int64_t rows = orc_pack_rows(P, T, H, scatter_dim);
+    return round16(rows * Dv * esize) + round16(rows * 4);
+}
+
+/* Strides are in elements; Dv is contiguous. */
+void orc_lse_pack(const void* out, int64_t o_sp, int64_t o_st, int64_t o_sh,
+                  const float* smax, int64_t m_sp, int64_t m_st, int64_t m_sh,
+                  const float* ssum, int64_t s_sp, int64_t s_st, int64_t s_sh,
+                  int64_t P, int64_t T, int64_t H, int64_t Dv, int scatter_dim,
+                  int64_t esize, void* packed)
+{
+    const char* src = (const char*)out;
+    char* dst = (char*)packed;
+    int64_t rows = orc_pack_rows(P, T, H, scatter_dim);
+    int64_t o_bytes = round16(rows * Dv * esize);
+    int64_t chunk = orc_pack_chunk_bytes(P, T, H, Dv, scatter_dim, esize);
+    for (int64_t p = 0; p < P; ++p)
+        for (int64_t r = 0; r < P; ++r) {
+            char* obase = dst + (p * P + r) * chunk;
+            float* lbase = (float*)(obase + o_bytes);
+            for (int64_t q = 0; q < rows; ++q) {
+                int64_t t, h;
+                if (scatter_dim == 1) {
+                    t = q / (H / P);
+                    h = r * (H / P) + q % (H / P);
+                } else {
+                    t = r * (T / P) + q / H;
+                    h = q % H;
+                }
+                memcpy(obase + q * Dv * esize, src + (p * o_sp + t * o_st + h * o_sh) * esize,
+                       (size_t)(Dv * esize));
+                float m = smax[p * m_sp + t * m_st + h * m_sh];
+                float s = ssum[p * s_sp + t * s_st + h * s_sh];
+                lbase[q] = (float)orc_lse_from_stats(m, s);
+            }
+        }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Stable LSE-weighted combine  ([VA] "existing stable combine")               */
+/* ------------------------------------------------------------------------ */
+/*
+ * For one output row: V = {p : L_p finite}; M = max_{p in V} L_p;
+ * w_p = exp(L_p - M); Z = sum w_p; out = sum_{p in V} w_p O_p / Z;
+ * lse_out = M + log Z.  Reading: an empty V gives out = +0 and lse_out = -inf,
+ * and an invalid partial's O row is never read (so it may hold anything).
+ * Partials are visited in ascending p.
+ *
+ * part_o[p*D + d] and part_l[p] for one row, valid[p] gates each partial.
+ */
+void orc_combine_row_f64(const double* part_o, const double* part_l, const int* valid,
+                         int64_t P, int64_t D, double* out, double* lse_out)
+{
+    double M = -INFINITY;
+    int any = 0;
+    for (int64_t p = 0; p < P; ++p)
+        if (valid[p] && isfinite(part_l[p])) {
+            if (!any || part_l[p] > M)
+                M = part_l[p];
+            any = 1;
+        }
+    if (!any) {
+        for (int64_t d = 0; d < D; ++d)
+            out[d] = 0.0;
+        *lse_out = -INFINITY;
+        return;
+    }
+    double Z = 0.0;
+    for (int64_t d = 0; d < D; ++d)
+        out[d] = 0.0;
+    for (int64_t p = 0; p < P; ++p) {
+        if (!(valid[p] && isfinite(part_l[p])))
+            continue;
+        double w = exp(part_l[p] - M);
+        Z += w;
+        for (int64_t d = 0; d < D; ++d)
+            out[d] += w * part_o[p * D + d];
+    }
+    for (int64_t d = 0; d < D; ++d)
+        out[d] /= Z;
+    *lse_out = M + log(Z);
+}
+
+/* Dense double combine: part_o [P][R][D], part_l [P][R] -> out [R][D], lse [R]. */
+void orc_combine_f64(const double* part_o, const double* part_l, int64_t P, int64_t R,
+                     int64_t D, double* out, double* lse)
+{
+    double* po = (double*)malloc(sizeof(double) * (size_t)(P * D + 1));
+    double* pl = (double*)malloc(sizeof(double) * (size_t)(P + 1));
+    int* valid = (int*)malloc(sizeof(int) * (size_t)(P + 1));
+    for (int64_t row = 0; row < R; ++row) {
+        for (int64_t p = 0; p < P; ++p) {
+            pl[p] = part_l[p * R + row];
+            valid[p] = 1;
+            for (int64_t d = 0; d < D; ++d)
+                po[p * D + d] = part_o[(p * R + row) * D + d];
+        }
+        orc_combine_row_f64(po, pl, valid, P, D, out + row * D, lse + row);
+    }
+    free(po);
+    free(pl);
+    free(valid);
+}
+
+/* Causal validity of KV piece p for token t of a packed THD batch (reading:
+ * partial p of token (i, k) is the attention of that query over piece p of its
+ * own sequence under a causal mask; it has at least one visible key, and is
+ * therefore valid, iff piece p is non-empty and starts at or before k). */
+int orc_causal_piece_valid(const int32_t* cu, int64_t nseq, int64_t P, int64_t p, int64_t t)
+{
+    for (int64_t i = 0; i < nseq; ++i) {
+        if (t >= cu[i] && t < cu[i + 1]) {
+            int64_t L = (int64_t)cu[i + 1] - cu[i];
+            int64_t k = t - cu[i];
+            int64_t a = piece_start(p, L, P), e = piece_start(p + 1, L, P);
+            return a < e && a <= k;
+        }
+    }
+    return 0;
+}
+
+/*
+ * Generic strided combine of P partials over rows (t, h), t in [t_begin, t_end):
+ *   part_out  element (p, t, h, d) at po_sp*p + po_st*(t - t_begin) + po_sh*h + d
+ *   part_lse  element (p, t, h)    at pl_sp*p + pl_st*(t - t_begin) + pl_sh*h
+ *   out       element (t, h, d)    at o_st*(t - t_begin) + o_sh*h + d
+ *   lse_out   (nullable)           at lo_st*(t - t_begin) + lo_sh*h
+ * (all strides in elements; the pointers address row t_begin, so a sample of
+ * rows can be passed without the rest).  With cu_seqlens non-null, partial p of
+ * row t is additionally gated by orc_causal_piece_valid (nseq sequences, the
+ * P partials being the P KV pieces of each sequence) and is not read when
+ * masked.  dtype 0 = bf16, 1 = fp16.
+ */
+void orc_lse_combine(const void* part_out, int64_t po_sp, int64_t po_st, int64_t po_sh,
+                     const float* part_lse, int64_t pl_sp, int64_t pl_st, int64_t pl_sh,
+                     int64_t P, int64_t t_begin, int64_t t_end, int64_t H, int64_t D,
+                     int dtype, void* out, int64_t o_st, int64_t o_sh, float* lse_out,
+                     int64_t lo_st, int64_t lo_sh, const int32_t* cu_seqlens, int64_t nseq)
+{
+    double* po = (double*)malloc(sizeof(double) * (size_t)(P * D + 1));
+    double* pl = (double*)malloc(sizeof(double) * (size_t)(P + 1));
+    int* valid = (int*)malloc(sizeof(int) * (size_t)(P + 1));
+    double* acc = (double*)malloc(sizeof(double) * (size_t)(D + 1));
+    for (int64_t t = t_begin; t < t_end; ++t)
+        for (int64_t h = 0; h < H; ++h) {
+            int64_t tr = t - t_begin;
+            for (int64_t p = 0; p < P; ++p) {
+                valid[p] = cu_seqlens ? orc_causal_piece_valid(cu_seqlens, nseq, P, p, t) : 1;
+                pl[p] = -INFINITY;
+                if (!valid[p])
+                    continue;
+                pl[p] = (double)part_lse[p * pl_sp + tr * pl_st + h * pl_sh];
+                if (!isfinite(pl[p]))
+                    continue;
+                for (int64_t d = 0; d < D; ++d)
+                    po[p * D + d] = load_half(part_out, p * po_sp + tr * po_st + h * po_sh + d, dtype);
+            }
+            double lse;
+            orc_combine_row_f64(po, pl, valid, P, D, acc, &lse);
+            for (int64_t d = 0; d < D; ++d)
+                store_half(out, tr * o_st + h * o_sh + d, dtype, acc[d]);
+            if (lse_out)
+                lse_out[tr * lo_st + h * lo_sh] = (float)lse;
+        }
+    free(po);
+    free(pl);
+    free(valid);
+    free(acc);
+}
+
+/*
+ * Combine over the emulated exchange: destination rank r receives chunk
+ * (p, r) from every source p (the all-to-all is a view of the packed buffer,
+ * no bytes move).  out row r*rows + q and lse_out (nullable) row r*rows + q,
+ * rows as in the pack; Dv contiguous.  For scatter_dim = 1 this is
+ * [P_dst][T][H/P][Dv]; for scatter_dim = 0 it is [T][H][Dv].
+ */
+void orc_lse_combine_packed(const void* packed, int64_t P, int64_t T, int64_t H, int64_t Dv,
+                            int scatter_dim, int dtype, void* out, float* lse_out)
+{
+    const char* src = (const char*)packed;
+    int64_t rows = orc_pack_rows(P, T, H, scatter_dim);
+    int64_t o_bytes = round16(rows * Dv * 2);
+    int64_t chunk = orc_pack_chunk_bytes(P, T, H, Dv, scatter_dim, 2);
+    double* po = (double*)malloc(sizeof(double) * (size_t)(P * Dv + 1));
+    double* pl = (double*)malloc(sizeof(double) * (size_t)(P + 1));
+    int* valid = (int*)malloc(sizeof(int) * (size_t)(P + 1));
+    double* acc = (double*)malloc(sizeof(double) * (size_t)(Dv + 1));
+    for (int64_t r = 0; r < P; ++r)
+        for (int64_t q = 0; q < rows; ++q) {
+            for (int64_t p = 0; p < P; ++p) {
+                const char* c = src + (p * P + r) * chunk;
+                float l;
+                memcpy(&l, c + o_bytes + 4 * q, 4);
+                pl[p] = (double)l;
+                valid[p] = 1;
+                if (!isfinite(pl[p]))
+                    continue;
+                for (int64_t d = 0; d < Dv; ++d)
+                    po[p * Dv + d] = load_half(c, q * Dv + d, dtype);
+            }
+            double lse;
+            orc_combine_row_f64(po, pl, valid, P, Dv, acc, &lse);
+            for (int64_t d = 0; d < Dv; ++d)
+                store_half(out, (r * rows + q) * Dv + d, dtype, acc[d]);
+            if (lse_out)
+                lse_out[r * rows + q] = (float)lse;
+        }
+    free(po);
+    free(pl);
+    free(valid);
+    free(acc);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Brute-force attention (tiny end-to-end check; produces partials)           */
+/* ------------------------------------------------------------------------ */
+/*
+ * q, k, v: [T][H][D] in bf16 (dtype 0) or fp16 (dtype 1).  For every query t
+ * and head h, attends the keys j in [kv_begin, kv_end) (and j <= t if causal):
+ *   score_j = (q_t . k_j) / sqrt(D)        (reading: softmax scale 1/sqrt(D))
+ *   softmax_max = max_j score_j,  softmax_sum = sum_j exp(score_j - max),
+ *   out = sum_j exp(score_j - max) v_j / softmax_sum.
+ * With no visible key: max = -inf, sum = 0, out = 0.  Outputs are double.
+ */
+void orc_attention(const void* q, const void* k, const void* v, int64_t T, int64_t H,
+                   int64_t D, int dtype, int64_t kv_begin, int64_t kv_end, int causal,
+                   double* out, double* smax, double* ssum)
+{
+    double scale = 1.0 / sqrt((double)D);
+    double* score = (double*)malloc(sizeof(double) * (size_t)(kv_end - kv_begin + 1));
+    for (int64_t t = 0; t < T; ++t)
+        for (int64_t h = 0; h < H; ++h) {
+            int64_t hi = kv_end;
+            if (causal && hi > t + 1)
+                hi = t + 1;
+            double m = -INFINITY;
+            for (int64_t j = kv_begin; j < hi; ++j) {
+                double dot = 0.0;
+                for (int64_t d = 0; d < D; ++d)
+                    dot += load_half(q, (t * H + h) * D + d, dtype) *
+                           load_half(k, (j * H + h) * D + d, dtype);
+                score[j - kv_begin] = dot * scale;
+                if (score[j - kv_begin] > m)
+                    m = score[j - kv_begin];
+            }
+            double* o = out + (t * H + h) * D;
+            for (int64_t d = 0; d < D; ++d)
+                o[d] = 0.0;
+            double sum = 0.0;
+            for (int64_t j = kv_begin; j < hi; ++j) {
+                double e = exp(score[j - kv_begin] - m);
+                sum += e;
+                for (int64_t d = 0; d < D; ++d)
+                    o[d] += e * load_half(v, (j * H + h) * D + d, dtype);
+            }
+            if (sum > 0.0)
+                for (int64_t d = 0; d < D; ++d)
+                    o[d] /= sum;
+            smax[t * H + h] = m;
+            ssum[t * H + h] = sum;
+        }
+    free(score);
+}
