@@ -1,0 +1,363 @@
+"""context_attention_movement_amd -- MI355X-native per-GPU hot path of
+sequence/context-parallel attention movement.
+
+A thin ctypes binding over ``libcam.so`` (C ABI in ``include/cam.h``): the
+Ulysses all-to-all relayout between sequence-sharded and head-sharded slabs of
+P logical ranks held in one GPU's HBM (dense and cu_seqlens varlen), the
+max/sum-aware LSE pack into the packed exchange layout, and the stable
+LSE-weighted combine.  Every step runs in the library's HIP kernels; this
+module only checks tensor metadata, allocates outputs with torch, and passes
+pointers, sizes and the current HIP stream.  There is no fallback: if the
+library is missing, every call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+from dataclasses import dataclass
+from pathlib import Path
+
+import numpy as np
+import torch
+
+__all__ = [
+    "CamError", "library", "abi_version",
+    "ulysses_seq_to_head", "ulysses_head_to_seq",
+    "VarlenPlan", "ulysses_varlen_plan", "ulysses_seq_to_head_varlen", "ulysses_head_to_seq_varlen",
+    "lse_pack_bytes", "lse_pack", "lse_combine_packed", "lse_combine", "lse_combine_varlen",
+    "copy",
+]
+
+LIB_PATH = Path(__file__).resolve().parent / "libcam.so"
+
+CAM_BF16, CAM_FP16, CAM_FP32 = 0, 1, 2
+STATUS = ["CAM_OK", "CAM_ERR_NULL", "CAM_ERR_SHAPE", "CAM_ERR_DIVISIBILITY", "CAM_ERR_ALIGNMENT",
+          "CAM_ERR_OVERLAP", "CAM_ERR_UNSUPPORTED", "CAM_ERR_HIP"]
+
+
+class CamError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        self.status = status
+        self.status_name = STATUS[status] if 0 <= status < len(STATUS) else str(status)
+        super().__init__(f"{self.status_name}: {message}")
+
+
+_lib = None
+_i64, _vp, _int = C.c_int64, C.c_void_p, C.c_int
+
+_SIGNATURES = {
+    "cam_status_string": (C.c_char_p, [_int]),
+    "cam_last_error": (C.c_char_p, []),
+    "cam_abi_version": (_int, []),
+    "ulysses_seq_to_head": (_int, [_vp, _vp, _i64, _i64, _i64, _i64, _i64, _int, _vp]),
+    "ulysses_head_to_seq": (_int, [_vp, _vp, _i64, _i64, _i64, _i64, _i64, _int, _vp]),
+    "ulysses_varlen_plan": (_int, [_vp, _i64, _i64, _vp, _vp]),
+    "ulysses_seq_to_head_varlen": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64,
+                                          _int, _vp]),
+    "ulysses_head_to_seq_varlen": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64,
+                                          _int, _vp]),
+    "lse_pack_bytes": (_i64, [_i64, _i64, _i64, _i64, _int, _int]),
+    "lse_pack": (_int, [_vp, _i64, _i64, _i64, _vp, _i64, _i64, _i64, _vp, _i64, _i64, _i64,
+                        _i64, _i64, _i64, _i64, _int, _int, _vp, _vp]),
+    "lse_combine_packed": (_int, [_vp, _i64, _i64, _i64, _i64, _int, _int, _vp, _vp, _vp]),
+    "lse_combine": (_int, [_vp, _i64, _i64, _i64, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _int,
+                           _vp, _i64, _i64, _vp, _i64, _i64, _vp]),
+    "lse_combine_varlen": (_int, [_vp, _i64, _i64, _i64, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _i64,
+                                  _int, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _vp]),
+    "cam_copy": (_int, [_vp, _vp, _i64, _vp]),
+}
+
+
+def library() -> C.CDLL:
+    """Load libcam.so (built by ``python -m context_attention_movement_amd.build``)."""
+    global _lib
+    if _lib is None:
+        if not LIB_PATH.exists():
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m context_attention_movement_amd.build` (no fallback exists)")
+        lib = C.CDLL(str(LIB_PATH))
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def abi_version() -> int:
+    return library().cam_abi_version()
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise CamError(status, library().cam_last_error().decode())
+
+
+def _dt(t: torch.Tensor, relayout: bool = False) -> int:
+    if t.dtype == torch.bfloat16:
+        return CAM_BF16
+    if t.dtype == torch.float16:
+        return CAM_FP16
+    if relayout and t.element_size() == 4:
+        return CAM_FP32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _dev(t: torch.Tensor, name: str) -> None:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _contig(t: torch.Tensor, name: str) -> None:
+    _dev(t, name)
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+# ---------------------------------------------------------------------------
+# Dense relayout
+# ---------------------------------------------------------------------------
+
+def ulysses_seq_to_head(x: torch.Tensor, P: int, out: torch.Tensor | None = None) -> torch.Tensor:
+    """[P][B][S/P][H][D] (rank j's sequence shard) -> [P][B][S][H/P][D]
+    (rank r's head shard), bits copied."""
+    _contig(x, "x")
+    if x.dim() != 5 or x.shape[0] != P:
+        raise ValueError("x must be [P][B][S/P][H][D]")
+    _, B, Sp, H, D = x.shape
+    S = Sp * P
+    if H % P:
+        raise ValueError("H must be a multiple of P")
+    if out is None:
+        out = torch.empty((P, B, S, H // P, D), dtype=x.dtype, device=x.device)
+    _contig(out, "out")
+    if out.numel() != x.numel() or out.dtype != x.dtype:
+        raise ValueError("out must match x in size and dtype")
+    _check(library().ulysses_seq_to_head(x.data_ptr(), out.data_ptr(), P, B, S, H, D, _dt(x, True),
+                                         _stream(x)))
+    return out
+
+
+def ulysses_head_to_seq(x: torch.Tensor, P: int, out: torch.Tensor | None = None) -> torch.Tensor:
+    """[P][B][S][H/P][D] -> [P][B][S/P][H][D] (inverse of ulysses_seq_to_head)."""
+    _contig(x, "x")
+    if x.dim() != 5 or x.shape[0] != P:
+        raise ValueError("x must be [P][B][S][H/P][D]")
+    _, B, S, Hp, D = x.shape
+    H = Hp * P
+    if S % P:
+        raise ValueError("S must be a multiple of P")
+    if out is None:
+        out = torch.empty((P, B, S // P, H, D), dtype=x.dtype, device=x.device)
+    _contig(out, "out")
+    if out.numel() != x.numel() or out.dtype != x.dtype:
+        raise ValueError("out must match x in size and dtype")
+    _check(library().ulysses_head_to_seq(x.data_ptr(), out.data_ptr(), P, B, S, H, D, _dt(x, True),
+                                         _stream(x)))
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Varlen relayout
+# ---------------------------------------------------------------------------
+
+@dataclass
+class VarlenPlan:
+    """Host plan and its device copies for a packed THD batch over P ranks."""
+    P: int
+    nseq: int
+    total_tokens: int
+    cu_host: np.ndarray        # int32 [nseq+1]
+    rank_cu_host: np.ndarray   # int32 [P][nseq+1]
+    rank_off_host: np.ndarray  # int64 [P+1]
+    cu: torch.Tensor           # device copies
+    rank_cu: torch.Tensor
+    rank_off: torch.Tensor
+
+    def tokens_on_rank(self, p: int) -> int:
+        return int(self.rank_off_host[p + 1] - self.rank_off_host[p])
+
+
+def ulysses_varlen_plan(cu_seqlens, P: int, device="cuda") -> VarlenPlan:
+    """Build the per-rank piece tables on the host (libcam) and upload them."""
+    cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int32))
+    nseq = cu.size - 1
+    if nseq < 0:
+        raise ValueError("cu_seqlens must have at least one entry")
+    rank_cu = np.empty((P, nseq + 1), dtype=np.int32)
+    rank_off = np.empty(P + 1, dtype=np.int64)
+    _check(library().ulysses_varlen_plan(cu.ctypes.data, nseq, P, rank_cu.ctypes.data, rank_off.ctypes.data))
+    dev = torch.device(device)
+    return VarlenPlan(P, nseq, int(cu[-1]), cu, rank_cu, rank_off,
+                      torch.from_numpy(cu).to(dev), torch.from_numpy(rank_cu).to(dev),
+                      torch.from_numpy(rank_off).to(dev))
+
+
+def ulysses_seq_to_head_varlen(x: torch.Tensor, plan: VarlenPlan, B: int = 1,
+                               out: torch.Tensor | None = None) -> torch.Tensor:
+    """Rank-major ragged [B*T][H][D] -> [P][B][T][H/P][D]."""
+    _contig(x, "x")
+    T, P = plan.total_tokens, plan.P
+    if x.dim() != 3 or x.shape[0] != B * T:
+        raise ValueError("x must be [B*T][H][D]")
+    H, D = x.shape[1], x.shape[2]
+    if out is None:
+        out = torch.empty((P, B, T, H // P, D), dtype=x.dtype, device=x.device)
+    _contig(out, "out")
+    if out.numel() != x.numel() or out.dtype != x.dtype:
+        raise ValueError("out must match x in size and dtype")
+    _check(library().ulysses_seq_to_head_varlen(
+        x.data_ptr(), out.data_ptr(), plan.cu.data_ptr(), plan.rank_cu.data_ptr(), plan.rank_off.data_ptr(),
+        plan.nseq, T, P, B, H, D, _dt(x, True), _stream(x)))
+    return out
+
+
+def ulysses_head_to_seq_varlen(x: torch.Tensor, plan: VarlenPlan, out: torch.Tensor | None = None) -> torch.Tensor:
+    """[P][B][T][H/P][D] -> rank-major ragged [B*T][H][D]."""
+    _contig(x, "x")
+    T, P = plan.total_tokens, plan.P
+    if x.dim() != 5 or x.shape[0] != P or x.shape[2] != T:
+        raise ValueError("x must be [P][B][T][H/P][D]")
+    B, D = x.shape[1], x.shape[4]
+    H = x.shape[3] * P
+    if out is None:
+        out = torch.empty((B * T, H, D), dtype=x.dtype, device=x.device)
+    _contig(out, "out")
+    if out.numel() != x.numel() or out.dtype != x.dtype:
+        raise ValueError("out must match x in size and dtype")
+    _check(library().ulysses_head_to_seq_varlen(
+        x.data_ptr(), out.data_ptr(), plan.cu.data_ptr(), plan.rank_cu.data_ptr(), plan.rank_off.data_ptr(),
+        plan.nseq, T, P, B, H, D, _dt(x, True), _stream(x)))
+    return out
+
+
+# ---------------------------------------------------------------------------
+# LSE pack and combine
+# ---------------------------------------------------------------------------
+
+def lse_pack_bytes(P: int, T: int, H: int, Dv: int, scatter_dim: int, dtype=torch.bfloat16) -> int:
+    code = CAM_BF16 if dtype == torch.bfloat16 else CAM_FP16
+    n = library().lse_pack_bytes(P, T, H, Dv, scatter_dim, code)
+    if n < 0:
+        raise CamError(2, library().cam_last_error().decode())
+    return n
+
+
+def lse_pack(out: torch.Tensor, smax: torch.Tensor, ssum: torch.Tensor, scatter_dim: int,
+             packed: torch.Tensor | None = None) -> torch.Tensor:
+    """Pack per-rank partial outputs [P][T][H][Dv] (any strides, Dv contiguous)
+    and fp32 softmax max/sum [P][T][H] (any strides) into the packed exchange
+    buffer (uint8, [P_src][P_dst][chunk]), forming the LSE on the way."""
+    for t, n in ((out, "out"), (smax, "smax"), (ssum, "ssum")):
+        _dev(t, n)
+    if out.dim() != 4 or out.stride(3) != 1:
+        raise ValueError("out must be [P][T][H][Dv] with Dv contiguous")
+    if smax.dtype != torch.float32 or ssum.dtype != torch.float32:
+        raise TypeError("softmax statistics must be float32")
+    P, T, H, Dv = out.shape
+    if tuple(smax.shape) != (P, T, H) or tuple(ssum.shape) != (P, T, H):
+        raise ValueError("statistics must be [P][T][H]")
+    n = lse_pack_bytes(P, T, H, Dv, scatter_dim, out.dtype)
+    if packed is None:
+        packed = torch.empty(n, dtype=torch.uint8, device=out.device)
+    _contig(packed, "packed")
+    if packed.numel() < n:
+        raise ValueError(f"packed needs {n} bytes")
+    _check(library().lse_pack(out.data_ptr(), *out.stride()[:3], smax.data_ptr(), *smax.stride(),
+                              ssum.data_ptr(), *ssum.stride(), P, T, H, Dv, scatter_dim, _dt(out),
+                              packed.data_ptr(), _stream(out)))
+    return packed
+
+
+def lse_combine_packed(packed: torch.Tensor, P: int, T: int, H: int, Dv: int, scatter_dim: int,
+                       dtype=torch.bfloat16, out: torch.Tensor | None = None,
+                       lse_out: torch.Tensor | None | bool = True):
+    """Combine, for every destination rank r, the chunks (p, r) of all sources
+    (the exchange is a strided view of the packed buffer).  Returns
+    (out [P*rows][Dv], lse_out [P*rows] or None)."""
+    _contig(packed, "packed")
+    rows = T * (H // P) if scatter_dim == 1 else (T // P) * H
+    if out is None:
+        out = torch.empty((P * rows, Dv), dtype=dtype, device=packed.device)
+    _contig(out, "out")
+    if lse_out is True:
+        lse_out = torch.empty(P * rows, dtype=torch.float32, device=packed.device)
+    elif lse_out is False:
+        lse_out = None
+    if lse_out is not None:
+        _contig(lse_out, "lse_out")
+    code = CAM_BF16 if dtype == torch.bfloat16 else CAM_FP16
+    _check(library().lse_combine_packed(packed.data_ptr(), P, T, H, Dv, scatter_dim, code, out.data_ptr(),
+                                        _ptr(lse_out), _stream(packed)))
+    return out, lse_out
+
+
+def _combine_common(part_out, part_lse, out, lse_out):
+    _dev(part_out, "part_out")
+    _dev(part_lse, "part_lse")
+    if part_out.dim() != 4 or part_out.stride(3) != 1:
+        raise ValueError("part_out must be [P][T][H][D] with D contiguous")
+    if part_lse.dtype != torch.float32:
+        raise TypeError("part_lse must be float32")
+    P, T, H, D = part_out.shape
+    if tuple(part_lse.shape) != (P, T, H):
+        raise ValueError("part_lse must be [P][T][H]")
+    if out is None:
+        out = torch.empty((T, H, D), dtype=part_out.dtype, device=part_out.device)
+    _dev(out, "out")
+    if out.dim() != 3 or out.stride(2) != 1:
+        raise ValueError("out must be [T][H][D] with D contiguous")
+    if lse_out is True:
+        lse_out = torch.empty((T, H), dtype=torch.float32, device=part_out.device)
+    elif lse_out is False:
+        lse_out = None
+    if lse_out is not None:
+        _dev(lse_out, "lse_out")
+    lo = lse_out.stride() if lse_out is not None else (0, 0)
+    return P, T, H, D, out, lse_out, lo
+
+
+def lse_combine(part_out: torch.Tensor, part_lse: torch.Tensor, out: torch.Tensor | None = None,
+                lse_out: torch.Tensor | None | bool = True):
+    """Stable combine of P partials: part_out [P][T][H][D], part_lse [P][T][H]
+    (any strides, D contiguous) -> (out [T][H][D], lse_out [T][H] or None)."""
+    P, T, H, D, out, lse_out, lo = _combine_common(part_out, part_lse, out, lse_out)
+    _check(library().lse_combine(part_out.data_ptr(), *part_out.stride()[:3], part_lse.data_ptr(),
+                                 *part_lse.stride(), P, T, H, D, _dt(part_out), out.data_ptr(),
+                                 *out.stride()[:2], _ptr(lse_out), *lo, _stream(part_out)))
+    return out, lse_out
+
+
+def lse_combine_varlen(part_out: torch.Tensor, part_lse: torch.Tensor, cu_seqlens: torch.Tensor,
+                       out: torch.Tensor | None = None, lse_out: torch.Tensor | None | bool = True):
+    """lse_combine for a packed THD batch whose P partials are the causal
+    attention over the P KV pieces of each token's own sequence; cu_seqlens is
+    a device int32 tensor [nseq+1]."""
+    P, T, H, D, out, lse_out, lo = _combine_common(part_out, part_lse, out, lse_out)
+    _contig(cu_seqlens, "cu_seqlens")
+    if cu_seqlens.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    _check(library().lse_combine_varlen(part_out.data_ptr(), *part_out.stride()[:3], part_lse.data_ptr(),
+                                        *part_lse.stride(), P, T, H, D, _dt(part_out), out.data_ptr(),
+                                        *out.stride()[:2], _ptr(lse_out), *lo, cu_seqlens.data_ptr(),
+                                        cu_seqlens.numel() - 1, _stream(part_out)))
+    return out, lse_out
+
+
+def copy(src: torch.Tensor, dst: torch.Tensor) -> torch.Tensor:
+    """Plain 16-byte-vector device copy (the copy ceiling of the relayouts)."""
+    _contig(src, "src")
+    _contig(dst, "dst")
+    n = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != n:
+        raise ValueError("src and dst sizes differ")
+    _check(library().cam_copy(src.data_ptr(), dst.data_ptr(), n, _stream(src)))
+    return dst

@@ -1,0 +1,639 @@
+// cam_api.cpp -- the extern "C" entry points declared in include/cam.h.
+//
+// Host-only: every argument is checked here before anything reaches the GPU
+// (this file makes no HIP call), then a launch record is built and handed to
+// one kernel launcher.  A rejected call launches nothing and writes nothing:
+// the "decline rather than half-run" rule of FastVideo's fused all-to-all
+// helper (commit message of "[perf] Probe H3 chunked all-to-all with direct
+// output slices"), applied per call.
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <initializer_list>
+
+#include "cam_internal.h"
+
+namespace cam {
+
+static thread_local char g_err[512];
+
+cam_status set_error(cam_status s, const char* fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+void clear_error() { g_err[0] = '\0'; }
+
+namespace {
+
+constexpr int64_t kI64Max = INT64_MAX;
+
+bool mul_ok(int64_t a, int64_t b, int64_t* out)
+{
+    if (a < 0 || b < 0)
+        return false;
+    if (a != 0 && b > kI64Max / a)
+        return false;
+    *out = a * b;
+    return true;
+}
+
+bool prod_ok(std::initializer_list<int64_t> xs, int64_t* out)
+{
+    int64_t acc = 1;
+    for (int64_t x : xs)
+        if (!mul_ok(acc, x, &acc))
+            return false;
+    *out = acc;
+    return true;
+}
+
+int elem_size(cam_dtype dt)
+{
+    switch (dt) {
+    case CAM_BF16:
+    case CAM_FP16:
+        return 2;
+    case CAM_FP32:
+        return 4;
+    }
+    return 0;
+}
+
+const char* dt_name(cam_dtype dt)
+{
+    switch (dt) {
+    case CAM_BF16: return "bf16";
+    case CAM_FP16: return "fp16";
+    case CAM_FP32: return "fp32";
+    }
+    return "unknown";
+}
+
+bool aligned(const void* p, int64_t n) { return (reinterpret_cast<uintptr_t>(p) % uint64_t(n)) == 0; }
+
+// Widest access (16, 8, 4 or 2 bytes) that divides every byte quantity given.
+int pick_width(std::initializer_list<uint64_t> quantities)
+{
+    for (int w : {16, 8, 4, 2}) {
+        bool ok = true;
+        for (uint64_t q : quantities)
+            ok = ok && (q % uint64_t(w) == 0);
+        if (ok)
+            return w;
+    }
+    return 0;
+}
+
+bool overlaps(const void* a, int64_t an, const void* b, int64_t bn)
+{
+    if (an <= 0 || bn <= 0)
+        return false;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+    return a0 < b0 + uint64_t(bn) && b0 < a0 + uint64_t(an);
+}
+
+// Byte extent of a strided tensor (non-negative element strides, esize bytes).
+bool extent(std::initializer_list<int64_t> dims, std::initializer_list<int64_t> strides,
+            int64_t esize, int64_t* out)
+{
+    int64_t last = 0;
+    auto s = strides.begin();
+    for (int64_t n : dims) {
+        if (n == 0) {
+            *out = 0;
+            return true;
+        }
+        int64_t term;
+        if (!mul_ok(n - 1, *s, &term) || last > kI64Max - term)
+            return false;
+        last += term;
+        ++s;
+    }
+    return mul_ok(last + 1, esize, out);
+}
+
+uint32_t pow2ceil(uint32_t x)
+{
+    uint32_t p = 1;
+    while (p < x)
+        p <<= 1;
+    return p;
+}
+
+uint32_t log2u(uint32_t x)
+{
+    uint32_t l = 0;
+    while ((1u << l) < x)
+        ++l;
+    return l;
+}
+
+constexpr uint64_t kU32Limit = (uint64_t(1) << 31);  // vector-index headroom inside one slab
+
+uint32_t tiles(uint64_t vecs, uint64_t per_tile) { return uint32_t((vecs + per_tile - 1) / per_tile); }
+
+// ---------------------------------------------------------------- relayouts
+
+cam_status dense_relayout(const void* in, void* out, int64_t P, int64_t B, int64_t S, int64_t H,
+                          int64_t D, cam_dtype dt, void* stream, bool seq_to_head)
+{
+    const char* op = seq_to_head ? "ulysses_seq_to_head" : "ulysses_head_to_seq";
+    clear_error();
+    if (P < 1 || B < 0 || S < 0 || H < 0 || D < 0)
+        return set_error(CAM_ERR_SHAPE, "%s: need P >= 1 and B, S, H, D >= 0 (P=%lld B=%lld S=%lld H=%lld D=%lld)",
+                         op, (long long)P, (long long)B, (long long)S, (long long)H, (long long)D);
+    const int es = elem_size(dt);
+    if (!es)
+        return set_error(CAM_ERR_UNSUPPORTED, "%s: unknown dtype code %d", op, int(dt));
+    if (S % P || H % P)
+        return set_error(CAM_ERR_DIVISIBILITY, "%s: S (%lld) and H (%lld) must be multiples of P (%lld)",
+                         op, (long long)S, (long long)H, (long long)P);
+    int64_t bytes;
+    if (!prod_ok({B, S, H, D, es}, &bytes))
+        return set_error(CAM_ERR_SHAPE, "%s: B*S*H*D*esize overflows", op);
+    if (bytes == 0)
+        return CAM_OK;
+    if (!in || !out)
+        return set_error(CAM_ERR_NULL, "%s: in and out must be non-null", op);
+    if (!aligned(in, es) || !aligned(out, es))
+        return set_error(CAM_ERR_ALIGNMENT, "%s: pointers must be aligned to the %s element size", op, dt_name(dt));
+    if (overlaps(in, bytes, out, bytes))
+        return set_error(CAM_ERR_OVERLAP, "%s: in and out overlap", op);
+    if (P > UINT32_MAX || B > UINT32_MAX)
+        return set_error(CAM_ERR_UNSUPPORTED, "%s: P and B must fit 32 bits", op);
+
+    const uint64_t run = uint64_t(H / P) * uint64_t(D) * es;
+    DenseRelayout a{};
+    a.width = pick_width({run, reinterpret_cast<uintptr_t>(in), reinterpret_cast<uintptr_t>(out)});
+    a.src = in;
+    a.dst = out;
+    a.P = uint32_t(P);
+    a.B = uint32_t(B);
+    a.div_P = make_fastdiv(a.P);
+    a.div_B = make_fastdiv(a.B);
+    a.c = uint32_t(run / a.width);
+    a.div_c = make_fastdiv(a.c);
+    a.Pc = uint64_t(P) * a.c;
+    a.Sp = uint64_t(S / P);
+    const uint64_t slab_vecs = a.Sp * a.c;
+    if (slab_vecs >= kU32Limit)
+        return set_error(CAM_ERR_UNSUPPORTED, "%s: one (rank, plane, rank) slab exceeds 2^31 vectors", op);
+    a.slab_vecs = uint32_t(slab_vecs);
+    a.tiles_per_slab = tiles(slab_vecs, kTileVecs);
+    a.div_tps = make_fastdiv(a.tiles_per_slab);
+    const uint64_t n_tiles = uint64_t(P) * uint64_t(B) * uint64_t(P) * a.tiles_per_slab;
+    if (n_tiles > UINT32_MAX)
+        return set_error(CAM_ERR_UNSUPPORTED, "%s: more than 2^32 tiles", op);
+    a.n_tiles = uint32_t(n_tiles);
+    a.seq_to_head = seq_to_head;
+    return launch_dense_relayout(a, stream);
+}
+
+cam_status varlen_relayout(const void* in, void* out, const int32_t* cu, const int32_t* rank_cu,
+                           const int64_t* rank_off, int64_t nseq, int64_t T, int64_t P, int64_t B,
+                           int64_t H, int64_t D, cam_dtype dt, void* stream, bool seq_to_head)
+{
+    const char* op = seq_to_head ? "ulysses_seq_to_head_varlen" : "ulysses_head_to_seq_varlen";
+    clear_error();
+    if (P < 1 || B < 0 || T < 0 || H < 0 || D < 0 || nseq < 0)
+        return set_error(CAM_ERR_SHAPE, "%s: need P >= 1 and nseq, total_tokens, B, H, D >= 0", op);
+    const int es = elem_size(dt);
+    if (!es)
+        return set_error(CAM_ERR_UNSUPPORTED, "%s: unknown dtype code %d", op, int(dt));
+    if (H % P)
+        return set_error(CAM_ERR_DIVISIBILITY, "%s: H (%lld) must be a multiple of P (%lld)", op,
+                         (long long)H, (long long)P);
+    if (T > INT32_MAX || nseq >= INT32_MAX)
+        return set_error(CAM_ERR_SHAPE, "%s: total_tokens and nseq must fit int32 (cu_seqlens is int32)", op);
+    if (T > 0 && nseq < 1)
+        return set_error(CAM_ERR_SHAPE, "%s: total_tokens > 0 needs nseq >= 1", op);
+    int64_t bytes;
+    if (!prod_ok({B, T, H, D, es}, &bytes))
+        return set_error(CAM_ERR_SHAPE, "%s: B*T*H*D*esize overflows", op);
+    if (bytes == 0)
+        return CAM_OK;
+    if (!in || !out || !cu || !rank_cu || !rank_off)
+        return set_error(CAM_ERR_NULL, "%s: in, out, cu_seqlens, rank_cu and rank_off must be non-null", op);
+    if (!aligned(in, es) || !aligned(out, es) || !aligned(cu, 4) || !aligned(rank_cu, 4) || !aligned(rank_off, 8))
+        return set_error(CAM_ERR_ALIGNMENT, "%s: misaligned pointer", op);
+    if (overlaps(in, bytes, out, bytes))
+        return set_error(CAM_ERR_OVERLAP, "%s: in and out overlap", op);
+    if (overlaps(out, bytes, cu, 4 * (nseq + 1)) || overlaps(out, bytes, rank_cu, 4 * P * (nseq + 1)) ||
+        overlaps(out, bytes, rank_off, 8 * (P + 1)))
+        return set_error(CAM_ERR_OVERLAP, "%s: out overlaps the plan arrays", op);
+    if (P > UINT32_MAX || B > UINT32_MAX)
+        return set_error(CAM_ERR_UNSUPPORTED, "%s: P and B must fit 32 bits", op);
+
+    const uint64_t run = uint64_t(H / P) * uint64_t(D) * es;
+    VarlenRelayout a{};
+    a.width = pick_width({run, reinterpret_cast<uintptr_t>(in), reinterpret_cast<uintptr_t>(out)});
+    a.src = in;
+    a.dst = out;
+    a.cu = cu;
+    a.rank_cu = rank_cu;
+    a.rank_off = rank_off;
+    a.nseq = int32_t(nseq);
+    a.P = uint32_t(P);
+    a.B = uint32_t(B);
+    a.div_B = make_fastdiv(a.B);
+    a.T = uint64_t(T);
+    a.c = uint32_t(run / a.width);
+    a.div_c = make_fastdiv(a.c);
+    a.Pc = uint64_t(P) * a.c;
+    a.plane_vecs = uint64_t(T) * a.c;
+    if (a.plane_vecs >= kU32Limit)
+        return set_error(CAM_ERR_UNSUPPORTED, "%s: one (rank, plane) exceeds 2^31 vectors", op);
+    a.tiles_per_plane = tiles(a.plane_vecs, kTileVecs);
+    a.div_tpp = make_fastdiv(a.tiles_per_plane);
+    const uint64_t n_tiles = uint64_t(P) * uint64_t(B) * a.tiles_per_plane;
+    if (n_tiles > UINT32_MAX)
+        return set_error(CAM_ERR_UNSUPPORTED, "%s: more than 2^32 tiles", op);
+    a.n_tiles = uint32_t(n_tiles);
+    a.seq_to_head = seq_to_head;
+    return launch_varlen_relayout(a, stream);
+}
+
+// --------------------------------------------------------------------- pack
+
+struct PackGeom {
+    int64_t rows, o_region, chunk, total;
+};
+
+cam_status pack_geometry(const char* op, int64_t P, int64_t T, int64_t H, int64_t Dv, int scatter_dim,
+                         cam_dtype dt, PackGeom* g)
+{
+    if (P < 1 || T < 0 || H < 0 || Dv < 0)
+        return set_error(CAM_ERR_SHAPE, "%s: need P >= 1 and T, H, Dv >= 0", op);
+    if (dt != CAM_BF16 && dt != CAM_FP16)
+        return set_error(CAM_ERR_UNSUPPORTED, "%s: payload dtype must be bf16 or fp16", op);
+    if (scatter_dim != 0 && scatter_dim != 1)
+        return set_error(CAM_ERR_UNSUPPORTED, "%s: scatter_dim must be 0 (tokens) or 1 (heads)", op);
+    if (scatter_dim == 1 && H % P)
+        return set_error(CAM_ERR_DIVISIBILITY, "%s: scatter_dim 1 needs H %% P == 0 (H=%lld P=%lld)", op,
+                         (long long)H, (long long)P);
+    if (scatter_dim == 0 && T % P)
+        return set_error(CAM_ERR_DIVISIBILITY, "%s: scatter_dim 0 needs T %% P == 0 (T=%lld P=%lld)", op,
+                         (long long)T, (long long)P);
+    int64_t rows, obytes, chunk, total;
+    if (!prod_ok({scatter_dim == 1 ? T : T / P, scatter_dim == 1 ? H / P : H}, &rows) ||
+        !prod_ok({rows, Dv, 2}, &obytes) || obytes > kI64Max / 2)
+        return set_error(CAM_ERR_SHAPE, "%s: sizes overflow", op);
+    obytes = (obytes + 15) / 16 * 16;
+    chunk = obytes + (rows * 4 + 15) / 16 * 16;
+    if (!prod_ok({P, P, chunk}, &total))
+        return set_error(CAM_ERR_SHAPE, "%s: packed size overflows", op);
+    g->rows = rows;
+    g->o_region = obytes;
+    g->chunk = chunk;
+    g->total = total;
+    return CAM_OK;
+}
+
+struct CombineIn {
+    const void* po;
+    int64_t po_sp, po_st, po_sh;  // elements
+    const float* pl;
+    int64_t pl_sp, pl_st, pl_sh;  // elements
+    int64_t P, T, H, D;
+    cam_dtype dt;
+    void* out;
+    int64_t o_st, o_sh;           // elements
+    float* lse_out;
+    int64_t lo_st, lo_sh;
+    const int32_t* cu;
+    int64_t nseq;
+};
+
+cam_status combine(const char* op, const CombineIn& c, void* stream)
+{
+    if (c.P < 1 || c.T < 0 || c.H < 0 || c.D < 0)
+        return set_error(CAM_ERR_SHAPE, "%s: need P >= 1 and T, H, D >= 0", op);
+    if (c.P > 64)
+        return set_error(CAM_ERR_UNSUPPORTED, "%s: at most 64 partials per row (P=%lld)", op, (long long)c.P);
+    if (c.dt != CAM_BF16 && c.dt != CAM_FP16)
+        return set_error(CAM_ERR_UNSUPPORTED, "%s: payload dtype must be bf16 or fp16", op);
+    for (int64_t s : {c.po_sp, c.po_st, c.po_sh, c.pl_sp, c.pl_st, c.pl_sh, c.o_st, c.o_sh, c.lo_st, c.lo_sh})
+        if (s < 0)
+            return set_error(CAM_ERR_UNSUPPORTED, "%s: strides must be non-negative", op);
+    int64_t n_rows;
+    if (!prod_ok({c.T, c.H}, &n_rows))
+        return set_error(CAM_ERR_SHAPE, "%s: T*H overflows", op);
+    if (n_rows == 0)
+        return CAM_OK;
+    if (n_rows > INT32_MAX)
+        return set_error(CAM_ERR_UNSUPPORTED, "%s: T*H must be below 2^31 rows", op);
+    if (c.cu && c.nseq < 1)
+        return set_error(CAM_ERR_SHAPE, "%s: nseq must be >= 1", op);
+    if (c.cu && c.T > INT32_MAX)
+        return set_error(CAM_ERR_SHAPE, "%s: total_tokens must fit int32", op);
+    if (!c.po || !c.pl || !c.out)
+        return set_error(CAM_ERR_NULL, "%s: partial outputs, partial LSEs and out must be non-null", op);
+    if (!aligned(c.po, 2) || !aligned(c.pl, 4) || !aligned(c.out, 2) || (c.lse_out && !aligned(c.lse_out, 4)) ||
+        (c.cu && !aligned(c.cu, 4)))
+        return set_error(CAM_ERR_ALIGNMENT, "%s: misaligned pointer", op);
+    int64_t ext_po, ext_pl, ext_o, ext_lo = 0;
+    if (!extent({c.P, c.T, c.H, c.D}, {c.po_sp, c.po_st, c.po_sh, 1}, 2, &ext_po) ||
+        !extent({c.P, c.T, c.H}, {c.pl_sp, c.pl_st, c.pl_sh}, 4, &ext_pl) ||
+        !extent({c.T, c.H, c.D}, {c.o_st, c.o_sh, 1}, 2, &ext_o) ||
+        (c.lse_out && !extent({c.T, c.H}, {c.lo_st, c.lo_sh}, 4, &ext_lo)))
+        return set_error(CAM_ERR_SHAPE, "%s: tensor extent overflows", op);
+    if (overlaps(c.out, ext_o, c.po, ext_po) || overlaps(c.out, ext_o, c.pl, ext_pl) ||
+        overlaps(c.lse_out, ext_lo, c.po, ext_po) || overlaps(c.lse_out, ext_lo, c.pl, ext_pl) ||
+        overlaps(c.out, ext_o, c.lse_out, ext_lo))
+        return set_error(CAM_ERR_OVERLAP, "%s: an output overlaps an input or the other output", op);
+    if (c.cu && (overlaps(c.out, ext_o, c.cu, 4 * (c.nseq + 1)) || overlaps(c.lse_out, ext_lo, c.cu, 4 * (c.nseq + 1))))
+        return set_error(CAM_ERR_OVERLAP, "%s: an output overlaps cu_seqlens", op);
+
+    Combine a{};
+    const uint64_t row_b = uint64_t(c.D) * 2;
+    a.width = pick_width({row_b == 0 ? 16 : row_b, reinterpret_cast<uintptr_t>(c.po), reinterpret_cast<uintptr_t>(c.out),
+                          uint64_t(c.po_sp) * 2, uint64_t(c.po_st) * 2, uint64_t(c.po_sh) * 2,
+                          uint64_t(c.o_st) * 2, uint64_t(c.o_sh) * 2});
+    a.po = c.po;
+    a.po_sp_b = c.po_sp * 2;
+    a.po_st_b = c.po_st * 2;
+    a.po_sh_b = c.po_sh * 2;
+    a.pl = c.pl;
+    a.pl_sp = c.pl_sp;
+    a.pl_st = c.pl_st;
+    a.pl_sh = c.pl_sh;
+    a.out = c.out;
+    a.o_st_b = c.o_st * 2;
+    a.o_sh_b = c.o_sh * 2;
+    a.lse_out = c.lse_out;
+    a.lo_st = c.lo_st;
+    a.lo_sh = c.lo_sh;
+    a.P = uint32_t(c.P);
+    a.H = uint32_t(c.H);
+    a.div_H = make_fastdiv(a.H);
+    a.n_rows = uint64_t(n_rows);
+    a.cv = uint32_t(row_b / a.width);
+    const uint32_t g = pow2ceil(a.cv < 64 ? (a.cv ? a.cv : 1) : 64);
+    const uint32_t gp = pow2ceil(a.P);
+    a.g_log2 = log2u(g > gp ? g : gp);
+    a.cu = c.cu;
+    a.nseq = int32_t(c.nseq);
+    a.fp16 = c.dt == CAM_FP16;
+    return launch_combine(a, stream);
+}
+
+}  // namespace
+}  // namespace cam
+
+using namespace cam;
+
+extern "C" {
+
+const char* cam_status_string(cam_status s)
+{
+    switch (s) {
+    case CAM_OK: return "CAM_OK";
+    case CAM_ERR_NULL: return "CAM_ERR_NULL";
+    case CAM_ERR_SHAPE: return "CAM_ERR_SHAPE";
+    case CAM_ERR_DIVISIBILITY: return "CAM_ERR_DIVISIBILITY";
+    case CAM_ERR_ALIGNMENT: return "CAM_ERR_ALIGNMENT";
+    case CAM_ERR_OVERLAP: return "CAM_ERR_OVERLAP";
+    case CAM_ERR_UNSUPPORTED: return "CAM_ERR_UNSUPPORTED";
+    case CAM_ERR_HIP: return "CAM_ERR_HIP";
+    }
+    return "CAM_ERR_UNKNOWN";
+}
+
+const char* cam_last_error(void) { return g_err; }
+
+int cam_abi_version(void) { return CAM_ABI_VERSION; }
+
+cam_status ulysses_seq_to_head(const void* in, void* out, int64_t P, int64_t B, int64_t S, int64_t H,
+                               int64_t D, cam_dtype dt, void* stream)
+{
+    return dense_relayout(in, out, P, B, S, H, D, dt, stream, true);
+}
+
+cam_status ulysses_head_to_seq(const void* in, void* out, int64_t P, int64_t B, int64_t S, int64_t H,
+                               int64_t D, cam_dtype dt, void* stream)
+{
+    return dense_relayout(in, out, P, B, S, H, D, dt, stream, false);
+}
+
+cam_status ulysses_varlen_plan(const int32_t* cu, int64_t nseq, int64_t P, int32_t* rank_cu,
+                               int64_t* rank_off)
+{
+    clear_error();
+    if (P < 1 || nseq < 0)
+        return set_error(CAM_ERR_SHAPE, "ulysses_varlen_plan: need P >= 1 and nseq >= 0");
+    if (!cu || !rank_cu || !rank_off)
+        return set_error(CAM_ERR_NULL, "ulysses_varlen_plan: cu_seqlens, rank_cu and rank_off must be non-null");
+    if (cu[0] != 0)
+        return set_error(CAM_ERR_SHAPE, "ulysses_varlen_plan: cu_seqlens[0] must be 0 (got %d)", cu[0]);
+    for (int64_t i = 0; i < nseq; ++i)
+        if (cu[i + 1] < cu[i])
+            return set_error(CAM_ERR_SHAPE, "ulysses_varlen_plan: cu_seqlens decreases at %lld", (long long)i);
+    // Sizes of the pieces of sequence i on rank p: floor((p+1)L/P) - floor(pL/P).
+    int64_t off = 0;
+    for (int64_t p = 0; p < P; ++p) {
+        rank_off[p] = off;
+        int64_t run = 0;
+        for (int64_t i = 0; i < nseq; ++i) {
+            rank_cu[p * (nseq + 1) + i] = int32_t(run);
+            const int64_t L = int64_t(cu[i + 1]) - cu[i];
+            run += (p + 1) * L / P - p * L / P;
+        }
+        rank_cu[p * (nseq + 1) + nseq] = int32_t(run);
+        off += run;
+    }
+    rank_off[P] = off;
+    return CAM_OK;
+}
+
+cam_status ulysses_seq_to_head_varlen(const void* in, void* out, const int32_t* cu, const int32_t* rank_cu,
+                                      const int64_t* rank_off, int64_t nseq, int64_t total_tokens, int64_t P,
+                                      int64_t B, int64_t H, int64_t D, cam_dtype dt, void* stream)
+{
+    return varlen_relayout(in, out, cu, rank_cu, rank_off, nseq, total_tokens, P, B, H, D, dt, stream, true);
+}
+
+cam_status ulysses_head_to_seq_varlen(const void* in, void* out, const int32_t* cu, const int32_t* rank_cu,
+                                      const int64_t* rank_off, int64_t nseq, int64_t total_tokens, int64_t P,
+                                      int64_t B, int64_t H, int64_t D, cam_dtype dt, void* stream)
+{
+    return varlen_relayout(in, out, cu, rank_cu, rank_off, nseq, total_tokens, P, B, H, D, dt, stream, false);
+}
+
+int64_t lse_pack_bytes(int64_t P, int64_t T, int64_t H, int64_t Dv, int scatter_dim, cam_dtype dt)
+{
+    clear_error();
+    PackGeom g;
+    if (pack_geometry("lse_pack_bytes", P, T, H, Dv, scatter_dim, dt, &g) != CAM_OK)
+        return -1;
+    return g.total;
+}
+
+cam_status lse_pack(const void* out, int64_t o_sp, int64_t o_st, int64_t o_sh, const float* smax, int64_t m_sp,
+                    int64_t m_st, int64_t m_sh, const float* ssum, int64_t s_sp, int64_t s_st, int64_t s_sh,
+                    int64_t P, int64_t T, int64_t H, int64_t Dv, int scatter_dim, cam_dtype dt, void* packed,
+                    void* stream)
+{
+    const char* op = "lse_pack";
+    clear_error();
+    PackGeom g;
+    cam_status st = pack_geometry(op, P, T, H, Dv, scatter_dim, dt, &g);
+    if (st != CAM_OK)
+        return st;
+    for (int64_t s : {o_sp, o_st, o_sh, m_sp, m_st, m_sh, s_sp, s_st, s_sh})
+        if (s < 0)
+            return set_error(CAM_ERR_UNSUPPORTED, "%s: strides must be non-negative", op);
+    if (g.total == 0 || g.rows == 0)
+        return CAM_OK;
+    if (!out || !smax || !ssum || !packed)
+        return set_error(CAM_ERR_NULL, "%s: out, softmax_max, softmax_sum and packed must be non-null", op);
+    if (!aligned(out, 2) || !aligned(smax, 4) || !aligned(ssum, 4))
+        return set_error(CAM_ERR_ALIGNMENT, "%s: out must be 2-byte and the statistics 4-byte aligned", op);
+    if (!aligned(packed, 16))
+        return set_error(CAM_ERR_ALIGNMENT, "%s: packed must be 16-byte aligned", op);
+    int64_t e_o, e_m, e_s;
+    if (!extent({P, T, H, Dv}, {o_sp, o_st, o_sh, 1}, 2, &e_o) || !extent({P, T, H}, {m_sp, m_st, m_sh}, 4, &e_m) ||
+        !extent({P, T, H}, {s_sp, s_st, s_sh}, 4, &e_s))
+        return set_error(CAM_ERR_SHAPE, "%s: tensor extent overflows", op);
+    if (overlaps(packed, g.total, out, e_o) || overlaps(packed, g.total, smax, e_m) ||
+        overlaps(packed, g.total, ssum, e_s))
+        return set_error(CAM_ERR_OVERLAP, "%s: packed overlaps an input", op);
+    if (P > 65535)
+        return set_error(CAM_ERR_UNSUPPORTED, "%s: P must be below 65536", op);
+
+    Pack a{};
+    const uint64_t row_b = uint64_t(Dv) * 2;
+    a.width = pick_width({row_b == 0 ? 16 : row_b, reinterpret_cast<uintptr_t>(out), uint64_t(o_sp) * 2,
+                          uint64_t(o_st) * 2, uint64_t(o_sh) * 2});
+    a.out = out;
+    a.o_sp_b = o_sp * 2;
+    a.o_st_b = o_st * 2;
+    a.o_sh_b = o_sh * 2;
+    a.smax = smax;
+    a.m_sp = m_sp;
+    a.m_st = m_st;
+    a.m_sh = m_sh;
+    a.ssum = ssum;
+    a.s_sp = s_sp;
+    a.s_st = s_st;
+    a.s_sh = s_sh;
+    a.packed = packed;
+    a.P = uint32_t(P);
+    a.div_P = make_fastdiv(a.P);
+    a.scatter_heads = scatter_dim == 1;
+    a.inner = uint32_t(scatter_dim == 1 ? H / P : H);
+    if (g.rows > INT32_MAX || a.inner == 0)
+        return set_error(CAM_ERR_UNSUPPORTED, "%s: rows per chunk must be below 2^31", op);
+    a.div_inner = make_fastdiv(a.inner);
+    a.Tp = uint64_t(T / P);
+    a.Hp = uint32_t(H / P);
+    a.rows = uint32_t(g.rows);
+    a.cv = uint32_t(row_b / a.width);
+    a.div_cv = make_fastdiv(a.cv ? a.cv : 1);
+    a.chunk_b = uint64_t(g.chunk);
+    a.o_region_b = uint64_t(g.o_region);
+    const uint64_t o_vecs = uint64_t(g.rows) * a.cv;
+    if (o_vecs >= kU32Limit)
+        return set_error(CAM_ERR_UNSUPPORTED, "%s: one chunk exceeds 2^31 vectors", op);
+    a.o_vecs = uint32_t(o_vecs);
+    a.o_tiles_per_chunk = tiles(o_vecs, kTileVecs);
+    a.div_otpc = make_fastdiv(a.o_tiles_per_chunk ? a.o_tiles_per_chunk : 1);
+    a.l_tiles_per_chunk = tiles(uint64_t(g.rows), kThreads);
+    a.div_ltpc = make_fastdiv(a.l_tiles_per_chunk);
+    const uint64_t n_o = uint64_t(P) * uint64_t(P) * a.o_tiles_per_chunk;
+    const uint64_t n_l = uint64_t(P) * uint64_t(P) * a.l_tiles_per_chunk;
+    if (n_o + n_l > UINT32_MAX)
+        return set_error(CAM_ERR_UNSUPPORTED, "%s: more than 2^32 tiles", op);
+    a.n_o_tiles = uint32_t(n_o);
+    a.n_l_tiles = uint32_t(n_l);
+    return launch_pack(a, stream);
+}
+
+cam_status lse_combine_packed(const void* packed, int64_t P, int64_t T, int64_t H, int64_t Dv, int scatter_dim,
+                              cam_dtype dt, void* out, float* lse_out, void* stream)
+{
+    const char* op = "lse_combine_packed";
+    clear_error();
+    PackGeom g;
+    cam_status st = pack_geometry(op, P, T, H, Dv, scatter_dim, dt, &g);
+    if (st != CAM_OK)
+        return st;
+    if (g.total == 0 || g.rows == 0)
+        return CAM_OK;
+    if (!packed || !out)
+        return set_error(CAM_ERR_NULL, "%s: packed and out must be non-null", op);
+    if (!aligned(packed, 16))
+        return set_error(CAM_ERR_ALIGNMENT, "%s: packed must be 16-byte aligned", op);
+    // Destination rank r reads chunk (p, r) of every source p: as a strided
+    // [P_src][P_dst][rows][Dv] view, p strides P chunks, r one chunk.
+    CombineIn c{};
+    c.po = packed;
+    c.po_sp = P * g.chunk / 2;
+    c.po_st = g.chunk / 2;
+    c.po_sh = Dv;
+    c.pl = reinterpret_cast<const float*>(static_cast<const char*>(packed) + g.o_region);
+    c.pl_sp = P * g.chunk / 4;
+    c.pl_st = g.chunk / 4;
+    c.pl_sh = 1;
+    c.P = P;
+    c.T = P;
+    c.H = g.rows;
+    c.D = Dv;
+    c.dt = dt;
+    c.out = out;
+    c.o_st = g.rows * Dv;
+    c.o_sh = Dv;
+    c.lse_out = lse_out;
+    c.lo_st = g.rows;
+    c.lo_sh = 1;
+    return combine(op, c, stream);
+}
+
+cam_status lse_combine(const void* part_out, int64_t po_sp, int64_t po_st, int64_t po_sh, const float* part_lse,
+                       int64_t pl_sp, int64_t pl_st, int64_t pl_sh, int64_t P, int64_t T, int64_t H, int64_t D,
+                       cam_dtype dt, void* out, int64_t o_st, int64_t o_sh, float* lse_out, int64_t lo_st,
+                       int64_t lo_sh, void* stream)
+{
+    clear_error();
+    CombineIn c{part_out, po_sp, po_st, po_sh, part_lse, pl_sp, pl_st, pl_sh, P, T, H, D, dt,
+                out, o_st, o_sh, lse_out, lo_st, lo_sh, nullptr, 0};
+    return combine("lse_combine", c, stream);
+}
+
+cam_status lse_combine_varlen(const void* part_out, int64_t po_sp, int64_t po_st, int64_t po_sh,
+                              const float* part_lse, int64_t pl_sp, int64_t pl_st, int64_t pl_sh, int64_t P,
+                              int64_t T, int64_t H, int64_t D, cam_dtype dt, void* out, int64_t o_st, int64_t o_sh,
+                              float* lse_out, int64_t lo_st, int64_t lo_sh, const int32_t* cu_seqlens,
+                              int64_t nseq, void* stream)
+{
+    clear_error();
+    if (T > 0 && !cu_seqlens)
+        return set_error(CAM_ERR_NULL, "lse_combine_varlen: cu_seqlens must be non-null");
+    CombineIn c{part_out, po_sp, po_st, po_sh, part_lse, pl_sp, pl_st, pl_sh, P, T, H, D, dt,
+                out, o_st, o_sh, lse_out, lo_st, lo_sh, cu_seqlens, nseq};
+    return combine("lse_combine_varlen", c, stream);
+}
+
+cam_status cam_copy(const void* src, void* dst, int64_t bytes, void* stream)
+{
+    clear_error();
+    if (bytes < 0)
+        return set_error(CAM_ERR_SHAPE, "cam_copy: bytes must be >= 0");
+    if (bytes == 0)
+        return CAM_OK;
+    if (!src || !dst)
+        return set_error(CAM_ERR_NULL, "cam_copy: src and dst must be non-null");
+    if (!aligned(src, 16) || !aligned(dst, 16) || bytes % 16)
+        return set_error(CAM_ERR_ALIGNMENT, "cam_copy: 16-byte aligned pointers and size required");
+    if (overlaps(src, bytes, dst, bytes))
+        return set_error(CAM_ERR_OVERLAP, "cam_copy: src and dst overlap");
+    Copy a{src, dst, uint64_t(bytes) / 16};
+    return launch_copy(a, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,84 @@
+// cam_device.h -- device-side helpers for the gfx950 kernels: access-width
+// vector types, run-time invariant division, payload conversions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "cam_internal.h"
+
+namespace cam {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Register type of one W-byte access.
+template <int W> struct VecOf;
+template <> struct VecOf<16> { typedef u32x4 type; };
+template <> struct VecOf<8> { typedef u32x2 type; };
+template <> struct VecOf<4> { typedef uint32_t type; };
+template <> struct VecOf<2> { typedef uint16_t type; };
+
+__device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv& f)
+{
+    return uint32_t((uint64_t(__umulhi(n, f.m)) + n) >> f.l);
+}
+
+template <int W>
+__device__ __forceinline__ typename VecOf<W>::type ld(const void* base, uint64_t vec_index)
+{
+    return reinterpret_cast<const typename VecOf<W>::type*>(base)[vec_index];
+}
+
+template <int W>
+__device__ __forceinline__ void st(void* base, uint64_t vec_index, typename VecOf<W>::type v)
+{
+    reinterpret_cast<typename VecOf<W>::type*>(base)[vec_index] = v;
+}
+
+// bf16 <-> fp32.  bf16 is the upper half of an fp32 word; narrowing rounds to
+// nearest, ties to even, and keeps NaN a (quiet) NaN.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u)
+        return (u >> 16) | 0x40u;
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+__device__ __forceinline__ float fp16_lo(uint32_t w)
+{
+    return float(__builtin_bit_cast(_Float16, uint16_t(w & 0xFFFFu)));
+}
+__device__ __forceinline__ float fp16_hi(uint32_t w)
+{
+    return float(__builtin_bit_cast(_Float16, uint16_t(w >> 16)));
+}
+__device__ __forceinline__ uint32_t f32_to_fp16_bits(float f)
+{
+    return uint32_t(__builtin_bit_cast(uint16_t, _Float16(f)));
+}
+
+// Launch `fn` over min(n_tiles, kMaxGrid) workgroups of kThreads on `stream`;
+// kernels walk their tiles with a grid stride.
+template <typename Args>
+inline cam_status launch(const void* fn, const Args& a, uint64_t n_tiles, void* stream,
+                         const char* what)
+{
+    if (n_tiles == 0)
+        return CAM_OK;
+    const uint32_t grid = uint32_t(n_tiles < kMaxGrid ? n_tiles : kMaxGrid);
+    Args copy = a;
+    void* args[] = {&copy};
+    hipError_t e = hipLaunchKernel(fn, dim3(grid), dim3(kThreads), args, 0,
+                                   reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return set_error(CAM_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));
+    return CAM_OK;
+}
+
+}  // namespace cam

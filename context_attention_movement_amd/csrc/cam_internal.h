@@ -1,0 +1,172 @@
+// cam_internal.h -- shared internals of libcam: the launch records the host
+// layer fills after validation, and division by run-time invariant integers.
+//
+// This header is included by the host-only API layer (cam_api.cpp, compiled
+// without any HIP call) and by the kernel sources (*.hip).
+#pragma once
+
+#include <stdint.h>
+
+#include "../../include/cam.h"
+
+namespace cam {
+
+// Unsigned 32-bit division by a run-time invariant d >= 1 with one high
+// multiply, one add and one shift (Granlund & Montgomery, "Division by
+// invariant integers using multiplication", PLDI 1994, section 4):
+//   l = ceil(log2 d),  m = floor(2^32 (2^l - d) / d) + 1,
+//   n / d = (umulhi(n, m) + n) >> l   for every 0 <= n < 2^32,
+// the add taken in 64 bits so that it cannot wrap.
+struct FastDiv {
+    uint32_t d;
+    uint32_t m;
+    uint32_t l;
+};
+
+inline FastDiv make_fastdiv(uint32_t d)
+{
+    FastDiv f;
+    f.d = d;
+    uint32_t l = 0;
+    while (l < 32 && (uint64_t(1) << l) < d)
+        ++l;
+    f.l = l;
+    f.m = uint32_t(((uint64_t(1) << 32) * ((uint64_t(1) << l) - d)) / d + 1);
+    return f;
+}
+
+// ---------------------------------------------------------------------------
+// Launch records: everything a kernel needs, computed and checked on the host.
+// Offsets and strides named *_b are in bytes; vector counts in units of the
+// access width W chosen for the launch.
+// ---------------------------------------------------------------------------
+
+// Dense relayout.  A slab is (r, b, j): the S/P rows moving between rank j's
+// sequence shard and rank r's head shard of plane b.  Slab index
+// ((r*B + b)*P + j) orders the head side exactly as it lies in memory, so the
+// head side of slab k starts at vector k*slab_vecs; its sequence side starts at
+// ((j*B + b)*(S/P)*P + r)*c with consecutive rows P*c vectors apart.
+struct DenseRelayout {
+    const void* src;
+    void* dst;
+    uint32_t P, B;
+    FastDiv div_P, div_B;
+    uint32_t c;            // vectors per row run ((H/P)*D*esize / W)
+    FastDiv div_c;
+    uint64_t Pc;           // sequence-side row stride in vectors (P*c)
+    uint64_t Sp;           // rows per slab (S/P)
+    uint32_t slab_vecs;    // Sp*c
+    uint32_t tiles_per_slab;
+    FastDiv div_tps;
+    uint32_t n_tiles;      // P*B*P*tiles_per_slab
+    int width;             // W in bytes: 16, 8, 4 or 2
+    bool seq_to_head;
+};
+
+// Varlen relayout.  A plane is (r, b); the head side of plane (r, b) is rows
+// t < T of c vectors each, contiguous at vector (r*B + b)*T*c.  Token t's
+// sequence-side row is found per tile from cu_seqlens and the plan.
+struct VarlenRelayout {
+    const void* src;
+    void* dst;
+    const int32_t* cu;
+    const int32_t* rank_cu;
+    const int64_t* rank_off;
+    int32_t nseq;
+    uint32_t P, B;
+    FastDiv div_B;
+    uint64_t T;
+    uint32_t c;
+    FastDiv div_c;
+    uint64_t Pc;
+    uint64_t plane_vecs;    // T*c
+    uint32_t tiles_per_plane;
+    FastDiv div_tpp;
+    uint32_t n_tiles;
+    int width;
+    bool seq_to_head;
+};
+
+// Max/sum-aware LSE pack.
+struct Pack {
+    const void* out;
+    int64_t o_sp_b, o_st_b, o_sh_b;
+    const float* smax;
+    int64_t m_sp, m_st, m_sh;
+    const float* ssum;
+    int64_t s_sp, s_st, s_sh;
+    void* packed;
+    uint32_t P;
+    FastDiv div_P;
+    uint32_t scatter_heads; // 1: scatter_dim 1 (heads), 0: scatter_dim 0 (tokens)
+    uint32_t inner;         // H/P (heads) or H (tokens): row q = outer*inner + inner_idx
+    FastDiv div_inner;
+    uint64_t Tp;            // T/P (tokens) -- token offset of destination r is r*Tp
+    uint32_t Hp;            // H/P (heads)
+    uint32_t rows;          // rows per chunk
+    uint32_t cv;            // vectors per row (Dv*esize / W)
+    FastDiv div_cv;
+    uint64_t chunk_b, o_region_b;
+    uint32_t o_vecs;        // rows*cv per chunk
+    uint32_t o_tiles_per_chunk;
+    FastDiv div_otpc;
+    uint32_t n_o_tiles;     // P*P*o_tiles_per_chunk
+    uint32_t l_tiles_per_chunk;
+    FastDiv div_ltpc;
+    uint32_t n_l_tiles;     // P*P*l_tiles_per_chunk
+    int width;
+};
+
+// Stable LSE combine over rows (t, h).
+struct Combine {
+    const void* po;
+    int64_t po_sp_b, po_st_b, po_sh_b;
+    const float* pl;
+    int64_t pl_sp, pl_st, pl_sh;
+    void* out;
+    int64_t o_st_b, o_sh_b;
+    float* lse_out;
+    int64_t lo_st, lo_sh;
+    uint32_t P;
+    uint32_t H;
+    FastDiv div_H;
+    uint64_t n_rows;        // T*H
+    uint32_t cv;            // vectors per row
+    uint32_t g_log2;        // lanes per row = 1 << g_log2 (>= P, <= 64)
+    const int32_t* cu;      // non-null: causal piece gating (varlen)
+    int32_t nseq;
+    int width;
+    int fp16;               // payload: 0 bf16, 1 fp16
+};
+
+struct Copy {
+    const void* src;
+    void* dst;
+    uint64_t n_vecs;        // 16-byte vectors
+};
+
+// Kernel launchers (defined in the .hip sources).  They only launch; the
+// records have been validated.  Return CAM_OK or CAM_ERR_HIP (message set).
+cam_status launch_dense_relayout(const DenseRelayout& a, void* stream);
+cam_status launch_varlen_relayout(const VarlenRelayout& a, void* stream);
+cam_status launch_pack(const Pack& a, void* stream);
+cam_status launch_combine(const Combine& a, void* stream);
+cam_status launch_copy(const Copy& a, void* stream);
+
+// Error reporting shared by the host layer and the launchers.
+cam_status set_error(cam_status s, const char* fmt, ...);
+void clear_error();
+
+// Launch shape shared by all streaming kernels.
+constexpr int kThreads = 256;
+#ifndef CAM_VECS_PER_THREAD
+#define CAM_VECS_PER_THREAD 4
+#endif
+constexpr int kVecsPerThread = CAM_VECS_PER_THREAD;
+constexpr int kTileVecs = kThreads * kVecsPerThread;
+#ifndef CAM_MAX_GRID
+#define CAM_MAX_GRID (1u << 20)
+#endif
+constexpr uint32_t kMaxGrid = CAM_MAX_GRID;
+
+}  // namespace cam

@@ -1,0 +1,192 @@
+// relayout.hip -- Ulysses all-to-all relayout between sequence-sharded and
+// head-sharded slabs of P logical ranks held in one GPU's HBM (FastVideo
+// "[perf] Probe H3 chunked all-to-all with direct output slices":
+// all_to_all_4D(x, 2, 1) and its inverse (1, 2), the fused kernel writing
+// straight into the output slices), plus the cu_seqlens varlen form (cuLA
+// "packed hybrid runtime and THD planner": packed THD batches).
+//
+// Design for gfx950.  The relayout is a pure permutation of runs of
+// (H/P)*D elements that are contiguous on both sides (>= 512 bytes at the
+// workloads here), so every wavefront access is already a coalesced run of
+// 64 x W bytes; nothing needs an LDS transpose.  Each thread moves
+// kVecsPerThread W-byte vectors: all loads are issued before any store so that
+// several 16-byte requests per lane are in flight, which is what keeps HBM3E
+// busy on a streaming kernel.  Work is cut into tiles of kTileVecs vectors
+// inside a slab (dense) or plane (varlen); one division by the run length per
+// vector (a multiply-high) recovers the row, everything else is per tile.
+#include "cam_device.h"
+
+namespace cam {
+
+template <int W, bool S2H>
+__global__ __launch_bounds__(kThreads) void k_dense_relayout(DenseRelayout a)
+{
+    typedef typename VecOf<W>::type V;
+    for (uint32_t tile = blockIdx.x; tile < a.n_tiles; tile += gridDim.x) {
+        const uint32_t slab = fdiv(tile, a.div_tps);
+        const uint32_t ti = tile - slab * a.tiles_per_slab;
+        const uint32_t rb = fdiv(slab, a.div_P);
+        const uint32_t j = slab - rb * a.P;
+        const uint32_t r = fdiv(rb, a.div_B);
+        const uint32_t b = rb - r * a.B;
+        const uint64_t head_base = uint64_t(slab) * a.slab_vecs;
+        const uint64_t seq_base = (uint64_t(j * a.B + b) * a.Sp * a.P + r) * a.c;
+        const uint32_t v0 = ti * uint32_t(kTileVecs) + threadIdx.x;
+
+        V x[kVecsPerThread];
+        uint64_t dst_off[kVecsPerThread];
+#pragma unroll
+        for (int u = 0; u < kVecsPerThread; ++u) {
+            const uint32_t v = v0 + uint32_t(u * kThreads);
+            if (v < a.slab_vecs) {
+                const uint32_t s = fdiv(v, a.div_c);
+                const uint32_t k = v - s * a.c;
+                const uint64_t so = seq_base + uint64_t(s) * a.Pc + k;
+                const uint64_t ho = head_base + v;
+                x[u] = ld<W>(a.src, S2H ? so : ho);
+                dst_off[u] = S2H ? ho : so;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kVecsPerThread; ++u) {
+            const uint32_t v = v0 + uint32_t(u * kThreads);
+            if (v < a.slab_vecs)
+                st<W>(a.dst, dst_off[u], x[u]);
+        }
+    }
+}
+
+// Sequence-side vector offset of token t's row for destination head block r
+// of plane b, or -1 if the plan does not place t inside the buffer.
+__device__ int64_t varlen_seq_row(const VarlenRelayout& a, uint32_t t, uint32_t r, uint32_t b)
+{
+    int32_t lo = 0, hi = a.nseq;  // largest i < nseq with cu[i] <= t
+    while (hi - lo > 1) {
+        const int32_t mid = (lo + hi) >> 1;
+        if (int64_t(a.cu[mid]) <= int64_t(t))
+            lo = mid;
+        else
+            hi = mid;
+    }
+    const int64_t c0 = a.cu[lo];
+    const int64_t L = int64_t(a.cu[lo + 1]) - c0;
+    const int64_t k = int64_t(t) - c0;
+    if (k < 0 || k >= L)
+        return -1;
+    const int64_t P = a.P;
+    const int64_t p = ((k + 1) * P - 1) / L;  // rank whose piece holds position k
+    const int64_t start = (p * L) / P;
+    const int64_t l = int64_t(a.rank_cu[p * (a.nseq + 1) + lo]) + (k - start);
+    const int64_t R = a.rank_off[p];
+    const int64_t Tp = a.rank_off[p + 1] - R;
+    if (l < 0 || l >= Tp)
+        return -1;
+    const int64_t row = int64_t(a.B) * R + int64_t(b) * Tp + l;
+    if (row < 0 || row >= int64_t(a.B) * int64_t(a.T))
+        return -1;
+    return row * int64_t(a.Pc) + int64_t(r) * a.c;
+}
+
+template <int W, bool S2H>
+__global__ __launch_bounds__(kThreads) void k_varlen_relayout(VarlenRelayout a)
+{
+    typedef typename VecOf<W>::type V;
+    // sequence-side offset of every row the tile touches (a tile spans at most
+    // kTileVecs + 1 rows when rows are one vector long)
+    __shared__ int64_t row_off[kTileVecs + 1];
+    for (uint32_t tile = blockIdx.x; tile < a.n_tiles; tile += gridDim.x) {
+        const uint32_t plane = fdiv(tile, a.div_tpp);
+        const uint32_t ti = tile - plane * a.tiles_per_plane;
+        const uint32_t r = fdiv(plane, a.div_B);
+        const uint32_t b = plane - r * a.B;
+        const uint64_t head_base = uint64_t(plane) * a.plane_vecs;
+        const uint32_t vb = ti * uint32_t(kTileVecs);
+        const uint64_t ve64 = uint64_t(vb) + kTileVecs;
+        const uint32_t ve = uint32_t(ve64 < a.plane_vecs ? ve64 : a.plane_vecs);
+        const uint32_t row0 = fdiv(vb, a.div_c);
+        const uint32_t nrows = fdiv(ve - 1, a.div_c) - row0 + 1;
+        __syncthreads();  // the previous tile's readers are done with row_off
+        for (uint32_t i = threadIdx.x; i < nrows; i += kThreads)
+            row_off[i] = varlen_seq_row(a, row0 + i, r, b);
+        __syncthreads();
+
+        V x[kVecsPerThread];
+        uint64_t dst_off[kVecsPerThread];
+        bool live[kVecsPerThread];
+#pragma unroll
+        for (int u = 0; u < kVecsPerThread; ++u) {
+            const uint32_t v = vb + threadIdx.x + uint32_t(u * kThreads);
+            live[u] = false;
+            if (v < ve) {
+                const uint32_t t = fdiv(v, a.div_c);
+                const uint32_t k = v - t * a.c;
+                const int64_t base = row_off[t - row0];
+                if (base >= 0) {
+                    const uint64_t so = uint64_t(base) + k;
+                    const uint64_t ho = head_base + v;
+                    x[u] = ld<W>(a.src, S2H ? so : ho);
+                    dst_off[u] = S2H ? ho : so;
+                    live[u] = true;
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kVecsPerThread; ++u)
+            if (live[u])
+                st<W>(a.dst, dst_off[u], x[u]);
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void k_copy16(Copy a)
+{
+    typedef typename VecOf<16>::type V;
+    const uint64_t n_tiles = (a.n_vecs + kTileVecs - 1) / kTileVecs;
+    for (uint64_t tile = blockIdx.x; tile < n_tiles; tile += gridDim.x) {
+        const uint64_t v0 = tile * kTileVecs + threadIdx.x;
+        V x[kVecsPerThread];
+#pragma unroll
+        for (int u = 0; u < kVecsPerThread; ++u) {
+            const uint64_t v = v0 + uint64_t(u * kThreads);
+            if (v < a.n_vecs)
+                x[u] = ld<16>(a.src, v);
+        }
+#pragma unroll
+        for (int u = 0; u < kVecsPerThread; ++u) {
+            const uint64_t v = v0 + uint64_t(u * kThreads);
+            if (v < a.n_vecs)
+                st<16>(a.dst, v, x[u]);
+        }
+    }
+}
+
+cam_status launch_dense_relayout(const DenseRelayout& a, void* stream)
+{
+    const void* fn = nullptr;
+#define CAM_PICK(Wd)                                                                       \
+    if (a.width == Wd)                                                                     \
+        fn = a.seq_to_head ? reinterpret_cast<const void*>(&k_dense_relayout<Wd, true>)  \
+                           : reinterpret_cast<const void*>(&k_dense_relayout<Wd, false>);
+    CAM_PICK(16) CAM_PICK(8) CAM_PICK(4) CAM_PICK(2)
+#undef CAM_PICK
+    return launch(fn, a, a.n_tiles, stream, "dense relayout");
+}
+
+cam_status launch_varlen_relayout(const VarlenRelayout& a, void* stream)
+{
+    const void* fn = nullptr;
+#define CAM_PICK(Wd)                                                                        \
+    if (a.width == Wd)                                                                      \
+        fn = a.seq_to_head ? reinterpret_cast<const void*>(&k_varlen_relayout<Wd, true>)  \
+                           : reinterpret_cast<const void*>(&k_varlen_relayout<Wd, false>);
+    CAM_PICK(16) CAM_PICK(8) CAM_PICK(4) CAM_PICK(2)
+#undef CAM_PICK
+    return launch(fn, a, a.n_tiles, stream, "varlen relayout");
+}
+
+cam_status launch_copy(const Copy& a, void* stream)
+{
+    const uint64_t n_tiles = (a.n_vecs + kTileVecs - 1) / kTileVecs;
+    return launch(reinterpret_cast<const void*>(&k_copy16), a, n_tiles, stream, "copy");
+}
+
+}  // namespace cam

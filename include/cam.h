@@ -1,0 +1,234 @@
+/*
+ * cam.h -- C ABI of the per-GPU hot path of sequence/context-parallel attention
+ * movement on MI355X (gfx950): the Ulysses all-to-all relayout, the
+ * max/sum-aware LSE pack and the stable LSE-weighted combine.
+ *
+ * Sources (web pages, cited by title and section):
+ *  [FV] FastVideo compare view "[perf] Probe H3 chunked all-to-all with direct
+ *       output slices": ulysses_a2a.py (fused all-to-all, "same layout,
+ *       byte-identical results, fewer passes over local memory"),
+ *       benchmark_ulysses_a2a.py (all_to_all_4D(x, 2, 1) on the scatter
+ *       operand [3, S/P, H, 128]; (1, 2) on the gather operand [1, S, H/P, 128]).
+ *  [VA] vllm-ascend PR "[Performance][Attention] Fuse local SFA LSE formation
+ *       into DCP pack": "What this PR does / why we need it?" and "How was this
+ *       patch tested?".
+ *  [CU] cuLA PR "feat(distributed): add packed hybrid runtime and THD planner":
+ *       packed THD batches described by cu_seqlens, logical context-parallel
+ *       ranks emulated in one process.
+ *
+ * Conventions common to every call
+ *  - The P logical ranks of one exchange live in one GPU's memory; the
+ *    all-to-all between them is the relayout itself (no peer traffic).
+ *  - The caller owns every buffer.  The library never allocates, frees or
+ *    retains a pointer; all device pointers must stay valid until the enqueued
+ *    work has finished on `stream`.
+ *  - `stream` is a hipStream_t (NULL = the null stream).  Calls only enqueue
+ *    work: no host synchronisation, no device-to-host read, no allocation, so
+ *    every call may be captured in a HIP graph.
+ *  - Every argument is validated before anything is launched.  On failure the
+ *    call returns a non-zero cam_status, records a message readable with
+ *    cam_last_error() (thread-local), launches nothing and writes nothing.
+ *  - Inputs and outputs must not overlap (CAM_ERR_OVERLAP).
+ *  - Device pointers must be aligned to the element size; the kernels then
+ *    pick the widest access (16, 8, 4 or 2 bytes) that the sizes, strides and
+ *    pointer alignment allow.
+ *  - No C++ exception crosses this boundary.  A failed launch returns
+ *    CAM_ERR_HIP with the HIP error text in cam_last_error().
+ */
+#ifndef CAM_H
+#define CAM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum cam_dtype {
+    CAM_BF16 = 0, /* bfloat16 payload */
+    CAM_FP16 = 1, /* IEEE binary16 payload */
+    CAM_FP32 = 2  /* 4-byte words (relayouts only; used for index payloads) */
+} cam_dtype;
+
+typedef enum cam_status {
+    CAM_OK = 0,
+    CAM_ERR_NULL = 1,         /* a required pointer is NULL */
+    CAM_ERR_SHAPE = 2,        /* a size is negative, or a size product overflows */
+    CAM_ERR_DIVISIBILITY = 3, /* S, H or T not divisible by P where the layout needs it */
+    CAM_ERR_ALIGNMENT = 4,    /* pointer or stride not a multiple of the element size */
+    CAM_ERR_OVERLAP = 5,      /* an output overlaps an input */
+    CAM_ERR_UNSUPPORTED = 6,  /* dtype, scatter_dim or P outside what the call supports */
+    CAM_ERR_HIP = 7           /* the HIP runtime rejected the launch */
+} cam_status;
+
+/* Name of a status code (static string). */
+const char* cam_status_string(cam_status s);
+
+/* Detail of the last failed call on this thread ("" after a success). */
+const char* cam_last_error(void);
+
+/* ABI version of this header (incremented on any signature change). */
+#define CAM_ABI_VERSION 1
+int cam_abi_version(void);
+
+/* ------------------------------------------------------------------------- */
+/* Dense Ulysses relayout  ([FV] all_to_all_4D, benchmark_ulysses_a2a.py)      */
+/* ------------------------------------------------------------------------- */
+/*
+ * Sequence-sharded side  seq[j][b][s][h][d]:  [P][B][S/P][H][D], rank j holds
+ *   tokens [j*S/P, (j+1)*S/P) of each of the B planes (B = 3 carries Q, K, V).
+ * Head-sharded side      head[r][b][t][h'][d]: [P][B][S][H/P][D], rank r holds
+ *   heads [r*H/P, (r+1)*H/P) for all S tokens, tokens in source-rank order.
+ *
+ * ulysses_seq_to_head:  head[r][b][j*S/P + s][h'][d] = seq[j][b][s][r*H/P + h'][d]
+ *   (all_to_all_4D scatter dim 2, gather dim 1: attention input Q, K, V).
+ * ulysses_head_to_seq:  the inverse (scatter dim 1, gather dim 2: attention
+ *   output O back to sequence shards).
+ *
+ * Elements are copied as bits (dt only sets the element size: 2 bytes for
+ * CAM_BF16 / CAM_FP16, 4 for CAM_FP32).  Requires P >= 1, S % P == 0,
+ * H % P == 0 (CAM_ERR_DIVISIBILITY).  Any of B, S, H, D may be 0 (no work).
+ * `in` and `out` are device buffers of B*S*H*D elements each.
+ */
+cam_status ulysses_seq_to_head(const void* in, void* out, int64_t P, int64_t B, int64_t S,
+                               int64_t H, int64_t D, cam_dtype dt, void* stream);
+cam_status ulysses_head_to_seq(const void* in, void* out, int64_t P, int64_t B, int64_t S,
+                               int64_t H, int64_t D, cam_dtype dt, void* stream);
+
+/* ------------------------------------------------------------------------- */
+/* Varlen (packed THD, cu_seqlens) relayout  ([CU] cu_seqlens shard offsets)   */
+/* ------------------------------------------------------------------------- */
+/*
+ * A packed batch of nseq sequences: sequence i is global tokens
+ * [cu_seqlens[i], cu_seqlens[i+1]) of length L_i, total T = cu_seqlens[nseq].
+ * Each sequence is cut into P pieces; piece p is the in-sequence positions
+ * [floor(p*L_i/P), floor((p+1)*L_i/P)) and lives on logical rank p.  Rank p
+ * stores its pieces in sequence order: T_p tokens, slab [B][T_p][H][D] at token
+ * offset R_p = T_0 + ... + T_{p-1} of a rank-major buffer (element offset
+ * B*R_p*H*D).  With nseq = 1 and P | T this is exactly the dense layout.
+ *
+ * ulysses_varlen_plan (host only, no GPU call): from the host copy of
+ *   cu_seqlens (nseq+1 int32, non-decreasing, cu_seqlens[0] = 0) fills
+ *   rank_cu[p*(nseq+1) + i] = tokens of rank p before sequence i
+ *   (rank_cu[p*(nseq+1) + nseq] = T_p) and rank_off[p] = R_p (rank_off[P] = T).
+ *   Both arrays are caller-allocated host memory.
+ *
+ * ulysses_seq_to_head_varlen: rank-major ragged [B*T][H][D] -> head-sharded
+ *   [P][B][T][H/P][D] (global packed token order).
+ * ulysses_head_to_seq_varlen: the inverse.
+ *   cu_seqlens, rank_cu, rank_off are DEVICE copies of the plan above and
+ *   total_tokens = T is passed by the host (nothing is read back).  A plan that
+ *   does not match cu_seqlens is not detected on the device; rows whose
+ *   computed source or destination falls outside the buffers are skipped, so
+ *   a malformed plan cannot make the kernel access out of bounds.
+ *   Requires H % P == 0.
+ */
+cam_status ulysses_varlen_plan(const int32_t* cu_seqlens_host, int64_t nseq, int64_t P,
+                               int32_t* rank_cu_host, int64_t* rank_off_host);
+cam_status ulysses_seq_to_head_varlen(const void* in, void* out, const int32_t* cu_seqlens,
+                                      const int32_t* rank_cu, const int64_t* rank_off,
+                                      int64_t nseq, int64_t total_tokens, int64_t P, int64_t B,
+                                      int64_t H, int64_t D, cam_dtype dt, void* stream);
+cam_status ulysses_head_to_seq_varlen(const void* in, void* out, const int32_t* cu_seqlens,
+                                      const int32_t* rank_cu, const int64_t* rank_off,
+                                      int64_t nseq, int64_t total_tokens, int64_t P, int64_t B,
+                                      int64_t H, int64_t D, cam_dtype dt, void* stream);
+
+/* ------------------------------------------------------------------------- */
+/* Max/sum-aware LSE pack  ([VA] "What this PR does": the pack forms the LSE    */
+/* while writing the packed layout, instead of materializing it first)        */
+/* ------------------------------------------------------------------------- */
+/*
+ * Inputs, for each source rank p < P (decode context parallel: rank p holds the
+ * attention of every query over its share of the KV):
+ *   out  [P][T][H][Dv] payload (CAM_BF16 / CAM_FP16), element strides o_sp,
+ *        o_st, o_sh, Dv contiguous;
+ *   smax, ssum  [P][T][H] fp32 softmax max and sum, element strides free.
+ * LSE = smax + log(ssum) (natural log, fp32 result); a non-finite smax, a
+ * non-finite ssum or ssum <= 0 (including -0.0 and NaN) gives -inf.
+ *
+ * Packed exchange layout: chunk (p, r) = what source p sends to destination r:
+ *   scatter_dim = 1 (heads):  rows = T*(H/P), row q = t*(H/P) + h' carries
+ *                             (t, head r*H/P + h');  requires H % P == 0;
+ *   scatter_dim = 0 (tokens): rows = (T/P)*H, row q = t'*H + h carries
+ *                             (token r*T/P + t', h); requires T % P == 0.
+ *   chunk = O-region [rows][Dv] payload bits, padded to 16 bytes, then the
+ *   L-region [rows] fp32, padded to 16 bytes.  Buffer = [P_src][P_dst][chunk],
+ *   lse_pack_bytes() bytes.  Padding bytes are not written.
+ * The O-region is a bit copy of `out`; the L-region is the LSE.
+ *
+ * lse_pack_bytes returns the packed buffer size in bytes, or -1 for invalid
+ * arguments (the reason is in cam_last_error()).
+ */
+int64_t lse_pack_bytes(int64_t P, int64_t T, int64_t H, int64_t Dv, int scatter_dim,
+                       cam_dtype dt);
+cam_status lse_pack(const void* out, int64_t o_sp, int64_t o_st, int64_t o_sh,
+                    const float* smax, int64_t m_sp, int64_t m_st, int64_t m_sh,
+                    const float* ssum, int64_t s_sp, int64_t s_st, int64_t s_sh,
+                    int64_t P, int64_t T, int64_t H, int64_t Dv, int scatter_dim, cam_dtype dt,
+                    void* packed, void* stream);
+
+/* ------------------------------------------------------------------------- */
+/* Stable LSE-weighted combine  ([VA] "existing stable combine", invalid (-inf) */
+/* contributions "handled by the existing combine semantics", all-invalid rows) */
+/* ------------------------------------------------------------------------- */
+/*
+ * Per output row, over the partials p < P in ascending order:
+ *   V = {p : L_p finite};  M = max_{p in V} L_p;  w_p = exp(L_p - M);
+ *   Z = sum w_p;  out = (sum_{p in V} w_p * O_p) / Z;  lse_out = M + log(Z).
+ * If V is empty: out = +0.0 in every element and lse_out = -inf (no NaN).
+ * The O row of a partial outside V is never read.  Arithmetic is fp32; the
+ * output is rounded to the payload dtype (round to nearest even).
+ *
+ * lse_combine_packed: destination rank r combines the chunks (p, r) of every
+ *   source p of a buffer written by lse_pack with the same P, T, H, Dv,
+ *   scatter_dim, dt (the all-to-all is a strided view, no bytes move).  Output
+ *   row r*rows + q: `out` is [P*rows][Dv] (= [P][T][H/P][Dv] for scatter_dim 1,
+ *   [T][H][Dv] for scatter_dim 0); `lse_out` [P*rows] fp32 or NULL.
+ *
+ * lse_combine: generic strided form for P partials over rows (t, h):
+ *   part_out (p, t, h, d) at element p*po_sp + t*po_st + h*po_sh + d;
+ *   part_lse (p, t, h)    at element p*pl_sp + t*pl_st + h*pl_sh;
+ *   out (t, h, d) at t*o_st + h*o_sh + d; lse_out (t, h) at t*lo_st + h*lo_sh
+ *   (lse_out may be NULL).
+ *
+ * lse_combine_varlen: lse_combine for a packed THD batch whose P partials are
+ *   the attention of each token over the P KV pieces of its own sequence
+ *   (pieces as in the varlen relayout) under a causal mask: partial p of token
+ *   t (position k of its sequence) is admitted only if piece p is non-empty and
+ *   starts at or before k; otherwise neither its LSE nor its O row is read.
+ *   cu_seqlens is a DEVICE array of nseq+1 int32; total_tokens = T.
+ */
+cam_status lse_combine_packed(const void* packed, int64_t P, int64_t T, int64_t H, int64_t Dv,
+                              int scatter_dim, cam_dtype dt, void* out, float* lse_out,
+                              void* stream);
+cam_status lse_combine(const void* part_out, int64_t po_sp, int64_t po_st, int64_t po_sh,
+                       const float* part_lse, int64_t pl_sp, int64_t pl_st, int64_t pl_sh,
+                       int64_t P, int64_t T, int64_t H, int64_t D, cam_dtype dt, void* out,
+                       int64_t o_st, int64_t o_sh, float* lse_out, int64_t lo_st, int64_t lo_sh,
+                       void* stream);
+cam_status lse_combine_varlen(const void* part_out, int64_t po_sp, int64_t po_st, int64_t po_sh,
+                              const float* part_lse, int64_t pl_sp, int64_t pl_st, int64_t pl_sh,
+                              int64_t P, int64_t T, int64_t H, int64_t D, cam_dtype dt, void* out,
+                              int64_t o_st, int64_t o_sh, float* lse_out, int64_t lo_st,
+                              int64_t lo_sh, const int32_t* cu_seqlens, int64_t nseq,
+                              void* stream);
+
+/* ------------------------------------------------------------------------- */
+/* Measurement helper                                                          */
+/* ------------------------------------------------------------------------- */
+/*
+ * cam_copy: plain 16-byte-vector device copy of `bytes` bytes (src and dst
+ * 16-byte aligned, bytes % 16 == 0, no overlap) with the same launch shape as
+ * the relayout kernels.  It is the achievable-copy ceiling measured beside
+ * every relayout ([FV] profile_ulysses_mfu.py times a plain dst.copy_ next to
+ * each all-to-all) and the known-size reference for hardware byte counters.
+ */
+cam_status cam_copy(const void* src, void* dst, int64_t bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CAM_H */

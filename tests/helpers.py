@@ -1,0 +1,68 @@
+"""Shared comparison helpers for the GPU parity tests (test code only)."""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+LSE_ATOL = 1e-5          # fp32 LSE: max abs error
+OUT_ROW_RTOL = 8e-3      # combined payload: per-row max|g - o| / max|o|
+
+
+def announce(msg: str) -> None:
+    print(f"[case] {msg}", flush=True)
+
+
+def to_host_bits(t: torch.Tensor) -> np.ndarray:
+    t = t.detach().contiguous().cpu()
+    if t.element_size() == 2:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    if t.element_size() == 4:
+        return t.view(torch.int32).numpy().view(np.uint32)
+    if t.element_size() == 1:
+        return t.view(torch.uint8).numpy()
+    raise TypeError(t.dtype)
+
+
+def from_host_bits(a: np.ndarray, dtype: torch.dtype, device="cuda") -> torch.Tensor:
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(dtype).to(device)
+    if a.dtype == np.uint32:
+        return torch.from_numpy(a.view(np.int32)).view(dtype).to(device)
+    raise TypeError(a.dtype)
+
+
+def assert_bits_equal(got: np.ndarray, want: np.ndarray, what: str) -> None:
+    got = got.reshape(-1)
+    want = want.reshape(-1)
+    assert got.shape == want.shape, what
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, f"{what}: {bad.size} mismatching elements, first at {bad[:5].tolist()}"
+
+
+def assert_lse_close(got: np.ndarray, want: np.ndarray, what: str) -> float:
+    got = got.reshape(-1).astype(np.float64)
+    want = want.reshape(-1).astype(np.float64)
+    assert not np.isnan(got).any(), f"{what}: NaN in LSE"
+    gi, wi = np.isneginf(got), np.isneginf(want)
+    assert np.array_equal(gi, wi), f"{what}: -inf pattern differs at {np.nonzero(gi != wi)[0][:5].tolist()}"
+    assert not np.isposinf(got).any()
+    f = ~wi
+    err = float(np.max(np.abs(got[f] - want[f]))) if f.any() else 0.0
+    assert err <= LSE_ATOL, f"{what}: max abs LSE error {err}"
+    return err
+
+
+def assert_rows_close(got: np.ndarray, want: np.ndarray, what: str) -> float:
+    """got, want: float64 [rows][D].  Per row max|g-o| / max|o| <= 8e-3; rows
+    whose reference is all zero must be exactly zero; no NaN."""
+    assert not np.isnan(got).any(), f"{what}: NaN in output"
+    num = np.max(np.abs(got - want), axis=-1)
+    den = np.max(np.abs(want), axis=-1)
+    zero = den == 0
+    assert np.all(num[zero] == 0), f"{what}: nonzero output where the oracle is zero"
+    rel = num[~zero] / den[~zero] if (~zero).any() else np.zeros(1)
+    worst = float(np.max(rel))
+    assert worst <= OUT_ROW_RTOL, f"{what}: worst row relative error {worst}"
+    return worst

@@ -1,0 +1,212 @@
+"""Host-side checks of the C ABI (no GPU): the library loads and exports every
+function include/cam.h declares; every rejection path returns its status
+before anything is launched; the host varlen plan equals the oracle's; the
+packed-buffer geometry equals the oracle's; the fast-division constants are
+exact."""
+
+import ctypes as C
+import re
+from pathlib import Path
+
+import numpy as np
+import pytest
+
+import synth
+
+ROOT = Path(__file__).resolve().parents[1]
+HEADER = ROOT / "include" / "cam.h"
+
+OK, NULL, SHAPE, DIV, ALIGN, OVERLAP, UNSUP = 0, 1, 2, 3, 4, 5, 6
+BF16, FP16, FP32 = 0, 1, 2
+A = 0x7F0000000000  # fake, 256-byte aligned "device" addresses: never dereferenced
+Bp = 0x7F0100000000
+
+
+@pytest.fixture(scope="module")
+def cam():
+    import context_attention_movement_amd as m
+    return m
+
+
+@pytest.fixture(scope="module")
+def lib(cam):
+    return cam.library()
+
+
+def declared_functions():
+    text = re.sub(r"/\*.*?\*/", "", HEADER.read_text(), flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s+([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ["ulysses_seq_to_head", "ulysses_head_to_seq", "ulysses_varlen_plan", "ulysses_seq_to_head_varlen",
+              "ulysses_head_to_seq_varlen", "lse_pack_bytes", "lse_pack", "lse_combine_packed", "lse_combine",
+              "lse_combine_varlen", "cam_status_string", "cam_last_error", "cam_abi_version", "cam_copy"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    raw = C.CDLL(str(ROOT / "context_attention_movement_amd" / "libcam.so"))
+    for n in declared_functions():
+        assert hasattr(raw, n), n
+    assert lib.cam_abi_version() == 1
+
+
+def test_status_strings(lib):
+    assert lib.cam_status_string(0) == b"CAM_OK"
+    assert lib.cam_status_string(5) == b"CAM_ERR_OVERLAP"
+
+
+def _s2h(lib, *a):
+    return lib.ulysses_seq_to_head(*a)
+
+
+def test_dense_relayout_rejections(lib):
+    f = lib.ulysses_seq_to_head
+    assert f(A, Bp, 0, 1, 8, 4, 8, BF16, None) == SHAPE
+    assert f(A, Bp, 2, -1, 8, 4, 8, BF16, None) == SHAPE
+    assert f(A, Bp, 3, 1, 8, 6, 8, BF16, None) == DIV          # S % P
+    assert f(A, Bp, 2, 1, 8, 3, 8, BF16, None) == DIV          # H % P
+    assert b"multiples of P" in lib.cam_last_error()
+    assert f(None, Bp, 2, 1, 8, 4, 8, BF16, None) == NULL
+    assert f(A + 1, Bp, 2, 1, 8, 4, 8, BF16, None) == ALIGN
+    assert f(A + 2, Bp, 2, 1, 8, 4, 8, FP32, None) == ALIGN
+    assert f(A, A + 64, 2, 1, 8, 4, 8, BF16, None) == OVERLAP
+    assert f(A, Bp, 2, 1, 8, 4, 8, 9, None) == UNSUP
+    assert f(A, Bp, 2, 1 << 40, 1 << 40, 2, 2, BF16, None) == SHAPE  # size overflow
+    # empty work is accepted without touching the (null) pointers
+    assert f(None, None, 2, 0, 8, 4, 8, BF16, None) == OK
+    assert f(None, None, 2, 1, 0, 4, 8, BF16, None) == OK
+    assert lib.cam_last_error() == b""
+    g = lib.ulysses_head_to_seq
+    assert g(A, Bp, 2, 1, 7, 4, 8, BF16, None) == DIV
+    assert g(A, A, 2, 1, 8, 4, 8, BF16, None) == OVERLAP
+
+
+def test_varlen_relayout_rejections(lib):
+    f = lib.ulysses_seq_to_head_varlen
+    cu, rc, ro = A + 0x1000_0000, A + 0x2000_0000, A + 0x3000_0000
+    assert f(A, Bp, cu, rc, ro, 3, 100, 3, 1, 4, 8, BF16, None) == DIV   # H % P
+    assert f(A, Bp, cu, rc, ro, 0, 100, 2, 1, 4, 8, BF16, None) == SHAPE  # tokens without sequences
+    assert f(A, Bp, None, rc, ro, 3, 100, 2, 1, 4, 8, BF16, None) == NULL
+    assert f(A, Bp, cu + 2, rc, ro, 3, 100, 2, 1, 4, 8, BF16, None) == ALIGN
+    assert f(A, Bp, cu, rc, ro + 4, 3, 100, 2, 1, 4, 8, BF16, None) == ALIGN
+    assert f(A, A + 16, cu, rc, ro, 3, 100, 2, 1, 4, 8, BF16, None) == OVERLAP
+    assert f(A, Bp, cu, rc, ro, 3, 1 << 33, 2, 1, 4, 8, BF16, None) == SHAPE
+    assert f(None, None, None, None, None, 0, 0, 2, 1, 4, 8, BF16, None) == OK
+
+
+def _plan(lib, cu, P):
+    cu = np.ascontiguousarray(cu, dtype=np.int32)
+    nseq = cu.size - 1
+    rank_cu = np.full((P, nseq + 1), -7, dtype=np.int32)
+    rank_off = np.full(P + 1, -7, dtype=np.int64)
+    st = lib.ulysses_varlen_plan(cu.ctypes.data, nseq, P, rank_cu.ctypes.data, rank_off.ctypes.data)
+    return st, rank_cu, rank_off
+
+
+@pytest.mark.parametrize("seed,nseq,P", [(1, 1, 1), (2, 5, 3), (3, 22, 8), (4, 40, 7), (5, 3, 16)])
+def test_varlen_plan_equals_oracle(lib, orc, seed, nseq, P):
+    cu = synth.cu_seqlens(synth.random_lengths(nseq, seed, lo=0, hi=50))
+    st, rank_cu, rank_off = _plan(lib, cu, P)
+    assert st == OK
+    o_cu, o_off = orc.varlen_plan(cu, P)
+    assert np.array_equal(rank_cu, o_cu) and np.array_equal(rank_off, o_off)
+
+
+def test_varlen_plan_thd_workload(lib, orc):
+    lens = synth.thd_lengths(20, 131072, seed=synth.BASE_SEED + 4)
+    assert lens.size == 22 and lens.sum() == 131072 and np.all(lens[lens < 4097] >= 512)
+    cu = synth.cu_seqlens(lens)
+    st, rank_cu, rank_off = _plan(lib, cu, 8)
+    assert st == OK and rank_off[-1] == 131072
+    o_cu, o_off = orc.varlen_plan(cu, 8)
+    assert np.array_equal(rank_cu, o_cu) and np.array_equal(rank_off, o_off)
+
+
+def test_varlen_plan_rejections(lib):
+    assert _plan(lib, [1, 4, 9], 2)[0] == SHAPE      # not zero-based
+    assert _plan(lib, [0, 4, 3], 2)[0] == SHAPE      # decreasing
+    assert _plan(lib, [0, 4], 0)[0] == SHAPE         # P < 1
+    assert lib.ulysses_varlen_plan(None, 1, 2, None, None) == NULL
+
+
+def test_pack_geometry_equals_oracle(lib, orc):
+    for P, T, H, Dv, sd in [(8, 128, 128, 512, 1), (8, 128, 128, 512, 0), (2, 256, 8, 64, 1), (3, 6, 6, 5, 0),
+                            (2, 3, 2, 3, 1), (1, 1, 1, 1, 1)]:
+        want = P * P * orc.pack_chunk_bytes(P, T, H, Dv, sd)
+        assert lib.lse_pack_bytes(P, T, H, Dv, sd, BF16) == want
+    assert lib.lse_pack_bytes(8, 128, 128, 512, 1, BF16) == 64 * 2_105_344
+    assert lib.lse_pack_bytes(3, 4, 4, 8, 1, BF16) == -1      # H % P
+    assert lib.lse_pack_bytes(3, 4, 6, 8, 0, BF16) == -1      # T % P
+    assert lib.lse_pack_bytes(2, 4, 4, 8, 2, BF16) == -1      # scatter_dim
+    assert lib.lse_pack_bytes(2, 4, 4, 8, 1, FP32) == -1      # payload dtype
+
+
+def test_pack_rejections(lib):
+    f = lib.lse_pack
+    M, S, PK = A + 0x1000_0000, A + 0x2000_0000, A + 0x4000_0000
+    args = lambda out=A, m=M, s=S, pk=PK, sd=1, dt=BF16, st=(512 * 128 * 128, 512 * 128, 512): \
+        (out, *st, m, 128 * 128, 128, 1, s, 128 * 128, 128, 1, 8, 128, 128, 512, sd, dt, pk, None)
+    assert f(*args(out=None)) == NULL
+    assert f(*args(out=A + 1)) == ALIGN
+    assert f(*args(m=M + 2)) == ALIGN
+    assert f(*args(pk=PK + 8)) == ALIGN
+    assert f(*args(pk=A + 64)) == OVERLAP
+    assert f(*args(sd=3)) == UNSUP
+    assert f(*args(dt=FP32)) == UNSUP
+    assert f(*args(st=(-1, 512, 1))) == UNSUP
+
+
+def test_combine_rejections(lib):
+    f = lib.lse_combine
+    L, O, LO = A + 0x1000_0000, A + 0x2000_0000, A + 0x3000_0000
+    ok = lambda **k: (k.get("po", A), 64 * 8 * 16, 8 * 16, 16, k.get("pl", L), 64 * 8, 8, 1, k.get("P", 4), 64, 8, 16,
+                      k.get("dt", BF16), k.get("out", O), 8 * 16, 16, k.get("lo", LO), 8, 1, None)
+    assert f(*ok(P=65)) == UNSUP
+    assert f(*ok(P=0)) == SHAPE
+    assert f(*ok(dt=FP32)) == UNSUP
+    assert f(*ok(po=None)) == NULL
+    assert f(*ok(pl=L + 2)) == ALIGN
+    assert f(*ok(out=A + 32)) == OVERLAP
+    assert f(*ok(lo=L)) == OVERLAP
+    assert f(*ok(lo=O + 64)) == OVERLAP
+    g = lib.lse_combine_varlen
+    assert g(A, 64 * 8 * 16, 8 * 16, 16, L, 64 * 8, 8, 1, 4, 64, 8, 16, BF16, O, 8 * 16, 16, LO, 8, 1,
+             None, 3, None) == NULL
+    assert g(A, 64 * 8 * 16, 8 * 16, 16, L, 64 * 8, 8, 1, 4, 64, 8, 16, BF16, O, 8 * 16, 16, LO, 8, 1,
+             A + 0x5000_0000, 0, None) == SHAPE
+    h = lib.lse_combine_packed
+    assert h(A + 8, 8, 128, 128, 512, 1, BF16, O, LO, None) == ALIGN
+    assert h(A, 8, 128, 128, 512, 1, BF16, A + 4096, LO, None) == OVERLAP
+    assert h(A, 3, 128, 128, 512, 1, BF16, O, LO, None) == DIV
+
+
+def test_copy_rejections(lib):
+    assert lib.cam_copy(A, Bp, 100, None) == ALIGN
+    assert lib.cam_copy(A, A + 16, 64, None) == OVERLAP
+    assert lib.cam_copy(None, Bp, 64, None) == NULL
+    assert lib.cam_copy(None, None, 0, None) == OK
+
+
+def _fastdiv(d):
+    l = 0
+    while (1 << l) < d:
+        l += 1
+    m = ((1 << 32) * ((1 << l) - d)) // d + 1
+    return m, l
+
+
+def test_fast_division_constants_are_exact():
+    rng = np.random.default_rng(0)
+    divisors = list(range(1, 300)) + [1023, 1024, 1025, 8190, 9450, 65535, 65536, 2**31 - 1, 2**31, 2**31 + 1,
+                                      2**32 - 1] + rng.integers(1, 2**32, size=200).tolist()
+    ns = [0, 1, 2, 3, 2**31 - 1, 2**31, 2**32 - 1, 2**32 - 2] + rng.integers(0, 2**32, size=300).tolist()
+    for d in divisors:
+        m, l = _fastdiv(d)
+        assert 0 <= m < 2**32
+        for n in ns + [d - 1, d, d + 1, 2 * d - 1, 2 * d, (2**32 - 1) // d * d, (2**32 - 1) // d * d - 1]:
+            if 0 <= n < 2**32:
+                assert ((n * m >> 32) + n) >> l == n // d, (d, n)
