@@ -1,0 +1,499 @@
+"""Benchmark of the per-GPU hot path of sequence/context-parallel attention
+movement on one MI355X.
+
+One step runs every operation of the path once, each on the workload the
+pages give for it:
+  - Ulysses relayout, video DiT at P = 4 (S = 32760, H = 24, D = 128, bf16):
+    seq->head of Q, K, V (B = 3) and head->seq of the attention output (B = 1);
+  - MLA-style decode context parallel, P = 8, T = 128, H = 128, Dv = 512:
+    max/sum-aware LSE pack (1% invalid statistics), the exchange as a strided
+    view, and the stable combine;
+  - packed THD, 20 short + 2 long sequences filling 131072 tokens, H = 32,
+    D = 128, P = 8: varlen seq->head of Q, K, V, head->seq of O, and the
+    causal combine of 8 KV-piece partials.
+Inputs are synthetic and seeded, resident in HBM before the timed region.
+Each buffer an operation reads was last touched a whole step earlier (more
+than 15 GB of other traffic in between), so no input is served from the
+256 MB Infinity Cache.
+
+Prints ONE JSON line.  `value` is the step's algorithmic bytes (each input
+read once, each output written once, invalid or causally masked partials not
+read) divided by the step time.  Per-operation figures are under "ops".
+
+    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py --summarize-rocprof DIR --kernel NAME ...   (profile text)
+"""
+
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import math
+import os
+import platform
+import statistics
+import sys
+import time
+from pathlib import Path
+
+ROOT = Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+METRIC = "achieved HBM GB/s (% of peak) and µs/call for relayout, LSE-pack, combine"
+HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E, published
+KERNEL_SOURCES = ["relayout.hip", "lse.hip", "cam_device.h", "cam_internal.h"]
+TRAFFIC_FILE = ROOT / "profiles" / "traffic.json"
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        h.update((ROOT / "context_attention_movement_amd" / "csrc" / name).read_bytes())
+    return h.hexdigest()[:16]
+
+
+# ---------------------------------------------------------------------------
+# Workloads
+# ---------------------------------------------------------------------------
+
+def thd_admitted_counts(cu, P):
+    """Number of (token, partial) pairs whose KV piece is admitted by the
+    causal rule (non-empty piece starting at or before the token)."""
+    total = 0
+    for i in range(len(cu) - 1):
+        L = int(cu[i + 1]) - int(cu[i])
+        for p in range(P):
+            a, e = (p * L) // P, ((p + 1) * L) // P
+            if a < e:
+                total += L - a
+    return total
+
+
+class Workload:
+    def __init__(self, torch, cam, synth):
+        self.torch, self.cam, self.synth = torch, cam, synth
+        dev = "cuda"
+        g = synth._gen(synth.BASE_SEED + 1, dev)
+        bf = torch.bfloat16
+
+        def randn(shape, std=1.0):
+            x = torch.randn(shape, generator=g, device=dev, dtype=torch.float32)
+            if std != 1.0:
+                x.mul_(std)
+            return x.to(bf)
+
+        # video DiT, P = 4
+        self.vP, self.vS, self.vH, self.vD = 4, 32760, 24, 128
+        P, S, H, D = self.vP, self.vS, self.vH, self.vD
+        self.v_qkv = randn((P, 3, S // P, H, D))
+        self.v_qkv_out = torch.empty((P, 3, S, H // P, D), dtype=bf, device=dev)
+        self.v_o = randn((P, 1, S, H // P, D))
+        self.v_o_out = torch.empty((P, 1, S // P, H, D), dtype=bf, device=dev)
+        # MLA decode, P = 8
+        self.mP, self.mT, self.mH, self.mDv = 8, 128, 128, 512
+        P, T, H, Dv = self.mP, self.mT, self.mH, self.mDv
+        self.m_out, self.m_max, self.m_sum, bad = synth.dcp_partials(P, T, H, Dv, synth.BASE_SEED + 3, device=dev)
+        n = cam.lse_pack_bytes(P, T, H, Dv, 1)
+        self.m_packed = [torch.empty(n, dtype=torch.uint8, device=dev) for _ in range(2)]
+        rows = T * H // P
+        self.m_comb = torch.empty((P * rows, Dv), dtype=bf, device=dev)
+        self.m_lse = torch.empty(P * rows, dtype=torch.float32, device=dev)
+        for pk in self.m_packed:
+            cam.lse_pack(self.m_out, self.m_max, self.m_sum, 1, packed=pk)
+        self.m_invalid = int(bad.size)
+        # packed THD, P = 8
+        self.tP, self.tH, self.tD = 8, 32, 128
+        P, H, D = self.tP, self.tH, self.tD
+        lens = synth.thd_lengths(20, 131072, seed=synth.BASE_SEED + 4)
+        self.t_cu = synth.cu_seqlens(lens)
+        T = self.tT = int(self.t_cu[-1])
+        self.t_plan = cam.ulysses_varlen_plan(self.t_cu, P)
+        self.t_qkv = randn((3 * T, H, D))
+        self.t_qkv_out = torch.empty((P, 3, T, H // P, D), dtype=bf, device=dev)
+        self.t_o = randn((P, 1, T, H // P, D))
+        self.t_o_out = torch.empty((T, H, D), dtype=bf, device=dev)
+        self.t_part = torch.empty((P, T, H, D), dtype=bf, device=dev)
+        for p in range(P):
+            self.t_part[p].copy_(randn((T, H, D)))
+        self.t_lse = torch.randn((P, T, H), generator=g, device=dev, dtype=torch.float32).mul_(2.0)
+        self.t_cu_dev = torch.from_numpy(self.t_cu).to(dev)
+        self.t_comb = torch.empty((T, H, D), dtype=bf, device=dev)
+        self.t_comb_lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+        self.t_admitted = thd_admitted_counts(self.t_cu, P)
+        self.step_index = 0
+        torch.cuda.synchronize()
+
+    # algorithmic bytes of each operation
+    def op_bytes(self):
+        vP, vS, vH, vD = self.vP, self.vS, self.vH, self.vD
+        mP, mT, mH, mDv = self.mP, self.mT, self.mH, self.mDv
+        tT, tH, tD = self.tT, self.tH, self.tD
+        m_rows = mP * mT * mH  # (source, token, head) partial rows
+        m_valid = m_rows - self.m_invalid
+        return {
+            "relayout_seq_to_head_video_p4_qkv": 2 * 3 * vS * vH * vD * 2,
+            "relayout_head_to_seq_video_p4_o": 2 * vS * vH * vD * 2,
+            "lse_pack_mla": m_rows * mDv * 2 + m_rows * 8 + m_rows * mDv * 2 + m_rows * 4,
+            "lse_combine_mla": m_valid * mDv * 2 + m_rows * 4 + (m_rows // mP) * (mDv * 2 + 4),
+            "relayout_seq_to_head_varlen_thd_qkv": 2 * 3 * tT * tH * tD * 2,
+            "relayout_head_to_seq_varlen_thd_o": 2 * tT * tH * tD * 2,
+            "lse_combine_varlen_thd": self.t_admitted * tH * (tD * 2 + 4) + tT * tH * (tD * 2 + 4),
+        }
+
+    def ops(self):
+        cam = self.cam
+        k = self.step_index
+
+        def pack():
+            cam.lse_pack(self.m_out, self.m_max, self.m_sum, 1, packed=self.m_packed[k % 2])
+
+        def combine():
+            # reads the packed buffer written one step earlier (the exchange is a view)
+            cam.lse_combine_packed(self.m_packed[(k + 1) % 2], self.mP, self.mT, self.mH, self.mDv, 1,
+                                   out=self.m_comb, lse_out=self.m_lse)
+
+        return [
+            ("relayout_seq_to_head_video_p4_qkv", "k_dense_relayout<16, true>",
+             lambda: cam.ulysses_seq_to_head(self.v_qkv, self.vP, out=self.v_qkv_out)),
+            ("relayout_head_to_seq_video_p4_o", "k_dense_relayout<16, false>",
+             lambda: cam.ulysses_head_to_seq(self.v_o, self.vP, out=self.v_o_out)),
+            ("lse_pack_mla", "k_pack<16>", pack),
+            ("lse_combine_mla", "k_combine<16, false, false>", combine),
+            ("relayout_seq_to_head_varlen_thd_qkv", "k_varlen_relayout<16, true>",
+             lambda: cam.ulysses_seq_to_head_varlen(self.t_qkv, self.t_plan, 3, out=self.t_qkv_out)),
+            ("relayout_head_to_seq_varlen_thd_o", "k_varlen_relayout<16, false>",
+             lambda: cam.ulysses_head_to_seq_varlen(self.t_o, self.t_plan, out=self.t_o_out)),
+            ("lse_combine_varlen_thd", "k_combine<16, false, true>",
+             lambda: cam.lse_combine_varlen(self.t_part, self.t_lse, self.t_cu_dev, out=self.t_comb,
+                                            lse_out=self.t_comb_lse)),
+        ]
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle as it stands, on a bounded sample
+# ---------------------------------------------------------------------------
+
+def cpu_baseline(w, budget_s: float = 25.0):
+    import numpy as np
+    import oracle
+    import synth
+
+    torch = w.torch
+
+    def bits(t):
+        t = t.detach().contiguous().cpu()
+        return t.view(torch.int16).numpy().view(np.uint16)
+
+    done_bytes = 0.0
+    secs = 0.0
+    parts = []
+    # 1) video P = 4 Q/K/V seq->head, whole operand
+    x = bits(w.v_qkv)
+    t0 = time.perf_counter()
+    oracle.seq_to_head(x, w.vP, 3, w.vS, w.vH, w.vD)
+    dt = time.perf_counter() - t0
+    nb = w.op_bytes()["relayout_seq_to_head_video_p4_qkv"]
+    done_bytes += nb
+    secs += dt
+    parts.append(f"video P=4 QKV seq->head (full, {dt:.2f} s)")
+    del x
+    # 2) MLA pack and combine, whole workload
+    ob = bits(w.m_out)
+    m = w.m_max.cpu().numpy()
+    s = w.m_sum.cpu().numpy()
+    t0 = time.perf_counter()
+    packed = oracle.lse_pack(ob, m, s, 1)
+    dt = time.perf_counter() - t0
+    done_bytes += w.op_bytes()["lse_pack_mla"]
+    secs += dt
+    parts.append(f"MLA pack (full, {dt:.2f} s)")
+    t0 = time.perf_counter()
+    oracle.lse_combine_packed(packed, w.mP, w.mT, w.mH, w.mDv, 1)
+    dt = time.perf_counter() - t0
+    done_bytes += w.op_bytes()["lse_combine_mla"]
+    secs += dt
+    parts.append(f"MLA combine (full, {dt:.2f} s)")
+    # 3) THD combine on a token window sized to the remaining budget
+    remaining = max(2.0, budget_s - secs)
+    win = 256
+    a = int(w.t_cu[3])
+    po = bits(w.t_part[:, a:a + win])
+    pl = w.t_lse[:, a:a + win].cpu().numpy()
+    t0 = time.perf_counter()
+    oracle.lse_combine(po, pl, cu=w.t_cu, t_begin=a)
+    dt = time.perf_counter() - t0
+    frac = win / w.tT
+    # scale the window to a bounded share of the remaining budget
+    reps = max(1, min(64, int(remaining / max(dt, 1e-3))))
+    win2 = min(w.tT - a, win * reps)
+    po = bits(w.t_part[:, a:a + win2])
+    pl = w.t_lse[:, a:a + win2].cpu().numpy()
+    t0 = time.perf_counter()
+    oracle.lse_combine(po, pl, cu=w.t_cu, t_begin=a)
+    dt = time.perf_counter() - t0
+    frac = win2 / w.tT
+    done_bytes += w.op_bytes()["lse_combine_varlen_thd"] * frac
+    secs += dt
+    parts.append(f"THD combine on tokens [{a}, {a + win2}) ({dt:.2f} s, {frac:.2%} of the batch)")
+    return {
+        "value": round(done_bytes / secs / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "seconds": round(secs, 2),
+        "sample": "; ".join(parts) + ". Single-threaded C oracle (fp64), same synthetic inputs "
+                  "downloaded from the GPU; GB/s = the sample's algorithmic bytes / oracle time.",
+        "cpu": platform.processor() or _cpu_model(),
+    }
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+# ---------------------------------------------------------------------------
+# rocprofv3 summaries
+# ---------------------------------------------------------------------------
+
+def _read_csvs(root, suffix):
+    rows = []
+    for f in sorted(glob.glob(os.path.join(root, "**", f"*{suffix}"), recursive=True)):
+        with open(f, newline="") as fh:
+            rows += list(csv.DictReader(fh))
+    return rows
+
+
+OP_KERNELS = [  # (op, kernel name fragment as rocprofv3 reports it)
+    ("relayout_seq_to_head_video_p4_qkv", "k_dense_relayout<16, true>"),
+    ("relayout_head_to_seq_video_p4_o", "k_dense_relayout<16, false>"),
+    ("lse_pack_mla", "k_pack<16>"),
+    ("lse_combine_mla", "k_combine<16, false, false>"),
+    ("relayout_seq_to_head_varlen_thd_qkv", "k_varlen_relayout<16, true>"),
+    ("relayout_head_to_seq_varlen_thd_o", "k_varlen_relayout<16, false>"),
+    ("lse_combine_varlen_thd", "k_combine<16, false, true>"),
+]
+COPY_KERNEL = "k_copy16"
+COPY_BYTES = 3 * 32760 * 24 * 128 * 2  # the video Q/K/V operand copied for the ceiling (each way)
+
+
+def summarize_rocprof(trace_dir, fetch_dir, write_dir, out_txt, command):
+    """Write a short text summary of rocprofv3 output (kernel statistics and
+    per-dispatch FETCH_SIZE / WRITE_SIZE) and, when both counters are given,
+    profiles/traffic.json: each kernel's HBM bytes per launch, scaled by what
+    the same counters read for the plain copy kernel of known size."""
+    lines = [f"command: {command}", ""]
+    stats = _read_csvs(trace_dir, "kernel_stats.csv") if trace_dir else []
+    if stats:
+        lines.append("kernel statistics (rocprofv3 --kernel-trace --stats), microseconds:")
+        lines.append(f"{'kernel':64s} {'calls':>6s} {'avg':>10s} {'min':>10s} {'max':>10s}")
+        for r in stats:
+            name = r.get("Name", r.get("KernelName", ""))
+            if "cam::" not in name:
+                continue
+            lines.append(f"{name[:64]:64s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.2f} "
+                         f"{float(r['MinNs']) / 1e3:10.2f} {float(r['MaxNs']) / 1e3:10.2f}")
+        lines.append("")
+    med = {}
+    for d, cname in ((fetch_dir, "FETCH_SIZE"), (write_dir, "WRITE_SIZE")):
+        if not d:
+            continue
+        per_kernel = {}
+        for r in _read_csvs(d, "counter_collection.csv"):
+            if r.get("Counter_Name") != cname:
+                continue
+            per_kernel.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        med[cname] = {k: statistics.median(v) for k, v in per_kernel.items()}
+        lines.append(f"{cname} per dispatch (KiB, median over dispatches):")
+        for k, v in sorted(per_kernel.items()):
+            if "cam::" in k:
+                lines.append(f"  {k[:90]:90s} n={len(v):3d} {statistics.median(v):14.1f}")
+        lines.append("")
+
+    def find(table, frag):
+        for k, v in table.items():
+            if frag in k:
+                return v
+        return None
+
+    if "FETCH_SIZE" in med and "WRITE_SIZE" in med:
+        cf, cw = find(med["FETCH_SIZE"], COPY_KERNEL), find(med["WRITE_SIZE"], COPY_KERNEL)
+        ff = COPY_BYTES / (cf * 1024.0)
+        fw = COPY_BYTES / (cw * 1024.0)
+        lines.append(f"copy calibration: {COPY_BYTES} bytes each way; FETCH_SIZE {cf:.1f} KiB (factor {ff:.4f}), "
+                     f"WRITE_SIZE {cw:.1f} KiB (factor {fw:.4f})")
+        ops = {}
+        for op, frag in OP_KERNELS:
+            f, wv = find(med["FETCH_SIZE"], frag), find(med["WRITE_SIZE"], frag)
+            if f is None or wv is None:
+                continue
+            fb, wb = f * 1024.0 * ff, wv * 1024.0 * fw
+            ops[op] = {"kernel": frag, "fetch_bytes": round(fb), "write_bytes": round(wb),
+                       "hbm_bytes_per_launch": round(fb + wb)}
+            lines.append(f"  {op:40s} fetch {fb / 1e6:10.2f} MB  write {wb / 1e6:10.2f} MB")
+        TRAFFIC_FILE.write_text(json.dumps({
+            "kernel_source_hash": kernel_source_hash(), "command": command,
+            "copy_calibration": {"bytes_each_way": COPY_BYTES, "fetch_kib": cf, "write_kib": cw,
+                                 "fetch_factor": ff, "write_factor": fw},
+            "ops": ops}, indent=1) + "\n")
+    Path(out_txt).write_text("\n".join(lines) + "\n")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=25.0)
+    ap.add_argument("--summarize-rocprof", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--summary-out", default=None)
+    ap.add_argument("--command", default="")
+    args = ap.parse_args()
+
+    if args.summarize_rocprof:
+        tr, fe, wr = [None if x in ("-", "") else x for x in args.summarize_rocprof]
+        summarize_rocprof(tr, fe, wr, args.summary_out, args.command)
+        return
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(json.dumps({"error": "this benchmark measures one GPU: the relayout, pack and combine of P "
+                                   "logical ranks run in one GPU's HBM; --gpus must be 1"}), flush=True)
+        sys.exit(2)
+
+    import torch
+    import context_attention_movement_amd as cam
+    import synth
+
+    cam.library()  # fails loudly without the HIP library
+    torch.cuda.set_device(0)
+    props = torch.cuda.get_device_properties(0)
+    w = Workload(torch, cam, synth)
+    ops = w.ops
+    nbytes = w.op_bytes()
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            for _, _, fn in ops():
+                fn()
+            w.step_index += 1
+        torch.cuda.synchronize()
+        names = [n for n, _, _ in ops()]
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(args.steps):
+            ev = evs[k]
+            ev[0].record(stream)
+            for i, (_, _, fn) in enumerate(ops()):
+                fn()
+                ev[i + 1].record(stream)
+            w.step_index += 1
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    per_op_us = {n: [] for n in names}
+    for k in range(args.steps):
+        for i, n in enumerate(names):
+            per_op_us[n].append(evs[k][i].elapsed_time(evs[k][i + 1]) * 1000.0)
+    step_ms = wall * 1000.0 / args.steps
+    step_bytes = sum(nbytes.values())
+
+    # plain-copy ceiling on the video Q/K/V operand size (outside the timed region)
+    cstream = torch.cuda.Stream()
+    with torch.cuda.stream(cstream):
+        src, dst = w.v_qkv, w.v_qkv_out
+        for _ in range(3):
+            cam.copy(src, dst)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(cstream)
+        for _ in range(10):
+            cam.copy(src, dst)
+        e1.record(cstream)
+        torch.cuda.synchronize()
+    copy_us = e0.elapsed_time(e1) * 100.0
+    copy_gbps = 2 * src.numel() * 2 / copy_us / 1e3
+
+    op_table = {}
+    kern = dict((n, k) for n, k, _ in ops())
+    for n in names:
+        us = statistics.mean(per_op_us[n])
+        gbps = nbytes[n] / us / 1e3
+        op_table[n] = {
+            "kernel": kern[n],
+            "us_per_call_mean": round(us, 2),
+            "us_per_call_median": round(statistics.median(per_op_us[n]), 2),
+            "us_per_call_p95": round(sorted(per_op_us[n])[int(0.95 * (len(per_op_us[n]) - 1))], 2),
+            "algorithmic_bytes": int(nbytes[n]),
+            "GBps": round(gbps, 1),
+            "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
+            "frac_of_copy_ceiling": round(gbps / copy_gbps, 4),
+        }
+    dom = max(names, key=lambda n: statistics.mean(per_op_us[n]))
+    dom_gbps = op_table[dom]["GBps"]
+    traffic = None
+    if TRAFFIC_FILE.exists():
+        try:
+            tf = json.loads(TRAFFIC_FILE.read_text())
+            if tf.get("kernel_source_hash") == kernel_source_hash() and dom in tf.get("ops", {}):
+                traffic = tf["ops"][dom]["hbm_bytes_per_launch"]
+        except (ValueError, KeyError):
+            traffic = None
+    result = {
+        "metric": METRIC,
+        "value": round(step_bytes / (step_ms * 1e-3) / 1e9, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "payload_dtype": "bf16",
+        "data": "synthetic (seeded torch generator on the device; shapes and distributions of the pages' workloads)",
+        "config": {
+            "workload": "one pass of every hot-path operation: video-DiT Ulysses relayout P=4 (S=32760, H=24, "
+                        "D=128; QKV seq->head B=3, O head->seq B=1) + MLA decode DCP P=8 (T=128, H=128, Dv=512; "
+                        "LSE pack with 1% invalid statistics, strided-view exchange, stable combine) + packed THD "
+                        "P=8 (20 short + 2 long sequences, 131072 tokens, H=32, D=128; varlen QKV seq->head, O "
+                        "head->seq, causal combine of 8 KV-piece partials)",
+            "step_algorithmic_bytes": int(step_bytes),
+            "ops": names,
+        },
+        "roofline": {
+            "kernel": kern[dom],
+            "op": dom,
+            "bound": "hbm",
+            "achieved": dom_gbps,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(dom_gbps / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+        },
+        "ops": op_table,
+        "copy_ceiling": {"GBps": round(copy_gbps, 1), "frac_of_hbm_peak": round(copy_gbps / HBM_PEAK_GBPS, 4),
+                         "bytes": int(2 * src.numel() * 2), "kernel": "k_copy16"},
+        "device": {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
+                   "compute_units": props.multi_processor_count,
+                   "hbm_GiB": round(props.total_memory / 2**30, 1)},
+        "kernel_source_hash": kernel_source_hash(),
+        "wall_s": round(wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

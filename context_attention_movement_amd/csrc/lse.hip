@@ -36,10 +36,34 @@ __device__ __forceinline__ void pack_row_th(const Pack& a, uint32_t r, uint32_t 
     }
 }
 
+template <int W, bool GUARD>
+__device__ __forceinline__ void pack_o_tile(const Pack& a, uint32_t r, const char* src, char* dst, uint32_t v0)
+{
+    typedef typename VecOf<W>::type V;
+    V x[kVecsPerThread];
+#pragma unroll
+    for (int u = 0; u < kVecsPerThread; ++u) {
+        const uint32_t v = v0 + uint32_t(u * kThreads);
+        if (!GUARD || v < a.o_vecs) {
+            const uint32_t q = fdiv(v, a.div_cv);
+            const uint32_t k = v - q * a.cv;
+            uint64_t t, h;
+            pack_row_th(a, r, q, t, h);
+            const int64_t off = int64_t(t) * a.o_st_b + int64_t(h) * a.o_sh_b + int64_t(k) * W;
+            x[u] = *reinterpret_cast<const V*>(src + off);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < kVecsPerThread; ++u) {
+        const uint32_t v = v0 + uint32_t(u * kThreads);
+        if (!GUARD || v < a.o_vecs)
+            st<W>(dst, v, x[u]);
+    }
+}
+
 template <int W>
 __global__ __launch_bounds__(kThreads) void k_pack(Pack a)
 {
-    typedef typename VecOf<W>::type V;
     const uint32_t n_total = a.n_o_tiles + a.n_l_tiles;
     for (uint32_t tile = blockIdx.x; tile < n_total; tile += gridDim.x) {
         if (tile < a.n_o_tiles) {
@@ -50,26 +74,11 @@ __global__ __launch_bounds__(kThreads) void k_pack(Pack a)
             const uint32_t r = chunk - p * a.P;
             const char* src = static_cast<const char*>(a.out) + int64_t(p) * a.o_sp_b;
             char* dst = static_cast<char*>(a.packed) + uint64_t(chunk) * a.chunk_b;
-            const uint32_t v0 = ti * uint32_t(kTileVecs) + threadIdx.x;
-            V x[kVecsPerThread];
-#pragma unroll
-            for (int u = 0; u < kVecsPerThread; ++u) {
-                const uint32_t v = v0 + uint32_t(u * kThreads);
-                if (v < a.o_vecs) {
-                    const uint32_t q = fdiv(v, a.div_cv);
-                    const uint32_t k = v - q * a.cv;
-                    uint64_t t, h;
-                    pack_row_th(a, r, q, t, h);
-                    const int64_t off = int64_t(t) * a.o_st_b + int64_t(h) * a.o_sh_b + int64_t(k) * W;
-                    x[u] = *reinterpret_cast<const V*>(src + off);
-                }
-            }
-#pragma unroll
-            for (int u = 0; u < kVecsPerThread; ++u) {
-                const uint32_t v = v0 + uint32_t(u * kThreads);
-                if (v < a.o_vecs)
-                    st<W>(dst, v, x[u]);
-            }
+            const uint32_t vt = ti * uint32_t(kTileVecs);
+            if (vt + uint32_t(kTileVecs) <= a.o_vecs)
+                pack_o_tile<W, false>(a, r, src, dst, vt + threadIdx.x);
+            else
+                pack_o_tile<W, true>(a, r, src, dst, vt + threadIdx.x);
         } else {
             // L-region: one row per lane, LSE formed from the statistics
             const uint32_t lt = tile - a.n_o_tiles;
@@ -153,17 +162,26 @@ __device__ __forceinline__ bool causal_piece_ok(const int32_t* cu, int32_t nseq,
     return start < end && start <= k;
 }
 
+// Number of partial rows fetched together: the valid partials of a row are
+// compacted and loaded CH at a time with no branch between the loads (a short
+// last batch repeats its last valid row with weight 0, so an invalid partial's
+// row is never touched).
+#ifndef CAM_COMBINE_BATCH
+#define CAM_COMBINE_BATCH 8
+#endif
+constexpr int kCombineBatch = CAM_COMBINE_BATCH;
+
 template <int W, bool FP16, bool VARLEN>
 __global__ __launch_bounds__(kThreads) void k_combine(Combine a)
 {
     typedef typename VecOf<W>::type V;
     constexpr int E = W / 2;  // payload elements per vector
-    __shared__ float wbuf[kThreads];
+    constexpr int CH = kCombineBatch;
 
     const uint32_t G = 1u << a.g_log2;
     const uint32_t lane = threadIdx.x & 63u;
-    const uint32_t gl = lane & (G - 1u);             // lane within the row group
-    const uint32_t gfirst = threadIdx.x & ~(G - 1u);  // first thread of the group
+    const uint32_t gl = lane & (G - 1u);      // lane within the row group
+    const uint32_t gbase = lane & ~(G - 1u);  // first lane of the group in the wave
     const uint64_t gmask = G == 64u ? ~0ull : ((1ull << G) - 1ull);
     const uint32_t rows_per_block = kThreads >> a.g_log2;
 
@@ -191,26 +209,22 @@ __global__ __launch_bounds__(kThreads) void k_combine(Combine a)
         float M = valid ? L : -__builtin_inff();
         for (uint32_t off = G >> 1; off > 0; off >>= 1)
             M = fmaxf(M, __shfl_xor(M, int(off), int(G)));
-        const uint64_t vmask = (__ballot(valid) >> (lane & ~(G - 1u))) & gmask;
+        const uint64_t vmask = (__ballot(valid) >> gbase) & gmask;
         const float w = valid ? expf(L - M) : 0.0f;
         float Z = w;
         for (uint32_t off = G >> 1; off > 0; off >>= 1)
             Z += __shfl_xor(Z, int(off), int(G));
-        __syncthreads();  // previous rows' readers are done with wbuf
-        wbuf[threadIdx.x] = w;
-        __syncthreads();
         if (!active)
             continue;
 
         char* orow = static_cast<char*>(a.out) + int64_t(t) * a.o_st_b + int64_t(h) * a.o_sh_b;
         if (vmask == 0) {
             // no valid partial: +0 everywhere, -inf LSE
-            V zero;
             Halves<W> zh;
 #pragma unroll
             for (int e = 0; e < E; ++e)
                 zh.h[e] = 0;
-            zero = __builtin_bit_cast(V, zh);
+            const V zero = __builtin_bit_cast(V, zh);
             for (uint32_t k = gl; k < a.cv; k += G)
                 *reinterpret_cast<V*>(orow + int64_t(k) * W) = zero;
             if (gl == 0 && a.lse_out)
@@ -219,36 +233,50 @@ __global__ __launch_bounds__(kThreads) void k_combine(Combine a)
         }
         const float invZ = 1.0f / Z;
         const char* prow = static_cast<const char*>(a.po) + int64_t(t) * a.po_st_b + int64_t(h) * a.po_sh_b;
-        for (uint32_t k = gl; k < a.cv; k += G) {
+        // Every lane of the group runs every iteration, so the weight shuffles
+        // below always read active lanes; a lane past the row's last vector
+        // re-reads the last vector (a valid address) and stores nothing.
+        for (uint32_t kb = 0; kb < a.cv; kb += G) {
+            const uint32_t k = kb + gl < a.cv ? kb + gl : a.cv - 1;
             float acc[E];
 #pragma unroll
             for (int e = 0; e < E; ++e)
                 acc[e] = 0.0f;
-            for (uint32_t p0 = 0; p0 < a.P; p0 += 8) {
-                V x[8];
+            const char* pk = prow + int64_t(k) * W;
+            uint64_t m = vmask;
+            while (m) {
+                int idx[CH];
+                float wv[CH];
+                int last = 0;
 #pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const uint32_t p = p0 + u;
-                    if (p < a.P && ((vmask >> p) & 1ull))
-                        x[u] = *reinterpret_cast<const V*>(prow + int64_t(p) * a.po_sp_b + int64_t(k) * W);
+                for (int u = 0; u < CH; ++u) {
+                    const bool take = m != 0;
+                    const int p = take ? __builtin_ctzll(m) : last;
+                    m = take ? (m & (m - 1)) : m;
+                    idx[u] = p;
+                    last = p;
+                    const float wp = __shfl(w, int(gbase + uint32_t(p)), 64);
+                    wv[u] = take ? wp : 0.0f;
                 }
+                V x[CH];
 #pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const uint32_t p = p0 + u;
-                    if (p < a.P && ((vmask >> p) & 1ull)) {
-                        const float wp = wbuf[gfirst + p];
-                        const Halves<W> xh = __builtin_bit_cast(Halves<W>, x[u]);
+                for (int u = 0; u < CH; ++u)
+                    x[u] = *reinterpret_cast<const V*>(pk + int64_t(idx[u]) * a.po_sp_b);
 #pragma unroll
-                        for (int e = 0; e < E; ++e)
-                            acc[e] = fmaf(wp, half_to_f32<FP16>(xh.h[e]), acc[e]);
-                    }
+                for (int u = 0; u < CH; ++u) {
+                    const Halves<W> xh = __builtin_bit_cast(Halves<W>, x[u]);
+#pragma unroll
+                    for (int e = 0; e < E; ++e)
+                        acc[e] = fmaf(wv[u], half_to_f32<FP16>(xh.h[e]), acc[e]);
                 }
             }
-            Halves<W> oh;
+            if (kb + gl < a.cv) {
+                Halves<W> oh;
 #pragma unroll
-            for (int e = 0; e < E; ++e)
-                oh.h[e] = f32_to_half<FP16>(acc[e] * invZ);
-            *reinterpret_cast<V*>(orow + int64_t(k) * W) = __builtin_bit_cast(V, oh);
+                for (int e = 0; e < E; ++e)
+                    oh.h[e] = f32_to_half<FP16>(acc[e] * invZ);
+                *reinterpret_cast<V*>(orow + int64_t(k) * W) = __builtin_bit_cast(V, oh);
+            }
         }
         if (gl == 0 && a.lse_out)
             a.lse_out[int64_t(t) * a.lo_st + int64_t(h) * a.lo_sh] = M + logf(Z);

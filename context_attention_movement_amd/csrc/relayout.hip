@@ -18,10 +18,40 @@
 
 namespace cam {
 
+// Move one tile of a dense slab: vectors v0 + u*kThreads, u < kVecsPerThread.
+// GUARD = false is the straight-line path for tiles that lie wholly inside the
+// slab: every load is issued before any store and no branch separates them,
+// so each lane keeps kVecsPerThread requests in flight.
+template <int W, bool S2H, bool GUARD>
+__device__ __forceinline__ void dense_tile(const DenseRelayout& a, uint64_t head_base, uint64_t seq_base,
+                                           uint32_t v0)
+{
+    typedef typename VecOf<W>::type V;
+    V x[kVecsPerThread];
+    uint64_t dst_off[kVecsPerThread];
+#pragma unroll
+    for (int u = 0; u < kVecsPerThread; ++u) {
+        const uint32_t v = v0 + uint32_t(u * kThreads);
+        if (!GUARD || v < a.slab_vecs) {
+            const uint32_t s = fdiv(v, a.div_c);
+            const uint32_t k = v - s * a.c;
+            const uint64_t so = seq_base + uint64_t(s) * a.Pc + k;
+            const uint64_t ho = head_base + v;
+            x[u] = ld<W>(a.src, S2H ? so : ho);
+            dst_off[u] = S2H ? ho : so;
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < kVecsPerThread; ++u) {
+        const uint32_t v = v0 + uint32_t(u * kThreads);
+        if (!GUARD || v < a.slab_vecs)
+            st<W>(a.dst, dst_off[u], x[u]);
+    }
+}
+
 template <int W, bool S2H>
 __global__ __launch_bounds__(kThreads) void k_dense_relayout(DenseRelayout a)
 {
-    typedef typename VecOf<W>::type V;
     for (uint32_t tile = blockIdx.x; tile < a.n_tiles; tile += gridDim.x) {
         const uint32_t slab = fdiv(tile, a.div_tps);
         const uint32_t ti = tile - slab * a.tiles_per_slab;
@@ -31,28 +61,11 @@ __global__ __launch_bounds__(kThreads) void k_dense_relayout(DenseRelayout a)
         const uint32_t b = rb - r * a.B;
         const uint64_t head_base = uint64_t(slab) * a.slab_vecs;
         const uint64_t seq_base = (uint64_t(j * a.B + b) * a.Sp * a.P + r) * a.c;
-        const uint32_t v0 = ti * uint32_t(kTileVecs) + threadIdx.x;
-
-        V x[kVecsPerThread];
-        uint64_t dst_off[kVecsPerThread];
-#pragma unroll
-        for (int u = 0; u < kVecsPerThread; ++u) {
-            const uint32_t v = v0 + uint32_t(u * kThreads);
-            if (v < a.slab_vecs) {
-                const uint32_t s = fdiv(v, a.div_c);
-                const uint32_t k = v - s * a.c;
-                const uint64_t so = seq_base + uint64_t(s) * a.Pc + k;
-                const uint64_t ho = head_base + v;
-                x[u] = ld<W>(a.src, S2H ? so : ho);
-                dst_off[u] = S2H ? ho : so;
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < kVecsPerThread; ++u) {
-            const uint32_t v = v0 + uint32_t(u * kThreads);
-            if (v < a.slab_vecs)
-                st<W>(a.dst, dst_off[u], x[u]);
-        }
+        const uint32_t vt = ti * uint32_t(kTileVecs);
+        if (vt + uint32_t(kTileVecs) <= a.slab_vecs)
+            dense_tile<W, S2H, false>(a, head_base, seq_base, vt + threadIdx.x);
+        else
+            dense_tile<W, S2H, true>(a, head_base, seq_base, vt + threadIdx.x);
     }
 }
 
@@ -87,10 +100,40 @@ __device__ int64_t varlen_seq_row(const VarlenRelayout& a, uint32_t t, uint32_t 
     return row * int64_t(a.Pc) + int64_t(r) * a.c;
 }
 
+template <int W, bool S2H, bool GUARD>
+__device__ __forceinline__ void varlen_tile(const VarlenRelayout& a, const int64_t* row_off, uint64_t head_base,
+                                            uint32_t vb, uint32_t ve, uint32_t row0)
+{
+    typedef typename VecOf<W>::type V;
+    V x[kVecsPerThread];
+    uint64_t dst_off[kVecsPerThread];
+    bool live[kVecsPerThread];
+#pragma unroll
+    for (int u = 0; u < kVecsPerThread; ++u) {
+        const uint32_t v = vb + threadIdx.x + uint32_t(u * kThreads);
+        live[u] = !GUARD || v < ve;
+        if (live[u]) {
+            const uint32_t t = fdiv(v, a.div_c);
+            const uint32_t k = v - t * a.c;
+            const int64_t base = row_off[t - row0];
+            live[u] = !GUARD || base >= 0;
+            if (live[u]) {
+                const uint64_t so = uint64_t(base) + k;
+                const uint64_t ho = head_base + v;
+                x[u] = ld<W>(a.src, S2H ? so : ho);
+                dst_off[u] = S2H ? ho : so;
+            }
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < kVecsPerThread; ++u)
+        if (live[u])
+            st<W>(a.dst, dst_off[u], x[u]);
+}
+
 template <int W, bool S2H>
 __global__ __launch_bounds__(kThreads) void k_varlen_relayout(VarlenRelayout a)
 {
-    typedef typename VecOf<W>::type V;
     // sequence-side offset of every row the tile touches (a tile spans at most
     // kTileVecs + 1 rows when rows are one vector long)
     __shared__ int64_t row_off[kTileVecs + 1];
@@ -106,56 +149,49 @@ __global__ __launch_bounds__(kThreads) void k_varlen_relayout(VarlenRelayout a)
         const uint32_t row0 = fdiv(vb, a.div_c);
         const uint32_t nrows = fdiv(ve - 1, a.div_c) - row0 + 1;
         __syncthreads();  // the previous tile's readers are done with row_off
-        for (uint32_t i = threadIdx.x; i < nrows; i += kThreads)
-            row_off[i] = varlen_seq_row(a, row0 + i, r, b);
-        __syncthreads();
-
-        V x[kVecsPerThread];
-        uint64_t dst_off[kVecsPerThread];
-        bool live[kVecsPerThread];
-#pragma unroll
-        for (int u = 0; u < kVecsPerThread; ++u) {
-            const uint32_t v = vb + threadIdx.x + uint32_t(u * kThreads);
-            live[u] = false;
-            if (v < ve) {
-                const uint32_t t = fdiv(v, a.div_c);
-                const uint32_t k = v - t * a.c;
-                const int64_t base = row_off[t - row0];
-                if (base >= 0) {
-                    const uint64_t so = uint64_t(base) + k;
-                    const uint64_t ho = head_base + v;
-                    x[u] = ld<W>(a.src, S2H ? so : ho);
-                    dst_off[u] = S2H ? ho : so;
-                    live[u] = true;
-                }
-            }
+        bool rows_ok = true;
+        for (uint32_t i = threadIdx.x; i < nrows; i += kThreads) {
+            const int64_t off = varlen_seq_row(a, row0 + i, r, b);
+            row_off[i] = off;
+            rows_ok = rows_ok && off >= 0;
         }
+        // full tile whose every row the plan places inside the buffer: no guards
+        const bool fast = __syncthreads_and(rows_ok && ve - vb == uint32_t(kTileVecs));
+        if (fast)
+            varlen_tile<W, S2H, false>(a, row_off, head_base, vb, ve, row0);
+        else
+            varlen_tile<W, S2H, true>(a, row_off, head_base, vb, ve, row0);
+    }
+}
+
+template <bool GUARD>
+__device__ __forceinline__ void copy_tile(const Copy& a, uint64_t v0)
+{
+    typedef typename VecOf<16>::type V;
+    V x[kVecsPerThread];
 #pragma unroll
-        for (int u = 0; u < kVecsPerThread; ++u)
-            if (live[u])
-                st<W>(a.dst, dst_off[u], x[u]);
+    for (int u = 0; u < kVecsPerThread; ++u) {
+        const uint64_t v = v0 + uint64_t(u * kThreads);
+        if (!GUARD || v < a.n_vecs)
+            x[u] = ld<16>(a.src, v);
+    }
+#pragma unroll
+    for (int u = 0; u < kVecsPerThread; ++u) {
+        const uint64_t v = v0 + uint64_t(u * kThreads);
+        if (!GUARD || v < a.n_vecs)
+            st<16>(a.dst, v, x[u]);
     }
 }
 
 __global__ __launch_bounds__(kThreads) void k_copy16(Copy a)
 {
-    typedef typename VecOf<16>::type V;
     const uint64_t n_tiles = (a.n_vecs + kTileVecs - 1) / kTileVecs;
     for (uint64_t tile = blockIdx.x; tile < n_tiles; tile += gridDim.x) {
-        const uint64_t v0 = tile * kTileVecs + threadIdx.x;
-        V x[kVecsPerThread];
-#pragma unroll
-        for (int u = 0; u < kVecsPerThread; ++u) {
-            const uint64_t v = v0 + uint64_t(u * kThreads);
-            if (v < a.n_vecs)
-                x[u] = ld<16>(a.src, v);
-        }
-#pragma unroll
-        for (int u = 0; u < kVecsPerThread; ++u) {
-            const uint64_t v = v0 + uint64_t(u * kThreads);
-            if (v < a.n_vecs)
-                st<16>(a.dst, v, x[u]);
-        }
+        const uint64_t vt = tile * kTileVecs;
+        if (vt + kTileVecs <= a.n_vecs)
+            copy_tile<false>(a, vt + threadIdx.x);
+        else
+            copy_tile<true>(a, vt + threadIdx.x);
     }
 }
 
