@@ -92,18 +92,25 @@ class Workload:
         self.v_qkv_out = torch.empty((P, 3, S, H // P, D), dtype=bf, device=dev)
         self.v_o = randn((P, 1, S, H // P, D))
         self.v_o_out = torch.empty((P, 1, S // P, H, D), dtype=bf, device=dev)
-        # MLA decode, P = 8
+        # MLA decode, P = 8; NSETS independent buffer sets (> 1 GiB together) so
+        # that repeated calls never find their inputs in the 256 MB Infinity Cache
         self.mP, self.mT, self.mH, self.mDv = 8, 128, 128, 512
         P, T, H, Dv = self.mP, self.mT, self.mH, self.mDv
-        self.m_out, self.m_max, self.m_sum, bad = synth.dcp_partials(P, T, H, Dv, synth.BASE_SEED + 3, device=dev)
+        self.NSETS = 8
         n = cam.lse_pack_bytes(P, T, H, Dv, 1)
-        self.m_packed = [torch.empty(n, dtype=torch.uint8, device=dev) for _ in range(2)]
         rows = T * H // P
-        self.m_comb = torch.empty((P * rows, Dv), dtype=bf, device=dev)
-        self.m_lse = torch.empty(P * rows, dtype=torch.float32, device=dev)
-        for pk in self.m_packed:
-            cam.lse_pack(self.m_out, self.m_max, self.m_sum, 1, packed=pk)
-        self.m_invalid = int(bad.size)
+        self.m_sets = []
+        for i in range(self.NSETS):
+            out, mx, sm, bad = synth.dcp_partials(P, T, H, Dv, synth.BASE_SEED + 3 + 1000 * i, device=dev)
+            packed_in = torch.empty(n, dtype=torch.uint8, device=dev)
+            cam.lse_pack(out, mx, sm, 1, packed=packed_in)
+            self.m_sets.append({
+                "out": out, "max": mx, "sum": sm, "invalid": int(bad.size),
+                "packed_out": torch.empty(n, dtype=torch.uint8, device=dev),   # written by the pack
+                "packed_in": packed_in,                                         # read by the combine
+                "comb": torch.empty((P * rows, Dv), dtype=bf, device=dev),
+                "lse": torch.empty(P * rows, dtype=torch.float32, device=dev)})
+        self.m_invalid = self.m_sets[0]["invalid"]
         # packed THD, P = 8
         self.tP, self.tH, self.tD = 8, 32, 128
         P, H, D = self.tP, self.tH, self.tD
@@ -143,17 +150,21 @@ class Workload:
             "lse_combine_varlen_thd": self.t_admitted * tH * (tD * 2 + 4) + tT * tH * (tD * 2 + 4),
         }
 
-    def ops(self):
+    def ops(self, k=None):
+        """The step's operations as (name, kernel, callable); `k` selects the
+        MLA buffer set (defaults to the step index)."""
         cam = self.cam
-        k = self.step_index
+        k = self.step_index if k is None else k
+        ms = self.m_sets[k % self.NSETS]
 
         def pack():
-            cam.lse_pack(self.m_out, self.m_max, self.m_sum, 1, packed=self.m_packed[k % 2])
+            cam.lse_pack(ms["out"], ms["max"], ms["sum"], 1, packed=ms["packed_out"])
 
         def combine():
-            # reads the packed buffer written one step earlier (the exchange is a view)
-            cam.lse_combine_packed(self.m_packed[(k + 1) % 2], self.mP, self.mT, self.mH, self.mDv, 1,
-                                   out=self.m_comb, lse_out=self.m_lse)
+            # the exchange is a strided view of a packed buffer; this set's
+            # input was packed before the timed region and is cold here
+            cam.lse_combine_packed(ms["packed_in"], self.mP, self.mT, self.mH, self.mDv, 1,
+                                   out=ms["comb"], lse_out=ms["lse"])
 
         return [
             ("relayout_seq_to_head_video_p4_qkv", "k_dense_relayout<16, true>",
@@ -161,12 +172,12 @@ class Workload:
             ("relayout_head_to_seq_video_p4_o", "k_dense_relayout<16, false>",
              lambda: cam.ulysses_head_to_seq(self.v_o, self.vP, out=self.v_o_out)),
             ("lse_pack_mla", "k_pack<16>", pack),
-            ("lse_combine_mla", "k_combine<16, false, false>", combine),
+            ("lse_combine_mla", "k_combine<16, false, false, 2>", combine),
             ("relayout_seq_to_head_varlen_thd_qkv", "k_varlen_relayout<16, true>",
              lambda: cam.ulysses_seq_to_head_varlen(self.t_qkv, self.t_plan, 3, out=self.t_qkv_out)),
             ("relayout_head_to_seq_varlen_thd_o", "k_varlen_relayout<16, false>",
              lambda: cam.ulysses_head_to_seq_varlen(self.t_o, self.t_plan, out=self.t_o_out)),
-            ("lse_combine_varlen_thd", "k_combine<16, false, true>",
+            ("lse_combine_varlen_thd", "k_combine<16, false, true, 1>",
              lambda: cam.lse_combine_varlen(self.t_part, self.t_lse, self.t_cu_dev, out=self.t_comb,
                                             lse_out=self.t_comb_lse)),
         ]
@@ -201,9 +212,9 @@ def cpu_baseline(w, budget_s: float = 25.0):
     parts.append(f"video P=4 QKV seq->head (full, {dt:.2f} s)")
     del x
     # 2) MLA pack and combine, whole workload
-    ob = bits(w.m_out)
-    m = w.m_max.cpu().numpy()
-    s = w.m_sum.cpu().numpy()
+    ob = bits(w.m_sets[0]["out"])
+    m = w.m_sets[0]["max"].cpu().numpy()
+    s = w.m_sets[0]["sum"].cpu().numpy()
     t0 = time.perf_counter()
     packed = oracle.lse_pack(ob, m, s, 1)
     dt = time.perf_counter() - t0
@@ -216,28 +227,34 @@ def cpu_baseline(w, budget_s: float = 25.0):
     done_bytes += w.op_bytes()["lse_combine_mla"]
     secs += dt
     parts.append(f"MLA combine (full, {dt:.2f} s)")
-    # 3) THD combine on a token window sized to the remaining budget
-    remaining = max(2.0, budget_s - secs)
-    win = 256
+    # 3) THD Q/K/V varlen seq->head, whole operand
+    x = bits(w.t_qkv)
+    t0 = time.perf_counter()
+    oracle.varlen_seq_to_head(x, w.t_cu, w.tP, 3, w.tH, w.tD)
+    dt = time.perf_counter() - t0
+    done_bytes += w.op_bytes()["relayout_seq_to_head_varlen_thd_qkv"]
+    secs += dt
+    parts.append(f"THD QKV varlen seq->head (full, {dt:.2f} s)")
+    del x
+    # 4) THD causal combine on a token window sized to the remaining budget
     a = int(w.t_cu[3])
+    probe = 256
+    po = bits(w.t_part[:, a:a + probe])
+    pl = w.t_lse[:, a:a + probe].cpu().numpy()
+    t0 = time.perf_counter()
+    oracle.lse_combine(po, pl, cu=w.t_cu, t_begin=a)
+    per_token = (time.perf_counter() - t0) / probe
+    remaining = max(1.0, budget_s - secs)
+    win = int(min(w.tT - a, max(probe, remaining / per_token)))
     po = bits(w.t_part[:, a:a + win])
     pl = w.t_lse[:, a:a + win].cpu().numpy()
     t0 = time.perf_counter()
     oracle.lse_combine(po, pl, cu=w.t_cu, t_begin=a)
     dt = time.perf_counter() - t0
     frac = win / w.tT
-    # scale the window to a bounded share of the remaining budget
-    reps = max(1, min(64, int(remaining / max(dt, 1e-3))))
-    win2 = min(w.tT - a, win * reps)
-    po = bits(w.t_part[:, a:a + win2])
-    pl = w.t_lse[:, a:a + win2].cpu().numpy()
-    t0 = time.perf_counter()
-    oracle.lse_combine(po, pl, cu=w.t_cu, t_begin=a)
-    dt = time.perf_counter() - t0
-    frac = win2 / w.tT
     done_bytes += w.op_bytes()["lse_combine_varlen_thd"] * frac
     secs += dt
-    parts.append(f"THD combine on tokens [{a}, {a + win2}) ({dt:.2f} s, {frac:.2%} of the batch)")
+    parts.append(f"THD causal combine on tokens [{a}, {a + win}) ({dt:.2f} s, {frac:.2%} of the batch)")
     return {
         "value": round(done_bytes / secs / 1e9, 4),
         "unit": "GB/s",
@@ -246,7 +263,7 @@ def cpu_baseline(w, budget_s: float = 25.0):
         "seconds": round(secs, 2),
         "sample": "; ".join(parts) + ". Single-threaded C oracle (fp64), same synthetic inputs "
                   "downloaded from the GPU; GB/s = the sample's algorithmic bytes / oracle time.",
-        "cpu": platform.processor() or _cpu_model(),
+        "cpu": _cpu_model(),
     }
 
 
@@ -276,10 +293,10 @@ OP_KERNELS = [  # (op, kernel name fragment as rocprofv3 reports it)
     ("relayout_seq_to_head_video_p4_qkv", "k_dense_relayout<16, true>"),
     ("relayout_head_to_seq_video_p4_o", "k_dense_relayout<16, false>"),
     ("lse_pack_mla", "k_pack<16>"),
-    ("lse_combine_mla", "k_combine<16, false, false>"),
+    ("lse_combine_mla", "k_combine<16, false, false, 2>"),
     ("relayout_seq_to_head_varlen_thd_qkv", "k_varlen_relayout<16, true>"),
     ("relayout_head_to_seq_varlen_thd_o", "k_varlen_relayout<16, false>"),
-    ("lse_combine_varlen_thd", "k_combine<16, false, true>"),
+    ("lse_combine_varlen_thd", "k_combine<16, false, true, 1>"),
 ]
 COPY_KERNEL = "k_copy16"
 COPY_BYTES = 3 * 32760 * 24 * 128 * 2  # the video Q/K/V operand copied for the ceiling (each way)
@@ -352,8 +369,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--calls", type=int, default=20, help="back-to-back calls per operation for µs/call")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=25.0)
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for the CPU baseline")
     ap.add_argument("--summarize-rocprof", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--summary-out", default=None)
     ap.add_argument("--command", default="")
@@ -377,67 +395,84 @@ def main():
     torch.cuda.set_device(0)
     props = torch.cuda.get_device_properties(0)
     w = Workload(torch, cam, synth)
-    ops = w.ops
     nbytes = w.op_bytes()
+    names = [n for n, _, _ in w.ops()]
+    kern = {n: k for n, k, _ in w.ops()}
     stream = torch.cuda.Stream()
+
+    # ---- timed region: K steps, every operation once per step, events around each
     with torch.cuda.stream(stream):
         for _ in range(args.warmup):
-            for _, _, fn in ops():
+            for _, _, fn in w.ops():
                 fn()
             w.step_index += 1
-        torch.cuda.synchronize()
-        names = [n for n, _, _ in ops()]
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for k in range(args.steps):
             ev = evs[k]
             ev[0].record(stream)
-            for i, (_, _, fn) in enumerate(ops()):
+            for i, (_, _, fn) in enumerate(w.ops()):
                 fn()
                 ev[i + 1].record(stream)
             w.step_index += 1
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-    per_op_us = {n: [] for n in names}
-    for k in range(args.steps):
-        for i, n in enumerate(names):
-            per_op_us[n].append(evs[k][i].elapsed_time(evs[k][i + 1]) * 1000.0)
+    in_step = {n: [evs[k][i].elapsed_time(evs[k][i + 1]) * 1000.0 for k in range(args.steps)]
+               for i, n in enumerate(names)}
     step_ms = wall * 1000.0 / args.steps
     step_bytes = sum(nbytes.values())
 
-    # plain-copy ceiling on the video Q/K/V operand size (outside the timed region)
-    cstream = torch.cuda.Stream()
-    with torch.cuda.stream(cstream):
+    # ---- µs per call, each operation alone: back-to-back calls between two
+    # events on the launch stream (the MLA calls rotate over the buffer sets)
+    iso_us = {}
+    with torch.cuda.stream(stream):
+        for i, n in enumerate(names):
+            for j in range(3):
+                w.ops(k=j)[i][2]()
+            fns = [w.ops(k=j)[i][2] for j in range(args.calls)]
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for fn in fns:
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            iso_us[n] = e0.elapsed_time(e1) * 1000.0 / args.calls
+
+    # ---- plain-copy ceiling on the video Q/K/V operand size
+    with torch.cuda.stream(stream):
         src, dst = w.v_qkv, w.v_qkv_out
         for _ in range(3):
             cam.copy(src, dst)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(cstream)
+        e0.record(stream)
         for _ in range(10):
             cam.copy(src, dst)
-        e1.record(cstream)
+        e1.record(stream)
         torch.cuda.synchronize()
-    copy_us = e0.elapsed_time(e1) * 100.0
-    copy_gbps = 2 * src.numel() * 2 / copy_us / 1e3
+    copy_bytes = 2 * src.numel() * src.element_size()
+    copy_gbps = copy_bytes / (e0.elapsed_time(e1) * 100.0) / 1e3
 
     op_table = {}
-    kern = dict((n, k) for n, k, _ in ops())
     for n in names:
-        us = statistics.mean(per_op_us[n])
+        us = iso_us[n]
         gbps = nbytes[n] / us / 1e3
+        mean_step = statistics.mean(in_step[n])
         op_table[n] = {
             "kernel": kern[n],
-            "us_per_call_mean": round(us, 2),
-            "us_per_call_median": round(statistics.median(per_op_us[n]), 2),
-            "us_per_call_p95": round(sorted(per_op_us[n])[int(0.95 * (len(per_op_us[n]) - 1))], 2),
             "algorithmic_bytes": int(nbytes[n]),
+            "us_per_call": round(us, 2),
             "GBps": round(gbps, 1),
             "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
             "frac_of_copy_ceiling": round(gbps / copy_gbps, 4),
+            "in_step_us_mean": round(mean_step, 2),
+            "in_step_us_median": round(statistics.median(in_step[n]), 2),
+            "in_step_us_p95": round(sorted(in_step[n])[int(0.95 * (len(in_step[n]) - 1))], 2),
+            "in_step_GBps": round(nbytes[n] / mean_step / 1e3, 1),
         }
-    dom = max(names, key=lambda n: statistics.mean(per_op_us[n]))
-    dom_gbps = op_table[dom]["GBps"]
+    dom = max(names, key=lambda n: statistics.mean(in_step[n]))
+    dom_us = statistics.mean(in_step[dom])
+    dom_gbps = nbytes[dom] / dom_us / 1e3
     traffic = None
     if TRAFFIC_FILE.exists():
         try:
@@ -473,25 +508,26 @@ def main():
             "kernel": kern[dom],
             "op": dom,
             "bound": "hbm",
-            "achieved": dom_gbps,
+            "achieved": round(dom_gbps, 1),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(dom_gbps / HBM_PEAK_GBPS, 4),
             "traffic": traffic,
+            "avg_launch_us": round(dom_us, 2),
+            "algorithmic_bytes_per_launch": int(nbytes[dom]),
         },
         "ops": op_table,
         "copy_ceiling": {"GBps": round(copy_gbps, 1), "frac_of_hbm_peak": round(copy_gbps / HBM_PEAK_GBPS, 4),
-                         "bytes": int(2 * src.numel() * 2), "kernel": "k_copy16"},
+                         "bytes": int(copy_bytes), "kernel": "k_copy16"},
         "device": {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
                    "compute_units": props.multi_processor_count,
                    "hbm_GiB": round(props.total_memory / 2**30, 1)},
         "kernel_source_hash": kernel_source_hash(),
-        "wall_s": round(wall, 3),
+        "timing": "value and ms_per_step: host clock around the K synchronized steps; ops[*].us_per_call: "
+                  f"{args.calls} back-to-back calls of that operation alone between two HIP events; "
+                  "ops[*].in_step_*: HIP events around the operation inside the steps",
     }
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
-    else:
-        result["cpu_baseline"] = None
+    result["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(w, args.cpu_budget)
     print(json.dumps(result), flush=True)
 
 

@@ -374,9 +374,15 @@ cam_status combine(const char* op, const CombineIn& c, void* stream)
     a.div_H = make_fastdiv(a.H);
     a.n_rows = uint64_t(n_rows);
     a.cv = uint32_t(row_b / a.width);
-    const uint32_t g = pow2ceil(a.cv < 64 ? (a.cv ? a.cv : 1) : 64);
-    const uint32_t gp = pow2ceil(a.P);
-    a.g_log2 = log2u(g > gp ? g : gp);
+    a.g_log2 = log2u(pow2ceil(a.cv < 64 ? (a.cv ? a.cv : 1) : 64));
+    a.gp_log2 = log2u(pow2ceil(a.P));
+    // rows per tile (measured per row width), at least one per payload group
+    uint32_t rows = uint64_t(a.cv) * a.width >= 512 ? CAM_COMBINE_ROWS_WIDE : CAM_COMBINE_ROWS_NARROW;
+    const uint32_t groups = uint32_t(kThreads) >> a.g_log2;
+    if (rows < groups)
+        rows = groups;
+    a.rows_per_tile = rows;
+    a.n_tiles = (uint64_t(n_rows) + rows - 1) / rows;
     a.cu = c.cu;
     a.nseq = int32_t(c.nseq);
     a.fp16 = c.dt == CAM_FP16;

@@ -24,16 +24,40 @@ __device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv& f)
     return uint32_t((uint64_t(__umulhi(n, f.m)) + n) >> f.l);
 }
 
-template <int W>
-__device__ __forceinline__ typename VecOf<W>::type ld(const void* base, uint64_t vec_index)
+// Cache policy of the streaming accesses.  Every byte these kernels move is
+// touched exactly once, so each access may carry the non-temporal hint (no
+// reuse expected).  Which side profits depends on the access pattern and was
+// chosen per kernel by measurement; a policy is two bits: 1 = non-temporal
+// loads, 2 = non-temporal stores.
+template <int W, bool NT>
+__device__ __forceinline__ typename VecOf<W>::type ld_at(const void* p)
 {
-    return reinterpret_cast<const typename VecOf<W>::type*>(base)[vec_index];
+    const typename VecOf<W>::type* q = reinterpret_cast<const typename VecOf<W>::type*>(p);
+    if (NT)
+        return __builtin_nontemporal_load(q);
+    return *q;
 }
 
-template <int W>
+template <int W, bool NT>
+__device__ __forceinline__ void st_at(void* p, typename VecOf<W>::type v)
+{
+    typename VecOf<W>::type* q = reinterpret_cast<typename VecOf<W>::type*>(p);
+    if (NT)
+        __builtin_nontemporal_store(v, q);
+    else
+        *q = v;
+}
+
+template <int W, bool NT>
+__device__ __forceinline__ typename VecOf<W>::type ld(const void* base, uint64_t vec_index)
+{
+    return ld_at<W, NT>(static_cast<const char*>(base) + vec_index * W);
+}
+
+template <int W, bool NT>
 __device__ __forceinline__ void st(void* base, uint64_t vec_index, typename VecOf<W>::type v)
 {
-    reinterpret_cast<typename VecOf<W>::type*>(base)[vec_index] = v;
+    st_at<W, NT>(static_cast<char*>(base) + vec_index * W, v);
 }
 
 // bf16 <-> fp32.  bf16 is the upper half of an fp32 word; narrowing rounds to
@@ -67,14 +91,14 @@ __device__ __forceinline__ uint32_t f32_to_fp16_bits(float f)
 // kernels walk their tiles with a grid stride.
 template <typename Args>
 inline cam_status launch(const void* fn, const Args& a, uint64_t n_tiles, void* stream,
-                         const char* what)
+                         const char* what, uint64_t lds_bytes = 0)
 {
     if (n_tiles == 0)
         return CAM_OK;
     const uint32_t grid = uint32_t(n_tiles < kMaxGrid ? n_tiles : kMaxGrid);
     Args copy = a;
     void* args[] = {&copy};
-    hipError_t e = hipLaunchKernel(fn, dim3(grid), dim3(kThreads), args, 0,
+    hipError_t e = hipLaunchKernel(fn, dim3(grid), dim3(kThreads), args, size_t(lds_bytes),
                                    reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess)
         return set_error(CAM_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));

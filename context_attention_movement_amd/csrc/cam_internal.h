@@ -7,7 +7,7 @@
 
 #include <stdint.h>
 
-#include "../../include/cam.h"
+#include "cam.h"
 
 namespace cam {
 
@@ -132,7 +132,10 @@ struct Combine {
     FastDiv div_H;
     uint64_t n_rows;        // T*H
     uint32_t cv;            // vectors per row
-    uint32_t g_log2;        // lanes per row = 1 << g_log2 (>= P, <= 64)
+    uint32_t g_log2;        // payload lanes per row = 1 << g_log2 (<= 64)
+    uint32_t gp_log2;       // statistics lanes per row = 1 << gp_log2 (>= P, <= 64)
+    uint32_t rows_per_tile; // rows per workgroup tile
+    uint64_t n_tiles;
     const int32_t* cu;      // non-null: causal piece gating (varlen)
     int32_t nseq;
     int width;
@@ -158,12 +161,50 @@ cam_status set_error(cam_status s, const char* fmt, ...);
 void clear_error();
 
 // Launch shape shared by all streaming kernels.
-constexpr int kThreads = 256;
+#ifndef CAM_THREADS
+#define CAM_THREADS 256
+#endif
+constexpr int kThreads = CAM_THREADS;
 #ifndef CAM_VECS_PER_THREAD
 #define CAM_VECS_PER_THREAD 4
 #endif
 constexpr int kVecsPerThread = CAM_VECS_PER_THREAD;
 constexpr int kTileVecs = kThreads * kVecsPerThread;
+// Non-temporal policy per kernel (bit 0: loads, bit 1: stores), chosen by
+// measurement on MI355X.
+#ifndef CAM_NT_SEQ_TO_HEAD
+#define CAM_NT_SEQ_TO_HEAD 3
+#endif
+#ifndef CAM_NT_HEAD_TO_SEQ
+#define CAM_NT_HEAD_TO_SEQ 2
+#endif
+#ifndef CAM_NT_VARLEN_SEQ_TO_HEAD
+#define CAM_NT_VARLEN_SEQ_TO_HEAD 3
+#endif
+#ifndef CAM_NT_VARLEN_HEAD_TO_SEQ
+#define CAM_NT_VARLEN_HEAD_TO_SEQ 2
+#endif
+#ifndef CAM_NT_PACK
+#define CAM_NT_PACK 3
+#endif
+#ifndef CAM_NT_COMBINE
+#define CAM_NT_COMBINE 3
+#endif
+#ifndef CAM_NT_COPY
+#define CAM_NT_COPY 3
+#endif
+// Combine tiling (measured on MI355X): rows per workgroup tile for rows of
+// >= 512 bytes and for shorter rows, and partial rows loaded per batch.
+#ifndef CAM_COMBINE_ROWS_WIDE
+#define CAM_COMBINE_ROWS_WIDE 8
+#endif
+#ifndef CAM_COMBINE_ROWS_NARROW
+#define CAM_COMBINE_ROWS_NARROW 32
+#endif
+#ifndef CAM_COMBINE_BATCH
+#define CAM_COMBINE_BATCH 4
+#endif
+constexpr int kCombineBatch = CAM_COMBINE_BATCH;
 #ifndef CAM_MAX_GRID
 #define CAM_MAX_GRID (1u << 20)
 #endif

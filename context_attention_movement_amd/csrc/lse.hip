@@ -50,14 +50,14 @@ __device__ __forceinline__ void pack_o_tile(const Pack& a, uint32_t r, const cha
             uint64_t t, h;
             pack_row_th(a, r, q, t, h);
             const int64_t off = int64_t(t) * a.o_st_b + int64_t(h) * a.o_sh_b + int64_t(k) * W;
-            x[u] = *reinterpret_cast<const V*>(src + off);
+            x[u] = ld_at<W, (CAM_NT_PACK & 1) != 0>(src + off);
         }
     }
 #pragma unroll
     for (int u = 0; u < kVecsPerThread; ++u) {
         const uint32_t v = v0 + uint32_t(u * kThreads);
         if (!GUARD || v < a.o_vecs)
-            st<W>(dst, v, x[u]);
+            st<W, (CAM_NT_PACK & 2) != 0>(dst, v, x[u]);
     }
 }
 
@@ -162,143 +162,205 @@ __device__ __forceinline__ bool causal_piece_ok(const int32_t* cu, int32_t nseq,
     return start < end && start <= k;
 }
 
-// Number of partial rows fetched together: the valid partials of a row are
-// compacted and loaded CH at a time with no branch between the loads (a short
-// last batch repeats its last valid row with weight 0, so an invalid partial's
-// row is never touched).
-#ifndef CAM_COMBINE_BATCH
-#define CAM_COMBINE_BATCH 8
-#endif
-constexpr int kCombineBatch = CAM_COMBINE_BATCH;
+// The combine works on tiles of kCombineRows consecutive rows per workgroup.
+// Phase 1 turns the tile's partial LSEs into weights in LDS: thread
+// (row, p) loads one LSE (consecutive rows are consecutive addresses), a group
+// of pow2(P) lanes reduces max and sum with shuffles, and the normalised
+// weights, the validity mask and the output LSE go to LDS.  Phase 2 only
+// streams payload: a group of G lanes covers one row (G 16-byte vectors at a
+// time), keeps RF rows in flight, and loads each row's valid
+// partials kCombineBatch at a time with no branch between the loads (a short
+// batch repeats its last valid row with weight 0, so an invalid partial's row
+// is never read).
 
-template <int W, bool FP16, bool VARLEN>
+template <int W, bool FP16, bool VARLEN, int RF>
 __global__ __launch_bounds__(kThreads) void k_combine(Combine a)
 {
     typedef typename VecOf<W>::type V;
     constexpr int E = W / 2;  // payload elements per vector
     constexpr int CH = kCombineBatch;
+    constexpr bool NTL = (CAM_NT_COMBINE & 1) != 0, NTS = (CAM_NT_COMBINE & 2) != 0;
+    // per tile: weights [rows][P], validity masks, 1/Z
+    extern __shared__ float smem[];
+    const uint32_t RB = a.rows_per_tile;
+    float* w_lds = smem;                                                   // RB * P
+    uint64_t* m_lds = reinterpret_cast<uint64_t*>(w_lds + ((RB * a.P + 1) & ~1u));  // RB
+    float* iz_lds = reinterpret_cast<float*>(m_lds + RB);                  // RB
 
-    const uint32_t G = 1u << a.g_log2;
     const uint32_t lane = threadIdx.x & 63u;
-    const uint32_t gl = lane & (G - 1u);      // lane within the row group
-    const uint32_t gbase = lane & ~(G - 1u);  // first lane of the group in the wave
-    const uint64_t gmask = G == 64u ? ~0ull : ((1ull << G) - 1ull);
-    const uint32_t rows_per_block = kThreads >> a.g_log2;
+    const uint32_t wave = threadIdx.x >> 6;
+    // phase-1 geometry: GP lanes per row
+    const uint32_t GP = 1u << a.gp_log2;
+    const uint32_t sp = lane & (GP - 1u);
+    const uint32_t sbase = lane & ~(GP - 1u);
+    const uint64_t spmask = GP == 64u ? ~0ull : ((1ull << GP) - 1ull);
+    // phase-2 geometry: G lanes per row
+    const uint32_t G = 1u << a.g_log2;
+    const uint32_t gl = lane & (G - 1u);
+    const uint32_t groups = (uint32_t(kThreads) >> a.g_log2);  // row groups per block
+    const uint32_t group = threadIdx.x >> a.g_log2;
 
-    for (uint64_t rb = uint64_t(blockIdx.x) * rows_per_block; rb < a.n_rows;
-         rb += uint64_t(gridDim.x) * rows_per_block) {
-        const uint64_t row = rb + (threadIdx.x >> a.g_log2);
-        const bool active = row < a.n_rows;
-        uint32_t t = 0, h = 0;
-        if (active) {
-            t = fdiv(uint32_t(row), a.div_H);
-            h = uint32_t(row) - t * a.H;
-        }
-        // statistics: lane gl of the group owns partial gl
-        bool valid = false;
-        float L = -__builtin_inff();
-        if (active && gl < a.P) {
-            bool admitted = true;
-            if (VARLEN)
-                admitted = causal_piece_ok(a.cu, a.nseq, a.P, gl, t);
-            if (admitted) {
-                L = a.pl[int64_t(gl) * a.pl_sp + int64_t(t) * a.pl_st + int64_t(h) * a.pl_sh];
-                valid = __builtin_isfinite(L);
+    for (uint64_t tile = blockIdx.x; tile < a.n_tiles; tile += gridDim.x) {
+        const uint64_t row0 = tile * RB;
+        // ---- phase 1: statistics of the tile's rows
+        __syncthreads();  // the previous tile's readers are done with LDS
+        for (uint32_t base = 0; base < RB * GP; base += kThreads) {
+            const uint32_t tau = base + threadIdx.x;
+            const uint32_t rl = tau >> a.gp_log2;  // row within the tile
+            const uint64_t row = row0 + rl;
+            const bool live = rl < RB && row < a.n_rows;
+            uint32_t t = 0, h = 0;
+            if (live) {
+                t = fdiv(uint32_t(row), a.div_H);
+                h = uint32_t(row) - t * a.H;
+            }
+            bool valid = false;
+            float L = -__builtin_inff();
+            if (live && sp < a.P) {
+                bool admitted = true;
+                if (VARLEN)
+                    admitted = causal_piece_ok(a.cu, a.nseq, a.P, sp, t);
+                if (admitted) {
+                    L = a.pl[int64_t(sp) * a.pl_sp + int64_t(t) * a.pl_st + int64_t(h) * a.pl_sh];
+                    valid = __builtin_isfinite(L);
+                }
+            }
+            float M = valid ? L : -__builtin_inff();
+            for (uint32_t off = GP >> 1; off > 0; off >>= 1)
+                M = fmaxf(M, __shfl_xor(M, int(off), int(GP)));
+            const uint64_t vmask = (__ballot(valid) >> sbase) & spmask;
+            const float w = valid ? expf(L - M) : 0.0f;
+            float Z = w;
+            for (uint32_t off = GP >> 1; off > 0; off >>= 1)
+                Z += __shfl_xor(Z, int(off), int(GP));
+            if (live) {
+                const float iz = vmask ? 1.0f / Z : 0.0f;
+                if (sp < a.P)
+                    w_lds[rl * a.P + sp] = w * iz;
+                if (sp == 0) {
+                    m_lds[rl] = vmask;
+                    iz_lds[rl] = iz;
+                    if (a.lse_out)
+                        a.lse_out[int64_t(t) * a.lo_st + int64_t(h) * a.lo_sh] =
+                            vmask ? M + logf(Z) : -__builtin_inff();
+                }
             }
         }
-        float M = valid ? L : -__builtin_inff();
-        for (uint32_t off = G >> 1; off > 0; off >>= 1)
-            M = fmaxf(M, __shfl_xor(M, int(off), int(G)));
-        const uint64_t vmask = (__ballot(valid) >> gbase) & gmask;
-        const float w = valid ? expf(L - M) : 0.0f;
-        float Z = w;
-        for (uint32_t off = G >> 1; off > 0; off >>= 1)
-            Z += __shfl_xor(Z, int(off), int(G));
-        if (!active)
-            continue;
+        __syncthreads();
 
-        char* orow = static_cast<char*>(a.out) + int64_t(t) * a.o_st_b + int64_t(h) * a.o_sh_b;
-        if (vmask == 0) {
-            // no valid partial: +0 everywhere, -inf LSE
-            Halves<W> zh;
+        // ---- phase 2: stream the payload rows, RF rows per group in flight
+        const uint64_t left = a.n_rows - row0;
+        const uint32_t nr = left < RB ? uint32_t(left) : RB;  // rows of this tile
+        for (uint32_t rl0 = group * RF; rl0 < nr; rl0 += groups * RF) {
+            uint32_t rl[RF];
+            bool have[RF];
+            uint64_t msk[RF];
+            char* orow[RF];
+            const char* prow[RF];
 #pragma unroll
-            for (int e = 0; e < E; ++e)
-                zh.h[e] = 0;
-            const V zero = __builtin_bit_cast(V, zh);
-            for (uint32_t k = gl; k < a.cv; k += G)
-                *reinterpret_cast<V*>(orow + int64_t(k) * W) = zero;
-            if (gl == 0 && a.lse_out)
-                a.lse_out[int64_t(t) * a.lo_st + int64_t(h) * a.lo_sh] = -__builtin_inff();
-            continue;
-        }
-        const float invZ = 1.0f / Z;
-        const char* prow = static_cast<const char*>(a.po) + int64_t(t) * a.po_st_b + int64_t(h) * a.po_sh_b;
-        // Every lane of the group runs every iteration, so the weight shuffles
-        // below always read active lanes; a lane past the row's last vector
-        // re-reads the last vector (a valid address) and stores nothing.
-        for (uint32_t kb = 0; kb < a.cv; kb += G) {
-            const uint32_t k = kb + gl < a.cv ? kb + gl : a.cv - 1;
-            float acc[E];
+            for (int f = 0; f < RF; ++f) {
+                rl[f] = rl0 + f;
+                have[f] = rl[f] < nr;
+                if (!have[f])
+                    rl[f] = rl0;  // stands in for the missing row; nothing is stored for it
+                const uint64_t row = row0 + rl[f];
+                const uint32_t t = fdiv(uint32_t(row), a.div_H);
+                const uint32_t h = uint32_t(row) - t * a.H;
+                msk[f] = m_lds[rl[f]];
+                orow[f] = static_cast<char*>(a.out) + int64_t(t) * a.o_st_b + int64_t(h) * a.o_sh_b;
+                // a row without valid partials reads (and discards) its own output
+                // row, so that no invalid partial row is ever read
+                prow[f] = msk[f] ? static_cast<const char*>(a.po) + int64_t(t) * a.po_st_b + int64_t(h) * a.po_sh_b
+                                 : orow[f];
+            }
+            for (uint32_t kb = 0; kb < a.cv; kb += G) {
+                const bool kin = kb + gl < a.cv;
+                const uint32_t k = kin ? kb + gl : a.cv - 1;
+                float acc[RF][E];
+                uint64_t m[RF];
 #pragma unroll
-            for (int e = 0; e < E; ++e)
-                acc[e] = 0.0f;
-            const char* pk = prow + int64_t(k) * W;
-            uint64_t m = vmask;
-            while (m) {
-                int idx[CH];
-                float wv[CH];
-                int last = 0;
-#pragma unroll
-                for (int u = 0; u < CH; ++u) {
-                    const bool take = m != 0;
-                    const int p = take ? __builtin_ctzll(m) : last;
-                    m = take ? (m & (m - 1)) : m;
-                    idx[u] = p;
-                    last = p;
-                    const float wp = __shfl(w, int(gbase + uint32_t(p)), 64);
-                    wv[u] = take ? wp : 0.0f;
-                }
-                V x[CH];
-#pragma unroll
-                for (int u = 0; u < CH; ++u)
-                    x[u] = *reinterpret_cast<const V*>(pk + int64_t(idx[u]) * a.po_sp_b);
-#pragma unroll
-                for (int u = 0; u < CH; ++u) {
-                    const Halves<W> xh = __builtin_bit_cast(Halves<W>, x[u]);
+                for (int f = 0; f < RF; ++f) {
+                    m[f] = msk[f];
 #pragma unroll
                     for (int e = 0; e < E; ++e)
-                        acc[e] = fmaf(wv[u], half_to_f32<FP16>(xh.h[e]), acc[e]);
+                        acc[f][e] = 0.0f;
+                }
+                for (;;) {
+                    int idx[RF][CH];
+                    float wv[RF][CH];
+                    bool tk[RF][CH];
+                    bool any = false;
+#pragma unroll
+                    for (int f = 0; f < RF; ++f) {
+                        int last = msk[f] ? __builtin_ctzll(msk[f]) : 0;
+#pragma unroll
+                        for (int u = 0; u < CH; ++u) {
+                            const bool take = m[f] != 0;
+                            const int p = take ? __builtin_ctzll(m[f]) : last;
+                            m[f] = take ? (m[f] & (m[f] - 1)) : m[f];
+                            idx[f][u] = p;
+                            last = p;
+                            tk[f][u] = take;
+                            wv[f][u] = w_lds[rl[f] * a.P + uint32_t(p)];
+                        }
+                        any = any || m[f] != 0;
+                    }
+                    V x[RF][CH];
+#pragma unroll
+                    for (int f = 0; f < RF; ++f)
+#pragma unroll
+                        for (int u = 0; u < CH; ++u)
+                            x[f][u] = ld_at<W, NTL>(prow[f] + int64_t(k) * W + int64_t(idx[f][u]) * a.po_sp_b);
+#pragma unroll
+                    for (int f = 0; f < RF; ++f)
+#pragma unroll
+                        for (int u = 0; u < CH; ++u) {
+                            const Halves<W> xh = __builtin_bit_cast(Halves<W>, x[f][u]);
+#pragma unroll
+                            for (int e = 0; e < E; ++e) {
+                                const float v = fmaf(wv[f][u], half_to_f32<FP16>(xh.h[e]), acc[f][e]);
+                                acc[f][e] = tk[f][u] ? v : acc[f][e];
+                            }
+                        }
+                    if (!any)
+                        break;
+                }
+#pragma unroll
+                for (int f = 0; f < RF; ++f) {
+                    if (have[f] && kin) {
+                        Halves<W> oh;
+#pragma unroll
+                        for (int e = 0; e < E; ++e)
+                            oh.h[e] = f32_to_half<FP16>(msk[f] ? acc[f][e] : 0.0f);
+                        st_at<W, NTS>(orow[f] + int64_t(k) * W, __builtin_bit_cast(V, oh));
+                    }
                 }
             }
-            if (kb + gl < a.cv) {
-                Halves<W> oh;
-#pragma unroll
-                for (int e = 0; e < E; ++e)
-                    oh.h[e] = f32_to_half<FP16>(acc[e] * invZ);
-                *reinterpret_cast<V*>(orow + int64_t(k) * W) = __builtin_bit_cast(V, oh);
-            }
         }
-        if (gl == 0 && a.lse_out)
-            a.lse_out[int64_t(t) * a.lo_st + int64_t(h) * a.lo_sh] = M + logf(Z);
     }
 }
 
 cam_status launch_combine(const Combine& a, void* stream)
 {
+    // Rows of at least 512 bytes (one or more full 64-lane passes) keep two
+    // rows in flight per lane group; shorter rows, packed several per wave,
+    // keep one (the lower register count buys occupancy) -- measured on MI355X.
+    const bool wide = uint64_t(a.cv) * a.width >= 512;
     const void* fn = nullptr;
-#define CAM_PICK(Wd)                                                                            \
-    if (a.width == Wd) {                                                                        \
-        if (a.cu)                                                                               \
-            fn = a.fp16 ? reinterpret_cast<const void*>(&k_combine<Wd, true, true>)            \
-                        : reinterpret_cast<const void*>(&k_combine<Wd, false, true>);          \
-        else                                                                                    \
-            fn = a.fp16 ? reinterpret_cast<const void*>(&k_combine<Wd, true, false>)           \
-                        : reinterpret_cast<const void*>(&k_combine<Wd, false, false>);         \
+#define CAM_PICK(Wd, RFv)                                                                             \
+    if (a.width == Wd && wide == (RFv == 2)) {                                                        \
+        if (a.cu)                                                                                     \
+            fn = a.fp16 ? reinterpret_cast<const void*>(&k_combine<Wd, true, true, RFv>)             \
+                        : reinterpret_cast<const void*>(&k_combine<Wd, false, true, RFv>);           \
+        else                                                                                          \
+            fn = a.fp16 ? reinterpret_cast<const void*>(&k_combine<Wd, true, false, RFv>)            \
+                        : reinterpret_cast<const void*>(&k_combine<Wd, false, false, RFv>);          \
     }
-    CAM_PICK(16) CAM_PICK(8) CAM_PICK(4) CAM_PICK(2)
+    CAM_PICK(16, 1) CAM_PICK(8, 1) CAM_PICK(4, 1) CAM_PICK(2, 1)
+    CAM_PICK(16, 2) CAM_PICK(8, 2) CAM_PICK(4, 2) CAM_PICK(2, 2)
 #undef CAM_PICK
-    const uint64_t rows_per_block = uint64_t(kThreads) >> a.g_log2;
-    return launch(fn, a, (a.n_rows + rows_per_block - 1) / rows_per_block, stream, "lse_combine");
+    const uint64_t lds = (uint64_t(a.rows_per_tile) * a.P + 2) * 4 + uint64_t(a.rows_per_tile) * 12;
+    return launch(fn, a, a.n_tiles, stream, "lse_combine", lds);
 }
 
 }  // namespace cam

@@ -22,7 +22,7 @@ namespace cam {
 // GUARD = false is the straight-line path for tiles that lie wholly inside the
 // slab: every load is issued before any store and no branch separates them,
 // so each lane keeps kVecsPerThread requests in flight.
-template <int W, bool S2H, bool GUARD>
+template <int W, bool S2H, bool GUARD, int NTP>
 __device__ __forceinline__ void dense_tile(const DenseRelayout& a, uint64_t head_base, uint64_t seq_base,
                                            uint32_t v0)
 {
@@ -37,7 +37,7 @@ __device__ __forceinline__ void dense_tile(const DenseRelayout& a, uint64_t head
             const uint32_t k = v - s * a.c;
             const uint64_t so = seq_base + uint64_t(s) * a.Pc + k;
             const uint64_t ho = head_base + v;
-            x[u] = ld<W>(a.src, S2H ? so : ho);
+            x[u] = ld<W, (NTP & 1) != 0>(a.src, S2H ? so : ho);
             dst_off[u] = S2H ? ho : so;
         }
     }
@@ -45,7 +45,7 @@ __device__ __forceinline__ void dense_tile(const DenseRelayout& a, uint64_t head
     for (int u = 0; u < kVecsPerThread; ++u) {
         const uint32_t v = v0 + uint32_t(u * kThreads);
         if (!GUARD || v < a.slab_vecs)
-            st<W>(a.dst, dst_off[u], x[u]);
+            st<W, (NTP & 2) != 0>(a.dst, dst_off[u], x[u]);
     }
 }
 
@@ -62,10 +62,11 @@ __global__ __launch_bounds__(kThreads) void k_dense_relayout(DenseRelayout a)
         const uint64_t head_base = uint64_t(slab) * a.slab_vecs;
         const uint64_t seq_base = (uint64_t(j * a.B + b) * a.Sp * a.P + r) * a.c;
         const uint32_t vt = ti * uint32_t(kTileVecs);
+        constexpr int NTP = S2H ? CAM_NT_SEQ_TO_HEAD : CAM_NT_HEAD_TO_SEQ;
         if (vt + uint32_t(kTileVecs) <= a.slab_vecs)
-            dense_tile<W, S2H, false>(a, head_base, seq_base, vt + threadIdx.x);
+            dense_tile<W, S2H, false, NTP>(a, head_base, seq_base, vt + threadIdx.x);
         else
-            dense_tile<W, S2H, true>(a, head_base, seq_base, vt + threadIdx.x);
+            dense_tile<W, S2H, true, NTP>(a, head_base, seq_base, vt + threadIdx.x);
     }
 }
 
@@ -100,7 +101,7 @@ __device__ int64_t varlen_seq_row(const VarlenRelayout& a, uint32_t t, uint32_t 
     return row * int64_t(a.Pc) + int64_t(r) * a.c;
 }
 
-template <int W, bool S2H, bool GUARD>
+template <int W, bool S2H, bool GUARD, int NTP>
 __device__ __forceinline__ void varlen_tile(const VarlenRelayout& a, const int64_t* row_off, uint64_t head_base,
                                             uint32_t vb, uint32_t ve, uint32_t row0)
 {
@@ -120,7 +121,7 @@ __device__ __forceinline__ void varlen_tile(const VarlenRelayout& a, const int64
             if (live[u]) {
                 const uint64_t so = uint64_t(base) + k;
                 const uint64_t ho = head_base + v;
-                x[u] = ld<W>(a.src, S2H ? so : ho);
+                x[u] = ld<W, (NTP & 1) != 0>(a.src, S2H ? so : ho);
                 dst_off[u] = S2H ? ho : so;
             }
         }
@@ -128,7 +129,7 @@ __device__ __forceinline__ void varlen_tile(const VarlenRelayout& a, const int64
 #pragma unroll
     for (int u = 0; u < kVecsPerThread; ++u)
         if (live[u])
-            st<W>(a.dst, dst_off[u], x[u]);
+            st<W, (NTP & 2) != 0>(a.dst, dst_off[u], x[u]);
 }
 
 template <int W, bool S2H>
@@ -157,10 +158,11 @@ __global__ __launch_bounds__(kThreads) void k_varlen_relayout(VarlenRelayout a)
         }
         // full tile whose every row the plan places inside the buffer: no guards
         const bool fast = __syncthreads_and(rows_ok && ve - vb == uint32_t(kTileVecs));
+        constexpr int NTP = S2H ? CAM_NT_VARLEN_SEQ_TO_HEAD : CAM_NT_VARLEN_HEAD_TO_SEQ;
         if (fast)
-            varlen_tile<W, S2H, false>(a, row_off, head_base, vb, ve, row0);
+            varlen_tile<W, S2H, false, NTP>(a, row_off, head_base, vb, ve, row0);
         else
-            varlen_tile<W, S2H, true>(a, row_off, head_base, vb, ve, row0);
+            varlen_tile<W, S2H, true, NTP>(a, row_off, head_base, vb, ve, row0);
     }
 }
 
@@ -173,13 +175,13 @@ __device__ __forceinline__ void copy_tile(const Copy& a, uint64_t v0)
     for (int u = 0; u < kVecsPerThread; ++u) {
         const uint64_t v = v0 + uint64_t(u * kThreads);
         if (!GUARD || v < a.n_vecs)
-            x[u] = ld<16>(a.src, v);
+            x[u] = ld<16, (CAM_NT_COPY & 1) != 0>(a.src, v);
     }
 #pragma unroll
     for (int u = 0; u < kVecsPerThread; ++u) {
         const uint64_t v = v0 + uint64_t(u * kThreads);
         if (!GUARD || v < a.n_vecs)
-            st<16>(a.dst, v, x[u]);
+            st<16, (CAM_NT_COPY & 2) != 0>(a.dst, v, x[u]);
     }
 }
 
