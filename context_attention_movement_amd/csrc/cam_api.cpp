@@ -376,9 +376,15 @@ cam_status combine(const char* op, const CombineIn& c, void* stream)
     a.cv = uint32_t(row_b / a.width);
     a.g_log2 = log2u(pow2ceil(a.cv < 64 ? (a.cv ? a.cv : 1) : 64));
     a.gp_log2 = log2u(pow2ceil(a.P));
-    // rows per tile (measured per row width), at least one per payload group
-    uint32_t rows = uint64_t(a.cv) * a.width >= 512 ? CAM_COMBINE_ROWS_WIDE : CAM_COMBINE_ROWS_NARROW;
-    const uint32_t groups = uint32_t(kThreads) >> a.g_log2;
+    // tile geometry (measured per row width): rows per tile, workgroup size,
+    // tile order; at least one row per payload group
+    const bool wave = a.g_log2 == 6;
+    a.threads = wave ? CAM_COMBINE_THREADS_WAVE : kThreads;
+    a.xcd = wave ? CAM_XCD_COMBINE_WAVE : CAM_XCD_COMBINE_NARROW;
+    uint32_t rows = wave                                   ? CAM_COMBINE_ROWS_WAVE
+                    : uint64_t(a.cv) * a.width >= 512 ? CAM_COMBINE_ROWS_WIDE
+                                                      : CAM_COMBINE_ROWS_NARROW;
+    const uint32_t groups = a.threads >> a.g_log2;
     if (rows < groups)
         rows = groups;
     a.rows_per_tile = rows;

@@ -24,6 +24,12 @@ __device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv& f)
     return uint32_t((uint64_t(__umulhi(n, f.m)) + n) >> f.l);
 }
 
+// Keep a batch of independent loads together: no instruction is scheduled
+// across this point, so every load above it is issued before anything below
+// it may wait for one (the register-saving interleave of loads with their
+// consumers would leave one request in flight per lane).
+__device__ __forceinline__ void issue_fence() { __builtin_amdgcn_sched_barrier(0); }
+
 // Cache policy of the streaming accesses.  Every byte these kernels move is
 // touched exactly once, so each access may carry the non-temporal hint (no
 // reuse expected).  Which side profits depends on the access pattern and was
@@ -87,18 +93,31 @@ __device__ __forceinline__ uint32_t f32_to_fp16_bits(float f)
     return uint32_t(__builtin_bit_cast(uint16_t, _Float16(f)));
 }
 
+// XCD-aware tile order.  Workgroup b of a grid of nb runs on XCD b % 8 (the
+// dispatcher deals workgroups to the eight XCDs in turn).  xcd_first(b, nb)
+// renumbers the grid so that the workgroups of one XCD take one contiguous
+// range of first tiles: XCD x owns [start(x), start(x) + count(x)) with
+// count(x) = nb/8 (+1 for x < nb%8).  It is a bijection of [0, nb).
+constexpr uint32_t kXcds = 8;
+__device__ __forceinline__ uint32_t xcd_first(uint32_t b, uint32_t nb)
+{
+    const uint32_t x = b % kXcds, j = b / kXcds;
+    const uint32_t q = nb / kXcds, rem = nb % kXcds;
+    return x * q + (x < rem ? x : rem) + j;
+}
+
 // Launch `fn` over min(n_tiles, kMaxGrid) workgroups of kThreads on `stream`;
 // kernels walk their tiles with a grid stride.
 template <typename Args>
 inline cam_status launch(const void* fn, const Args& a, uint64_t n_tiles, void* stream,
-                         const char* what, uint64_t lds_bytes = 0)
+                         const char* what, uint64_t lds_bytes = 0, uint32_t threads = kThreads)
 {
     if (n_tiles == 0)
         return CAM_OK;
     const uint32_t grid = uint32_t(n_tiles < kMaxGrid ? n_tiles : kMaxGrid);
     Args copy = a;
     void* args[] = {&copy};
-    hipError_t e = hipLaunchKernel(fn, dim3(grid), dim3(kThreads), args, size_t(lds_bytes),
+    hipError_t e = hipLaunchKernel(fn, dim3(grid), dim3(threads), args, size_t(lds_bytes),
                                    reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess)
         return set_error(CAM_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));

@@ -136,6 +136,8 @@ struct Combine {
     uint32_t gp_log2;       // statistics lanes per row = 1 << gp_log2 (>= P, <= 64)
     uint32_t rows_per_tile; // rows per workgroup tile
     uint64_t n_tiles;
+    uint32_t threads;       // workgroup size (64, 128 or 256)
+    uint32_t xcd;           // 1: XCD-aware tile order
     const int32_t* cu;      // non-null: causal piece gating (varlen)
     int32_t nseq;
     int width;
@@ -205,6 +207,45 @@ constexpr int kTileVecs = kThreads * kVecsPerThread;
 #define CAM_COMBINE_BATCH 4
 #endif
 constexpr int kCombineBatch = CAM_COMBINE_BATCH;
+// rows of >= 64 vectors (a whole wave per row): rows per tile, rows in flight
+// per wave, partial rows per batch
+#ifndef CAM_COMBINE_THREADS_WAVE
+#define CAM_COMBINE_THREADS_WAVE 64
+#endif
+#ifndef CAM_COMBINE_ROWS_WAVE
+#define CAM_COMBINE_ROWS_WAVE 1
+#endif
+#ifndef CAM_COMBINE_INFLIGHT_WAVE
+#define CAM_COMBINE_INFLIGHT_WAVE 1
+#endif
+#ifndef CAM_COMBINE_BATCH_WAVE
+#define CAM_COMBINE_BATCH_WAVE 8
+#endif
+constexpr int kCombineInFlightWave = CAM_COMBINE_INFLIGHT_WAVE;
+constexpr int kCombineBatchWave = CAM_COMBINE_BATCH_WAVE;
+// XCD-aware tile order per kernel (1 = each XCD takes a contiguous range of
+// tiles, 0 = hardware order), chosen by measurement on MI355X.
+#ifndef CAM_XCD_SEQ_TO_HEAD
+#define CAM_XCD_SEQ_TO_HEAD 0
+#endif
+#ifndef CAM_XCD_HEAD_TO_SEQ
+#define CAM_XCD_HEAD_TO_SEQ 1
+#endif
+#ifndef CAM_XCD_VARLEN
+#define CAM_XCD_VARLEN 0
+#endif
+#ifndef CAM_XCD_PACK
+#define CAM_XCD_PACK 0
+#endif
+#ifndef CAM_XCD_COMBINE_WAVE
+#define CAM_XCD_COMBINE_WAVE 1
+#endif
+#ifndef CAM_XCD_COMBINE_NARROW
+#define CAM_XCD_COMBINE_NARROW 0
+#endif
+#ifndef CAM_XCD_COPY
+#define CAM_XCD_COPY 0
+#endif
 #ifndef CAM_MAX_GRID
 #define CAM_MAX_GRID (1u << 20)
 #endif

@@ -53,6 +53,7 @@ __device__ __forceinline__ void pack_o_tile(const Pack& a, uint32_t r, const cha
             x[u] = ld_at<W, (CAM_NT_PACK & 1) != 0>(src + off);
         }
     }
+    issue_fence();
 #pragma unroll
     for (int u = 0; u < kVecsPerThread; ++u) {
         const uint32_t v = v0 + uint32_t(u * kThreads);
@@ -65,7 +66,8 @@ template <int W>
 __global__ __launch_bounds__(kThreads) void k_pack(Pack a)
 {
     const uint32_t n_total = a.n_o_tiles + a.n_l_tiles;
-    for (uint32_t tile = blockIdx.x; tile < n_total; tile += gridDim.x) {
+    const uint32_t first = CAM_XCD_PACK ? xcd_first(blockIdx.x, gridDim.x) : blockIdx.x;
+    for (uint32_t tile = first; tile < n_total; tile += gridDim.x) {
         if (tile < a.n_o_tiles) {
             // O-region: bit copy of the payload rows into chunk (p, r)
             const uint32_t chunk = fdiv(tile, a.div_otpc);
@@ -173,12 +175,23 @@ __device__ __forceinline__ bool causal_piece_ok(const int32_t* cu, int32_t nseq,
 // batch repeats its last valid row with weight 0, so an invalid partial's row
 // is never read).
 
-template <int W, bool FP16, bool VARLEN, int RF>
+__device__ __forceinline__ uint32_t uniform32(uint32_t x)
+{
+    return uint32_t(__builtin_amdgcn_readfirstlane(int(x)));
+}
+__device__ __forceinline__ uint64_t uniform64(uint64_t x)
+{
+    return uint64_t(uniform32(uint32_t(x))) | (uint64_t(uniform32(uint32_t(x >> 32))) << 32);
+}
+
+// WAVE: one row group is a whole wave (rows of >= 64 vectors), so every
+// per-row quantity of phase 2 is wave-uniform and is kept in scalar registers.
+template <int W, bool FP16, bool VARLEN, int RF, bool WAVE>
 __global__ __launch_bounds__(kThreads) void k_combine(Combine a)
 {
     typedef typename VecOf<W>::type V;
     constexpr int E = W / 2;  // payload elements per vector
-    constexpr int CH = kCombineBatch;
+    constexpr int CH = WAVE ? kCombineBatchWave : kCombineBatch;
     constexpr bool NTL = (CAM_NT_COMBINE & 1) != 0, NTS = (CAM_NT_COMBINE & 2) != 0;
     // per tile: weights [rows][P], validity masks, 1/Z
     extern __shared__ float smem[];
@@ -197,14 +210,16 @@ __global__ __launch_bounds__(kThreads) void k_combine(Combine a)
     // phase-2 geometry: G lanes per row
     const uint32_t G = 1u << a.g_log2;
     const uint32_t gl = lane & (G - 1u);
-    const uint32_t groups = (uint32_t(kThreads) >> a.g_log2);  // row groups per block
+    const uint32_t nthr = blockDim.x;                           // 64, 128 or 256
+    const uint32_t groups = nthr >> a.g_log2;                   // row groups per block
     const uint32_t group = threadIdx.x >> a.g_log2;
 
-    for (uint64_t tile = blockIdx.x; tile < a.n_tiles; tile += gridDim.x) {
+    const uint64_t first = a.xcd ? xcd_first(blockIdx.x, gridDim.x) : blockIdx.x;
+    for (uint64_t tile = first; tile < a.n_tiles; tile += gridDim.x) {
         const uint64_t row0 = tile * RB;
         // ---- phase 1: statistics of the tile's rows
         __syncthreads();  // the previous tile's readers are done with LDS
-        for (uint32_t base = 0; base < RB * GP; base += kThreads) {
+        for (uint32_t base = 0; base < RB * GP; base += nthr) {
             const uint32_t tau = base + threadIdx.x;
             const uint32_t rl = tau >> a.gp_log2;  // row within the tile
             const uint64_t row = row0 + rl;
@@ -251,7 +266,8 @@ __global__ __launch_bounds__(kThreads) void k_combine(Combine a)
         // ---- phase 2: stream the payload rows, RF rows per group in flight
         const uint64_t left = a.n_rows - row0;
         const uint32_t nr = left < RB ? uint32_t(left) : RB;  // rows of this tile
-        for (uint32_t rl0 = group * RF; rl0 < nr; rl0 += groups * RF) {
+        const uint32_t first = WAVE ? uniform32(group * RF) : group * RF;
+        for (uint32_t rl0 = first; rl0 < nr; rl0 += groups * RF) {
             uint32_t rl[RF];
             bool have[RF];
             uint64_t msk[RF];
@@ -266,7 +282,7 @@ __global__ __launch_bounds__(kThreads) void k_combine(Combine a)
                 const uint64_t row = row0 + rl[f];
                 const uint32_t t = fdiv(uint32_t(row), a.div_H);
                 const uint32_t h = uint32_t(row) - t * a.H;
-                msk[f] = m_lds[rl[f]];
+                msk[f] = WAVE ? uniform64(m_lds[rl[f]]) : m_lds[rl[f]];
                 orow[f] = static_cast<char*>(a.out) + int64_t(t) * a.o_st_b + int64_t(h) * a.o_sh_b;
                 // a row without valid partials reads (and discards) its own output
                 // row, so that no invalid partial row is ever read
@@ -301,7 +317,8 @@ __global__ __launch_bounds__(kThreads) void k_combine(Combine a)
                             idx[f][u] = p;
                             last = p;
                             tk[f][u] = take;
-                            wv[f][u] = w_lds[rl[f] * a.P + uint32_t(p)];
+                            const float wl = w_lds[rl[f] * a.P + uint32_t(p)];
+                            wv[f][u] = WAVE ? __uint_as_float(uniform32(__float_as_uint(wl))) : wl;
                         }
                         any = any || m[f] != 0;
                     }
@@ -311,6 +328,7 @@ __global__ __launch_bounds__(kThreads) void k_combine(Combine a)
 #pragma unroll
                         for (int u = 0; u < CH; ++u)
                             x[f][u] = ld_at<W, NTL>(prow[f] + int64_t(k) * W + int64_t(idx[f][u]) * a.po_sp_b);
+                    issue_fence();
 #pragma unroll
                     for (int f = 0; f < RF; ++f)
 #pragma unroll
@@ -346,21 +364,24 @@ cam_status launch_combine(const Combine& a, void* stream)
     // rows in flight per lane group; shorter rows, packed several per wave,
     // keep one (the lower register count buys occupancy) -- measured on MI355X.
     const bool wide = uint64_t(a.cv) * a.width >= 512;
+    const bool wave = a.g_log2 == 6;  // a whole wave per row (implies wide)
     const void* fn = nullptr;
-#define CAM_PICK(Wd, RFv)                                                                             \
-    if (a.width == Wd && wide == (RFv == 2)) {                                                        \
-        if (a.cu)                                                                                     \
-            fn = a.fp16 ? reinterpret_cast<const void*>(&k_combine<Wd, true, true, RFv>)             \
-                        : reinterpret_cast<const void*>(&k_combine<Wd, false, true, RFv>);           \
-        else                                                                                          \
-            fn = a.fp16 ? reinterpret_cast<const void*>(&k_combine<Wd, true, false, RFv>)            \
-                        : reinterpret_cast<const void*>(&k_combine<Wd, false, false, RFv>);          \
+#define CAM_PICK(Wd, RFv, WV)                                                                          \
+    if (a.width == Wd && wave == WV && (WV || wide == (RFv == 2))) {                                            \
+        if (a.cu)                                                                                       \
+            fn = a.fp16 ? reinterpret_cast<const void*>(&k_combine<Wd, true, true, RFv, WV>)           \
+                        : reinterpret_cast<const void*>(&k_combine<Wd, false, true, RFv, WV>);         \
+        else                                                                                            \
+            fn = a.fp16 ? reinterpret_cast<const void*>(&k_combine<Wd, true, false, RFv, WV>)          \
+                        : reinterpret_cast<const void*>(&k_combine<Wd, false, false, RFv, WV>);        \
     }
-    CAM_PICK(16, 1) CAM_PICK(8, 1) CAM_PICK(4, 1) CAM_PICK(2, 1)
-    CAM_PICK(16, 2) CAM_PICK(8, 2) CAM_PICK(4, 2) CAM_PICK(2, 2)
+    CAM_PICK(16, 1, false) CAM_PICK(8, 1, false) CAM_PICK(4, 1, false) CAM_PICK(2, 1, false)
+    CAM_PICK(16, 2, false) CAM_PICK(8, 2, false) CAM_PICK(4, 2, false) CAM_PICK(2, 2, false)
+    CAM_PICK(16, kCombineInFlightWave, true) CAM_PICK(8, kCombineInFlightWave, true)
+    CAM_PICK(4, kCombineInFlightWave, true) CAM_PICK(2, kCombineInFlightWave, true)
 #undef CAM_PICK
     const uint64_t lds = (uint64_t(a.rows_per_tile) * a.P + 2) * 4 + uint64_t(a.rows_per_tile) * 12;
-    return launch(fn, a, a.n_tiles, stream, "lse_combine", lds);
+    return launch(fn, a, a.n_tiles, stream, "lse_combine", lds, a.threads);
 }
 
 }  // namespace cam

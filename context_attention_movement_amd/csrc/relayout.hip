@@ -41,6 +41,7 @@ __device__ __forceinline__ void dense_tile(const DenseRelayout& a, uint64_t head
             dst_off[u] = S2H ? ho : so;
         }
     }
+    issue_fence();
 #pragma unroll
     for (int u = 0; u < kVecsPerThread; ++u) {
         const uint32_t v = v0 + uint32_t(u * kThreads);
@@ -52,7 +53,9 @@ __device__ __forceinline__ void dense_tile(const DenseRelayout& a, uint64_t head
 template <int W, bool S2H>
 __global__ __launch_bounds__(kThreads) void k_dense_relayout(DenseRelayout a)
 {
-    for (uint32_t tile = blockIdx.x; tile < a.n_tiles; tile += gridDim.x) {
+    constexpr bool XCD = S2H ? CAM_XCD_SEQ_TO_HEAD : CAM_XCD_HEAD_TO_SEQ;
+    const uint32_t first = XCD ? xcd_first(blockIdx.x, gridDim.x) : blockIdx.x;
+    for (uint32_t tile = first; tile < a.n_tiles; tile += gridDim.x) {
         const uint32_t slab = fdiv(tile, a.div_tps);
         const uint32_t ti = tile - slab * a.tiles_per_slab;
         const uint32_t rb = fdiv(slab, a.div_P);
@@ -126,6 +129,7 @@ __device__ __forceinline__ void varlen_tile(const VarlenRelayout& a, const int64
             }
         }
     }
+    issue_fence();
 #pragma unroll
     for (int u = 0; u < kVecsPerThread; ++u)
         if (live[u])
@@ -138,7 +142,8 @@ __global__ __launch_bounds__(kThreads) void k_varlen_relayout(VarlenRelayout a)
     // sequence-side offset of every row the tile touches (a tile spans at most
     // kTileVecs + 1 rows when rows are one vector long)
     __shared__ int64_t row_off[kTileVecs + 1];
-    for (uint32_t tile = blockIdx.x; tile < a.n_tiles; tile += gridDim.x) {
+    const uint32_t first = CAM_XCD_VARLEN ? xcd_first(blockIdx.x, gridDim.x) : blockIdx.x;
+    for (uint32_t tile = first; tile < a.n_tiles; tile += gridDim.x) {
         const uint32_t plane = fdiv(tile, a.div_tpp);
         const uint32_t ti = tile - plane * a.tiles_per_plane;
         const uint32_t r = fdiv(plane, a.div_B);
@@ -177,6 +182,7 @@ __device__ __forceinline__ void copy_tile(const Copy& a, uint64_t v0)
         if (!GUARD || v < a.n_vecs)
             x[u] = ld<16, (CAM_NT_COPY & 1) != 0>(a.src, v);
     }
+    issue_fence();
 #pragma unroll
     for (int u = 0; u < kVecsPerThread; ++u) {
         const uint64_t v = v0 + uint64_t(u * kThreads);
@@ -188,7 +194,8 @@ __device__ __forceinline__ void copy_tile(const Copy& a, uint64_t v0)
 __global__ __launch_bounds__(kThreads) void k_copy16(Copy a)
 {
     const uint64_t n_tiles = (a.n_vecs + kTileVecs - 1) / kTileVecs;
-    for (uint64_t tile = blockIdx.x; tile < n_tiles; tile += gridDim.x) {
+    const uint64_t first = CAM_XCD_COPY ? xcd_first(blockIdx.x, gridDim.x) : blockIdx.x;
+    for (uint64_t tile = first; tile < n_tiles; tile += gridDim.x) {
         const uint64_t vt = tile * kTileVecs;
         if (vt + kTileVecs <= a.n_vecs)
             copy_tile<false>(a, vt + threadIdx.x);
