@@ -241,6 +241,7 @@ cam_status varlen_relayout(const void* in, void* out, const int32_t* cu, const i
     a.nseq = int32_t(nseq);
     a.P = uint32_t(P);
     a.B = uint32_t(B);
+    a.div_P = make_fastdiv(a.P);
     a.div_B = make_fastdiv(a.B);
     a.T = uint64_t(T);
     a.c = uint32_t(run / a.width);
@@ -391,6 +392,7 @@ cam_status combine(const char* op, const CombineIn& c, void* stream)
     a.n_tiles = (uint64_t(n_rows) + rows - 1) / rows;
     a.cu = c.cu;
     a.nseq = int32_t(c.nseq);
+    a.div_P = make_fastdiv(a.P);
     a.fp16 = c.dt == CAM_FP16;
     return launch_combine(a, stream);
 }

@@ -24,6 +24,56 @@ __device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv& f)
     return uint32_t((uint64_t(__umulhi(n, f.m)) + n) >> f.l);
 }
 
+// ---------------------------------------------------------------------------
+// Packed-THD piece arithmetic.  Sequence i of length L is cut into P pieces,
+// piece p = positions [floor(p*L/P), floor((p+1)*L/P)).
+// ---------------------------------------------------------------------------
+
+// floor(p*L/P): one multiply-high while p*L fits 32 bits (L < 2^26 at P <= 64),
+// a 64-bit division beyond.
+__device__ __forceinline__ uint32_t piece_start(uint32_t p, uint32_t L, const FastDiv& divP)
+{
+    const uint64_t n = uint64_t(p) * L;
+    if (n <= 0xFFFFFFFFull)
+        return fdiv(uint32_t(n), divP);
+    return uint32_t(n / divP.d);
+}
+
+// The rank whose piece holds position k (0 <= k < L): the largest p with
+// piece_start(p) <= k, i.e. floor(((k+1)*P - 1)/L).  An fp32 estimate of that
+// quotient is within one of it; two exact integer checks settle it.
+__device__ __forceinline__ uint32_t piece_owner(uint32_t k, uint32_t L, const FastDiv& divP)
+{
+    const uint32_t P = divP.d;
+    const float est = (float(k) * float(P) + float(P - 1)) / float(L);
+    uint32_t p = est <= 0.0f ? 0u : uint32_t(est);
+    if (p > P - 1)
+        p = P - 1;
+    if (p + 1 < P && piece_start(p + 1, L, divP) <= k)
+        ++p;
+    if (p > 0 && piece_start(p, L, divP) > k)
+        --p;
+    return p;
+}
+
+// Largest i < nseq with cu[i] <= t (cu non-decreasing, cu[0] = 0).
+__device__ __forceinline__ int32_t seq_of_token(const int32_t* cu, int32_t nseq, uint32_t t)
+{
+    int32_t lo = 0, hi = nseq;
+    while (hi - lo > 1) {
+        const int32_t mid = (lo + hi) >> 1;
+        if (int64_t(cu[mid]) <= int64_t(t))
+            lo = mid;
+        else
+            hi = mid;
+    }
+    return lo;
+}
+
+// cu_seqlens entries staged in LDS by the varlen kernels (larger tables are
+// searched in global memory).
+constexpr int32_t kCuCache = 1024;
+
 // Keep a batch of independent loads together: no instruction is scheduled
 // across this point, so every load above it is issued before anything below
 // it may wait for one (the register-saving interleave of loads with their

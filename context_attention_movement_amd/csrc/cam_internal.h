@@ -74,7 +74,7 @@ struct VarlenRelayout {
     const int64_t* rank_off;
     int32_t nseq;
     uint32_t P, B;
-    FastDiv div_B;
+    FastDiv div_P, div_B;
     uint64_t T;
     uint32_t c;
     FastDiv div_c;
@@ -140,6 +140,7 @@ struct Combine {
     uint32_t xcd;           // 1: XCD-aware tile order
     const int32_t* cu;      // non-null: causal piece gating (varlen)
     int32_t nseq;
+    FastDiv div_P;
     int width;
     int fp16;               // payload: 0 bf16, 1 fp16
 };

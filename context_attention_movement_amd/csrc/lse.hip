@@ -143,25 +143,18 @@ __device__ __forceinline__ uint16_t f32_to_half(float f)
 
 // Causal admission of KV piece p for the token t of a packed THD batch: the
 // piece must be non-empty and start at or before t's position in its sequence.
-__device__ __forceinline__ bool causal_piece_ok(const int32_t* cu, int32_t nseq, uint32_t P,
+__device__ __forceinline__ bool causal_piece_ok(const int32_t* cu, int32_t nseq, const FastDiv& divP,
                                                 uint32_t p, uint32_t t)
 {
-    int32_t lo = 0, hi = nseq;
-    while (hi - lo > 1) {
-        const int32_t mid = (lo + hi) >> 1;
-        if (int64_t(cu[mid]) <= int64_t(t))
-            lo = mid;
-        else
-            hi = mid;
-    }
-    const int64_t c0 = cu[lo];
-    const int64_t L = int64_t(cu[lo + 1]) - c0;
+    const int32_t i = seq_of_token(cu, nseq, t);
+    const int64_t c0 = cu[i];
+    const int64_t L = int64_t(cu[i + 1]) - c0;
     const int64_t k = int64_t(t) - c0;
     if (k < 0 || k >= L)
         return false;
-    const int64_t start = (int64_t(p) * L) / P;
-    const int64_t end = (int64_t(p + 1) * L) / P;
-    return start < end && start <= k;
+    const uint32_t start = piece_start(p, uint32_t(L), divP);
+    const uint32_t end = piece_start(p + 1, uint32_t(L), divP);
+    return start < end && int64_t(start) <= k;
 }
 
 // The combine works on tiles of kCombineRows consecutive rows per workgroup.
@@ -199,6 +192,11 @@ __global__ __launch_bounds__(kThreads) void k_combine(Combine a)
     float* w_lds = smem;                                                   // RB * P
     uint64_t* m_lds = reinterpret_cast<uint64_t*>(w_lds + ((RB * a.P + 1) & ~1u));  // RB
     float* iz_lds = reinterpret_cast<float*>(m_lds + RB);                  // RB
+    int32_t* cu_lds = reinterpret_cast<int32_t*>(iz_lds + RB);             // nseq + 1 (varlen)
+    const bool cached = VARLEN && a.nseq < kCuCache;
+    if (cached)  // visible after the barrier that opens every tile
+        for (uint32_t i = threadIdx.x; i <= uint32_t(a.nseq); i += blockDim.x)
+            cu_lds[i] = a.cu[i];
 
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t wave = threadIdx.x >> 6;
@@ -234,7 +232,9 @@ __global__ __launch_bounds__(kThreads) void k_combine(Combine a)
             if (live && sp < a.P) {
                 bool admitted = true;
                 if (VARLEN)
-                    admitted = causal_piece_ok(a.cu, a.nseq, a.P, sp, t);
+                    // the two calls differ only in the address space of the table
+                    admitted = cached ? causal_piece_ok(cu_lds, a.nseq, a.div_P, sp, t)
+                                      : causal_piece_ok(a.cu, a.nseq, a.div_P, sp, t);
                 if (admitted) {
                     L = a.pl[int64_t(sp) * a.pl_sp + int64_t(t) * a.pl_st + int64_t(h) * a.pl_sh];
                     valid = __builtin_isfinite(L);
@@ -380,7 +380,9 @@ cam_status launch_combine(const Combine& a, void* stream)
     CAM_PICK(16, kCombineInFlightWave, true) CAM_PICK(8, kCombineInFlightWave, true)
     CAM_PICK(4, kCombineInFlightWave, true) CAM_PICK(2, kCombineInFlightWave, true)
 #undef CAM_PICK
-    const uint64_t lds = (uint64_t(a.rows_per_tile) * a.P + 2) * 4 + uint64_t(a.rows_per_tile) * 12;
+    uint64_t lds = (uint64_t(a.rows_per_tile) * a.P + 2) * 4 + uint64_t(a.rows_per_tile) * 12;
+    if (a.cu && a.nseq < kCuCache)
+        lds += uint64_t(a.nseq + 1) * 4;
     return launch(fn, a, a.n_tiles, stream, "lse_combine", lds, a.threads);
 }
 

@@ -75,25 +75,18 @@ __global__ __launch_bounds__(kThreads) void k_dense_relayout(DenseRelayout a)
 
 // Sequence-side vector offset of token t's row for destination head block r
 // of plane b, or -1 if the plan does not place t inside the buffer.
-__device__ int64_t varlen_seq_row(const VarlenRelayout& a, uint32_t t, uint32_t r, uint32_t b)
+__device__ __forceinline__ int64_t varlen_seq_row(const VarlenRelayout& a, const int32_t* cu, uint32_t t,
+                                                  uint32_t r, uint32_t b)
 {
-    int32_t lo = 0, hi = a.nseq;  // largest i < nseq with cu[i] <= t
-    while (hi - lo > 1) {
-        const int32_t mid = (lo + hi) >> 1;
-        if (int64_t(a.cu[mid]) <= int64_t(t))
-            lo = mid;
-        else
-            hi = mid;
-    }
-    const int64_t c0 = a.cu[lo];
-    const int64_t L = int64_t(a.cu[lo + 1]) - c0;
+    const int32_t i = seq_of_token(cu, a.nseq, t);
+    const int64_t c0 = cu[i];
+    const int64_t L = int64_t(cu[i + 1]) - c0;
     const int64_t k = int64_t(t) - c0;
     if (k < 0 || k >= L)
         return -1;
-    const int64_t P = a.P;
-    const int64_t p = ((k + 1) * P - 1) / L;  // rank whose piece holds position k
-    const int64_t start = (p * L) / P;
-    const int64_t l = int64_t(a.rank_cu[p * (a.nseq + 1) + lo]) + (k - start);
+    const uint32_t p = piece_owner(uint32_t(k), uint32_t(L), a.div_P);
+    const int64_t start = piece_start(p, uint32_t(L), a.div_P);
+    const int64_t l = int64_t(a.rank_cu[int64_t(p) * (a.nseq + 1) + i]) + (k - start);
     const int64_t R = a.rank_off[p];
     const int64_t Tp = a.rank_off[p + 1] - R;
     if (l < 0 || l >= Tp)
@@ -142,6 +135,11 @@ __global__ __launch_bounds__(kThreads) void k_varlen_relayout(VarlenRelayout a)
     // sequence-side offset of every row the tile touches (a tile spans at most
     // kTileVecs + 1 rows when rows are one vector long)
     __shared__ int64_t row_off[kTileVecs + 1];
+    __shared__ int32_t cu_lds[kCuCache];
+    const bool cached = a.nseq < kCuCache;
+    if (cached)  // visible after the barrier that opens every tile
+        for (uint32_t i = threadIdx.x; i <= uint32_t(a.nseq); i += kThreads)
+            cu_lds[i] = a.cu[i];
     const uint32_t first = CAM_XCD_VARLEN ? xcd_first(blockIdx.x, gridDim.x) : blockIdx.x;
     for (uint32_t tile = first; tile < a.n_tiles; tile += gridDim.x) {
         const uint32_t plane = fdiv(tile, a.div_tpp);
@@ -157,7 +155,10 @@ __global__ __launch_bounds__(kThreads) void k_varlen_relayout(VarlenRelayout a)
         __syncthreads();  // the previous tile's readers are done with row_off
         bool rows_ok = true;
         for (uint32_t i = threadIdx.x; i < nrows; i += kThreads) {
-            const int64_t off = varlen_seq_row(a, row0 + i, r, b);
+            // the two calls differ only in the address space of the table,
+            // so each compiles to plain LDS or global loads
+            const int64_t off = cached ? varlen_seq_row(a, cu_lds, row0 + i, r, b)
+                                       : varlen_seq_row(a, a.cu, row0 + i, r, b);
             row_off[i] = off;
             rows_ok = rows_ok && off >= 0;
         }
