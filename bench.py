@@ -130,6 +130,14 @@ class Workload:
         self.t_comb = torch.empty((T, H, D), dtype=bf, device=dev)
         self.t_comb_lse = torch.empty((T, H), dtype=torch.float32, device=dev)
         self.t_admitted = thd_admitted_counts(self.t_cu, P)
+        # sequence-sharded outputs of the fused combine epilogues
+        self.t_comb_seq = torch.empty((T, H, D), dtype=bf, device=dev)
+        self.t_comb_seq_lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+        Pm, Tm, Hm, Dvm = self.mP, self.mT, self.mH, self.mDv
+        for ms in self.m_sets:
+            ms["comb_seq"] = torch.empty((Tm, Hm, Dvm), dtype=bf, device=dev)
+            ms["lse_seq"] = torch.empty((Tm, Hm), dtype=torch.float32, device=dev)
+            ms["comb_h2s"] = torch.empty((Pm, 1, Tm // Pm, Hm, Dvm), dtype=bf, device=dev)
         self.step_index = 0
         torch.cuda.synchronize()
 
@@ -180,6 +188,34 @@ class Workload:
             ("lse_combine_varlen_thd", "k_combine<16, false, true, 1, false>",
              lambda: cam.lse_combine_varlen(self.t_part, self.t_lse, self.t_cu_dev, out=self.t_comb,
                                             lse_out=self.t_comb_lse)),
+        ]
+
+
+    def extension_ops(self, k=0):
+        """Operations beyond the step: the combine epilogues that write the
+        sequence-sharded layout directly, and the unfused sequence they
+        replace.  (name, algorithmic bytes, callable)."""
+        cam = self.cam
+        ms = self.m_sets[k % self.NSETS]
+        Pm, Tm, Hm, Dvm = self.mP, self.mT, self.mH, self.mDv
+        comb_bytes = self.op_bytes()["lse_combine_mla"]
+        out_bytes = Tm * Hm * Dvm * 2
+
+        def fused():
+            cam.lse_combine_packed_seq(ms["packed_in"], Pm, Tm, Hm, Dvm, 1, out=ms["comb_seq"], lse_out=ms["lse_seq"])
+
+        def unfused():
+            cam.lse_combine_packed(ms["packed_in"], Pm, Tm, Hm, Dvm, 1, out=ms["comb"], lse_out=ms["lse"])
+            cam.ulysses_head_to_seq(ms["comb"].view(Pm, 1, Tm, Hm // Pm, Dvm), Pm, out=ms["comb_h2s"])
+
+        def thd_fused():
+            cam.lse_combine_varlen_seq(self.t_part, self.t_lse, self.t_plan, out=self.t_comb_seq,
+                                       lse_out=self.t_comb_seq_lse)
+
+        return [
+            ("combine_to_sequence_shards_mla (fused)", comb_bytes, fused),
+            ("combine_then_head_to_seq_mla (unfused)", comb_bytes + 2 * out_bytes, unfused),
+            ("combine_varlen_to_sequence_shards_thd (fused)", self.op_bytes()["lse_combine_varlen_thd"], thd_fused),
         ]
 
 
@@ -439,6 +475,23 @@ def main():
             torch.cuda.synchronize()
             iso_us[n] = e0.elapsed_time(e1) * 1000.0 / args.calls
 
+    # ---- operations beyond the step (same µs/call method)
+    ext = {}
+    with torch.cuda.stream(stream):
+        for i, (n, nb_ext, _) in enumerate(w.extension_ops()):
+            for j in range(3):
+                w.extension_ops(k=j)[i][2]()
+            fns = [w.extension_ops(k=j)[i][2] for j in range(args.calls)]
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for fn in fns:
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1000.0 / args.calls
+            ext[n] = {"us_per_call": round(us, 2), "algorithmic_bytes": int(nb_ext),
+                      "GBps": round(nb_ext / us / 1e3, 1), "frac_of_hbm_peak": round(nb_ext / us / 1e3 / HBM_PEAK_GBPS, 4)}
+
     # ---- plain-copy ceiling on the video Q/K/V operand size
     with torch.cuda.stream(stream):
         src, dst = w.v_qkv, w.v_qkv_out
@@ -517,6 +570,7 @@ def main():
             "algorithmic_bytes_per_launch": int(nbytes[dom]),
         },
         "ops": op_table,
+        "extensions": ext,
         "copy_ceiling": {"GBps": round(copy_gbps, 1), "frac_of_hbm_peak": round(copy_gbps / HBM_PEAK_GBPS, 4),
                          "bytes": int(copy_bytes), "kernel": "k_copy16"},
         "device": {"name": props.name, "arch": getattr(props, "gcnArchName", ""),

@@ -25,6 +25,7 @@ __all__ = [
     "ulysses_seq_to_head", "ulysses_head_to_seq",
     "VarlenPlan", "ulysses_varlen_plan", "ulysses_seq_to_head_varlen", "ulysses_head_to_seq_varlen",
     "lse_pack_bytes", "lse_pack", "lse_combine_packed", "lse_combine", "lse_combine_varlen",
+    "lse_combine_packed_seq", "lse_combine_varlen_seq",
     "copy",
 ]
 
@@ -65,6 +66,9 @@ _SIGNATURES = {
     "lse_combine_varlen": (_int, [_vp, _i64, _i64, _i64, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _i64,
                                   _int, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _vp]),
     "cam_copy": (_int, [_vp, _vp, _i64, _vp]),
+    "lse_combine_packed_seq": (_int, [_vp, _i64, _i64, _i64, _i64, _int, _int, _vp, _vp, _vp]),
+    "lse_combine_varlen_seq": (_int, [_vp, _i64, _i64, _i64, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _i64,
+                                      _int, _vp, _vp, _vp, _vp, _vp, _i64, _vp]),
 }
 
 
@@ -349,6 +353,53 @@ def lse_combine_varlen(part_out: torch.Tensor, part_lse: torch.Tensor, cu_seqlen
                                         *part_lse.stride(), P, T, H, D, _dt(part_out), out.data_ptr(),
                                         *out.stride()[:2], _ptr(lse_out), *lo, cu_seqlens.data_ptr(),
                                         cu_seqlens.numel() - 1, _stream(part_out)))
+    return out, lse_out
+
+
+def lse_combine_packed_seq(packed: torch.Tensor, P: int, T: int, H: int, Dv: int, scatter_dim: int,
+                           dtype=torch.bfloat16, out: torch.Tensor | None = None,
+                           lse_out: torch.Tensor | None | bool = True):
+    """lse_combine_packed with token-major output: (out [T][H][Dv], lse_out [T][H])."""
+    _contig(packed, "packed")
+    if out is None:
+        out = torch.empty((T, H, Dv), dtype=dtype, device=packed.device)
+    _contig(out, "out")
+    if lse_out is True:
+        lse_out = torch.empty((T, H), dtype=torch.float32, device=packed.device)
+    elif lse_out is False:
+        lse_out = None
+    if lse_out is not None:
+        _contig(lse_out, "lse_out")
+    code = CAM_BF16 if dtype == torch.bfloat16 else CAM_FP16
+    _check(library().lse_combine_packed_seq(packed.data_ptr(), P, T, H, Dv, scatter_dim, code, out.data_ptr(),
+                                            _ptr(lse_out), _stream(packed)))
+    return out, lse_out
+
+
+def lse_combine_varlen_seq(part_out: torch.Tensor, part_lse: torch.Tensor, plan: "VarlenPlan",
+                           out: torch.Tensor | None = None, lse_out: torch.Tensor | None | bool = True):
+    """lse_combine_varlen whose token rows go to the rank-major (sequence-
+    sharded) order of the varlen relayout: (out [T][H][D], lse_out [T][H])."""
+    _dev(part_out, "part_out")
+    _dev(part_lse, "part_lse")
+    if part_out.dim() != 4 or part_out.stride(3) != 1 or part_lse.dtype != torch.float32:
+        raise ValueError("part_out must be [P][T][H][D] (D contiguous), part_lse float32 [P][T][H]")
+    P, T, H, D = part_out.shape
+    if P != plan.P or T != plan.total_tokens:
+        raise ValueError("the plan must match the partials' P and T")
+    if out is None:
+        out = torch.empty((T, H, D), dtype=part_out.dtype, device=part_out.device)
+    _contig(out, "out")
+    if lse_out is True:
+        lse_out = torch.empty((T, H), dtype=torch.float32, device=part_out.device)
+    elif lse_out is False:
+        lse_out = None
+    if lse_out is not None:
+        _contig(lse_out, "lse_out")
+    _check(library().lse_combine_varlen_seq(part_out.data_ptr(), *part_out.stride()[:3], part_lse.data_ptr(),
+                                            *part_lse.stride(), P, T, H, D, _dt(part_out), out.data_ptr(),
+                                            _ptr(lse_out), plan.cu.data_ptr(), plan.rank_cu.data_ptr(),
+                                            plan.rank_off.data_ptr(), plan.nseq, _stream(part_out)))
     return out, lse_out
 
 

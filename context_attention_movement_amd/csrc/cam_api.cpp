@@ -309,6 +309,10 @@ struct CombineIn {
     int64_t lo_st, lo_sh;
     const int32_t* cu;
     int64_t nseq;
+    uint32_t out_mode = 0;           // see Combine::out_mode
+    int64_t Hp = 0, Hq = 0;          // mode 1
+    const int32_t* rank_cu = nullptr;  // mode 2
+    const int64_t* rank_off = nullptr;
 };
 
 cam_status combine(const char* op, const CombineIn& c, void* stream)
@@ -393,6 +397,13 @@ cam_status combine(const char* op, const CombineIn& c, void* stream)
     a.cu = c.cu;
     a.nseq = int32_t(c.nseq);
     a.div_P = make_fastdiv(a.P);
+    a.out_mode = c.out_mode;
+    a.Hp = uint32_t(c.Hp);
+    a.Hq = uint32_t(c.Hq);
+    a.div_Hp = make_fastdiv(c.Hp > 0 ? uint32_t(c.Hp) : 1u);
+    a.o_row_b = uint64_t(c.D) * 2;
+    a.rank_cu = c.rank_cu;
+    a.rank_off = c.rank_off;
     a.fp16 = c.dt == CAM_FP16;
     return launch_combine(a, stream);
 }
@@ -631,6 +642,80 @@ cam_status lse_combine_varlen(const void* part_out, int64_t po_sp, int64_t po_st
     CombineIn c{part_out, po_sp, po_st, po_sh, part_lse, pl_sp, pl_st, pl_sh, P, T, H, D, dt,
                 out, o_st, o_sh, lse_out, lo_st, lo_sh, cu_seqlens, nseq};
     return combine("lse_combine_varlen", c, stream);
+}
+
+cam_status lse_combine_packed_seq(const void* packed, int64_t P, int64_t T, int64_t H, int64_t Dv, int scatter_dim,
+                                  cam_dtype dt, void* out, float* lse_out, void* stream)
+{
+    const char* op = "lse_combine_packed_seq";
+    clear_error();
+    PackGeom g;
+    cam_status st = pack_geometry(op, P, T, H, Dv, scatter_dim, dt, &g);
+    if (st != CAM_OK)
+        return st;
+    if (g.total == 0 || g.rows == 0)
+        return CAM_OK;
+    if (!packed || !out)
+        return set_error(CAM_ERR_NULL, "%s: packed and out must be non-null", op);
+    if (!aligned(packed, 16))
+        return set_error(CAM_ERR_ALIGNMENT, "%s: packed must be 16-byte aligned", op);
+    if (P > INT32_MAX || H > INT32_MAX)
+        return set_error(CAM_ERR_UNSUPPORTED, "%s: P and H must fit 32 bits", op);
+    // the exchange view as in lse_combine_packed; the output (extent T*H*Dv)
+    // is placed token-major by out_mode 1 (head scatter) -- for the token
+    // scatter the destination-major order already is token-major
+    CombineIn c{};
+    c.po = packed;
+    c.po_sp = P * g.chunk / 2;
+    c.po_st = g.chunk / 2;
+    c.po_sh = Dv;
+    c.pl = reinterpret_cast<const float*>(static_cast<const char*>(packed) + g.o_region);
+    c.pl_sp = P * g.chunk / 4;
+    c.pl_st = g.chunk / 4;
+    c.pl_sh = 1;
+    c.P = P;
+    c.T = P;
+    c.H = g.rows;
+    c.D = Dv;
+    c.dt = dt;
+    c.out = out;
+    c.o_st = g.rows * Dv;
+    c.o_sh = Dv;
+    c.lse_out = lse_out;
+    c.lo_st = g.rows;
+    c.lo_sh = 1;
+    if (scatter_dim == 1) {
+        c.out_mode = 1;
+        c.Hp = H / P;
+        c.Hq = H;
+    }
+    return combine(op, c, stream);
+}
+
+cam_status lse_combine_varlen_seq(const void* part_out, int64_t po_sp, int64_t po_st, int64_t po_sh,
+                                  const float* part_lse, int64_t pl_sp, int64_t pl_st, int64_t pl_sh, int64_t P,
+                                  int64_t T, int64_t H, int64_t D, cam_dtype dt, void* out, float* lse_out,
+                                  const int32_t* cu_seqlens, const int32_t* rank_cu, const int64_t* rank_off,
+                                  int64_t nseq, void* stream)
+{
+    const char* op = "lse_combine_varlen_seq";
+    clear_error();
+    if (T > 0 && (!cu_seqlens || !rank_cu || !rank_off))
+        return set_error(CAM_ERR_NULL, "%s: cu_seqlens, rank_cu and rank_off must be non-null", op);
+    if ((rank_cu && !aligned(rank_cu, 4)) || (rank_off && !aligned(rank_off, 8)))
+        return set_error(CAM_ERR_ALIGNMENT, "%s: misaligned plan array", op);
+    if (P > 0 && nseq >= 0 && T > 0 && D >= 0 && H >= 0) {
+        const int64_t ob = T * H * D * 2, lb = lse_out ? T * H * 4 : 0;
+        if (overlaps(out, ob, rank_cu, 4 * P * (nseq + 1)) || overlaps(out, ob, rank_off, 8 * (P + 1)) ||
+            overlaps(lse_out, lb, rank_cu, 4 * P * (nseq + 1)) || overlaps(lse_out, lb, rank_off, 8 * (P + 1)))
+            return set_error(CAM_ERR_OVERLAP, "%s: an output overlaps the plan arrays", op);
+    }
+    CombineIn c{part_out, po_sp, po_st, po_sh, part_lse, pl_sp, pl_st, pl_sh, P, T, H, D, dt,
+                out, H * D, D, lse_out, H, 1, cu_seqlens, nseq};
+    c.out_mode = 2;
+    c.rank_cu = rank_cu;
+    c.rank_off = rank_off;
+    return combine(op, c, stream);
 }
 
 cam_status cam_copy(const void* src, void* dst, int64_t bytes, void* stream)

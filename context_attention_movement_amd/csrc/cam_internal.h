@@ -138,6 +138,18 @@ struct Combine {
     uint64_t n_tiles;
     uint32_t threads;       // workgroup size (64, 128 or 256)
     uint32_t xcd;           // 1: XCD-aware tile order
+    // output placement of row (t, h):
+    //   0: out + t*o_st_b + h*o_sh_b, lse_out + t*lo_st + h*lo_sh
+    //   1: the exchange view's row (r = t, q = h) goes to token-major row
+    //      g = (q / Hp)*Hq + r*Hp + q % Hp  (head scatter: [T][H][Dv])
+    //   2: token t goes to its rank-major (sequence-sharded) row of a packed
+    //      THD batch, from cu_seqlens and the varlen plan: g = row*H + h
+    uint32_t out_mode;
+    uint32_t Hp, Hq;        // mode 1: heads per rank, heads in total
+    FastDiv div_Hp;
+    uint64_t o_row_b;       // modes 1, 2: bytes per output row
+    const int32_t* rank_cu; // mode 2: the varlen plan
+    const int64_t* rank_off;
     const int32_t* cu;      // non-null: causal piece gating (varlen)
     int32_t nseq;
     FastDiv div_P;

@@ -157,6 +157,18 @@ __device__ __forceinline__ bool causal_piece_ok(const int32_t* cu, int32_t nseq,
     return start < end && int64_t(start) <= k;
 }
 
+// Rank-major (sequence-sharded) row of token t of a packed THD batch: the
+// row of the varlen relayout's sequence side for B = 1.
+__device__ __forceinline__ int64_t varlen_token_row(const int32_t* cu, const Combine& a, uint32_t t)
+{
+    const int32_t i = seq_of_token(cu, a.nseq, t);
+    const uint32_t c0 = uint32_t(cu[i]);
+    const uint32_t L = uint32_t(cu[i + 1]) - c0;
+    const uint32_t k = t - c0;
+    const uint32_t p = piece_owner(k, L, a.div_P);
+    return a.rank_off[p] + int64_t(a.rank_cu[int64_t(p) * (a.nseq + 1) + i]) + (k - piece_start(p, L, a.div_P));
+}
+
 // The combine works on tiles of kCombineRows consecutive rows per workgroup.
 // Phase 1 turns the tile's partial LSEs into weights in LDS: thread
 // (row, p) loads one LSE (consecutive rows are consecutive addresses), a group
@@ -191,7 +203,8 @@ __global__ __launch_bounds__(kThreads) void k_combine(Combine a)
     const uint32_t RB = a.rows_per_tile;
     float* w_lds = smem;                                                   // RB * P
     uint64_t* m_lds = reinterpret_cast<uint64_t*>(w_lds + ((RB * a.P + 1) & ~1u));  // RB
-    float* iz_lds = reinterpret_cast<float*>(m_lds + RB);                  // RB
+    int64_t* o_lds = reinterpret_cast<int64_t*>(m_lds + RB);               // RB: output row offsets
+    float* iz_lds = reinterpret_cast<float*>(o_lds + RB);                  // RB
     int32_t* cu_lds = reinterpret_cast<int32_t*>(iz_lds + RB);             // nseq + 1 (varlen)
     const bool cached = VARLEN && a.nseq < kCuCache;
     if (cached)  // visible after the barrier that opens every tile
@@ -253,11 +266,28 @@ __global__ __launch_bounds__(kThreads) void k_combine(Combine a)
                 if (sp < a.P)
                     w_lds[rl * a.P + sp] = w * iz;
                 if (sp == 0) {
+                    int64_t o_off, l_off;
+                    if (a.out_mode == 0) {
+                        o_off = int64_t(t) * a.o_st_b + int64_t(h) * a.o_sh_b;
+                        l_off = int64_t(t) * a.lo_st + int64_t(h) * a.lo_sh;
+                    } else {
+                        int64_t g;
+                        if (a.out_mode == 1) {
+                            const uint32_t tq = fdiv(h, a.div_Hp);
+                            g = int64_t(tq) * a.Hq + int64_t(t) * a.Hp + (h - tq * a.Hp);
+                        } else {
+                            g = (cached ? varlen_token_row(cu_lds, a, t) : varlen_token_row(a.cu, a, t)) * a.H + h;
+                        }
+                        // a plan that places the token outside [0, T) skips the row
+                        const bool in = g >= 0 && uint64_t(g) < a.n_rows;
+                        o_off = in ? g * int64_t(a.o_row_b) : -1;
+                        l_off = in ? g : -1;
+                    }
                     m_lds[rl] = vmask;
+                    o_lds[rl] = o_off;
                     iz_lds[rl] = iz;
-                    if (a.lse_out)
-                        a.lse_out[int64_t(t) * a.lo_st + int64_t(h) * a.lo_sh] =
-                            vmask ? M + logf(Z) : -__builtin_inff();
+                    if (a.lse_out && l_off >= 0)
+                        a.lse_out[l_off] = vmask ? M + logf(Z) : -__builtin_inff();
                 }
             }
         }
@@ -283,7 +313,9 @@ __global__ __launch_bounds__(kThreads) void k_combine(Combine a)
                 const uint32_t t = fdiv(uint32_t(row), a.div_H);
                 const uint32_t h = uint32_t(row) - t * a.H;
                 msk[f] = WAVE ? uniform64(m_lds[rl[f]]) : m_lds[rl[f]];
-                orow[f] = static_cast<char*>(a.out) + int64_t(t) * a.o_st_b + int64_t(h) * a.o_sh_b;
+                const int64_t ooff = WAVE ? int64_t(uniform64(uint64_t(o_lds[rl[f]]))) : o_lds[rl[f]];
+                have[f] = have[f] && ooff >= 0;
+                orow[f] = static_cast<char*>(a.out) + (ooff >= 0 ? ooff : 0);
                 // a row without valid partials reads (and discards) its own output
                 // row, so that no invalid partial row is ever read
                 prow[f] = msk[f] ? static_cast<const char*>(a.po) + int64_t(t) * a.po_st_b + int64_t(h) * a.po_sh_b
@@ -380,7 +412,7 @@ cam_status launch_combine(const Combine& a, void* stream)
     CAM_PICK(16, kCombineInFlightWave, true) CAM_PICK(8, kCombineInFlightWave, true)
     CAM_PICK(4, kCombineInFlightWave, true) CAM_PICK(2, kCombineInFlightWave, true)
 #undef CAM_PICK
-    uint64_t lds = (uint64_t(a.rows_per_tile) * a.P + 2) * 4 + uint64_t(a.rows_per_tile) * 12;
+    uint64_t lds = (uint64_t(a.rows_per_tile) * a.P + 2) * 4 + uint64_t(a.rows_per_tile) * 20;
     if (a.cu && a.nseq < kCuCache)
         lds += uint64_t(a.nseq + 1) * 4;
     return launch(fn, a, a.n_tiles, stream, "lse_combine", lds, a.threads);

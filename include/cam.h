@@ -216,6 +216,33 @@ cam_status lse_combine_varlen(const void* part_out, int64_t po_sp, int64_t po_st
                               void* stream);
 
 /* ------------------------------------------------------------------------- */
+/* Combine straight into the sequence-sharded layout ([FV] "direct output      */
+/* slices": write the destination slices directly instead of a further pass)  */
+/* ------------------------------------------------------------------------- */
+/*
+ * lse_combine_packed_seq: lse_combine_packed whose output rows go straight to
+ *   token-major order, out [T][H][Dv] and lse_out [T][H] (nullable): the row of
+ *   destination rank r for (t, head r*H/P + h') lands at (t, r*H/P + h').  This
+ *   is the combine followed by ulysses_head_to_seq of its result, in one pass.
+ *   For scatter_dim = 0 it writes what lse_combine_packed writes.
+ *
+ * lse_combine_varlen_seq: lse_combine_varlen whose combined token rows land in
+ *   the rank-major (sequence-sharded) order of the varlen relayout: the token
+ *   at local row l of rank p goes to row R_p + l of out [T][H][D] and lse_out
+ *   [T][H] (both contiguous; lse_out nullable).  cu_seqlens, rank_cu and
+ *   rank_off are the DEVICE copies of ulysses_varlen_plan's tables for the same
+ *   P (the P partials are the P KV pieces, as in lse_combine_varlen).
+ */
+cam_status lse_combine_packed_seq(const void* packed, int64_t P, int64_t T, int64_t H, int64_t Dv,
+                                  int scatter_dim, cam_dtype dt, void* out, float* lse_out,
+                                  void* stream);
+cam_status lse_combine_varlen_seq(const void* part_out, int64_t po_sp, int64_t po_st, int64_t po_sh,
+                                  const float* part_lse, int64_t pl_sp, int64_t pl_st, int64_t pl_sh,
+                                  int64_t P, int64_t T, int64_t H, int64_t D, cam_dtype dt, void* out,
+                                  float* lse_out, const int32_t* cu_seqlens, const int32_t* rank_cu,
+                                  const int64_t* rank_off, int64_t nseq, void* stream);
+
+/* ------------------------------------------------------------------------- */
 /* Measurement helper                                                          */
 /* ------------------------------------------------------------------------- */
 /*

@@ -73,6 +73,8 @@ def _load():
         "orc_lse_combine_packed": (None, [vp, i64, i64, i64, i64, C.c_int, C.c_int, vp, vp]),
         "orc_attention": (None, [vp, vp, vp, i64, i64, i64, C.c_int, i64, i64, C.c_int,
                                  vp, vp, vp]),
+        "orc_varlen_token_rows": (None, [vp, i64, i64, vp]),
+        "orc_lse_combine_packed_seq": (None, [vp, i64, i64, i64, i64, C.c_int, C.c_int, vp, vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -285,6 +287,36 @@ def lse_combine_packed(packed: np.ndarray, P, T, H, Dv, scatter_dim, dtype="bf16
     _load().orc_lse_combine_packed(_p(np.ascontiguousarray(packed)), P, T, H, Dv, scatter_dim,
                                    _dt(dtype), _p(out), _p(lse))
     return out, lse
+
+
+def varlen_token_rows(cu: np.ndarray, P: int) -> np.ndarray:
+    """Rank-major (sequence-sharded) row of every global token."""
+    cu = np.ascontiguousarray(cu, dtype=np.int32)
+    rows = np.empty(int(cu[-1]), dtype=np.int64)
+    _load().orc_varlen_token_rows(_p(cu), cu.size - 1, P, _p(rows))
+    return rows
+
+
+def lse_combine_packed_seq(packed: np.ndarray, P, T, H, Dv, scatter_dim, dtype="bf16"):
+    """Packed combine with token-major output: (out [T][H][Dv], lse [T][H])."""
+    out = np.empty((T, H, Dv), dtype=np.uint16)
+    lse = np.empty((T, H), dtype=np.float32)
+    _load().orc_lse_combine_packed_seq(_p(np.ascontiguousarray(packed)), P, T, H, Dv, scatter_dim,
+                                       _dt(dtype), _p(out), _p(lse))
+    return out, lse
+
+
+def lse_combine_varlen_seq(part_out: np.ndarray, part_lse: np.ndarray, cu: np.ndarray, dtype="bf16"):
+    """Causal varlen combine whose token rows land in the rank-major
+    (sequence-sharded) order of the varlen relayout: (out [T][H][D], lse [T][H])."""
+    P = part_out.shape[0]
+    out, lse = lse_combine(part_out, part_lse, dtype=dtype, cu=cu)
+    rows = varlen_token_rows(cu, P)
+    o2 = np.empty_like(out)
+    l2 = np.empty_like(lse)
+    o2[rows] = out
+    l2[rows] = lse
+    return o2, l2
 
 
 # -- attention --------------------------------------------------------------

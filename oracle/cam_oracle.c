@@ -585,3 +585,55 @@ void orc_attention(const void* q, const void* k, const void* v, int64_t T, int64
         }
     free(score);
 }
+
+/* ------------------------------------------------------------------------ */
+/* Combine with the sequence-sharded output layout (the combine followed by   */
+/* the head->seq relayout of its result, [FV] "direct output slices")         */
+/* ------------------------------------------------------------------------ */
+
+/* Rank-major (sequence-sharded) row of every global token of a packed THD
+ * batch: token cu[i] + k at position k of piece p of sequence i sits at row
+ * R_p + (tokens of rank p before sequence i) + (k - floor(p*L/P)), the order
+ * of the varlen relayout's sequence side.  row[t] for t < cu[nseq]. */
+void orc_varlen_token_rows(const int32_t* cu, int64_t nseq, int64_t P, int64_t* row)
+{
+    int64_t R = 0;
+    for (int64_t p = 0; p < P; ++p) {
+        int64_t l = 0;
+        for (int64_t i = 0; i < nseq; ++i) {
+            int64_t L = (int64_t)cu[i + 1] - cu[i];
+            for (int64_t k = piece_start(p, L, P); k < piece_start(p + 1, L, P); ++k)
+                row[cu[i] + k] = R + l++;
+        }
+        R += l;
+    }
+}
+
+/* The packed combine, then its result moved to token-major order:
+ * out [T][H][Dv], lse_out [T][H] (nullable).  For scatter_dim = 1 the
+ * destination-major result row (r, t*(H/P) + h') goes to (t, r*H/P + h');
+ * for scatter_dim = 0 the two orders coincide. */
+void orc_lse_combine_packed_seq(const void* packed, int64_t P, int64_t T, int64_t H, int64_t Dv,
+                                int scatter_dim, int dtype, void* out, float* lse_out)
+{
+    int64_t rows = orc_pack_rows(P, T, H, scatter_dim);
+    uint16_t* tmp = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)(P * rows * Dv + 1));
+    float* ltmp = (float*)malloc(sizeof(float) * (size_t)(P * rows + 1));
+    orc_lse_combine_packed(packed, P, T, H, Dv, scatter_dim, dtype, tmp, ltmp);
+    for (int64_t r = 0; r < P; ++r)
+        for (int64_t q = 0; q < rows; ++q) {
+            int64_t t, h;
+            if (scatter_dim == 1) {
+                t = q / (H / P);
+                h = r * (H / P) + q % (H / P);
+            } else {
+                t = r * (T / P) + q / H;
+                h = q % H;
+            }
+            memcpy((char*)out + (t * H + h) * Dv * 2, tmp + (r * rows + q) * Dv, (size_t)(Dv * 2));
+            if (lse_out)
+                lse_out[t * H + h] = ltmp[r * rows + q];
+        }
+    free(tmp);
+    free(ltmp);
+}

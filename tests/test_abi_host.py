@@ -42,6 +42,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ["ulysses_seq_to_head", "ulysses_head_to_seq", "ulysses_varlen_plan", "ulysses_seq_to_head_varlen",
+              "lse_combine_packed_seq", "lse_combine_varlen_seq",
               "ulysses_head_to_seq_varlen", "lse_pack_bytes", "lse_pack", "lse_combine_packed", "lse_combine",
               "lse_combine_varlen", "cam_status_string", "cam_last_error", "cam_abi_version", "cam_copy"]:
         assert n in names
@@ -210,3 +211,19 @@ def test_fast_division_constants_are_exact():
         for n in ns + [d - 1, d, d + 1, 2 * d - 1, 2 * d, (2**32 - 1) // d * d, (2**32 - 1) // d * d - 1]:
             if 0 <= n < 2**32:
                 assert ((n * m >> 32) + n) >> l == n // d, (d, n)
+
+
+def test_fused_epilogue_rejections(lib):
+    O, LO, PK = A + 0x3000_0000, A + 0x4000_0000, A
+    f = lib.lse_combine_packed_seq
+    assert f(PK + 8, 8, 128, 128, 512, 1, BF16, O, LO, None) == ALIGN
+    assert f(PK, 8, 128, 128, 512, 1, BF16, PK + 64, LO, None) == OVERLAP
+    assert f(PK, 3, 128, 128, 512, 1, BF16, O, LO, None) == DIV
+    assert f(None, 8, 128, 128, 512, 1, BF16, O, LO, None) == NULL
+    g = lib.lse_combine_varlen_seq
+    cu, rc, ro = A + 0x5000_0000, A + 0x6000_0000, A + 0x7000_0000
+    args = lambda out=O, rc=rc, ro=ro: (A, 64 * 8 * 16, 8 * 16, 16, A + 0x1000_0000, 64 * 8, 8, 1, 4, 64, 8, 16, BF16,
+                                        out, LO, cu, rc, ro, 3, None)
+    assert g(*args(rc=None)) == NULL
+    assert g(*args(ro=ro + 4)) == ALIGN
+    assert g(*args(out=rc)) == OVERLAP

@@ -307,3 +307,36 @@ def test_varlen_combine_skips_masked_partials(orc):
     a, b = 4, 13
     wo, wl = orc.lse_combine(np.ascontiguousarray(o[:, a:b]), np.ascontiguousarray(l[:, a:b]), cu=cu, t_begin=a)
     assert np.array_equal(wo, out[a:b]) and np.array_equal(wl, lse[a:b])
+
+
+# ------------------- combine with sequence-sharded output -------------------
+
+def test_token_rows_match_varlen_relayout(orc):
+    """The rank-major row of each token is where the varlen head->seq relayout
+    puts that token's row (checked with an index payload over P = 1 heads)."""
+    for lengths, P in (([5, 0, 9, 1, 3], 3), ([17, 33, 2, 64], 4), ([3], 8)):
+        cu = synth.cu_seqlens(lengths)
+        T = int(cu[-1])
+        rows = orc.varlen_token_rows(cu, P)
+        assert np.array_equal(np.sort(rows), np.arange(T))
+        # head-sharded payload whose value is the token index, one head per rank
+        x = np.broadcast_to(np.arange(T, dtype=np.uint32)[None, None, :, None, None], (P, 1, T, 1, 1)).copy()
+        y = orc.varlen_head_to_seq(x, cu, P, 1, P, 1).reshape(T, P)
+        assert np.array_equal(y[rows, 0], np.arange(T))
+
+
+@pytest.mark.parametrize("sd", [0, 1])
+def test_packed_seq_is_combine_then_head_to_seq(orc, sd):
+    P, T, H, Dv = 4, 8, 8, 16
+    o, m, s, _ = synth.dcp_partials(P, T, H, Dv, seed=17, corrupt_frac=0.1)
+    packed = orc.lse_pack(synth.bits(o), m.numpy(), s.numpy(), sd)
+    out, lse = orc.lse_combine_packed_seq(packed, P, T, H, Dv, sd)
+    comb, clse = orc.lse_combine_packed(packed, P, T, H, Dv, sd)
+    if sd == 0:
+        assert np.array_equal(out.reshape(-1, Dv), comb) and np.array_equal(lse.reshape(-1), clse)
+    else:
+        # destination-major [P][T][H/P][Dv] moved by the dense head->seq relayout (B = 1)
+        ref = orc.head_to_seq(comb.reshape(P, 1, T, H // P, Dv), P, 1, T, H, Dv).reshape(T, H, Dv)
+        assert np.array_equal(out, ref)
+        lref = orc.head_to_seq(clse.reshape(P, 1, T, H // P, 1), P, 1, T, H, 1).reshape(T, H)
+        assert np.array_equal(lse, lref)
