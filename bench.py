@@ -130,6 +130,10 @@ class Workload:
         self.t_comb = torch.empty((T, H, D), dtype=bf, device=dev)
         self.t_comb_lse = torch.empty((T, H), dtype=torch.float32, device=dev)
         self.t_admitted = thd_admitted_counts(self.t_cu, P)
+        # ring of online merges: fp32 accumulator (payload and LSE) per token row
+        self.t_acc = torch.empty((T, H, D), dtype=torch.float32, device=dev)
+        self.t_acc_lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+        self.t_ring_out = torch.empty((T, H, D), dtype=bf, device=dev)
         # sequence-sharded outputs of the fused combine epilogues
         self.t_comb_seq = torch.empty((T, H, D), dtype=bf, device=dev)
         self.t_comb_seq_lse = torch.empty((T, H), dtype=torch.float32, device=dev)
@@ -212,7 +216,23 @@ class Workload:
             cam.lse_combine_varlen_seq(self.t_part, self.t_lse, self.t_plan, out=self.t_comb_seq,
                                        lse_out=self.t_comb_seq_lse)
 
+        T, H, D, P = self.tT, self.tH, self.tD, self.tP
+
+        def ring():
+            # P hops; the partial that arrives at hop h is t_part[h]; the empty
+            # accumulator is marked by LSE = -inf (its payload is ignored)
+            self.t_acc_lse.fill_(float("-inf"))
+            for hop in range(P):
+                cam.lse_merge(self.t_acc, self.t_acc_lse, self.t_part[hop], self.t_lse[hop],
+                              out_final=self.t_ring_out if hop == P - 1 else None)
+
+        rows = T * H
+        # hop 0 reads no accumulator; every hop reads the partial and both LSEs
+        # and writes the accumulator; the last hop also writes the rounded rows
+        ring_bytes = rows * (P * (2 * D + 4 + 4 * D + 4 + 4) + (P - 1) * (4 * D) + 2 * D + 4)
+
         return [
+            ("ring_of_8_online_merges_thd (fp32 accumulator)", ring_bytes, ring),
             ("combine_to_sequence_shards_mla (fused)", comb_bytes, fused),
             ("combine_then_head_to_seq_mla (unfused)", comb_bytes + 2 * out_bytes, unfused),
             ("combine_varlen_to_sequence_shards_thd (fused)", self.op_bytes()["lse_combine_varlen_thd"], thd_fused),

@@ -25,7 +25,7 @@ __all__ = [
     "ulysses_seq_to_head", "ulysses_head_to_seq",
     "VarlenPlan", "ulysses_varlen_plan", "ulysses_seq_to_head_varlen", "ulysses_head_to_seq_varlen",
     "lse_pack_bytes", "lse_pack", "lse_combine_packed", "lse_combine", "lse_combine_varlen",
-    "lse_combine_packed_seq", "lse_combine_varlen_seq",
+    "lse_combine_packed_seq", "lse_combine_varlen_seq", "lse_merge",
     "copy",
 ]
 
@@ -69,6 +69,8 @@ _SIGNATURES = {
     "lse_combine_packed_seq": (_int, [_vp, _i64, _i64, _i64, _i64, _int, _int, _vp, _vp, _vp]),
     "lse_combine_varlen_seq": (_int, [_vp, _i64, _i64, _i64, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _i64,
                                       _int, _vp, _vp, _vp, _vp, _vp, _i64, _vp]),
+    "lse_merge": (_int, [_vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _i64, _i64, _i64,
+                         _int, _vp, _i64, _i64, _vp]),
 }
 
 
@@ -401,6 +403,32 @@ def lse_combine_varlen_seq(part_out: torch.Tensor, part_lse: torch.Tensor, plan:
                                             _ptr(lse_out), plan.cu.data_ptr(), plan.rank_cu.data_ptr(),
                                             plan.rank_off.data_ptr(), plan.nseq, _stream(part_out)))
     return out, lse_out
+
+
+def lse_merge(acc_out: torch.Tensor, acc_lse: torch.Tensor, part_out: torch.Tensor, part_lse: torch.Tensor,
+              out_final: torch.Tensor | None = None):
+    """In place: (acc_out fp32 [T][H][D], acc_lse fp32 [T][H]) <- stable combine of
+    the accumulator and one partial (part_out [T][H][D] bf16/fp16, part_lse
+    [T][H]); optionally also writes the rounded result to out_final."""
+    for t_, n in ((acc_out, "acc_out"), (acc_lse, "acc_lse"), (part_out, "part_out"), (part_lse, "part_lse")):
+        _dev(t_, n)
+    if acc_out.dtype != torch.float32 or acc_lse.dtype != torch.float32 or part_lse.dtype != torch.float32:
+        raise TypeError("accumulator and LSEs must be float32")
+    if acc_out.dim() != 3 or part_out.dim() != 3 or acc_out.stride(2) != 1 or part_out.stride(2) != 1:
+        raise ValueError("payloads must be [T][H][D] with D contiguous")
+    T, H, D = part_out.shape
+    if tuple(acc_out.shape) != (T, H, D) or tuple(acc_lse.shape) != (T, H) or tuple(part_lse.shape) != (T, H):
+        raise ValueError("shape mismatch")
+    fs = (0, 0)
+    if out_final is not None:
+        _dev(out_final, "out_final")
+        if out_final.dim() != 3 or out_final.stride(2) != 1 or out_final.dtype != part_out.dtype:
+            raise ValueError("out_final must be [T][H][D] like part_out")
+        fs = out_final.stride()[:2]
+    _check(library().lse_merge(acc_out.data_ptr(), *acc_out.stride()[:2], acc_lse.data_ptr(), *acc_lse.stride(),
+                               part_out.data_ptr(), *part_out.stride()[:2], part_lse.data_ptr(), *part_lse.stride(),
+                               T, H, D, _dt(part_out), _ptr(out_final), *fs, _stream(part_out)))
+    return acc_out, acc_lse
 
 
 def copy(src: torch.Tensor, dst: torch.Tensor) -> torch.Tensor:

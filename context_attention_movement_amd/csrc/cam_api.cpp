@@ -718,6 +718,71 @@ cam_status lse_combine_varlen_seq(const void* part_out, int64_t po_sp, int64_t p
     return combine(op, c, stream);
 }
 
+cam_status lse_merge(float* acc_out, int64_t a_st, int64_t a_sh, float* acc_lse, int64_t al_st, int64_t al_sh,
+                     const void* part_out, int64_t p_st, int64_t p_sh, const float* part_lse, int64_t pl_st,
+                     int64_t pl_sh, int64_t T, int64_t H, int64_t D, cam_dtype dt, void* out_final, int64_t f_st,
+                     int64_t f_sh, void* stream)
+{
+    const char* op = "lse_merge";
+    clear_error();
+    if (T < 0 || H < 0 || D < 0)
+        return set_error(CAM_ERR_SHAPE, "%s: need T, H, D >= 0", op);
+    if (dt != CAM_BF16 && dt != CAM_FP16)
+        return set_error(CAM_ERR_UNSUPPORTED, "%s: payload dtype must be bf16 or fp16", op);
+    for (int64_t s : {a_st, a_sh, al_st, al_sh, p_st, p_sh, pl_st, pl_sh, f_st, f_sh})
+        if (s < 0)
+            return set_error(CAM_ERR_UNSUPPORTED, "%s: strides must be non-negative", op);
+    int64_t n_rows;
+    if (!prod_ok({T, H}, &n_rows))
+        return set_error(CAM_ERR_SHAPE, "%s: T*H overflows", op);
+    if (n_rows == 0)
+        return CAM_OK;
+    if (n_rows > INT32_MAX)
+        return set_error(CAM_ERR_UNSUPPORTED, "%s: T*H must be below 2^31 rows", op);
+    if (!acc_out || !acc_lse || !part_out || !part_lse)
+        return set_error(CAM_ERR_NULL, "%s: accumulator and partial pointers must be non-null", op);
+    if (D % 4)
+        return set_error(CAM_ERR_ALIGNMENT, "%s: D must be a multiple of 4 (4-element accesses)", op);
+    if (!aligned(acc_out, 16) || a_st % 4 || a_sh % 4 || !aligned(part_out, 8) || p_st % 4 || p_sh % 4 ||
+        !aligned(acc_lse, 4) || !aligned(part_lse, 4) ||
+        (out_final && (!aligned(out_final, 8) || f_st % 4 || f_sh % 4)))
+        return set_error(CAM_ERR_ALIGNMENT, "%s: rows must start 16-byte (accumulator) / 8-byte (payload) aligned", op);
+    int64_t e_a, e_al, e_p, e_pl, e_f = 0;
+    if (!extent({T, H, D}, {a_st, a_sh, 1}, 4, &e_a) || !extent({T, H}, {al_st, al_sh}, 4, &e_al) ||
+        !extent({T, H, D}, {p_st, p_sh, 1}, 2, &e_p) || !extent({T, H}, {pl_st, pl_sh}, 4, &e_pl) ||
+        (out_final && !extent({T, H, D}, {f_st, f_sh, 1}, 2, &e_f)))
+        return set_error(CAM_ERR_SHAPE, "%s: tensor extent overflows", op);
+    if (overlaps(acc_out, e_a, part_out, e_p) || overlaps(acc_out, e_a, part_lse, e_pl) ||
+        overlaps(acc_lse, e_al, part_out, e_p) || overlaps(acc_lse, e_al, part_lse, e_pl) ||
+        overlaps(acc_out, e_a, acc_lse, e_al) || overlaps(out_final, e_f, acc_out, e_a) ||
+        overlaps(out_final, e_f, acc_lse, e_al) || overlaps(out_final, e_f, part_out, e_p) ||
+        overlaps(out_final, e_f, part_lse, e_pl))
+        return set_error(CAM_ERR_OVERLAP, "%s: buffers overlap", op);
+    Merge a{};
+    a.acc = acc_out;
+    a.a_st = a_st;
+    a.a_sh = a_sh;
+    a.acc_lse = acc_lse;
+    a.al_st = al_st;
+    a.al_sh = al_sh;
+    a.part = part_out;
+    a.p_st_b = p_st * 2;
+    a.p_sh_b = p_sh * 2;
+    a.part_lse = part_lse;
+    a.pl_st = pl_st;
+    a.pl_sh = pl_sh;
+    a.fin = out_final;
+    a.f_st_b = f_st * 2;
+    a.f_sh_b = f_sh * 2;
+    a.H = uint32_t(H);
+    a.div_H = make_fastdiv(a.H);
+    a.n_rows = uint64_t(n_rows);
+    a.cv = uint32_t(D / 4);
+    a.g_log2 = log2u(pow2ceil(a.cv < 64 ? (a.cv ? a.cv : 1) : 64));
+    a.fp16 = dt == CAM_FP16;
+    return launch_merge(a, stream);
+}
+
 cam_status cam_copy(const void* src, void* dst, int64_t bytes, void* stream)
 {
     clear_error();

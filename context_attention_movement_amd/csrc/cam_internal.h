@@ -157,6 +157,27 @@ struct Combine {
     int fp16;               // payload: 0 bf16, 1 fp16
 };
 
+// Online two-way merge: accumulator (fp32 payload + fp32 LSE) <- stable
+// combine of itself and one partial.  Rows (t, h); a lane moves 4 elements.
+struct Merge {
+    float* acc;
+    int64_t a_st, a_sh;     // element strides (4-element aligned)
+    float* acc_lse;
+    int64_t al_st, al_sh;
+    const void* part;
+    int64_t p_st_b, p_sh_b; // byte strides
+    const float* part_lse;
+    int64_t pl_st, pl_sh;
+    void* fin;              // optional rounded payload (nullable)
+    int64_t f_st_b, f_sh_b;
+    uint32_t H;
+    FastDiv div_H;
+    uint64_t n_rows;
+    uint32_t cv;            // 4-element chunks per row
+    uint32_t g_log2;        // lanes per row
+    int fp16;
+};
+
 struct Copy {
     const void* src;
     void* dst;
@@ -170,6 +191,7 @@ cam_status launch_varlen_relayout(const VarlenRelayout& a, void* stream);
 cam_status launch_pack(const Pack& a, void* stream);
 cam_status launch_combine(const Combine& a, void* stream);
 cam_status launch_copy(const Copy& a, void* stream);
+cam_status launch_merge(const Merge& a, void* stream);
 
 // Error reporting shared by the host layer and the launchers.
 cam_status set_error(cam_status s, const char* fmt, ...);

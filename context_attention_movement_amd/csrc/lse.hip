@@ -390,6 +390,82 @@ __global__ __launch_bounds__(kThreads) void k_combine(Combine a)
     }
 }
 
+// ---------------------------------------------------------------------------
+// Online two-way merge (ring / context-parallel accumulation)
+// ---------------------------------------------------------------------------
+
+// Per row: La = accumulator LSE (-inf: empty), Lb = partial LSE; the valid ones
+// (finite) are combined with weights exp(L - max); the accumulator row is
+// rewritten in fp32 and, if asked, the rounded payload too.  A group of G lanes
+// covers a row, 4 elements per lane; an invalid partial's row is never read
+// (its lane re-reads the accumulator row, a valid address, and discards it).
+template <bool FP16, bool FINAL>
+__global__ __launch_bounds__(kThreads) void k_merge(Merge a)
+{
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    const uint32_t G = 1u << a.g_log2;
+    const uint32_t gl = threadIdx.x & (G - 1u);
+    const uint64_t rows_per_block = uint64_t(kThreads) >> a.g_log2;
+    for (uint64_t rb = uint64_t(blockIdx.x) * rows_per_block; rb < a.n_rows;
+         rb += uint64_t(gridDim.x) * rows_per_block) {
+        const uint64_t row = rb + (threadIdx.x >> a.g_log2);
+        if (row >= a.n_rows)
+            continue;
+        const uint32_t t = fdiv(uint32_t(row), a.div_H);
+        const uint32_t h = uint32_t(row) - t * a.H;
+        const float La = a.acc_lse[int64_t(t) * a.al_st + int64_t(h) * a.al_sh];
+        const float Lb = a.part_lse[int64_t(t) * a.pl_st + int64_t(h) * a.pl_sh];
+        const bool va = __builtin_isfinite(La), vb = __builtin_isfinite(Lb);
+        const float M = va ? (vb ? fmaxf(La, Lb) : La) : Lb;
+        const float wa = va ? expf(La - M) : 0.0f;
+        const float wb = vb ? expf(Lb - M) : 0.0f;
+        const float Z = wa + wb;
+        const bool any = va || vb;
+        const float sa = any ? wa / Z : 0.0f, sb = any ? wb / Z : 0.0f;
+        float* arow = a.acc + int64_t(t) * a.a_st + int64_t(h) * a.a_sh;
+        const char* prow = vb ? static_cast<const char*>(a.part) + int64_t(t) * a.p_st_b + int64_t(h) * a.p_sh_b
+                              : reinterpret_cast<const char*>(arow);
+        char* frow = FINAL ? static_cast<char*>(a.fin) + int64_t(t) * a.f_st_b + int64_t(h) * a.f_sh_b : nullptr;
+        for (uint32_t k = gl; k < a.cv; k += G) {
+            const f32x4 x = *reinterpret_cast<const f32x4*>(arow + 4 * k);
+            const u32x2 y = *reinterpret_cast<const u32x2*>(prow + 8 * k);
+            issue_fence();
+            const float b0 = FP16 ? fp16_lo(y.x) : bf16_lo(y.x), b1 = FP16 ? fp16_hi(y.x) : bf16_hi(y.x);
+            const float b2 = FP16 ? fp16_lo(y.y) : bf16_lo(y.y), b3 = FP16 ? fp16_hi(y.y) : bf16_hi(y.y);
+            f32x4 r;
+            r.x = (va ? sa * x.x : 0.0f) + (vb ? sb * b0 : 0.0f);
+            r.y = (va ? sa * x.y : 0.0f) + (vb ? sb * b1 : 0.0f);
+            r.z = (va ? sa * x.z : 0.0f) + (vb ? sb * b2 : 0.0f);
+            r.w = (va ? sa * x.w : 0.0f) + (vb ? sb * b3 : 0.0f);
+            *reinterpret_cast<f32x4*>(arow + 4 * k) = r;
+            if (FINAL) {
+                u32x2 o;
+                if (FP16) {
+                    o.x = f32_to_fp16_bits(r.x) | (f32_to_fp16_bits(r.y) << 16);
+                    o.y = f32_to_fp16_bits(r.z) | (f32_to_fp16_bits(r.w) << 16);
+                } else {
+                    o.x = f32_to_bf16_bits(r.x) | (f32_to_bf16_bits(r.y) << 16);
+                    o.y = f32_to_bf16_bits(r.z) | (f32_to_bf16_bits(r.w) << 16);
+                }
+                *reinterpret_cast<u32x2*>(frow + 8 * k) = o;
+            }
+        }
+        if (gl == 0)
+            a.acc_lse[int64_t(t) * a.al_st + int64_t(h) * a.al_sh] = any ? M + logf(Z) : -__builtin_inff();
+    }
+}
+
+cam_status launch_merge(const Merge& a, void* stream)
+{
+    const void* fn = a.fin ? (a.fp16 ? reinterpret_cast<const void*>(&k_merge<true, true>)
+                                     : reinterpret_cast<const void*>(&k_merge<false, true>))
+                           : (a.fp16 ? reinterpret_cast<const void*>(&k_merge<true, false>)
+                                     : reinterpret_cast<const void*>(&k_merge<false, false>));
+    const uint64_t rows_per_block = uint64_t(kThreads) >> a.g_log2;
+    return launch(fn, a, (a.n_rows + rows_per_block - 1) / rows_per_block, stream, "lse_merge");
+}
+
 cam_status launch_combine(const Combine& a, void* stream)
 {
     // Rows of at least 512 bytes (one or more full 64-lane passes) keep two

@@ -243,6 +243,33 @@ cam_status lse_combine_varlen_seq(const void* part_out, int64_t po_sp, int64_t p
                                   const int64_t* rank_off, int64_t nseq, void* stream);
 
 /* ------------------------------------------------------------------------- */
+/* Online two-way merge for ring / context-parallel accumulation ([CU] ring    */
+/* transport of the logical-CP emulation; [VA] stable combine semantics)       */
+/* ------------------------------------------------------------------------- */
+/*
+ * lse_merge: per row (t, h) the accumulator (acc_out fp32 [T][H][D], acc_lse
+ *   fp32 [T][H]) becomes the stable combine of itself and one partial
+ *   (part_out [T][H][D] payload dt, part_lse fp32 [T][H]):
+ *     M = max of the finite LSEs; w = exp(L - M) for each finite one;
+ *     acc_out = (w_a*acc_out + w_b*part_out) / (w_a + w_b);
+ *     acc_lse = M + log(w_a + w_b).
+ *   An accumulator whose LSE is not finite is empty (its payload is ignored,
+ *   so it may start uninitialised with acc_lse = -inf); if both are invalid the
+ *   row becomes +0 with -inf LSE.  An invalid partial's row is never read.
+ *   Merging the P partials of a row one hop at a time gives their one-shot
+ *   combine (the combine is associative); the accumulator stays fp32 between
+ *   hops.  out_final (nullable, payload dt [T][H][D]) also receives the
+ *   rounded result, for the last hop.  All strides are in elements (D
+ *   contiguous); D % 4 == 0; accumulator rows 16-byte and payload rows 8-byte
+ *   aligned.  Updates in place; no buffer may overlap another.
+ */
+cam_status lse_merge(float* acc_out, int64_t a_st, int64_t a_sh, float* acc_lse, int64_t al_st,
+                     int64_t al_sh, const void* part_out, int64_t p_st, int64_t p_sh,
+                     const float* part_lse, int64_t pl_st, int64_t pl_sh, int64_t T, int64_t H,
+                     int64_t D, cam_dtype dt, void* out_final, int64_t f_st, int64_t f_sh,
+                     void* stream);
+
+/* ------------------------------------------------------------------------- */
 /* Measurement helper                                                          */
 /* ------------------------------------------------------------------------- */
 /*

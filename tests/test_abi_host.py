@@ -42,7 +42,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ["ulysses_seq_to_head", "ulysses_head_to_seq", "ulysses_varlen_plan", "ulysses_seq_to_head_varlen",
-              "lse_combine_packed_seq", "lse_combine_varlen_seq",
+              "lse_combine_packed_seq", "lse_combine_varlen_seq", "lse_merge",
               "ulysses_head_to_seq_varlen", "lse_pack_bytes", "lse_pack", "lse_combine_packed", "lse_combine",
               "lse_combine_varlen", "cam_status_string", "cam_last_error", "cam_abi_version", "cam_copy"]:
         assert n in names
@@ -227,3 +227,16 @@ def test_fused_epilogue_rejections(lib):
     assert g(*args(rc=None)) == NULL
     assert g(*args(ro=ro + 4)) == ALIGN
     assert g(*args(out=rc)) == OVERLAP
+
+
+def test_merge_rejections(lib):
+    f = lib.lse_merge
+    AL, PP, PL, F = A + 0x1000_0000, A + 0x2000_0000, A + 0x3000_0000, A + 0x4000_0000
+    args = lambda acc=A, D=64, part=PP, fin=F, dt=BF16: (acc, 8 * D, D, AL, 8, 1, part, 8 * D, D, PL, 8, 1, 16, 8, D,
+                                                         dt, fin, 8 * D, D, None)
+    assert f(*args(D=6)) == ALIGN
+    assert f(*args(acc=A + 8)) == ALIGN
+    assert f(*args(part=A + 64)) == OVERLAP
+    assert f(*args(fin=PP)) == OVERLAP
+    assert f(*args(dt=FP32)) == UNSUP
+    assert f(*args(acc=None)) == NULL
