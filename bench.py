@@ -21,7 +21,7 @@ read once, each output written once, invalid or causally masked partials not
 read) divided by the step time.  Per-operation figures are under "ops".
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
-    python bench.py --summarize-rocprof DIR --kernel NAME ...   (profile text)
+    python bench.py --summarize-rocprof TRACE FETCH WRITE BENCH_JSON --summary-out F --command TEXT
 """
 
 from __future__ import annotations
@@ -184,12 +184,12 @@ class Workload:
             ("relayout_head_to_seq_video_p4_o", "k_dense_relayout<16, false>",
              lambda: cam.ulysses_head_to_seq(self.v_o, self.vP, out=self.v_o_out)),
             ("lse_pack_mla", "k_pack<16>", pack),
-            ("lse_combine_mla", "k_combine<16, false, false, 1, true>", combine),
+            ("lse_combine_mla", "k_combine<16, false, false, 1, true, 0>", combine),
             ("relayout_seq_to_head_varlen_thd_qkv", "k_varlen_relayout<16, true>",
              lambda: cam.ulysses_seq_to_head_varlen(self.t_qkv, self.t_plan, 3, out=self.t_qkv_out)),
             ("relayout_head_to_seq_varlen_thd_o", "k_varlen_relayout<16, false>",
              lambda: cam.ulysses_head_to_seq_varlen(self.t_o, self.t_plan, out=self.t_o_out)),
-            ("lse_combine_varlen_thd", "k_combine<16, false, true, 1, false>",
+            ("lse_combine_varlen_thd", "k_combine<16, false, true, 1, false, 0>",
              lambda: cam.lse_combine_varlen(self.t_part, self.t_lse, self.t_cu_dev, out=self.t_comb,
                                             lse_out=self.t_comb_lse)),
         ]
@@ -345,78 +345,108 @@ def _read_csvs(root, suffix):
     return rows
 
 
-OP_KERNELS = [  # (op, kernel name fragment as rocprofv3 reports it)
-    ("relayout_seq_to_head_video_p4_qkv", "k_dense_relayout<16, true>"),
-    ("relayout_head_to_seq_video_p4_o", "k_dense_relayout<16, false>"),
-    ("lse_pack_mla", "k_pack<16>"),
-    ("lse_combine_mla", "k_combine<16, false, false, 1, true>"),
-    ("relayout_seq_to_head_varlen_thd_qkv", "k_varlen_relayout<16, true>"),
-    ("relayout_head_to_seq_varlen_thd_o", "k_varlen_relayout<16, false>"),
-    ("lse_combine_varlen_thd", "k_combine<16, false, true, 1, false>"),
-]
 COPY_KERNEL = "k_copy16"
 COPY_BYTES = 3 * 32760 * 24 * 128 * 2  # the video Q/K/V operand copied for the ceiling (each way)
 
 
-def summarize_rocprof(trace_dir, fetch_dir, write_dir, out_txt, command):
-    """Write a short text summary of rocprofv3 output (kernel statistics and
-    per-dispatch FETCH_SIZE / WRITE_SIZE) and, when both counters are given,
-    profiles/traffic.json: each kernel's HBM bytes per launch, scaled by what
-    the same counters read for the plain copy kernel of known size."""
+def _grid_threads(r):
+    g = r.get("Grid_Size_X", r.get("Grid_Size"))
+    return int(float(g)) if g not in (None, "") else -1
+
+
+def summarize_rocprof(trace_dir, fetch_dir, write_dir, bench_json, out_txt, command):
+    """Write a short text summary of rocprofv3 output and, when both counters
+    are given, profiles/traffic.json.
+
+    - rocprofv3's own kernel statistics (--stats), as printed;
+    - per kernel and grid size, the dispatch durations from the kernel trace
+      (one kernel can serve several operations at different grid sizes);
+    - each operation of the step, matched to its dispatches by kernel name and
+      grid size (bench.py records both per operation), with its average
+      duration and its HBM bytes per launch: FETCH_SIZE and WRITE_SIZE per
+      dispatch, each scaled by what the same counter reads for the plain copy
+      kernel of known size."""
     lines = [f"command: {command}", ""]
     stats = _read_csvs(trace_dir, "kernel_stats.csv") if trace_dir else []
     if stats:
         lines.append("kernel statistics (rocprofv3 --kernel-trace --stats), microseconds:")
-        lines.append(f"{'kernel':64s} {'calls':>6s} {'avg':>10s} {'min':>10s} {'max':>10s}")
+        lines.append(f"{'kernel':70s} {'calls':>6s} {'avg':>10s} {'min':>10s} {'max':>10s}")
         for r in stats:
             name = r.get("Name", r.get("KernelName", ""))
             if "cam::" not in name:
                 continue
-            lines.append(f"{name[:64]:64s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.2f} "
+            lines.append(f"{name[:70]:70s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.2f} "
                          f"{float(r['MinNs']) / 1e3:10.2f} {float(r['MaxNs']) / 1e3:10.2f}")
+        lines.append("")
+    durs = {}
+    for r in (_read_csvs(trace_dir, "kernel_trace.csv") if trace_dir else []):
+        name = r.get("Kernel_Name", "")
+        if "cam::" in name:
+            durs.setdefault((name, _grid_threads(r)), []).append(
+                (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    if durs:
+        lines.append("per kernel and grid size (kernel trace), microseconds:")
+        lines.append(f"{'kernel':70s} {'grid':>10s} {'calls':>6s} {'avg':>10s} {'min':>10s} {'max':>10s}")
+        for (name, g), v in sorted(durs.items(), key=lambda kv: -sum(kv[1])):
+            lines.append(f"{name[:70]:70s} {g:10d} {len(v):6d} {statistics.mean(v):10.2f} "
+                         f"{min(v):10.2f} {max(v):10.2f}")
         lines.append("")
     med = {}
     for d, cname in ((fetch_dir, "FETCH_SIZE"), (write_dir, "WRITE_SIZE")):
         if not d:
             continue
-        per_kernel = {}
+        per = {}
         for r in _read_csvs(d, "counter_collection.csv"):
-            if r.get("Counter_Name") != cname:
-                continue
-            per_kernel.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
-        med[cname] = {k: statistics.median(v) for k, v in per_kernel.items()}
+            if r.get("Counter_Name") == cname and "cam::" in r["Kernel_Name"]:
+                per.setdefault((r["Kernel_Name"], _grid_threads(r)), []).append(float(r["Counter_Value"]))
+        med[cname] = {k: statistics.median(v) for k, v in per.items()}
         lines.append(f"{cname} per dispatch (KiB, median over dispatches):")
-        for k, v in sorted(per_kernel.items()):
-            if "cam::" in k:
-                lines.append(f"  {k[:90]:90s} n={len(v):3d} {statistics.median(v):14.1f}")
+        for (name, g), v in sorted(per.items()):
+            lines.append(f"  {name[:80]:80s} {g:10d} n={len(v):3d} {statistics.median(v):14.1f}")
         lines.append("")
 
-    def find(table, frag):
-        for k, v in table.items():
-            if frag in k:
+    def find(table, frag, grid=None):
+        for (name, g), v in table.items():
+            if frag in name and (grid is None or g == grid):
                 return v
         return None
 
+    ops = json.loads(Path(bench_json).read_text()).get("ops", {}) if bench_json else {}
+    if ops and durs:
+        lines.append("operations of the step, matched by kernel and grid size:")
+        for op, rec in ops.items():
+            la = rec.get("launch") or {}
+            grid = la.get("workgroups", 0) * la.get("threads", 0)
+            d = find(durs, rec["kernel"] + "(", grid)
+            if d:
+                lines.append(f"  {op:40s} {rec['kernel']:42s} grid {grid:9d}  avg {statistics.mean(d):9.2f} us "
+                             f"over {len(d)} dispatches")
+        lines.append("")
     if "FETCH_SIZE" in med and "WRITE_SIZE" in med:
         cf, cw = find(med["FETCH_SIZE"], COPY_KERNEL), find(med["WRITE_SIZE"], COPY_KERNEL)
         ff = COPY_BYTES / (cf * 1024.0)
         fw = COPY_BYTES / (cw * 1024.0)
         lines.append(f"copy calibration: {COPY_BYTES} bytes each way; FETCH_SIZE {cf:.1f} KiB (factor {ff:.4f}), "
                      f"WRITE_SIZE {cw:.1f} KiB (factor {fw:.4f})")
-        ops = {}
-        for op, frag in OP_KERNELS:
-            f, wv = find(med["FETCH_SIZE"], frag), find(med["WRITE_SIZE"], frag)
+        traffic = {}
+        for op, rec in ops.items():
+            la = rec.get("launch") or {}
+            grid = la.get("workgroups", 0) * la.get("threads", 0)
+            f = find(med["FETCH_SIZE"], rec["kernel"] + "(", grid)
+            wv = find(med["WRITE_SIZE"], rec["kernel"] + "(", grid)
             if f is None or wv is None:
                 continue
             fb, wb = f * 1024.0 * ff, wv * 1024.0 * fw
-            ops[op] = {"kernel": frag, "fetch_bytes": round(fb), "write_bytes": round(wb),
-                       "hbm_bytes_per_launch": round(fb + wb)}
-            lines.append(f"  {op:40s} fetch {fb / 1e6:10.2f} MB  write {wb / 1e6:10.2f} MB")
+            traffic[op] = {"kernel": rec["kernel"], "grid_threads": grid, "fetch_bytes": round(fb),
+                           "write_bytes": round(wb), "hbm_bytes_per_launch": round(fb + wb),
+                           "algorithmic_bytes": rec.get("algorithmic_bytes")}
+            lines.append(f"  {op:40s} fetch {fb / 1e6:10.2f} MB  write {wb / 1e6:10.2f} MB  "
+                         f"algorithmic {rec.get('algorithmic_bytes', 0) / 1e6:10.2f} MB")
         TRAFFIC_FILE.write_text(json.dumps({
             "kernel_source_hash": kernel_source_hash(), "command": command,
             "copy_calibration": {"bytes_each_way": COPY_BYTES, "fetch_kib": cf, "write_kib": cw,
                                  "fetch_factor": ff, "write_factor": fw},
-            "ops": ops}, indent=1) + "\n")
+            "ops": traffic}, indent=1) + "\n")
     Path(out_txt).write_text("\n".join(lines) + "\n")
 
 
@@ -428,14 +458,14 @@ def main():
     ap.add_argument("--calls", type=int, default=20, help="back-to-back calls per operation for µs/call")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for the CPU baseline")
-    ap.add_argument("--summarize-rocprof", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--summarize-rocprof", nargs=4, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR", "BENCH_JSON"))
     ap.add_argument("--summary-out", default=None)
     ap.add_argument("--command", default="")
     args = ap.parse_args()
 
     if args.summarize_rocprof:
-        tr, fe, wr = [None if x in ("-", "") else x for x in args.summarize_rocprof]
-        summarize_rocprof(tr, fe, wr, args.summary_out, args.command)
+        tr, fe, wr, bj = [None if x in ("-", "") else x for x in args.summarize_rocprof]
+        summarize_rocprof(tr, fe, wr, bj, args.summary_out, args.command)
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -481,11 +511,12 @@ def main():
 
     # ---- µs per call, each operation alone: back-to-back calls between two
     # events on the launch stream (the MLA calls rotate over the buffer sets)
-    iso_us = {}
+    iso_us, launches = {}, {}
     with torch.cuda.stream(stream):
         for i, n in enumerate(names):
             for j in range(3):
                 w.ops(k=j)[i][2]()
+            launches[n] = cam.last_launch()
             fns = [w.ops(k=j)[i][2] for j in range(args.calls)]
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
@@ -542,6 +573,7 @@ def main():
             "in_step_us_median": round(statistics.median(in_step[n]), 2),
             "in_step_us_p95": round(sorted(in_step[n])[int(0.95 * (len(in_step[n]) - 1))], 2),
             "in_step_GBps": round(nbytes[n] / mean_step / 1e3, 1),
+            "launch": launches[n],
         }
     dom = max(names, key=lambda n: statistics.mean(in_step[n]))
     dom_us = statistics.mean(in_step[dom])

@@ -26,7 +26,7 @@ __all__ = [
     "VarlenPlan", "ulysses_varlen_plan", "ulysses_seq_to_head_varlen", "ulysses_head_to_seq_varlen",
     "lse_pack_bytes", "lse_pack", "lse_combine_packed", "lse_combine", "lse_combine_varlen",
     "lse_combine_packed_seq", "lse_combine_varlen_seq", "lse_merge",
-    "copy",
+    "copy", "last_launch",
 ]
 
 LIB_PATH = Path(__file__).resolve().parent / "libcam.so"
@@ -50,6 +50,7 @@ _SIGNATURES = {
     "cam_status_string": (C.c_char_p, [_int]),
     "cam_last_error": (C.c_char_p, []),
     "cam_abi_version": (_int, []),
+    "cam_last_launch": (_int, [_vp, _vp, _vp]),
     "ulysses_seq_to_head": (_int, [_vp, _vp, _i64, _i64, _i64, _i64, _i64, _int, _vp]),
     "ulysses_head_to_seq": (_int, [_vp, _vp, _i64, _i64, _i64, _i64, _i64, _int, _vp]),
     "ulysses_varlen_plan": (_int, [_vp, _i64, _i64, _vp, _vp]),
@@ -440,3 +441,11 @@ def copy(src: torch.Tensor, dst: torch.Tensor) -> torch.Tensor:
         raise ValueError("src and dst sizes differ")
     _check(library().cam_copy(src.data_ptr(), dst.data_ptr(), n, _stream(src)))
     return dst
+
+
+def last_launch() -> dict:
+    """Geometry of this thread's latest kernel launch: workgroups, threads per
+    workgroup, dynamic LDS bytes (profilers match calls to dispatches by it)."""
+    wg, th, lds = C.c_uint64(0), C.c_uint32(0), C.c_uint64(0)
+    _check(library().cam_last_launch(C.addressof(wg), C.addressof(th), C.addressof(lds)))
+    return {"workgroups": wg.value, "threads": th.value, "lds_bytes": lds.value}

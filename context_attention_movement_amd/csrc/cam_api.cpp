@@ -17,6 +17,7 @@
 namespace cam {
 
 static thread_local char g_err[512];
+static thread_local uint64_t g_launch[3];  // workgroups, threads, LDS bytes
 
 cam_status set_error(cam_status s, const char* fmt, ...)
 {
@@ -28,6 +29,13 @@ cam_status set_error(cam_status s, const char* fmt, ...)
 }
 
 void clear_error() { g_err[0] = '\0'; }
+
+void note_launch(uint64_t workgroups, uint32_t threads, uint64_t lds_bytes)
+{
+    g_launch[0] = workgroups;
+    g_launch[1] = threads;
+    g_launch[2] = lds_bytes;
+}
 
 namespace {
 
@@ -431,6 +439,16 @@ const char* cam_status_string(cam_status s)
 }
 
 const char* cam_last_error(void) { return g_err; }
+
+cam_status cam_last_launch(uint64_t* workgroups, uint32_t* threads, uint64_t* lds_bytes)
+{
+    if (!workgroups || !threads || !lds_bytes)
+        return set_error(CAM_ERR_NULL, "cam_last_launch: null output pointer");
+    *workgroups = g_launch[0];
+    *threads = uint32_t(g_launch[1]);
+    *lds_bytes = g_launch[2];
+    return CAM_OK;
+}
 
 int cam_abi_version(void) { return CAM_ABI_VERSION; }
 

@@ -165,6 +165,7 @@ inline cam_status launch(const void* fn, const Args& a, uint64_t n_tiles, void* 
     if (n_tiles == 0)
         return CAM_OK;
     const uint32_t grid = uint32_t(n_tiles < kMaxGrid ? n_tiles : kMaxGrid);
+    note_launch(grid, threads, lds_bytes);
     Args copy = a;
     void* args[] = {&copy};
     hipError_t e = hipLaunchKernel(fn, dim3(grid), dim3(threads), args, size_t(lds_bytes),

@@ -195,6 +195,8 @@ cam_status launch_merge(const Merge& a, void* stream);
 
 // Error reporting shared by the host layer and the launchers.
 cam_status set_error(cam_status s, const char* fmt, ...);
+// records the geometry of this thread's latest launch (cam_last_launch)
+void note_launch(uint64_t workgroups, uint32_t threads, uint64_t lds_bytes);
 void clear_error();
 
 // Launch shape shared by all streaming kernels.

@@ -191,7 +191,9 @@ __device__ __forceinline__ uint64_t uniform64(uint64_t x)
 
 // WAVE: one row group is a whole wave (rows of >= 64 vectors), so every
 // per-row quantity of phase 2 is wave-uniform and is kept in scalar registers.
-template <int W, bool FP16, bool VARLEN, int RF, bool WAVE>
+// OM: where the combined rows go -- 0 at the caller's strides, 1 token-major
+// (head-scattered rows of the exchange), 2 rank-major (varlen sequence shards).
+template <int W, bool FP16, bool VARLEN, int RF, bool WAVE, int OM>
 __global__ __launch_bounds__(kThreads) void k_combine(Combine a)
 {
     typedef typename VecOf<W>::type V;
@@ -267,12 +269,12 @@ __global__ __launch_bounds__(kThreads) void k_combine(Combine a)
                     w_lds[rl * a.P + sp] = w * iz;
                 if (sp == 0) {
                     int64_t o_off, l_off;
-                    if (a.out_mode == 0) {
+                    if (OM == 0) {
                         o_off = int64_t(t) * a.o_st_b + int64_t(h) * a.o_sh_b;
                         l_off = int64_t(t) * a.lo_st + int64_t(h) * a.lo_sh;
                     } else {
                         int64_t g;
-                        if (a.out_mode == 1) {
+                        if (OM == 1) {
                             const uint32_t tq = fdiv(h, a.div_Hp);
                             g = int64_t(tq) * a.Hq + int64_t(t) * a.Hp + (h - tq * a.Hp);
                         } else {
@@ -475,14 +477,22 @@ cam_status launch_combine(const Combine& a, void* stream)
     const bool wave = a.g_log2 == 6;  // a whole wave per row (implies wide)
     const void* fn = nullptr;
 #define CAM_PICK(Wd, RFv, WV)                                                                          \
-    if (a.width == Wd && wave == WV && (WV || wide == (RFv == 2))) {                                            \
-        if (a.cu)                                                                                       \
-            fn = a.fp16 ? reinterpret_cast<const void*>(&k_combine<Wd, true, true, RFv, WV>)           \
-                        : reinterpret_cast<const void*>(&k_combine<Wd, false, true, RFv, WV>);         \
-        else                                                                                            \
-            fn = a.fp16 ? reinterpret_cast<const void*>(&k_combine<Wd, true, false, RFv, WV>)          \
-                        : reinterpret_cast<const void*>(&k_combine<Wd, false, false, RFv, WV>);        \
+    if (a.width == Wd && wave == WV && (WV || wide == (RFv == 2))) {                                   \
+        if (a.cu)                                                                                      \
+            fn = a.out_mode == 2                                                                       \
+                     ? (a.fp16 ? reinterpret_cast<const void*>(&k_combine<Wd, true, true, RFv, WV, 2>)  \
+                               : reinterpret_cast<const void*>(&k_combine<Wd, false, true, RFv, WV, 2>)) \
+                     : (a.fp16 ? reinterpret_cast<const void*>(&k_combine<Wd, true, true, RFv, WV, 0>)  \
+                               : reinterpret_cast<const void*>(&k_combine<Wd, false, true, RFv, WV, 0>)); \
+        else                                                                                           \
+            fn = a.out_mode == 1                                                                       \
+                     ? (a.fp16 ? reinterpret_cast<const void*>(&k_combine<Wd, true, false, RFv, WV, 1>) \
+                               : reinterpret_cast<const void*>(&k_combine<Wd, false, false, RFv, WV, 1>)) \
+                     : (a.fp16 ? reinterpret_cast<const void*>(&k_combine<Wd, true, false, RFv, WV, 0>) \
+                               : reinterpret_cast<const void*>(&k_combine<Wd, false, false, RFv, WV, 0>)); \
     }
+    if ((a.out_mode == 1 && a.cu) || (a.out_mode == 2 && !a.cu) || a.out_mode > 2)
+        return CAM_ERR_UNSUPPORTED;
     CAM_PICK(16, 1, false) CAM_PICK(8, 1, false) CAM_PICK(4, 1, false) CAM_PICK(2, 1, false)
     CAM_PICK(16, 2, false) CAM_PICK(8, 2, false) CAM_PICK(4, 2, false) CAM_PICK(2, 2, false)
     CAM_PICK(16, kCombineInFlightWave, true) CAM_PICK(8, kCombineInFlightWave, true)

@@ -72,6 +72,12 @@ const char* cam_last_error(void);
 #define CAM_ABI_VERSION 1
 int cam_abi_version(void);
 
+/* Geometry of the latest kernel launched by this thread: workgroups, threads
+ * per workgroup and dynamic LDS bytes (all zero before the first launch; a
+ * call that launches nothing leaves the previous record).  For profilers and
+ * benchmarks, which match a call to its kernel dispatches by grid size. */
+cam_status cam_last_launch(uint64_t* workgroups, uint32_t* threads, uint64_t* lds_bytes);
+
 /* ------------------------------------------------------------------------- */
 /* Dense Ulysses relayout  ([FV] all_to_all_4D, benchmark_ulysses_a2a.py)      */
 /* ------------------------------------------------------------------------- */

@@ -240,3 +240,11 @@ def test_merge_rejections(lib):
     assert f(*args(fin=PP)) == OVERLAP
     assert f(*args(dt=FP32)) == UNSUP
     assert f(*args(acc=None)) == NULL
+
+
+def test_last_launch_record(cam):
+    import ctypes as C
+    lib = cam.library()
+    wg, th, lds = C.c_uint64(7), C.c_uint32(7), C.c_uint64(7)
+    assert lib.cam_last_launch(C.addressof(wg), C.addressof(th), C.addressof(lds)) == 0
+    assert lib.cam_last_launch(None, C.addressof(th), C.addressof(lds)) != 0
