@@ -75,6 +75,10 @@ def _load():
                                  vp, vp, vp]),
         "orc_varlen_token_rows": (None, [vp, i64, i64, vp]),
         "orc_lse_combine_packed_seq": (None, [vp, i64, i64, i64, i64, C.c_int, C.c_int, vp, vp]),
+        "orc_combine_row_backward_f64": (None, [vp, vp, vp, i64, i64, vp, C.c_double, vp, vp]),
+        "orc_lse_combine_backward": (None, [vp, i64, i64, i64, vp, i64, i64, i64, i64, i64, i64, i64, i64,
+                                            C.c_int, vp, i64, i64, vp, i64, i64, vp, i64, i64, i64,
+                                            vp, i64, i64, i64, vp, i64]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -334,3 +338,50 @@ def attention(q_bits, k_bits, v_bits, kv_begin: int, kv_end: int, causal: bool =
     _load().orc_attention(_p(q_bits), _p(k_bits), _p(v_bits), T, H, D, _dt(dtype), kv_begin,
                           kv_end, int(causal), _p(out), _p(m), _p(s))
     return out, m, s
+
+
+# -- gradient of the combine --------------------------------------------------
+
+def combine_row_backward_f64(part_o: np.ndarray, part_l: np.ndarray, g: np.ndarray, g_lse: float = 0.0,
+                             valid: np.ndarray | None = None):
+    """One row in double: part_o [P][D], part_l [P], g [D] -> (dO [P][D], dL [P])."""
+    part_o = np.ascontiguousarray(part_o, dtype=np.float64)
+    part_l = np.ascontiguousarray(part_l, dtype=np.float64)
+    g = np.ascontiguousarray(g, dtype=np.float64)
+    P, D = part_o.shape
+    v = np.ones(P, dtype=np.int32) if valid is None else np.ascontiguousarray(valid, dtype=np.int32)
+    d_o = np.empty((P, D))
+    d_l = np.empty(P)
+    _load().orc_combine_row_backward_f64(_p(part_o), _p(part_l), _p(v), P, D, _p(g), float(g_lse),
+                                         _p(d_o), _p(d_l))
+    return d_o, d_l
+
+
+def lse_combine_backward(part_out: np.ndarray, part_lse: np.ndarray, g_out: np.ndarray,
+                         g_lse: np.ndarray | None = None, dtype: str = "bf16",
+                         cu: np.ndarray | None = None, t_begin: int = 0):
+    """Gradient of lse_combine.  part_out uint16 view [P][T'][H][D], part_lse
+    float32 view [P][T'][H], g_out uint16 view [T'][H][D], g_lse float32 view
+    [T'][H] or None -- T' rows starting at global token t_begin.  Returns
+    (d_part_out uint16 [P][T'][H][D], d_part_lse float32 [P][T'][H])."""
+    P, Tw, H, D = part_out.shape
+    assert part_out.strides[3] == part_out.itemsize and g_out.strides[2] == g_out.itemsize
+
+    def ptr(view):
+        return view.__array_interface__["data"][0]
+
+    po = _strides_el(part_out)
+    pl = _strides_el(part_lse)
+    go = _strides_el(g_out)
+    gl = _strides_el(g_lse) if g_lse is not None else (0, 0)
+    d_po = np.empty((P, Tw, H, D), dtype=np.uint16)
+    d_pl = np.empty((P, Tw, H), dtype=np.float32)
+    cu_arr = None if cu is None else np.ascontiguousarray(cu, dtype=np.int32)
+    _load().orc_lse_combine_backward(
+        ptr(part_out), po[0], po[1], po[2], ptr(part_lse), pl[0], pl[1], pl[2],
+        P, t_begin, t_begin + Tw, H, D, _dt(dtype), ptr(g_out), go[0], go[1],
+        ptr(g_lse) if g_lse is not None else None, gl[0], gl[1],
+        _p(d_po), Tw * H * D, H * D, D, _p(d_pl), Tw * H, H, 1,
+        _p(cu_arr) if cu_arr is not None else None, 0 if cu_arr is None else cu_arr.size - 1)
+    return d_po, d_pl
+

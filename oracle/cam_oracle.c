@@ -18,6 +18,11 @@
  *  [CU]  cuLA PR "feat(distributed): add packed hybrid runtime and THD
  *        planner": packed THD cu_seqlens, logical CP ranks in one process.
  *
+ * Training: the relayout's gradient is its inverse relayout ([FV] benchmark's
+ * forward/backward pair, whose gradients must equal the collective's), and the
+ * combine's gradient is its derivative, written out below ([CU] forward and
+ * backward comparison of context parallelism; the pages print no formula).
+ *
  * Arithmetic: every floating-point result is computed in double and rounded
  * once at the end (bf16 / fp16 round-to-nearest-even, fp32 by the C cast),
  * since the pages do not fix the precision of the reduction.
@@ -636,4 +641,121 @@ void orc_lse_combine_packed_seq(const void* packed, int64_t P, int64_t T, int64_
         }
     free(tmp);
     free(ltmp);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Gradient of the stable combine (training use of the combine)            */
+/* ------------------------------------------------------------------------ */
+/*
+ * Within V the combine of one row is a smooth function of the partials: with
+ * lse = log sum_{q in V} exp(L_q) and w_p = exp(L_p - lse),
+ *   out = sum_{p in V} w_p O_p,  d out / d O_p = w_p I,
+ *   d w_q / d L_p = w_q (delta_pq - w_p),  d lse / d L_p = w_p.
+ * So, for the upstream gradients g (of out, D values) and g_lse (of lse_out):
+ *   dO_p = w_p g,
+ *   dL_p = w_p (<g, O_p> - <g, out> + g_lse)   for p in V,
+ * and both are zero outside V (an invalid or masked partial does not enter
+ * the combine).  An empty V gives zeros throughout.  The weights are formed as
+ * in orc_combine_row_f64 (max subtracted first) and normalised by Z.
+ */
+void orc_combine_row_backward_f64(const double* part_o, const double* part_l, const int* valid,
+                                  int64_t P, int64_t D, const double* g, double g_lse,
+                                  double* d_o, double* d_l)
+{
+    double M = -INFINITY;
+    int any = 0;
+    for (int64_t p = 0; p < P; ++p) {
+        d_l[p] = 0.0;
+        for (int64_t d = 0; d < D; ++d)
+            d_o[p * D + d] = 0.0;
+        if (valid[p] && isfinite(part_l[p])) {
+            if (!any || part_l[p] > M)
+                M = part_l[p];
+            any = 1;
+        }
+    }
+    if (!any)
+        return;
+    double Z = 0.0;
+    for (int64_t p = 0; p < P; ++p)
+        if (valid[p] && isfinite(part_l[p]))
+            Z += exp(part_l[p] - M);
+    /* <g, out> with out = sum w_p O_p */
+    double g_out = 0.0;
+    for (int64_t d = 0; d < D; ++d) {
+        double o = 0.0;
+        for (int64_t p = 0; p < P; ++p)
+            if (valid[p] && isfinite(part_l[p]))
+                o += exp(part_l[p] - M) / Z * part_o[p * D + d];
+        g_out += g[d] * o;
+    }
+    for (int64_t p = 0; p < P; ++p) {
+        if (!(valid[p] && isfinite(part_l[p])))
+            continue;
+        double w = exp(part_l[p] - M) / Z;
+        double gp = 0.0;
+        for (int64_t d = 0; d < D; ++d) {
+            gp += g[d] * part_o[p * D + d];
+            d_o[p * D + d] = w * g[d];
+        }
+        d_l[p] = w * (gp - g_out + g_lse);
+    }
+}
+
+/*
+ * Typed strided gradient of orc_lse_combine over rows (t, h), t in
+ * [t_begin, t_end), the pointers addressing row t_begin as there:
+ *   g_out       (t, h, d) at go_st*(t - t_begin) + go_sh*h + d       (payload dtype)
+ *   g_lse       (t, h)    at gl_st*(t - t_begin) + gl_sh*h (nullable: zero)
+ *   d_part_out  (p, t, h, d) at dpo_sp*p + dpo_st*(t - t_begin) + dpo_sh*h + d
+ *   d_part_lse  (p, t, h)    at dpl_sp*p + dpl_st*(t - t_begin) + dpl_sh*h  (fp32)
+ * With cu_seqlens non-null the causal piece rule gates partial p as in the
+ * forward.  dO is rounded once to the payload dtype, dL once to fp32; the O row
+ * of a partial outside V is not read.
+ */
+void orc_lse_combine_backward(const void* part_out, int64_t po_sp, int64_t po_st, int64_t po_sh,
+                              const float* part_lse, int64_t pl_sp, int64_t pl_st, int64_t pl_sh,
+                              int64_t P, int64_t t_begin, int64_t t_end, int64_t H, int64_t D,
+                              int dtype, const void* g_out, int64_t go_st, int64_t go_sh,
+                              const float* g_lse, int64_t gl_st, int64_t gl_sh, void* d_part_out,
+                              int64_t dpo_sp, int64_t dpo_st, int64_t dpo_sh, float* d_part_lse,
+                              int64_t dpl_sp, int64_t dpl_st, int64_t dpl_sh,
+                              const int32_t* cu_seqlens, int64_t nseq)
+{
+    double* po = (double*)malloc(sizeof(double) * (size_t)(P * D + 1));
+    double* pl = (double*)malloc(sizeof(double) * (size_t)(P + 1));
+    int* valid = (int*)malloc(sizeof(int) * (size_t)(P + 1));
+    double* g = (double*)malloc(sizeof(double) * (size_t)(D + 1));
+    double* d_o = (double*)malloc(sizeof(double) * (size_t)(P * D + 1));
+    double* d_l = (double*)malloc(sizeof(double) * (size_t)(P + 1));
+    for (int64_t t = t_begin; t < t_end; ++t)
+        for (int64_t h = 0; h < H; ++h) {
+            int64_t tr = t - t_begin;
+            for (int64_t p = 0; p < P; ++p) {
+                valid[p] = cu_seqlens ? orc_causal_piece_valid(cu_seqlens, nseq, P, p, t) : 1;
+                pl[p] = -INFINITY;
+                if (!valid[p])
+                    continue;
+                pl[p] = (double)part_lse[p * pl_sp + tr * pl_st + h * pl_sh];
+                if (!isfinite(pl[p]))
+                    continue;
+                for (int64_t d = 0; d < D; ++d)
+                    po[p * D + d] = load_half(part_out, p * po_sp + tr * po_st + h * po_sh + d, dtype);
+            }
+            for (int64_t d = 0; d < D; ++d)
+                g[d] = load_half(g_out, tr * go_st + h * go_sh + d, dtype);
+            double gl = g_lse ? (double)g_lse[tr * gl_st + h * gl_sh] : 0.0;
+            orc_combine_row_backward_f64(po, pl, valid, P, D, g, gl, d_o, d_l);
+            for (int64_t p = 0; p < P; ++p) {
+                for (int64_t d = 0; d < D; ++d)
+                    store_half(d_part_out, p * dpo_sp + tr * dpo_st + h * dpo_sh + d, dtype, d_o[p * D + d]);
+                d_part_lse[p * dpl_sp + tr * dpl_st + h * dpl_sh] = (float)d_l[p];
+            }
+        }
+    free(po);
+    free(pl);
+    free(valid);
+    free(g);
+    free(d_o);
+    free(d_l);
 }
