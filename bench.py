@@ -142,6 +142,14 @@ class Workload:
             ms["comb_seq"] = torch.empty((Tm, Hm, Dvm), dtype=bf, device=dev)
             ms["lse_seq"] = torch.empty((Tm, Hm), dtype=torch.float32, device=dev)
             ms["comb_h2s"] = torch.empty((Pm, 1, Tm // Pm, Hm, Dvm), dtype=bf, device=dev)
+        # training: gradient buffers of the relayout pair and of the THD combine
+        P, S, H, D = self.vP, self.vS, self.vH, self.vD
+        self.v_dqkv = torch.empty((P, 3, S // P, H, D), dtype=bf, device=dev)
+        self.v_do = torch.empty((P, 1, S, H // P, D), dtype=bf, device=dev)
+        P, T, H, D = self.tP, self.tT, self.tH, self.tD
+        self.t_dpart = torch.empty((P, T, H, D), dtype=bf, device=dev)
+        self.t_dlse = torch.empty((P, T, H), dtype=torch.float32, device=dev)
+        self.t_gout = randn((T, H, D))
         self.step_index = 0
         torch.cuda.synchronize()
 
@@ -196,9 +204,11 @@ class Workload:
 
 
     def extension_ops(self, k=0):
-        """Operations beyond the step: the combine epilogues that write the
-        sequence-sharded layout directly, and the unfused sequence they
-        replace.  (name, algorithmic bytes, callable)."""
+        """Operations beyond the step: the gradient of the THD combine, the
+        relayout training pair (forward and backward), the ring of online
+        merges, the combine epilogues that write the sequence-sharded layout
+        directly and the unfused sequence they replace.
+        (name, algorithmic bytes, callable)."""
         cam = self.cam
         ms = self.m_sets[k % self.NSETS]
         Pm, Tm, Hm, Dvm = self.mP, self.mT, self.mH, self.mDv
@@ -231,7 +241,28 @@ class Workload:
         # and writes the accumulator; the last hop also writes the rounded rows
         ring_bytes = rows * (P * (2 * D + 4 + 4 * D + 4 + 4) + (P - 1) * (4 * D) + 2 * D + 4)
 
+        def training_pair():
+            # forward scatter of Q/K/V and gather of O, then their gradients:
+            # the inverse relayouts of the upstream gradients
+            cam.ulysses_seq_to_head(self.v_qkv, self.vP, out=self.v_qkv_out)
+            cam.ulysses_head_to_seq(self.v_o, self.vP, out=self.v_o_out)
+            cam.ulysses_head_to_seq(self.v_qkv_out, self.vP, out=self.v_dqkv)
+            cam.ulysses_seq_to_head(self.v_o_out, self.vP, out=self.v_do)
+
+        pair_bytes = 2 * (self.op_bytes()["relayout_seq_to_head_video_p4_qkv"]
+                          + self.op_bytes()["relayout_head_to_seq_video_p4_o"])
+
+        def thd_backward():
+            cam.lse_combine_backward(self.t_part, self.t_lse, self.t_gout, None, cu_seqlens=self.t_cu_dev,
+                                     d_part_out=self.t_dpart, d_part_lse=self.t_dlse)
+
+        # admitted partials: O row and LSE read; every row: upstream gradient
+        # read; every partial: its two gradients written
+        bwd_bytes = self.t_admitted * H * (2 * D + 4) + rows * 2 * D + P * rows * (2 * D + 4)
+
         return [
+            ("lse_combine_varlen_backward_thd", bwd_bytes, thd_backward),
+            ("relayout_training_pair_video_p4 (fwd + bwd)", pair_bytes, training_pair),
             ("ring_of_8_online_merges_thd (fp32 accumulator)", ring_bytes, ring),
             ("combine_to_sequence_shards_mla (fused)", comb_bytes, fused),
             ("combine_then_head_to_seq_mla (unfused)", comb_bytes + 2 * out_bytes, unfused),
@@ -540,7 +571,7 @@ def main():
             e1.record(stream)
             torch.cuda.synchronize()
             us = e0.elapsed_time(e1) * 1000.0 / args.calls
-            ext[n] = {"us_per_call": round(us, 2), "algorithmic_bytes": int(nb_ext),
+            ext[n] = {"us_per_call": round(us, 2), "algorithmic_bytes": int(nb_ext), "last_launch": cam.last_launch(),
                       "GBps": round(nb_ext / us / 1e3, 1), "frac_of_hbm_peak": round(nb_ext / us / 1e3 / HBM_PEAK_GBPS, 4)}
 
     # ---- plain-copy ceiling on the video Q/K/V operand size

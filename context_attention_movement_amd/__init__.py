@@ -25,7 +25,7 @@ __all__ = [
     "ulysses_seq_to_head", "ulysses_head_to_seq",
     "VarlenPlan", "ulysses_varlen_plan", "ulysses_seq_to_head_varlen", "ulysses_head_to_seq_varlen",
     "lse_pack_bytes", "lse_pack", "lse_combine_packed", "lse_combine", "lse_combine_varlen",
-    "lse_combine_packed_seq", "lse_combine_varlen_seq", "lse_merge",
+    "lse_combine_packed_seq", "lse_combine_varlen_seq", "lse_merge", "lse_combine_backward",
     "copy", "last_launch",
 ]
 
@@ -67,6 +67,12 @@ _SIGNATURES = {
     "lse_combine_varlen": (_int, [_vp, _i64, _i64, _i64, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _i64,
                                   _int, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _vp]),
     "cam_copy": (_int, [_vp, _vp, _i64, _vp]),
+    "lse_combine_backward": (_int, [_vp, _i64, _i64, _i64, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _i64,
+                                    _int, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _i64,
+                                    _vp, _i64, _i64, _i64, _vp]),
+    "lse_combine_varlen_backward": (_int, [_vp, _i64, _i64, _i64, _vp, _i64, _i64, _i64, _i64, _i64, _i64,
+                                           _i64, _int, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64,
+                                           _i64, _vp, _i64, _i64, _i64, _vp, _i64, _vp]),
     "lse_combine_packed_seq": (_int, [_vp, _i64, _i64, _i64, _i64, _int, _int, _vp, _vp, _vp]),
     "lse_combine_varlen_seq": (_int, [_vp, _i64, _i64, _i64, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _i64,
                                       _int, _vp, _vp, _vp, _vp, _vp, _i64, _vp]),
@@ -357,6 +363,48 @@ def lse_combine_varlen(part_out: torch.Tensor, part_lse: torch.Tensor, cu_seqlen
                                         *out.stride()[:2], _ptr(lse_out), *lo, cu_seqlens.data_ptr(),
                                         cu_seqlens.numel() - 1, _stream(part_out)))
     return out, lse_out
+
+
+def lse_combine_backward(part_out: torch.Tensor, part_lse: torch.Tensor, g_out: torch.Tensor,
+                         g_lse: torch.Tensor | None = None, cu_seqlens: torch.Tensor | None = None,
+                         d_part_out: torch.Tensor | None = None, d_part_lse: torch.Tensor | None = None):
+    """Gradient of lse_combine (or, with cu_seqlens, of lse_combine_varlen):
+    part_out [P][T][H][D], part_lse [P][T][H], g_out [T][H][D] (the upstream
+    gradient of out, payload dtype), g_lse [T][H] fp32 or None (zero) ->
+    (d_part_out [P][T][H][D], d_part_lse [P][T][H] fp32).  Any strides with D
+    contiguous."""
+    P, T, H, D, _, _, _ = _combine_common(part_out, part_lse, g_out, None)
+    if g_out.dtype != part_out.dtype:
+        raise TypeError("g_out must have the payload dtype of part_out")
+    if tuple(g_out.shape) != (T, H, D):
+        raise ValueError("g_out must be [T][H][D]")
+    if g_lse is not None:
+        _dev(g_lse, "g_lse")
+        if g_lse.dtype != torch.float32 or tuple(g_lse.shape) != (T, H):
+            raise ValueError("g_lse must be float32 [T][H]")
+    if d_part_out is None:
+        d_part_out = torch.empty_like(part_out, memory_format=torch.contiguous_format)
+    if d_part_lse is None:
+        d_part_lse = torch.empty((P, T, H), dtype=torch.float32, device=part_out.device)
+    _dev(d_part_out, "d_part_out")
+    _dev(d_part_lse, "d_part_lse")
+    if tuple(d_part_out.shape) != (P, T, H, D) or d_part_out.stride(3) != 1 or d_part_out.dtype != part_out.dtype:
+        raise ValueError("d_part_out must be [P][T][H][D] of the payload dtype with D contiguous")
+    if tuple(d_part_lse.shape) != (P, T, H) or d_part_lse.dtype != torch.float32:
+        raise ValueError("d_part_lse must be float32 [P][T][H]")
+    gl = g_lse.stride() if g_lse is not None else (0, 0)
+    args = [part_out.data_ptr(), *part_out.stride()[:3], part_lse.data_ptr(), *part_lse.stride(), P, T, H, D,
+            _dt(part_out), g_out.data_ptr(), *g_out.stride()[:2], _ptr(g_lse), *gl, d_part_out.data_ptr(),
+            *d_part_out.stride()[:3], d_part_lse.data_ptr(), *d_part_lse.stride()]
+    if cu_seqlens is None:
+        _check(library().lse_combine_backward(*args, _stream(part_out)))
+    else:
+        _contig(cu_seqlens, "cu_seqlens")
+        if cu_seqlens.dtype != torch.int32:
+            raise TypeError("cu_seqlens must be int32")
+        _check(library().lse_combine_varlen_backward(*args, cu_seqlens.data_ptr(), cu_seqlens.numel() - 1,
+                                                     _stream(part_out)))
+    return d_part_out, d_part_lse
 
 
 def lse_combine_packed_seq(packed: torch.Tensor, P: int, T: int, H: int, Dv: int, scatter_dim: int,

@@ -11,6 +11,7 @@
 #include <cstdio>
 #include <cstring>
 #include <initializer_list>
+#include <utility>
 
 #include "cam_internal.h"
 
@@ -416,6 +417,118 @@ cam_status combine(const char* op, const CombineIn& c, void* stream)
     return launch_combine(a, stream);
 }
 
+struct CombineBwdIn {
+    const void* po;
+    int64_t po_sp, po_st, po_sh;
+    const float* pl;
+    int64_t pl_sp, pl_st, pl_sh;
+    int64_t P, T, H, D;
+    cam_dtype dt;
+    const void* go;
+    int64_t go_st, go_sh;
+    const float* gl;
+    int64_t gl_st, gl_sh;
+    void* dpo;
+    int64_t dpo_sp, dpo_st, dpo_sh;
+    float* dpl;
+    int64_t dpl_sp, dpl_st, dpl_sh;
+    const int32_t* cu;
+    int64_t nseq;
+};
+
+cam_status combine_backward(const char* op, const CombineBwdIn& c, void* stream)
+{
+    if (c.P < 1 || c.T < 0 || c.H < 0 || c.D < 0)
+        return set_error(CAM_ERR_SHAPE, "%s: need P >= 1 and T, H, D >= 0", op);
+    if (c.P > 64)
+        return set_error(CAM_ERR_UNSUPPORTED, "%s: at most 64 partials per row (P=%lld)", op, (long long)c.P);
+    if (c.dt != CAM_BF16 && c.dt != CAM_FP16)
+        return set_error(CAM_ERR_UNSUPPORTED, "%s: payload dtype must be bf16 or fp16", op);
+    for (int64_t s : {c.po_sp, c.po_st, c.po_sh, c.pl_sp, c.pl_st, c.pl_sh, c.go_st, c.go_sh, c.gl_st, c.gl_sh,
+                      c.dpo_sp, c.dpo_st, c.dpo_sh, c.dpl_sp, c.dpl_st, c.dpl_sh})
+        if (s < 0)
+            return set_error(CAM_ERR_UNSUPPORTED, "%s: strides must be non-negative", op);
+    int64_t n_rows;
+    if (!prod_ok({c.T, c.H}, &n_rows))
+        return set_error(CAM_ERR_SHAPE, "%s: T*H overflows", op);
+    if (n_rows == 0)
+        return CAM_OK;
+    if (n_rows > INT32_MAX)
+        return set_error(CAM_ERR_UNSUPPORTED, "%s: T*H must be below 2^31 rows", op);
+    if (c.cu && c.nseq < 1)
+        return set_error(CAM_ERR_SHAPE, "%s: nseq must be >= 1", op);
+    if (!c.po || !c.pl || !c.go || !c.dpo || !c.dpl)
+        return set_error(CAM_ERR_NULL, "%s: partials, their LSEs, the output gradient and both input "
+                                       "gradients must be non-null", op);
+    if (!aligned(c.po, 2) || !aligned(c.pl, 4) || !aligned(c.go, 2) || (c.gl && !aligned(c.gl, 4)) ||
+        !aligned(c.dpo, 2) || !aligned(c.dpl, 4) || (c.cu && !aligned(c.cu, 4)))
+        return set_error(CAM_ERR_ALIGNMENT, "%s: misaligned pointer", op);
+    int64_t ext_po, ext_pl, ext_go, ext_gl = 0, ext_dpo, ext_dpl;
+    if (!extent({c.P, c.T, c.H, c.D}, {c.po_sp, c.po_st, c.po_sh, 1}, 2, &ext_po) ||
+        !extent({c.P, c.T, c.H}, {c.pl_sp, c.pl_st, c.pl_sh}, 4, &ext_pl) ||
+        !extent({c.T, c.H, c.D}, {c.go_st, c.go_sh, 1}, 2, &ext_go) ||
+        (c.gl && !extent({c.T, c.H}, {c.gl_st, c.gl_sh}, 4, &ext_gl)) ||
+        !extent({c.P, c.T, c.H, c.D}, {c.dpo_sp, c.dpo_st, c.dpo_sh, 1}, 2, &ext_dpo) ||
+        !extent({c.P, c.T, c.H}, {c.dpl_sp, c.dpl_st, c.dpl_sh}, 4, &ext_dpl))
+        return set_error(CAM_ERR_SHAPE, "%s: tensor extent overflows", op);
+    const int64_t ext_cu = c.cu ? 4 * (c.nseq + 1) : 0;
+    for (auto out : {std::make_pair(static_cast<const void*>(c.dpo), ext_dpo),
+                     std::make_pair(static_cast<const void*>(c.dpl), ext_dpl)})
+        if (overlaps(out.first, out.second, c.po, ext_po) || overlaps(out.first, out.second, c.pl, ext_pl) ||
+            overlaps(out.first, out.second, c.go, ext_go) || overlaps(out.first, out.second, c.gl, ext_gl) ||
+            overlaps(out.first, out.second, c.cu, ext_cu))
+            return set_error(CAM_ERR_OVERLAP, "%s: an output overlaps an input", op);
+    if (overlaps(c.dpo, ext_dpo, c.dpl, ext_dpl))
+        return set_error(CAM_ERR_OVERLAP, "%s: the two outputs overlap", op);
+
+    CombineBwd a{};
+    const uint64_t row_b = uint64_t(c.D) * 2;
+    a.width = pick_width({row_b == 0 ? 16 : row_b, reinterpret_cast<uintptr_t>(c.po), reinterpret_cast<uintptr_t>(c.go),
+                          reinterpret_cast<uintptr_t>(c.dpo), uint64_t(c.po_sp) * 2, uint64_t(c.po_st) * 2,
+                          uint64_t(c.po_sh) * 2, uint64_t(c.go_st) * 2, uint64_t(c.go_sh) * 2,
+                          uint64_t(c.dpo_sp) * 2, uint64_t(c.dpo_st) * 2, uint64_t(c.dpo_sh) * 2});
+    a.po = c.po;
+    a.po_sp_b = c.po_sp * 2;
+    a.po_st_b = c.po_st * 2;
+    a.po_sh_b = c.po_sh * 2;
+    a.pl = c.pl;
+    a.pl_sp = c.pl_sp;
+    a.pl_st = c.pl_st;
+    a.pl_sh = c.pl_sh;
+    a.go = c.go;
+    a.go_st_b = c.go_st * 2;
+    a.go_sh_b = c.go_sh * 2;
+    a.gl = c.gl;
+    a.gl_st = c.gl_st;
+    a.gl_sh = c.gl_sh;
+    a.dpo = c.dpo;
+    a.dpo_sp_b = c.dpo_sp * 2;
+    a.dpo_st_b = c.dpo_st * 2;
+    a.dpo_sh_b = c.dpo_sh * 2;
+    a.dpl = c.dpl;
+    a.dpl_sp = c.dpl_sp;
+    a.dpl_st = c.dpl_st;
+    a.dpl_sh = c.dpl_sh;
+    a.P = uint32_t(c.P);
+    a.H = uint32_t(c.H);
+    a.div_H = make_fastdiv(a.H);
+    a.n_rows = uint64_t(n_rows);
+    a.cv = uint32_t(row_b / a.width);
+    a.g_log2 = log2u(pow2ceil(a.cv < 64 ? (a.cv ? a.cv : 1) : 64));
+    a.gp_log2 = log2u(pow2ceil(a.P));
+    uint32_t rows = uint64_t(a.cv) * a.width >= 512 ? CAM_COMBINE_BWD_ROWS_WIDE : CAM_COMBINE_BWD_ROWS_NARROW;
+    const uint32_t groups = uint32_t(kThreads) >> a.g_log2;
+    if (rows < groups)
+        rows = groups;
+    a.rows_per_tile = rows;
+    a.n_tiles = (uint64_t(n_rows) + rows - 1) / rows;
+    a.cu = c.cu;
+    a.nseq = int32_t(c.nseq);
+    a.div_P = make_fastdiv(a.P);
+    a.fp16 = c.dt == CAM_FP16;
+    return launch_combine_bwd(a, stream);
+}
+
 }  // namespace
 }  // namespace cam
 
@@ -660,6 +773,39 @@ cam_status lse_combine_varlen(const void* part_out, int64_t po_sp, int64_t po_st
     CombineIn c{part_out, po_sp, po_st, po_sh, part_lse, pl_sp, pl_st, pl_sh, P, T, H, D, dt,
                 out, o_st, o_sh, lse_out, lo_st, lo_sh, cu_seqlens, nseq};
     return combine("lse_combine_varlen", c, stream);
+}
+
+cam_status lse_combine_backward(const void* part_out, int64_t po_sp, int64_t po_st, int64_t po_sh,
+                                const float* part_lse, int64_t pl_sp, int64_t pl_st, int64_t pl_sh, int64_t P,
+                                int64_t T, int64_t H, int64_t D, cam_dtype dt, const void* g_out, int64_t go_st,
+                                int64_t go_sh, const float* g_lse, int64_t gl_st, int64_t gl_sh, void* d_part_out,
+                                int64_t dpo_sp, int64_t dpo_st, int64_t dpo_sh, float* d_part_lse, int64_t dpl_sp,
+                                int64_t dpl_st, int64_t dpl_sh, void* stream)
+{
+    clear_error();
+    CombineBwdIn c{part_out, po_sp, po_st, po_sh, part_lse, pl_sp, pl_st, pl_sh, P, T, H, D, dt,
+                   g_out, go_st, go_sh, g_lse, gl_st, gl_sh, d_part_out, dpo_sp, dpo_st, dpo_sh,
+                   d_part_lse, dpl_sp, dpl_st, dpl_sh, nullptr, 0};
+    return combine_backward("lse_combine_backward", c, stream);
+}
+
+cam_status lse_combine_varlen_backward(const void* part_out, int64_t po_sp, int64_t po_st, int64_t po_sh,
+                                       const float* part_lse, int64_t pl_sp, int64_t pl_st, int64_t pl_sh,
+                                       int64_t P, int64_t T, int64_t H, int64_t D, cam_dtype dt, const void* g_out,
+                                       int64_t go_st, int64_t go_sh, const float* g_lse, int64_t gl_st,
+                                       int64_t gl_sh, void* d_part_out, int64_t dpo_sp, int64_t dpo_st,
+                                       int64_t dpo_sh, float* d_part_lse, int64_t dpl_sp, int64_t dpl_st,
+                                       int64_t dpl_sh, const int32_t* cu_seqlens, int64_t nseq, void* stream)
+{
+    clear_error();
+    if (T > 0 && !cu_seqlens)
+        return set_error(CAM_ERR_NULL, "lse_combine_varlen_backward: cu_seqlens must be non-null");
+    if (T > INT32_MAX)
+        return set_error(CAM_ERR_SHAPE, "lse_combine_varlen_backward: total_tokens must fit int32");
+    CombineBwdIn c{part_out, po_sp, po_st, po_sh, part_lse, pl_sp, pl_st, pl_sh, P, T, H, D, dt,
+                   g_out, go_st, go_sh, g_lse, gl_st, gl_sh, d_part_out, dpo_sp, dpo_st, dpo_sh,
+                   d_part_lse, dpl_sp, dpl_st, dpl_sh, cu_seqlens, nseq};
+    return combine_backward("lse_combine_varlen_backward", c, stream);
 }
 
 cam_status lse_combine_packed_seq(const void* packed, int64_t P, int64_t T, int64_t H, int64_t Dv, int scatter_dim,

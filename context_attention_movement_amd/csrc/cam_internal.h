@@ -178,6 +178,39 @@ struct Merge {
     int fp16;
 };
 
+// Gradient of the combine: for each row (t, h), from the partials, their
+// LSEs and the upstream gradients (g of the output row, g_lse of its LSE),
+// dO_p = w_p g and dL_p = w_p (<g, O_p> - <g, out> + g_lse) over the valid
+// partials, zero for the others.
+struct CombineBwd {
+    const void* po;
+    int64_t po_sp_b, po_st_b, po_sh_b;
+    const float* pl;
+    int64_t pl_sp, pl_st, pl_sh;
+    const void* go;         // upstream gradient of out (payload dtype)
+    int64_t go_st_b, go_sh_b;
+    const float* gl;        // upstream gradient of lse_out (nullable: zero)
+    int64_t gl_st, gl_sh;
+    void* dpo;              // gradient of the partial outputs (payload dtype)
+    int64_t dpo_sp_b, dpo_st_b, dpo_sh_b;
+    float* dpl;             // gradient of the partial LSEs
+    int64_t dpl_sp, dpl_st, dpl_sh;
+    uint32_t P;
+    uint32_t H;
+    FastDiv div_H;
+    uint64_t n_rows;
+    uint32_t cv;
+    uint32_t g_log2;
+    uint32_t gp_log2;
+    uint32_t rows_per_tile;
+    uint64_t n_tiles;
+    const int32_t* cu;      // non-null: causal piece gating (varlen)
+    int32_t nseq;
+    FastDiv div_P;
+    int width;
+    int fp16;
+};
+
 struct Copy {
     const void* src;
     void* dst;
@@ -192,6 +225,7 @@ cam_status launch_pack(const Pack& a, void* stream);
 cam_status launch_combine(const Combine& a, void* stream);
 cam_status launch_copy(const Copy& a, void* stream);
 cam_status launch_merge(const Merge& a, void* stream);
+cam_status launch_combine_bwd(const CombineBwd& a, void* stream);
 
 // Error reporting shared by the host layer and the launchers.
 cam_status set_error(cam_status s, const char* fmt, ...);
@@ -231,6 +265,16 @@ constexpr int kTileVecs = kThreads * kVecsPerThread;
 #endif
 #ifndef CAM_NT_COPY
 #define CAM_NT_COPY 3
+#endif
+#ifndef CAM_NT_COMBINE_BWD
+#define CAM_NT_COMBINE_BWD 3
+#endif
+// Combine gradient tiling: rows per tile for rows of >= 512 bytes and shorter.
+#ifndef CAM_COMBINE_BWD_ROWS_WIDE
+#define CAM_COMBINE_BWD_ROWS_WIDE 8
+#endif
+#ifndef CAM_COMBINE_BWD_ROWS_NARROW
+#define CAM_COMBINE_BWD_ROWS_NARROW 32
 #endif
 // Combine tiling (measured on MI355X): rows per workgroup tile for rows of
 // >= 512 bytes and for shorter rows, and partial rows loaded per batch.

@@ -468,6 +468,211 @@ cam_status launch_merge(const Merge& a, void* stream)
     return launch(fn, a, (a.n_rows + rows_per_block - 1) / rows_per_block, stream, "lse_merge");
 }
 
+// ---------------------------------------------------------------------------
+// Gradient of the combine
+// ---------------------------------------------------------------------------
+
+// Tiles of RB rows, three phases.  Phase 1 recomputes each row's normalised
+// weights exactly as the forward does (same admission, max and sum), with the
+// statistics lanes of the forward.  Phase 2 streams each row once: the
+// upstream gradient g, then the valid partials' O rows in branch-free batches;
+// the lanes of a row form <g, O_p> (a shuffle reduction across the row's lanes,
+// summed over the row's vector blocks in LDS) and write dO_p = w_p g for every
+// partial, zero for those outside the valid set.  Phase 3 forms
+// dL_p = w_p (<g, O_p> - sum_q w_q <g, O_q> + g_lse) on the statistics lanes.
+// As in the forward, an invalid or masked partial's O row is never read.
+template <int W, bool FP16, bool VARLEN>
+__global__ __launch_bounds__(kThreads) void k_combine_bwd(CombineBwd a)
+{
+    typedef typename VecOf<W>::type V;
+    constexpr int E = W / 2;
+    constexpr int CH = kCombineBatch;
+    constexpr bool NTL = (CAM_NT_COMBINE_BWD & 1) != 0, NTS = (CAM_NT_COMBINE_BWD & 2) != 0;
+    extern __shared__ float smem[];
+    const uint32_t RB = a.rows_per_tile;
+    float* w_lds = smem;                                                       // RB * P weights
+    float* d_lds = w_lds + RB * a.P;                                           // RB * P  <g, O_p>
+    float* gl_lds = d_lds + RB * a.P;                                          // RB  g_lse
+    uint64_t* m_lds = reinterpret_cast<uint64_t*>(gl_lds + ((RB + 1) & ~1u));  // RB  validity masks
+    int32_t* cu_lds = reinterpret_cast<int32_t*>(m_lds + RB);                  // nseq + 1 (varlen)
+    const bool cached = VARLEN && a.nseq < kCuCache;
+    if (cached)
+        for (uint32_t i = threadIdx.x; i <= uint32_t(a.nseq); i += kThreads)
+            cu_lds[i] = a.cu[i];
+
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t GP = 1u << a.gp_log2;
+    const uint32_t sp = lane & (GP - 1u);
+    const uint32_t sbase = lane & ~(GP - 1u);
+    const uint64_t spmask = GP == 64u ? ~0ull : ((1ull << GP) - 1ull);
+    const uint32_t G = 1u << a.g_log2;
+    const uint32_t gl = lane & (G - 1u);
+    const uint32_t groups = uint32_t(kThreads) >> a.g_log2;
+    const uint32_t group = threadIdx.x >> a.g_log2;
+
+    for (uint64_t tile = blockIdx.x; tile < a.n_tiles; tile += gridDim.x) {
+        const uint64_t row0 = tile * RB;
+        // ---- phase 1: weights of the tile's rows
+        __syncthreads();
+        for (uint32_t base = 0; base < RB * GP; base += kThreads) {
+            const uint32_t tau = base + threadIdx.x;
+            const uint32_t rl = tau >> a.gp_log2;
+            const uint64_t row = row0 + rl;
+            const bool live = rl < RB && row < a.n_rows;
+            uint32_t t = 0, h = 0;
+            if (live) {
+                t = fdiv(uint32_t(row), a.div_H);
+                h = uint32_t(row) - t * a.H;
+            }
+            bool valid = false;
+            float L = -__builtin_inff();
+            if (live && sp < a.P) {
+                bool admitted = true;
+                if (VARLEN)
+                    admitted = cached ? causal_piece_ok(cu_lds, a.nseq, a.div_P, sp, t)
+                                      : causal_piece_ok(a.cu, a.nseq, a.div_P, sp, t);
+                if (admitted) {
+                    L = a.pl[int64_t(sp) * a.pl_sp + int64_t(t) * a.pl_st + int64_t(h) * a.pl_sh];
+                    valid = __builtin_isfinite(L);
+                }
+            }
+            float M = valid ? L : -__builtin_inff();
+            for (uint32_t off = GP >> 1; off > 0; off >>= 1)
+                M = fmaxf(M, __shfl_xor(M, int(off), int(GP)));
+            const uint64_t vmask = (__ballot(valid) >> sbase) & spmask;
+            const float w = valid ? expf(L - M) : 0.0f;
+            float Z = w;
+            for (uint32_t off = GP >> 1; off > 0; off >>= 1)
+                Z += __shfl_xor(Z, int(off), int(GP));
+            if (live) {
+                const float iz = vmask ? 1.0f / Z : 0.0f;
+                if (sp < a.P) {
+                    w_lds[rl * a.P + sp] = w * iz;
+                    d_lds[rl * a.P + sp] = 0.0f;
+                }
+                if (sp == 0) {
+                    m_lds[rl] = vmask;
+                    gl_lds[rl] = a.gl ? a.gl[int64_t(t) * a.gl_st + int64_t(h) * a.gl_sh] : 0.0f;
+                }
+            }
+        }
+        __syncthreads();
+
+        // ---- phase 2: one pass over each row's payload
+        const uint64_t left = a.n_rows - row0;
+        const uint32_t nr = left < RB ? uint32_t(left) : RB;
+        for (uint32_t rl = group; rl < nr; rl += groups) {
+            const uint64_t row = row0 + rl;
+            const uint32_t t = fdiv(uint32_t(row), a.div_H);
+            const uint32_t h = uint32_t(row) - t * a.H;
+            const uint64_t msk = m_lds[rl];
+            const char* prow = static_cast<const char*>(a.po) + int64_t(t) * a.po_st_b + int64_t(h) * a.po_sh_b;
+            const char* grow = static_cast<const char*>(a.go) + int64_t(t) * a.go_st_b + int64_t(h) * a.go_sh_b;
+            char* drow = static_cast<char*>(a.dpo) + int64_t(t) * a.dpo_st_b + int64_t(h) * a.dpo_sh_b;
+            for (uint32_t kb = 0; kb < a.cv; kb += G) {
+                const bool kin = kb + gl < a.cv;
+                const uint32_t k = kin ? kb + gl : a.cv - 1;
+                float ge[E];
+                if (msk) {
+                    const Halves<W> gh = __builtin_bit_cast(Halves<W>, ld_at<W, NTL>(grow + int64_t(k) * W));
+#pragma unroll
+                    for (int e = 0; e < E; ++e)
+                        ge[e] = half_to_f32<FP16>(gh.h[e]);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < E; ++e)
+                        ge[e] = 0.0f;
+                }
+                // <g, O_p> over the valid partials, CH rows per batch; a short
+                // batch repeats its last valid partial and discards the result
+                uint64_t m = msk;
+                int last = msk ? __builtin_ctzll(msk) : 0;
+                while (m) {
+                    int idx[CH];
+                    bool tk[CH];
+#pragma unroll
+                    for (int u = 0; u < CH; ++u) {
+                        const bool take = m != 0;
+                        const int p = take ? __builtin_ctzll(m) : last;
+                        m = take ? (m & (m - 1)) : m;
+                        idx[u] = p;
+                        last = p;
+                        tk[u] = take;
+                    }
+                    V x[CH];
+#pragma unroll
+                    for (int u = 0; u < CH; ++u)
+                        x[u] = ld_at<W, NTL>(prow + int64_t(k) * W + int64_t(idx[u]) * a.po_sp_b);
+                    issue_fence();
+#pragma unroll
+                    for (int u = 0; u < CH; ++u) {
+                        const Halves<W> xh = __builtin_bit_cast(Halves<W>, x[u]);
+                        float d = 0.0f;
+#pragma unroll
+                        for (int e = 0; e < E; ++e)
+                            d = fmaf(ge[e], half_to_f32<FP16>(xh.h[e]), d);
+                        d = kin ? d : 0.0f;  // a clamped tail lane repeats a vector
+                        for (uint32_t off = G >> 1; off > 0; off >>= 1)
+                            d += __shfl_xor(d, int(off), int(G));
+                        if (gl == 0 && tk[u])
+                            d_lds[rl * a.P + uint32_t(idx[u])] += d;
+                    }
+                }
+                // dO_p = w_p g for every partial (exact zero outside the valid set)
+                if (kin)
+                    for (uint32_t p = 0; p < a.P; ++p) {
+                        const float wp = w_lds[rl * a.P + p];
+                        const bool vp = ((msk >> p) & 1ull) != 0;
+                        Halves<W> oh;
+#pragma unroll
+                        for (int e = 0; e < E; ++e)
+                            oh.h[e] = f32_to_half<FP16>(vp ? wp * ge[e] : 0.0f);
+                        st_at<W, NTS>(drow + int64_t(k) * W + int64_t(p) * a.dpo_sp_b, __builtin_bit_cast(V, oh));
+                    }
+            }
+        }
+        __syncthreads();
+
+        // ---- phase 3: gradient of the partial LSEs
+        for (uint32_t base = 0; base < RB * GP; base += kThreads) {
+            const uint32_t tau = base + threadIdx.x;
+            const uint32_t rl = tau >> a.gp_log2;
+            const uint64_t row = row0 + rl;
+            const bool live = rl < RB && row < a.n_rows;
+            const bool mine = live && sp < a.P;
+            const float w = mine ? w_lds[rl * a.P + sp] : 0.0f;
+            const float d = mine ? d_lds[rl * a.P + sp] : 0.0f;
+            float s = w * d;
+            for (uint32_t off = GP >> 1; off > 0; off >>= 1)
+                s += __shfl_xor(s, int(off), int(GP));
+            if (mine) {
+                const uint32_t t = fdiv(uint32_t(row), a.div_H);
+                const uint32_t h = uint32_t(row) - t * a.H;
+                const bool valid = ((m_lds[rl] >> sp) & 1ull) != 0;
+                a.dpl[int64_t(sp) * a.dpl_sp + int64_t(t) * a.dpl_st + int64_t(h) * a.dpl_sh] =
+                    valid ? w * (d - s + gl_lds[rl]) : 0.0f;
+            }
+        }
+    }
+}
+
+cam_status launch_combine_bwd(const CombineBwd& a, void* stream)
+{
+    const void* fn = nullptr;
+#define CAM_PICK_BWD(Wd)                                                                               \
+    if (a.width == Wd)                                                                                 \
+        fn = a.cu ? (a.fp16 ? reinterpret_cast<const void*>(&k_combine_bwd<Wd, true, true>)           \
+                            : reinterpret_cast<const void*>(&k_combine_bwd<Wd, false, true>))         \
+                  : (a.fp16 ? reinterpret_cast<const void*>(&k_combine_bwd<Wd, true, false>)          \
+                            : reinterpret_cast<const void*>(&k_combine_bwd<Wd, false, false>));
+    CAM_PICK_BWD(16) CAM_PICK_BWD(8) CAM_PICK_BWD(4) CAM_PICK_BWD(2)
+#undef CAM_PICK_BWD
+    uint64_t lds = (2ull * a.rows_per_tile * a.P + ((a.rows_per_tile + 1) & ~1u)) * 4 + uint64_t(a.rows_per_tile) * 8;
+    if (a.cu && a.nseq < kCuCache)
+        lds += uint64_t(a.nseq + 1) * 4;
+    return launch(fn, a, a.n_tiles, stream, "lse_combine_backward", lds, kThreads);
+}
+
 cam_status launch_combine(const Combine& a, void* stream)
 {
     // Rows of at least 512 bytes (one or more full 64-lane passes) keep two

@@ -276,6 +276,50 @@ cam_status lse_merge(float* acc_out, int64_t a_st, int64_t a_sh, float* acc_lse,
                      void* stream);
 
 /* ------------------------------------------------------------------------- */
+/* Training: gradient of the combine ([CU] forward and backward comparison of  */
+/* context parallelism; [FV] benchmark training pair).  The gradient of a      */
+/* relayout is the inverse relayout (ulysses_head_to_seq for            */
+/* ulysses_seq_to_head and the other way round, the same for varlen).          */
+/* ------------------------------------------------------------------------- */
+/*
+ * lse_combine_backward: the gradient of lse_combine.  For each row (t, h), with
+ *   V the valid partials (finite LSE), w_p = exp(L_p - lse_out) their
+ *   normalised weights (formed as in the forward), g the upstream gradient of
+ *   out[t][h][:] and g_lse that of lse_out[t][h]:
+ *     d_part_out[p][t][h][:] = w_p * g                        (p in V)
+ *     d_part_lse[p][t][h]    = w_p * (<g, O_p> - sum_{q in V} w_q <g, O_q> + g_lse)
+ *   and exact zeros for p outside V (an empty V gives zeros throughout).  The
+ *   O row of a partial outside V is never read.  fp32 arithmetic; d_part_out
+ *   rounded to the payload dtype (RNE), d_part_lse fp32.
+ * Layouts (element strides, D contiguous): part_out, part_lse as in
+ *   lse_combine; g_out (t, h, d) at go_st*t + go_sh*h + d, payload dt;
+ *   g_lse (t, h) fp32 at gl_st*t + gl_sh*h, nullable (then zero);
+ *   d_part_out (p, t, h, d) at dpo_sp*p + dpo_st*t + dpo_sh*h + d, payload dt;
+ *   d_part_lse (p, t, h) at dpl_sp*p + dpl_st*t + dpl_sh*h, fp32.
+ *   Every element of both gradients is written.  1 <= P <= 64; T*H < 2^31.
+ *   Outputs may overlap neither an input nor each other.
+ *
+ * lse_combine_varlen_backward: the gradient of lse_combine_varlen (the causal
+ *   piece rule decides V: a masked partial gets zero gradient and is not read).
+ */
+cam_status lse_combine_backward(const void* part_out, int64_t po_sp, int64_t po_st, int64_t po_sh,
+                                const float* part_lse, int64_t pl_sp, int64_t pl_st, int64_t pl_sh,
+                                int64_t P, int64_t T, int64_t H, int64_t D, cam_dtype dt,
+                                const void* g_out, int64_t go_st, int64_t go_sh, const float* g_lse,
+                                int64_t gl_st, int64_t gl_sh, void* d_part_out, int64_t dpo_sp,
+                                int64_t dpo_st, int64_t dpo_sh, float* d_part_lse, int64_t dpl_sp,
+                                int64_t dpl_st, int64_t dpl_sh, void* stream);
+cam_status lse_combine_varlen_backward(const void* part_out, int64_t po_sp, int64_t po_st,
+                                       int64_t po_sh, const float* part_lse, int64_t pl_sp,
+                                       int64_t pl_st, int64_t pl_sh, int64_t P, int64_t T, int64_t H,
+                                       int64_t D, cam_dtype dt, const void* g_out, int64_t go_st,
+                                       int64_t go_sh, const float* g_lse, int64_t gl_st, int64_t gl_sh,
+                                       void* d_part_out, int64_t dpo_sp, int64_t dpo_st,
+                                       int64_t dpo_sh, float* d_part_lse, int64_t dpl_sp,
+                                       int64_t dpl_st, int64_t dpl_sh, const int32_t* cu_seqlens,
+                                       int64_t nseq, void* stream);
+
+/* ------------------------------------------------------------------------- */
 /* Measurement helper                                                          */
 /* ------------------------------------------------------------------------- */
 /*

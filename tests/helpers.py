@@ -66,3 +66,34 @@ def assert_rows_close(got: np.ndarray, want: np.ndarray, what: str) -> float:
     worst = float(np.max(rel))
     assert worst <= OUT_ROW_RTOL, f"{what}: worst row relative error {worst}"
     return worst
+
+
+GRAD_LSE_RTOL = 1e-5     # gradient of the partial LSEs, relative to the row scale
+
+
+def grad_lse_scale(po: np.ndarray, go: np.ndarray, gl: np.ndarray | None) -> np.ndarray:
+    """Row scale of dL_p = w_p (<g, O_p> - sum_q w_q <g, O_q> + g_lse): with
+    the weights in [0, 1] summing to one, |dL_p| <= 2 sum_d |g_d| max_p |O_pd|
+    + |g_lse|, and fp32 rounding of the dot products is relative to that sum.
+    po float64 [P][R][D] (non-finite entries of invalid partials ignored),
+    go float64 [R][D], gl float64 [R] or None -> [R]."""
+    amax = np.max(np.where(np.isfinite(po), np.abs(po), 0.0), axis=0)
+    s = np.sum(np.abs(go) * amax, axis=-1)
+    return s + (np.abs(gl) if gl is not None else 0.0)
+
+
+def assert_grad_lse_close(got: np.ndarray, want: np.ndarray, scale: np.ndarray, what: str) -> float:
+    """got, want: [P][R] fp32; scale [R].  |got - want| <= 1e-5 * scale (plus
+    the fp32 spacing of the value), exact zeros where the oracle is exactly
+    zero (partials outside the valid set), no NaN."""
+    got = got.astype(np.float64)
+    want = want.astype(np.float64)
+    assert not np.isnan(got).any(), f"{what}: NaN in the LSE gradient"
+    zero = want == 0
+    assert np.all(got[zero] == 0), f"{what}: nonzero gradient where the oracle is exactly zero"
+    err = np.abs(got - want)
+    tol = GRAD_LSE_RTOL * scale[None, :] + np.spacing(np.abs(want).astype(np.float32)).astype(np.float64)
+    bad = err > tol
+    assert not bad.any(), f"{what}: {int(bad.sum())} LSE-gradient entries out of tolerance, worst " \
+                          f"{float(np.max(err / np.maximum(tol, 1e-300)))} x tol"
+    return float(np.max(err / np.maximum(scale[None, :], 1e-30)))

@@ -248,3 +248,28 @@ def test_last_launch_record(cam):
     wg, th, lds = C.c_uint64(7), C.c_uint32(7), C.c_uint64(7)
     assert lib.cam_last_launch(C.addressof(wg), C.addressof(th), C.addressof(lds)) == 0
     assert lib.cam_last_launch(None, C.addressof(th), C.addressof(lds)) != 0
+
+
+def test_combine_backward_rejections(lib):
+    f = lib.lse_combine_backward
+    L, G, GL, DO, DL = (A + 0x1000_0000, A + 0x2000_0000, A + 0x3000_0000, A + 0x4000_0000,
+                        A + 0x5000_0000)
+    P, T, H, D = 4, 64, 8, 16
+
+    def args(po=A, pl=L, go=G, gl=GL, do=DO, dl=DL, P=P, dt=BF16):
+        return (po, T * H * D, H * D, D, pl, T * H, H, 1, P, T, H, D, dt, go, H * D, D, gl, H, 1,
+                do, T * H * D, H * D, D, dl, T * H, H, 1, None)
+
+    assert f(*args(P=65)) == UNSUP
+    assert f(*args(P=0)) == SHAPE
+    assert f(*args(dt=FP32)) == UNSUP
+    assert f(*args(go=None)) == NULL
+    assert f(*args(do=None)) == NULL
+    assert f(*args(dl=DL + 2)) == ALIGN
+    assert f(*args(do=A + 64)) == OVERLAP        # gradient over the partials
+    assert f(*args(dl=G + 4)) == OVERLAP         # gradient over the upstream gradient
+    assert f(*args(dl=DO + 8)) == OVERLAP        # the two gradients overlap
+    g = lib.lse_combine_varlen_backward
+    assert g(*args()[:-1], None, 3, None) == NULL
+    assert g(*args()[:-1], A + 0x6000_0000, 0, None) == SHAPE
+    assert g(*args(dl=A + 0x6000_0000)[:-1], A + 0x6000_0000, 3, None) == OVERLAP
