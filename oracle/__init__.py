@@ -75,6 +75,10 @@ def _load():
                                  vp, vp, vp]),
         "orc_varlen_token_rows": (None, [vp, i64, i64, vp]),
         "orc_lse_combine_packed_seq": (None, [vp, i64, i64, i64, i64, C.c_int, C.c_int, vp, vp]),
+        "orc_thd_plan": (C.c_int, [vp, i64, i64, i64, i64, i64, C.c_double, C.c_double, i64, vp, vp, vp, vp,
+                                   vp, vp, vp]),
+        "orc_span_seq_to_head": (None, [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64]),
+        "orc_span_head_to_seq": (None, [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64]),
         "orc_combine_row_backward_f64": (None, [vp, vp, vp, i64, i64, vp, C.c_double, vp, vp]),
         "orc_lse_combine_backward": (None, [vp, i64, i64, i64, vp, i64, i64, i64, i64, i64, i64, i64, i64,
                                             C.c_int, vp, i64, i64, vp, i64, i64, vp, i64, i64, i64,
@@ -384,4 +388,63 @@ def lse_combine_backward(part_out: np.ndarray, part_lse: np.ndarray, g_out: np.n
         _p(d_po), Tw * H * D, H * D, D, _p(d_pl), Tw * H, H, 1,
         _p(cu_arr) if cu_arr is not None else None, 0 if cu_arr is None else cu_arr.size - 1)
     return d_po, d_pl
+
+
+# -- THD layout planner and planned-span relayout ------------------------------
+
+PLAN_ERRORS = {-1: "config", -2: "lengths", -3: "blocks", -4: "capacity"}
+
+
+def thd_plan(cu, world_size: int, block_size: int = 64, min_split_tokens: int = 8192,
+             max_chunks_per_rank: int = 64, token_weight: float = 1.0, causal_weight: float = 1.0):
+    """Plan a packed THD batch over world_size ranks.  Returns a dict with
+    span_start [n+1], span_rank [n], span_local [n] (int32), rank_off [W+1]
+    (int64), rank_cost [W] (float64) and grid (0 = contiguous); raises
+    ValueError(kind) on a rejected input."""
+    cu = np.ascontiguousarray(np.asarray(cu, dtype=np.int32))
+    nseq = cu.size - 1
+    cap = max(16, 4 * (nseq + world_size))
+    while True:
+        ss = np.empty(cap + 1, dtype=np.int32)
+        sr = np.empty(cap, dtype=np.int32)
+        sl = np.empty(cap, dtype=np.int32)
+        ro = np.empty(max(world_size, 0) + 1, dtype=np.int64)
+        rc = np.empty(max(world_size, 1), dtype=np.float64)
+        n = np.zeros(1, dtype=np.int64)
+        g = np.zeros(1, dtype=np.int32)
+        code = _load().orc_thd_plan(_p(cu), nseq, world_size, block_size, min_split_tokens, max_chunks_per_rank,
+                                    token_weight, causal_weight, cap, _p(ss), _p(sr), _p(sl), _p(ro), _p(rc),
+                                    _p(n), _p(g))
+        if code == -4:
+            cap = int(n[0])
+            continue
+        if code != 0:
+            raise ValueError(PLAN_ERRORS.get(code, str(code)))
+        k = int(n[0])
+        return {"span_start": ss[:k + 1].copy(), "span_rank": sr[:k].copy(), "span_local": sl[:k].copy(),
+                "rank_off": ro.copy(), "rank_cost": rc[:world_size].copy(), "grid": int(g[0])}
+
+
+def span_seq_to_head(x: np.ndarray, plan: dict, P: int, B: int, H: int, D: int) -> np.ndarray:
+    """Rank-major planned slabs [B*T][H][D] -> [P][B][T][H/P][D]."""
+    x = np.ascontiguousarray(x)
+    T = int(plan["span_start"][-1])
+    assert x.size == B * T * H * D
+    out = np.empty(P * B * T * (H // P) * D, dtype=x.dtype)
+    _load().orc_span_seq_to_head(_p(x), _p(out), _p(plan["span_start"]), _p(plan["span_rank"]),
+                                 _p(plan["span_local"]), _p(plan["rank_off"]), plan["span_rank"].size,
+                                 P, B, H, D, x.dtype.itemsize)
+    return out.reshape(P, B, T, H // P, D)
+
+
+def span_head_to_seq(x: np.ndarray, plan: dict, P: int, B: int, H: int, D: int) -> np.ndarray:
+    """[P][B][T][H/P][D] -> rank-major planned slabs [B*T][H][D]."""
+    x = np.ascontiguousarray(x)
+    T = int(plan["span_start"][-1])
+    assert x.size == B * T * H * D
+    out = np.empty(B * T * H * D, dtype=x.dtype)
+    _load().orc_span_head_to_seq(_p(x), _p(out), _p(plan["span_start"]), _p(plan["span_rank"]),
+                                 _p(plan["span_local"]), _p(plan["rank_off"]), plan["span_rank"].size,
+                                 P, B, H, D, x.dtype.itemsize)
+    return out.reshape(B * T, H, D)
 

@@ -759,3 +759,422 @@ void orc_lse_combine_backward(const void* part_out, int64_t po_sp, int64_t po_st
     free(d_o);
     free(d_l);
 }
+
+/* ------------------------------------------------------------------------ */
+/* THD layout planner and planned-span relayout  ([CU] "THD layout planner")  */
+/* ------------------------------------------------------------------------ */
+/*
+ * The page states the planner's contract, not its steps: balance token-linear
+ * and causal (position-dependent) work of an arbitrary packed THD batch over
+ * the context-parallel ranks; block-aligned shards with exact balanced token
+ * capacity (non-power-of-two rank counts allowed); short samples kept whole;
+ * long sequences sharded with a direction that alternates across ranks;
+ * several planning grids, each a greedy assignment plus token rebalancing,
+ * with a contiguous fallback; deterministic per-rank spans; and its input
+ * rules (positive block size, block-aligned min_split_tokens and lengths,
+ * positive max_chunks_per_rank, finite non-negative weights not both zero,
+ * at least one block per rank).  Reading (the concrete algorithm):
+ *
+ *  n_i = L_i / b blocks, N = sum n_i; rank r holds exactly
+ *  cap_r = floor((r+1)N/W) - floor(rN/W) blocks (the balanced shards).
+ *  Work of a token at position k of its sequence: token_weight
+ *  + causal_weight * (k + 1) (a causal query sees k + 1 keys); a rank's cost
+ *  is token_weight * tokens + causal_weight * sum(k + 1) over its tokens.
+ *  Candidate 0 (contiguous): rank r takes global blocks
+ *  [floor(rN/W), floor((r+1)N/W)).  Candidate g = 1..6 (grid g): a sequence
+ *  is long if L_i >= min_split_tokens (and n_i >= 2), else short.
+ *   B. shorts, costliest first (ties: batch order), each whole to the
+ *      cheapest rank (ties: lowest) with room for it; a short that fits
+ *      nowhere waits for C2 (placing the shorts first splits a short only
+ *      when it does not fit beside the shorts already placed);
+ *   A. then each long sequence (the l-th, in batch order) is cut into
+ *      m = min(n_i, W * 2^(g-1)) chunks [floor(c n_i/m), floor((c+1) n_i/m));
+ *      chunk c goes to rank psi = c mod W if floor(c/W) + l is even, else to
+ *      W - 1 - psi (a snake whose direction alternates per round and per
+ *      long sequence), capacity notwithstanding;
+ *   C1. while a rank is over capacity (only long chunks overfill): the
+ *      lowest such rank o gives the last
+ *      x blocks of its long-sequence span that ends at the highest block
+ *      position (ties: later sequence) to the cheapest rank u with room
+ *      (ties: lowest), x = min(excess of o, room of u, span length);
+ *   C2. each waiting short, in B's order, is laid into the cheapest ranks
+ *      with room, in order, as far as their room allows;
+ *   then spans of one sequence that meet on one rank are merged, and a
+ *   candidate with more than max_chunks_per_rank spans on a rank is dropped.
+ *  The plan is the candidate with the least maximum rank cost, ties to fewer
+ *  spans, then to the lower candidate number (so the contiguous layout wins
+ *  ties and is the fallback).
+ *
+ *  Output: spans in packed token order: span_start[n + 1] (global token of
+ *  each span's first row, span_start[n] = T), span_rank[n], span_local[n]
+ *  (the span's first row within its rank's slab; a rank's slab lists its
+ *  spans in packed order), rank_off[W + 1] (token prefix of the slabs),
+ *  rank_cost[W], and the chosen candidate.  Returns 0, or a negative code:
+ *  -1 bad config or world size, -2 misaligned or malformed lengths,
+ *  -3 fewer blocks than ranks, -4 span capacity too small (*n_spans is then
+ *  the count needed).
+ */
+typedef struct {
+    int64_t seq, a, e, rank; /* blocks [a, e) of sequence seq */
+} orc_span;
+
+typedef struct {
+    orc_span* s;
+    int64_t n, cap;
+} orc_spans;
+
+static void spans_add(orc_spans* v, int64_t seq, int64_t a, int64_t e, int64_t rank)
+{
+    if (a >= e)
+        return;
+    if (v->n == v->cap) {
+        v->cap = v->cap ? 2 * v->cap : 64;
+        v->s = (orc_span*)realloc(v->s, sizeof(orc_span) * (size_t)v->cap);
+    }
+    v->s[v->n].seq = seq;
+    v->s[v->n].a = a;
+    v->s[v->n].e = e;
+    v->s[v->n].rank = rank;
+    v->n++;
+}
+
+/* 1 + 2 + ... + n */
+static int64_t tri(int64_t n) { return n * (n + 1) / 2; }
+
+/* sum of (k + 1) over token positions k in [ta, te) */
+static int64_t causal_work(int64_t ta, int64_t te) { return tri(te) - tri(ta); }
+
+static double work_cost(double wt, double wc, int64_t tokens, int64_t causal)
+{
+    double x = wt * (double)tokens;
+    double y = wc * (double)causal;
+    return x + y;
+}
+
+typedef struct {
+    int64_t W, b;
+    double wt, wc;
+    int64_t *blk, *caus; /* per rank: blocks and causal work held */
+    const int64_t* capb;
+} orc_loads;
+
+static double rank_cost_of(const orc_loads* L, int64_t r)
+{
+    return work_cost(L->wt, L->wc, L->blk[r] * L->b, L->caus[r]);
+}
+
+static void loads_add(orc_loads* L, int64_t r, int64_t a, int64_t e, int sign)
+{
+    L->blk[r] += sign * (e - a);
+    L->caus[r] += sign * causal_work(a * L->b, e * L->b);
+}
+
+/* cheapest rank with room for `need` blocks (ties: lowest), -1 if none */
+static int64_t cheapest_with_room(const orc_loads* L, int64_t need)
+{
+    int64_t best = -1;
+    for (int64_t r = 0; r < L->W; ++r)
+        if (L->capb[r] - L->blk[r] >= need && (best < 0 || rank_cost_of(L, r) < rank_cost_of(L, best)))
+            best = r;
+    return best;
+}
+
+static int span_order(const void* x, const void* y)
+{
+    const orc_span* p = (const orc_span*)x;
+    const orc_span* q = (const orc_span*)y;
+    if (p->seq != q->seq)
+        return p->seq < q->seq ? -1 : 1;
+    return p->a < q->a ? -1 : (p->a > q->a ? 1 : 0);
+}
+
+/* merge spans of one sequence that meet on one rank (spans sorted) */
+static void spans_normalize(orc_spans* v)
+{
+    qsort(v->s, (size_t)v->n, sizeof(orc_span), span_order);
+    int64_t m = 0;
+    for (int64_t k = 0; k < v->n; ++k) {
+        if (m > 0 && v->s[m - 1].seq == v->s[k].seq && v->s[m - 1].rank == v->s[k].rank && v->s[m - 1].e == v->s[k].a)
+            v->s[m - 1].e = v->s[k].e;
+        else
+            v->s[m++] = v->s[k];
+    }
+    v->n = m;
+}
+
+/* grid g >= 1, or the contiguous layout for g = 0 */
+static void plan_candidate(int g, const int64_t* nb, int64_t nseq, int64_t W, int64_t b, int64_t min_split,
+                           double wt, double wc, const int64_t* capb, orc_spans* out)
+{
+    int64_t* blk = (int64_t*)calloc((size_t)W, sizeof(int64_t));
+    int64_t* caus = (int64_t*)calloc((size_t)W, sizeof(int64_t));
+    orc_loads L = {W, b, wt, wc, blk, caus, capb};
+    out->n = 0;
+    if (g == 0) {
+        int64_t N = 0;
+        for (int64_t i = 0; i < nseq; ++i)
+            N += nb[i];
+        int64_t base = 0;
+        for (int64_t i = 0; i < nseq; ++i) {
+            for (int64_t r = 0; r < W; ++r) {
+                int64_t lo = r * N / W, hi = (r + 1) * N / W;
+                int64_t a = lo > base ? lo - base : 0;
+                int64_t e = hi - base < nb[i] ? hi - base : nb[i];
+                spans_add(out, i, a, e, r);
+            }
+            base += nb[i];
+        }
+    } else {
+        const int64_t M = W << (g - 1);
+        /* B: shorts, costliest first, whole where they fit (before any long chunk) */
+        int64_t* order = (int64_t*)malloc(sizeof(int64_t) * (size_t)(nseq + 1));
+        int64_t ns = 0;
+        for (int64_t i = 0; i < nseq; ++i)
+            if (nb[i] > 0 && !(nb[i] * b >= min_split && nb[i] >= 2))
+                order[ns++] = i;
+        for (int64_t x = 1; x < ns; ++x) /* insertion sort: cost desc, index asc */
+            for (int64_t y = x; y > 0; --y) {
+                int64_t i = order[y - 1], j = order[y];
+                double ci = work_cost(wt, wc, nb[i] * b, causal_work(0, nb[i] * b));
+                double cj = work_cost(wt, wc, nb[j] * b, causal_work(0, nb[j] * b));
+                if (cj > ci || (cj == ci && j < i)) {
+                    order[y - 1] = j;
+                    order[y] = i;
+                } else {
+                    break;
+                }
+            }
+        int64_t* aside = (int64_t*)malloc(sizeof(int64_t) * (size_t)(nseq + 1));
+        int64_t na = 0;
+        for (int64_t x = 0; x < ns; ++x) {
+            int64_t i = order[x];
+            int64_t r = cheapest_with_room(&L, nb[i]);
+            if (r < 0) {
+                aside[na++] = i;
+                continue;
+            }
+            spans_add(out, i, 0, nb[i], r);
+            loads_add(&L, r, 0, nb[i], +1);
+        }
+        /* A: long sequences, snake */
+        int64_t ell = 0;
+        for (int64_t i = 0; i < nseq; ++i) {
+            if (!(nb[i] * b >= min_split && nb[i] >= 2))
+                continue;
+            int64_t m = nb[i] < M ? nb[i] : M;
+            for (int64_t c = 0; c < m; ++c) {
+                int64_t a = c * nb[i] / m, e = (c + 1) * nb[i] / m;
+                int64_t psi = c % W;
+                int64_t r = ((c / W + ell) % 2 == 0) ? psi : W - 1 - psi;
+                spans_add(out, i, a, e, r);
+                loads_add(&L, r, a, e, +1);
+            }
+            ell++;
+        }
+        /* C1: rebalance to exact capacity */
+        for (;;) {
+            int64_t o = -1;
+            for (int64_t r = 0; r < W && o < 0; ++r)
+                if (blk[r] > capb[r])
+                    o = r;
+            if (o < 0)
+                break;
+            int64_t d = -1;
+            for (int64_t k = 0; k < out->n; ++k) {
+                const orc_span* s = &out->s[k];
+                if (s->rank != o || s->a >= s->e || !(nb[s->seq] * b >= min_split && nb[s->seq] >= 2))
+                    continue;
+                if (d < 0 || s->e > out->s[d].e || (s->e == out->s[d].e && s->seq > out->s[d].seq))
+                    d = k;
+            }
+            int64_t u = cheapest_with_room(&L, 1);
+            int64_t x = blk[o] - capb[o];
+            if (capb[u] - blk[u] < x)
+                x = capb[u] - blk[u];
+            if (out->s[d].e - out->s[d].a < x)
+                x = out->s[d].e - out->s[d].a;
+            int64_t seq = out->s[d].seq, e = out->s[d].e;
+            out->s[d].e = e - x;
+            loads_add(&L, o, e - x, e, -1);
+            spans_add(out, seq, e - x, e, u);
+            loads_add(&L, u, e - x, e, +1);
+        }
+        /* C2: shorts that fit nowhere whole */
+        for (int64_t x = 0; x < na; ++x) {
+            int64_t i = aside[x];
+            int64_t a = 0;
+            while (a < nb[i]) {
+                int64_t u = cheapest_with_room(&L, 1);
+                int64_t k = capb[u] - blk[u];
+                if (nb[i] - a < k)
+                    k = nb[i] - a;
+                spans_add(out, i, a, a + k, u);
+                loads_add(&L, u, a, a + k, +1);
+                a += k;
+            }
+        }
+        free(order);
+        free(aside);
+        /* drop spans emptied by C1 */
+        int64_t m = 0;
+        for (int64_t k = 0; k < out->n; ++k)
+            if (out->s[k].a < out->s[k].e)
+                out->s[m++] = out->s[k];
+        out->n = m;
+    }
+    spans_normalize(out);
+    free(blk);
+    free(caus);
+}
+
+int orc_thd_plan(const int32_t* cu, int64_t nseq, int64_t W, int64_t block_size, int64_t min_split_tokens,
+                 int64_t max_chunks_per_rank, double token_weight, double causal_weight, int64_t max_spans,
+                 int32_t* span_start, int32_t* span_rank, int32_t* span_local, int64_t* rank_off,
+                 double* rank_cost, int64_t* n_spans, int32_t* chosen)
+{
+    const int64_t b = block_size;
+    if (W < 1 || b < 1 || min_split_tokens < 1 || min_split_tokens % b != 0 || max_chunks_per_rank < 1 ||
+        !isfinite(token_weight) || !isfinite(causal_weight) || token_weight < 0 || causal_weight < 0 ||
+        (token_weight == 0 && causal_weight == 0))
+        return -1;
+    if (nseq < 0 || cu[0] != 0)
+        return -2;
+    int64_t* nb = (int64_t*)malloc(sizeof(int64_t) * (size_t)(nseq + 1));
+    int64_t N = 0;
+    for (int64_t i = 0; i < nseq; ++i) {
+        int64_t L = (int64_t)cu[i + 1] - cu[i];
+        if (L < 0 || L % b != 0) {
+            free(nb);
+            return -2;
+        }
+        nb[i] = L / b;
+        N += nb[i];
+    }
+    if (N < W) {
+        free(nb);
+        return -3;
+    }
+    int64_t* capb = (int64_t*)malloc(sizeof(int64_t) * (size_t)W);
+    for (int64_t r = 0; r < W; ++r)
+        capb[r] = (r + 1) * N / W - r * N / W;
+
+    orc_spans best = {0, 0, 0}, cand = {0, 0, 0};
+    double best_max = 0.0;
+    int best_g = -1;
+    int64_t* blk = (int64_t*)malloc(sizeof(int64_t) * (size_t)W);
+    int64_t* caus = (int64_t*)malloc(sizeof(int64_t) * (size_t)W);
+    int64_t* cnt = (int64_t*)malloc(sizeof(int64_t) * (size_t)W);
+    for (int g = 0; g <= 6; ++g) {
+        plan_candidate(g, nb, nseq, W, b, min_split_tokens, token_weight, causal_weight, capb, &cand);
+        for (int64_t r = 0; r < W; ++r)
+            blk[r] = caus[r] = cnt[r] = 0;
+        for (int64_t k = 0; k < cand.n; ++k) {
+            const orc_span* s = &cand.s[k];
+            blk[s->rank] += s->e - s->a;
+            caus[s->rank] += causal_work(s->a * b, s->e * b);
+            cnt[s->rank]++;
+        }
+        int fits = 1;
+        double mx = 0.0;
+        for (int64_t r = 0; r < W; ++r) {
+            if (cnt[r] > max_chunks_per_rank)
+                fits = 0;
+            double c = work_cost(token_weight, causal_weight, blk[r] * b, caus[r]);
+            if (r == 0 || c > mx)
+                mx = c;
+        }
+        if (g > 0 && !fits)
+            continue;
+        if (best_g < 0 || mx < best_max || (mx == best_max && cand.n < best.n)) {
+            orc_spans t = best;
+            best = cand;
+            cand = t;
+            best_max = mx;
+            best_g = g;
+        }
+    }
+    free(cand.s);
+    *n_spans = best.n;
+    int rc = 0;
+    if (best.n > max_spans) {
+        rc = -4;
+    } else {
+        int64_t* fill = (int64_t*)calloc((size_t)W, sizeof(int64_t));
+        rank_off[0] = 0;
+        for (int64_t r = 0; r < W; ++r) {
+            rank_off[r + 1] = rank_off[r] + capb[r] * b;
+            blk[r] = caus[r] = 0;
+        }
+        for (int64_t k = 0; k < best.n; ++k) {
+            const orc_span* s = &best.s[k];
+            span_start[k] = (int32_t)(cu[s->seq] + s->a * b);
+            span_rank[k] = (int32_t)s->rank;
+            span_local[k] = (int32_t)fill[s->rank];
+            fill[s->rank] += (s->e - s->a) * b;
+            blk[s->rank] += s->e - s->a;
+            caus[s->rank] += causal_work(s->a * b, s->e * b);
+        }
+        span_start[best.n] = cu[nseq];
+        for (int64_t r = 0; r < W; ++r)
+            rank_cost[r] = work_cost(token_weight, causal_weight, blk[r] * b, caus[r]);
+        *chosen = best_g;
+        free(fill);
+    }
+    free(best.s);
+    free(nb);
+    free(capb);
+    free(blk);
+    free(caus);
+    free(cnt);
+    return rc;
+}
+
+/*
+ * Relayout over planned spans (B planes, D contiguous, es-byte elements):
+ *   sequence side: rank p's slab [B][T_p][H][D] at token row B*rank_off[p];
+ *   head side:     [P][B][T][H/P][D] in packed token order.
+ * Token t of span s (span_start[s] <= t < span_start[s+1]) is row
+ * span_local[s] + t - span_start[s] of rank span_rank[s]'s slab.  dir 1:
+ * sequence side -> head side; dir 0: the inverse.
+ */
+static void span_relayout(const void* in, void* out, const int32_t* span_start, const int32_t* span_rank,
+                          const int32_t* span_local, const int64_t* rank_off, int64_t n_spans, int64_t P,
+                          int64_t B, int64_t H, int64_t D, int64_t es, int dir)
+{
+    const int64_t T = span_start[n_spans];
+    const int64_t Hp = H / P;
+    const int64_t run = Hp * D * es;
+    for (int64_t s = 0; s < n_spans; ++s) {
+        const int64_t p = span_rank[s];
+        const int64_t Tp = rank_off[p + 1] - rank_off[p];
+        for (int64_t t = span_start[s]; t < span_start[s + 1]; ++t) {
+            const int64_t l = span_local[s] + (t - span_start[s]);
+            for (int64_t bb = 0; bb < B; ++bb) {
+                const int64_t seq_row = B * rank_off[p] + bb * Tp + l;
+                for (int64_t r = 0; r < P; ++r) {
+                    const int64_t head_row = (r * B + bb) * T + t;
+                    char* sq = (char*)(dir ? in : out) + (seq_row * H + r * Hp) * D * es;
+                    char* hd = (char*)(dir ? out : in) + head_row * Hp * D * es;
+                    if (dir)
+                        memcpy(hd, sq, (size_t)run);
+                    else
+                        memcpy(sq, hd, (size_t)run);
+                }
+            }
+        }
+    }
+}
+
+void orc_span_seq_to_head(const void* in, void* out, const int32_t* span_start, const int32_t* span_rank,
+                          const int32_t* span_local, const int64_t* rank_off, int64_t n_spans, int64_t P,
+                          int64_t B, int64_t H, int64_t D, int64_t es)
+{
+    span_relayout(in, out, span_start, span_rank, span_local, rank_off, n_spans, P, B, H, D, es, 1);
+}
+
+void orc_span_head_to_seq(const void* in, void* out, const int32_t* span_start, const int32_t* span_rank,
+                          const int32_t* span_local, const int64_t* rank_off, int64_t n_spans, int64_t P,
+                          int64_t B, int64_t H, int64_t D, int64_t es)
+{
+    span_relayout(in, out, span_start, span_rank, span_local, rank_off, n_spans, P, B, H, D, es, 0);
+}

@@ -1,0 +1,265 @@
+"""Pins of the oracle's THD layout planner and planned-span relayout.
+
+Planner: the input rules the page lists; the hand-worked plan in
+tests/golden/thd_plan_small.json; on random packed batches (non-power-of-two
+rank counts included) the invariants the page states -- every token placed
+once, block-aligned spans, exact balanced token capacity per rank, short
+samples whole when they fit, at most max_chunks_per_rank spans per rank
+(except the contiguous fallback), deterministic output -- with rank costs
+recomputed exactly from the spans, and never worse than the contiguous
+layout (computed here from the balanced-shard closed form); brute force over
+every capacity-respecting block assignment bounds the plan on tiny batches.
+
+Span relayout: with the spans of the per-sequence split it equals the pinned
+varlen relayout bit for bit; round trip and exactly-once coverage; per-element
+brute force on a tiny case."""
+
+import itertools
+import json
+from pathlib import Path
+
+import numpy as np
+import pytest
+
+import synth
+
+GOLDEN = Path(__file__).resolve().parent / "golden"
+
+
+def _exact_costs(plan, cu, wt=1.0, wc=1.0):
+    """Per rank (tokens, causal work) from the spans, in Python integers."""
+    W = plan["rank_off"].size - 1
+    tok = [0] * W
+    caus = [0] * W
+    ss, sr = plan["span_start"], plan["span_rank"]
+    for s in range(sr.size):
+        a, e = int(ss[s]), int(ss[s + 1])
+        i = int(np.searchsorted(cu, a, side="right")) - 1
+        k0, k1 = a - int(cu[i]), e - int(cu[i])
+        tok[int(sr[s])] += e - a
+        caus[int(sr[s])] += sum(range(k0 + 1, k1 + 1))
+    return tok, caus
+
+
+def _contiguous_max(cu, W, b, wt=1.0, wc=1.0):
+    T = int(cu[-1])
+    N = T // b
+    worst = 0.0
+    for r in range(W):
+        lo, hi = (r * N // W) * b, ((r + 1) * N // W) * b
+        c = 0
+        for t in range(lo, hi):
+            i = int(np.searchsorted(cu, t, side="right")) - 1
+            c += t - int(cu[i]) + 1
+        worst = max(worst, wt * (hi - lo) + wc * c)
+    return worst
+
+
+def _check_invariants(plan, cu, W, b, min_split, max_chunks):
+    T = int(cu[-1])
+    N = T // b
+    ss, sr, sl, ro = plan["span_start"], plan["span_rank"], plan["span_local"], plan["rank_off"]
+    assert ss[0] == 0 and ss[-1] == T and np.all(np.diff(ss) > 0)
+    assert np.all(ss % b == 0), "spans must be block-aligned"
+    cap = np.array([((r + 1) * N // W - r * N // W) * b for r in range(W)])
+    assert np.array_equal(np.diff(ro), cap) and ro[0] == 0, "exact balanced token capacity"
+    for s in range(sr.size):  # a span never crosses a sequence boundary
+        i = int(np.searchsorted(cu, ss[s], side="right")) - 1
+        assert ss[s + 1] <= cu[i + 1]
+    fill = np.zeros(W, dtype=np.int64)
+    for s in range(sr.size):  # slabs list their spans in packed order, back to back
+        r = int(sr[s])
+        assert sl[s] == fill[r]
+        fill[r] += ss[s + 1] - ss[s]
+    assert np.array_equal(fill, cap)
+    tok, caus = _exact_costs(plan, cu)
+    assert np.array_equal(np.array(tok), cap)
+    for r in range(W):
+        assert plan["rank_cost"][r] == float(tok[r]) * 1.0 + float(caus[r]) * 1.0
+    if plan["grid"] > 0:
+        assert np.all(np.bincount(sr, minlength=W) <= max_chunks)
+    assert plan["rank_cost"].max() <= _contiguous_max(cu, W, b) + 1e-9
+
+
+def test_golden_hand_plan(orc):
+    g = json.loads((GOLDEN / "thd_plan_small.json").read_text())
+    i, e = g["input"], g["expected"]
+    cu = synth.cu_seqlens(i["lengths"])
+    p = orc.thd_plan(cu, i["world_size"], i["block_size"], i["min_split_tokens"], i["max_chunks_per_rank"],
+                     i["token_weight"], i["causal_weight"])
+    assert p["grid"] == e["grid"]
+    for k in ("span_start", "span_rank", "span_local", "rank_off"):
+        assert p[k].tolist() == e[k], k
+    assert p["rank_cost"].tolist() == e["rank_cost"]
+
+
+@pytest.mark.parametrize("kw,W,kind", [
+    (dict(min_split_tokens=6, block_size=4), 4, "config"),     # min_split not block-aligned
+    (dict(max_chunks_per_rank=0), 4, "config"),
+    (dict(block_size=0), 4, "config"),
+    (dict(min_split_tokens=0), 4, "config"),
+    (dict(token_weight=float("nan")), 4, "config"),
+    (dict(causal_weight=-1.0), 4, "config"),
+    (dict(token_weight=0.0, causal_weight=0.0), 4, "config"),
+    (dict(), 0, "config"),
+])
+def test_rejects_invalid_config(orc, kw, W, kind):
+    args = dict(block_size=64, min_split_tokens=128)
+    args.update(kw)
+    with pytest.raises(ValueError, match=kind):
+        orc.thd_plan(synth.cu_seqlens([1 << 12]), W, **args)
+
+
+def test_rejects_misaligned_lengths_and_too_few_blocks(orc):
+    with pytest.raises(ValueError, match="lengths"):
+        orc.thd_plan(synth.cu_seqlens([128, 100]), 2, block_size=64, min_split_tokens=128)
+    with pytest.raises(ValueError, match="blocks"):
+        orc.thd_plan(synth.cu_seqlens([64, 64, 64]), 4, block_size=64, min_split_tokens=128)
+
+
+def _random_batch(seed, b):
+    rng = np.random.default_rng(seed)
+    n_short = int(rng.integers(0, 12))
+    shorts = list(rng.integers(0, 20, size=n_short))
+    longs = list(rng.integers(20, 300, size=int(rng.integers(0, 4))))
+    lens = shorts + longs
+    rng.shuffle(lens)
+    if not lens or sum(lens) == 0:
+        lens = [40]
+    return synth.cu_seqlens([int(x) * b for x in lens])
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_invariants_random_batches(orc, seed):
+    b = [1, 4, 16][seed % 3]
+    cu = _random_batch(seed, b)
+    N = int(cu[-1]) // b
+    for W in (1, 2, 3, 5, 8):
+        if N < W:
+            continue
+        p = orc.thd_plan(cu, W, block_size=b, min_split_tokens=16 * b, max_chunks_per_rank=12)
+        _check_invariants(p, cu, W, b, 16 * b, 12)
+        q = orc.thd_plan(cu, W, block_size=b, min_split_tokens=16 * b, max_chunks_per_rank=12)
+        for k in p:
+            assert np.array_equal(np.asarray(p[k]), np.asarray(q[k])), "the plan must be deterministic"
+
+
+def test_short_samples_kept_whole(orc):
+    """Shorts that fit beside the long sequences stay in one span each."""
+    b = 16
+    lens = [40 * b, 3 * b, 200 * b, 5 * b, 2 * b, 1 * b, 7 * b, 150 * b]
+    cu = synth.cu_seqlens(lens)
+    for W in (2, 3, 4, 6):
+        p = orc.thd_plan(cu, W, block_size=b, min_split_tokens=32 * b)
+        if p["grid"] == 0:
+            continue
+        for i, L in enumerate(lens):
+            if L < 32 * b:
+                inside = (p["span_start"][:-1] >= cu[i]) & (p["span_start"][:-1] < cu[i + 1])
+                assert inside.sum() == 1, (W, i)
+
+
+def test_long_sequence_snake_direction(orc):
+    """One long sequence alone, 2W equal chunks (grid 2 chosen or not, the
+    chunk -> rank map of every candidate follows the alternating snake):
+    with causal weight only, the snake pairs early and late chunks, so every
+    rank's cost is equal and the planner picks it over the contiguous cut."""
+    W, b = 4, 1
+    cu = synth.cu_seqlens([8 * W])
+    p = orc.thd_plan(cu, W, block_size=b, min_split_tokens=2, token_weight=0.0, causal_weight=1.0)
+    assert p["grid"] >= 2
+    # chunk c of 2W chunks of W blocks... the chosen grid's first 2W chunk owners
+    owners = [int(p["span_rank"][np.searchsorted(p["span_start"], t, side="right") - 1]) for t in range(0, 8 * W)]
+    rounds = [owners[c * (8 * W) // (2 * W)] for c in range(2 * W)] if p["grid"] == 2 else None
+    if rounds is not None:
+        assert rounds == [0, 1, 2, 3, 3, 2, 1, 0]
+    costs = p["rank_cost"]
+    assert costs.max() < _contiguous_max(cu, W, b, wt=0.0, wc=1.0)
+
+
+def test_brute_force_bound_tiny(orc):
+    """The plan is a valid exact-capacity assignment, so its maximum rank cost
+    is at least the optimum over all block assignments, found by brute force."""
+    for lens, W in (([3, 1, 2], 2), ([4, 2], 3), ([2, 2, 1, 1], 2), ([5, 1], 2)):
+        cu = synth.cu_seqlens(lens)
+        N = sum(lens)
+        blocks = [(i, k) for i, L in enumerate(lens) for k in range(L)]
+        cap = [(r + 1) * N // W - r * N // W for r in range(W)]
+        best = None
+        for assign in itertools.product(range(W), repeat=N):
+            if [assign.count(r) for r in range(W)] != cap:
+                continue
+            cost = [0.0] * W
+            for (i, k), r in zip(blocks, assign):
+                cost[r] += 1.0 + (k + 1)
+            m = max(cost)
+            best = m if best is None else min(best, m)
+        p = orc.thd_plan(cu, W, block_size=1, min_split_tokens=3)
+        assert p["rank_cost"].max() >= best - 1e-12
+        assert p["rank_cost"].max() <= _contiguous_max(cu, W, 1)
+
+
+# -- planned-span relayout -------------------------------------------------------
+
+def _spans_of_sequence_split(orc, cu, P):
+    """The per-sequence P-way split as a span table (piece p of each sequence
+    on rank p, local rows from the varlen plan)."""
+    rank_cu, rank_off = orc.varlen_plan(cu, P)
+    starts, ranks, local = [], [], []
+    for i in range(cu.size - 1):
+        L = int(cu[i + 1] - cu[i])
+        for p in range(P):
+            a, e = p * L // P, (p + 1) * L // P
+            if a < e:
+                starts.append(int(cu[i]) + a)
+                ranks.append(p)
+                local.append(int(rank_cu[p][i]))
+    order = np.argsort(starts, kind="stable")
+    return {"span_start": np.array([starts[k] for k in order] + [int(cu[-1])], dtype=np.int32),
+            "span_rank": np.array([ranks[k] for k in order], dtype=np.int32),
+            "span_local": np.array([local[k] for k in order], dtype=np.int32),
+            "rank_off": np.ascontiguousarray(rank_off, dtype=np.int64)}
+
+
+@pytest.mark.parametrize("P,B", [(2, 1), (4, 3), (8, 2)])
+def test_span_relayout_equals_sequence_split_relayout(orc, P, B):
+    H, D = 8, 4
+    cu = synth.cu_seqlens([5, 0, 17, 3, 40, 1])
+    T = int(cu[-1])
+    plan = _spans_of_sequence_split(orc, cu, P)
+    x = synth.iota32(B * T * H * D)
+    assert np.array_equal(orc.span_seq_to_head(x, plan, P, B, H, D), orc.varlen_seq_to_head(x, cu, P, B, H, D))
+    y = synth.iota32(B * T * H * D)
+    assert np.array_equal(orc.span_head_to_seq(y, plan, P, B, H, D), orc.varlen_head_to_seq(y, cu, P, B, H, D))
+
+
+@pytest.mark.parametrize("W,B", [(3, 1), (4, 2), (8, 3)])
+def test_span_relayout_round_trip_and_coverage(orc, W, B):
+    b, H, D = 4, W * 2, 3
+    cu = synth.cu_seqlens([4 * x for x in (3, 60, 1, 7, 90, 2)])
+    plan = orc.thd_plan(cu, W, block_size=b, min_split_tokens=32)
+    T = int(cu[-1])
+    x = synth.iota32(B * T * H * D)
+    y = orc.span_seq_to_head(x, plan, W, B, H, D)
+    assert np.array_equal(np.sort(y.reshape(-1)), x)
+    assert np.array_equal(orc.span_head_to_seq(y, plan, W, B, H, D).reshape(-1), x)
+
+
+def test_span_relayout_brute_force(orc):
+    W, B, H, D, b = 3, 2, 6, 2, 1
+    cu = synth.cu_seqlens([2, 9, 1, 4])
+    plan = orc.thd_plan(cu, W, block_size=b, min_split_tokens=4)
+    T = int(cu[-1])
+    Hp = H // W
+    x = synth.iota32(B * T * H * D).reshape(B * T, H, D)
+    y = orc.span_seq_to_head(x, plan, W, B, H, D)
+    ss, sr, sl, ro = plan["span_start"], plan["span_rank"], plan["span_local"], plan["rank_off"]
+    for t in range(T):
+        s = int(np.searchsorted(ss, t, side="right")) - 1
+        p = int(sr[s])
+        l = int(sl[s]) + t - int(ss[s])
+        Tp = int(ro[p + 1] - ro[p])
+        for bb in range(B):
+            row = B * int(ro[p]) + bb * Tp + l
+            for r in range(W):
+                assert np.array_equal(y[r, bb, t], x[row, r * Hp:(r + 1) * Hp])
