@@ -793,12 +793,20 @@ void orc_lse_combine_backward(const void* part_out, int64_t po_sp, int64_t po_st
  *      W - 1 - psi (a snake whose direction alternates per round and per
  *      long sequence), capacity notwithstanding;
  *   C1. while a rank is over capacity (only long chunks overfill): the
- *      lowest such rank o gives the last
- *      x blocks of its long-sequence span that ends at the highest block
- *      position (ties: later sequence) to the cheapest rank u with room
- *      (ties: lowest), x = min(excess of o, room of u, span length);
+ *      lowest such rank o moves x = min(excess of o, room of u, span length)
+ *      blocks to the cheapest rank u with room (ties: lowest): either the
+ *      last blocks of its long-sequence span ending highest (ties: later
+ *      sequence) or the first blocks of its long-sequence span starting
+ *      lowest (ties: earlier sequence), whichever leaves the larger of the
+ *      two ranks' costs smaller (ties: the last blocks);
  *   C2. each waiting short, in B's order, is laid into the cheapest ranks
  *      with room, in order, as far as their room allows;
+ *   D. up to 4W exchanges between the costliest and the cheapest rank (ties:
+ *      lowest): the costliest gives the last x blocks of its long-sequence
+ *      span ending highest, the cheapest gives the first x blocks of its
+ *      long-sequence span starting lowest (token counts stay exact), x chosen
+ *      to minimise the larger of the two costs (ties: smallest x); stop when
+ *      no exchange lowers it;
  *   then spans of one sequence that meet on one rank are merged, and a
  *   candidate with more than max_chunks_per_rank spans on a rank is dropped.
  *  The plan is the candidate with the least maximum rank cost, ties to fewer
@@ -1013,9 +1021,74 @@ static void plan_candidate(int g, const int64_t* nb, int64_t nseq, int64_t W, in
                 a += k;
             }
         }
+        /* D: exchanges between the costliest and the cheapest rank (ties:
+         * lowest rank), at most 4W: the costliest gives the last x blocks of
+         * its long span ending highest, the cheapest the first x blocks of its
+         * long span starting lowest (token counts unchanged); x minimises the
+         * larger of their two costs; stop when no exchange lowers it */
+        for (int64_t round = 0; round < 4 * W; ++round) {
+            int64_t hi = 0, lo = 0;
+            for (int64_t r = 1; r < W; ++r) {
+                if (rank_cost_of(&L, r) > rank_cost_of(&L, hi))
+                    hi = r;
+                if (rank_cost_of(&L, r) < rank_cost_of(&L, lo))
+                    lo = r;
+            }
+            if (hi == lo)
+                break;
+            int64_t dh = -1, dl = -1;
+            for (int64_t k = 0; k < out->n; ++k) {
+                const orc_span* s = &out->s[k];
+                if (s->a >= s->e || !(nb[s->seq] * b >= min_split && nb[s->seq] >= 2))
+                    continue;
+                if (s->rank == hi &&
+                    (dh < 0 || s->e > out->s[dh].e || (s->e == out->s[dh].e && s->seq > out->s[dh].seq)))
+                    dh = k;
+                if (s->rank == lo &&
+                    (dl < 0 || s->a < out->s[dl].a || (s->a == out->s[dl].a && s->seq < out->s[dl].seq)))
+                    dl = k;
+            }
+            if (dh < 0 || dl < 0)
+                break;
+            const double c_hi = rank_cost_of(&L, hi), c_lo = rank_cost_of(&L, lo);
+            double now = c_hi > c_lo ? c_hi : c_lo;
+            int64_t eh = out->s[dh].e, al = out->s[dl].a;
+            int64_t xmax = out->s[dh].e - out->s[dh].a;
+            if (out->s[dl].e - out->s[dl].a < xmax)
+                xmax = out->s[dl].e - out->s[dl].a;
+            int64_t best_x = 0;
+            double best = now;
+            for (int64_t x = 1; x <= xmax; ++x) {
+                loads_add(&L, hi, eh - x, eh, -1);
+                loads_add(&L, lo, eh - x, eh, +1);
+                loads_add(&L, lo, al, al + x, -1);
+                loads_add(&L, hi, al, al + x, +1);
+                double a1 = rank_cost_of(&L, hi), a2 = rank_cost_of(&L, lo);
+                double m = a1 > a2 ? a1 : a2;
+                loads_add(&L, hi, al, al + x, -1);
+                loads_add(&L, lo, al, al + x, +1);
+                loads_add(&L, lo, eh - x, eh, -1);
+                loads_add(&L, hi, eh - x, eh, +1);
+                if (m < best) {
+                    best = m;
+                    best_x = x;
+                }
+            }
+            if (best_x == 0)
+                break;
+            int64_t sh = out->s[dh].seq, sl = out->s[dl].seq;
+            out->s[dh].e = eh - best_x;
+            out->s[dl].a = al + best_x;
+            loads_add(&L, hi, eh - best_x, eh, -1);
+            loads_add(&L, lo, al, al + best_x, -1);
+            spans_add(out, sh, eh - best_x, eh, lo);
+            loads_add(&L, lo, eh - best_x, eh, +1);
+            spans_add(out, sl, al, al + best_x, hi);
+            loads_add(&L, hi, al, al + best_x, +1);
+        }
         free(order);
         free(aside);
-        /* drop spans emptied by C1 */
+        /* drop spans emptied by C1 and D */
         int64_t m = 0;
         for (int64_t k = 0; k < out->n; ++k)
             if (out->s[k].a < out->s[k].e)

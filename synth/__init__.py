@@ -137,15 +137,19 @@ def dcp_partials(P, T, H, Dv, seed, dtype="bf16", corrupt_frac=0.01, device="cpu
 # -- packed THD (varlen) workload ---------------------------------------------
 
 def thd_lengths(n_short: int, total: int, seed: int, lo: int = 512, hi: int = 4096,
-                n_long: int = 2) -> np.ndarray:
+                n_long: int = 2, align: int = 1) -> np.ndarray:
     """n_short lengths ~U{lo..hi} plus n_long long sequences that fill `total`
     tokens (the remainder split as evenly as integers allow), in a seeded
-    random order."""
+    random order.  With align > 1 every length is a multiple of it (short
+    lengths rounded down, at least align; total must be a multiple)."""
     rng = np.random.default_rng(seed)
     short = rng.integers(lo, hi + 1, size=n_short).astype(np.int64)
-    rem = total - int(short.sum())
+    if align > 1:
+        assert total % align == 0
+        short = np.maximum(short // align * align, align)
+    rem = (total - int(short.sum())) // align
     assert rem >= n_long, "total too small for the short sequences"
-    longs = [rem // n_long + (1 if i < rem % n_long else 0) for i in range(n_long)]
+    longs = [align * (rem // n_long + (1 if i < rem % n_long else 0)) for i in range(n_long)]
     lens = np.concatenate([short, np.array(sorted(longs), dtype=np.int64)])
     rng.shuffle(lens)
     return lens
