@@ -987,25 +987,53 @@ static void plan_candidate(int g, const int64_t* nb, int64_t nseq, int64_t W, in
                     o = r;
             if (o < 0)
                 break;
-            int64_t d = -1;
+            /* two candidate moves: the last blocks of o's long span that ends
+             * highest (ties: later sequence), or the first blocks of its long
+             * span that starts lowest (ties: earlier sequence) */
+            int64_t dh = -1, dl = -1;
             for (int64_t k = 0; k < out->n; ++k) {
                 const orc_span* s = &out->s[k];
                 if (s->rank != o || s->a >= s->e || !(nb[s->seq] * b >= min_split && nb[s->seq] >= 2))
                     continue;
-                if (d < 0 || s->e > out->s[d].e || (s->e == out->s[d].e && s->seq > out->s[d].seq))
-                    d = k;
+                if (dh < 0 || s->e > out->s[dh].e || (s->e == out->s[dh].e && s->seq > out->s[dh].seq))
+                    dh = k;
+                if (dl < 0 || s->a < out->s[dl].a || (s->a == out->s[dl].a && s->seq < out->s[dl].seq))
+                    dl = k;
             }
             int64_t u = cheapest_with_room(&L, 1);
             int64_t x = blk[o] - capb[o];
             if (capb[u] - blk[u] < x)
                 x = capb[u] - blk[u];
-            if (out->s[d].e - out->s[d].a < x)
-                x = out->s[d].e - out->s[d].a;
-            int64_t seq = out->s[d].seq, e = out->s[d].e;
-            out->s[d].e = e - x;
-            loads_add(&L, o, e - x, e, -1);
-            spans_add(out, seq, e - x, e, u);
-            loads_add(&L, u, e - x, e, +1);
+            int64_t xh = out->s[dh].e - out->s[dh].a < x ? out->s[dh].e - out->s[dh].a : x;
+            int64_t xl = out->s[dl].e - out->s[dl].a < x ? out->s[dl].e - out->s[dl].a : x;
+            /* the larger of o's and u's costs after each move */
+            int64_t eh = out->s[dh].e, al = out->s[dl].a;
+            loads_add(&L, o, eh - xh, eh, -1);
+            loads_add(&L, u, eh - xh, eh, +1);
+            double co = rank_cost_of(&L, o), cu = rank_cost_of(&L, u);
+            double mh = co > cu ? co : cu;
+            loads_add(&L, u, eh - xh, eh, -1);
+            loads_add(&L, o, eh - xh, eh, +1);
+            loads_add(&L, o, al, al + xl, -1);
+            loads_add(&L, u, al, al + xl, +1);
+            co = rank_cost_of(&L, o);
+            cu = rank_cost_of(&L, u);
+            double ml = co > cu ? co : cu;
+            loads_add(&L, u, al, al + xl, -1);
+            loads_add(&L, o, al, al + xl, +1);
+            if (ml < mh) {
+                int64_t seq = out->s[dl].seq;
+                out->s[dl].a = al + xl;
+                loads_add(&L, o, al, al + xl, -1);
+                spans_add(out, seq, al, al + xl, u);
+                loads_add(&L, u, al, al + xl, +1);
+            } else {
+                int64_t seq = out->s[dh].seq;
+                out->s[dh].e = eh - xh;
+                loads_add(&L, o, eh - xh, eh, -1);
+                spans_add(out, seq, eh - xh, eh, u);
+                loads_add(&L, u, eh - xh, eh, +1);
+            }
         }
         /* C2: shorts that fit nowhere whole */
         for (int64_t x = 0; x < na; ++x) {
