@@ -24,6 +24,7 @@ __all__ = [
     "CamError", "library", "abi_version",
     "ulysses_seq_to_head", "ulysses_head_to_seq",
     "VarlenPlan", "ulysses_varlen_plan", "ulysses_seq_to_head_varlen", "ulysses_head_to_seq_varlen",
+    "ThdPlannerConfig", "ThdPlan", "thd_plan", "ulysses_seq_to_head_spans", "ulysses_head_to_seq_spans",
     "lse_pack_bytes", "lse_pack", "lse_combine_packed", "lse_combine", "lse_combine_varlen",
     "lse_combine_packed_seq", "lse_combine_varlen_seq", "lse_merge", "lse_combine_backward",
     "copy", "last_launch",
@@ -67,6 +68,11 @@ _SIGNATURES = {
     "lse_combine_varlen": (_int, [_vp, _i64, _i64, _i64, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _i64,
                                   _int, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _vp]),
     "cam_copy": (_int, [_vp, _vp, _i64, _vp]),
+    "thd_plan": (_int, [_vp, _i64, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "ulysses_seq_to_head_spans": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64,
+                                         _int, _vp]),
+    "ulysses_head_to_seq_spans": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64,
+                                         _int, _vp]),
     "lse_combine_backward": (_int, [_vp, _i64, _i64, _i64, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _i64,
                                     _int, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _i64,
                                     _vp, _i64, _i64, _i64, _vp]),
@@ -249,6 +255,165 @@ def ulysses_head_to_seq_varlen(x: torch.Tensor, plan: VarlenPlan, out: torch.Ten
     _check(library().ulysses_head_to_seq_varlen(
         x.data_ptr(), out.data_ptr(), plan.cu.data_ptr(), plan.rank_cu.data_ptr(), plan.rank_off.data_ptr(),
         plan.nseq, T, P, B, H, D, _dt(x, True), _stream(x)))
+    return out
+
+
+# ---------------------------------------------------------------------------
+# THD layout planner and planned relayout
+# ---------------------------------------------------------------------------
+
+class _PlannerConfig(C.Structure):
+    _fields_ = [("block_size", C.c_int64), ("min_split_tokens", C.c_int64), ("max_chunks_per_rank", C.c_int64),
+                ("token_weight", C.c_double), ("causal_weight", C.c_double), ("mode", C.c_int64)]
+
+
+@dataclass
+class ThdPlannerConfig:
+    """Planner inputs (cuLA THD planner): block size, the length below which a
+    sample is short (kept whole), the span limit per rank, the cost weights of
+    a token at position k (token_weight + causal_weight * (k + 1)), and
+    contiguous=True for the contiguous block-balanced layout only."""
+    block_size: int = 64
+    min_split_tokens: int = 8192
+    max_chunks_per_rank: int = 64
+    token_weight: float = 1.0
+    causal_weight: float = 1.0
+    contiguous: bool = False
+
+    def _c(self) -> _PlannerConfig:
+        for name in ("block_size", "min_split_tokens", "max_chunks_per_rank"):
+            v = getattr(self, name)
+            if isinstance(v, bool) or not isinstance(v, (int, np.integer)):
+                raise TypeError(f"{name} must be an integer")
+        for name in ("token_weight", "causal_weight"):
+            v = getattr(self, name)
+            if isinstance(v, bool) or not isinstance(v, (int, float, np.floating, np.integer)):
+                raise TypeError(f"{name} must be a number")
+        return _PlannerConfig(int(self.block_size), int(self.min_split_tokens), int(self.max_chunks_per_rank),
+                              float(self.token_weight), float(self.causal_weight), 1 if self.contiguous else 0)
+
+
+@dataclass
+class ThdPlan:
+    """A THD layout plan: host tables, their device copies, per-rank costs and
+    the chosen candidate (0 = contiguous layout, g >= 1 = grid g)."""
+    world_size: int
+    total_tokens: int
+    cu_host: np.ndarray
+    span_start_host: np.ndarray  # int32 [n+1]
+    span_rank_host: np.ndarray   # int32 [n]
+    span_local_host: np.ndarray  # int32 [n]
+    rank_off_host: np.ndarray    # int64 [W+1]
+    rank_cost: np.ndarray        # float64 [W]
+    grid: int
+    span_start: torch.Tensor | None = None
+    span_rank: torch.Tensor | None = None
+    span_local: torch.Tensor | None = None
+    rank_off: torch.Tensor | None = None
+
+    @property
+    def n_spans(self) -> int:
+        return int(self.span_rank_host.size)
+
+    def tokens_on_rank(self, r: int) -> int:
+        return int(self.rank_off_host[r + 1] - self.rank_off_host[r])
+
+    def for_rank(self, r: int) -> list[tuple[int, int, int]]:
+        """Rank r's spans in slab order as (sequence, start in the sequence, length)."""
+        if not 0 <= r < self.world_size:
+            raise ValueError(f"rank must be in [0, {self.world_size})")
+        out = []
+        for s in np.nonzero(self.span_rank_host == r)[0]:
+            a, e = int(self.span_start_host[s]), int(self.span_start_host[s + 1])
+            i = int(np.searchsorted(self.cu_host, a, side="right")) - 1
+            out.append((i, a - int(self.cu_host[i]), e - a))
+        return out
+
+    def to(self, device) -> "ThdPlan":
+        dev = torch.device(device)
+        self.span_start = torch.from_numpy(self.span_start_host).to(dev)
+        self.span_rank = torch.from_numpy(self.span_rank_host).to(dev)
+        self.span_local = torch.from_numpy(self.span_local_host).to(dev)
+        self.rank_off = torch.from_numpy(self.rank_off_host).to(dev)
+        return self
+
+
+def thd_plan(cu_seqlens, world_size: int, config: ThdPlannerConfig | None = None, device=None) -> ThdPlan:
+    """Plan a packed THD batch over world_size ranks on the host (libcam);
+    with device given, the tables are also uploaded there."""
+    if isinstance(world_size, bool) or not isinstance(world_size, (int, np.integer)):
+        raise TypeError("world_size must be an integer")
+    cfg = (config or ThdPlannerConfig())._c()
+    cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int32))
+    nseq = cu.size - 1
+    if nseq < 0:
+        raise ValueError("cu_seqlens must have at least one entry")
+    W = int(world_size)
+    n = C.c_int64(0)
+    grid = C.c_int32(0)
+    lib = library()
+    cap = 4 * (nseq + max(W, 1)) + 16
+    for _ in range(2):
+        ss = np.empty(cap + 1, dtype=np.int32)
+        sr = np.empty(cap, dtype=np.int32)
+        sl = np.empty(cap, dtype=np.int32)
+        ro = np.empty(max(W, 0) + 1, dtype=np.int64)
+        rc = np.empty(max(W, 1), dtype=np.float64)
+        st = lib.thd_plan(cu.ctypes.data, nseq, W, C.addressof(cfg), cap, ss.ctypes.data, sr.ctypes.data,
+                          sl.ctypes.data, ro.ctypes.data, rc.ctypes.data, C.addressof(n), C.addressof(grid))
+        if st != 0 and n.value > cap:
+            cap = n.value
+            continue
+        _check(st)
+        break
+    k = n.value
+    plan = ThdPlan(W, int(cu[-1]), cu, ss[:k + 1].copy(), sr[:k].copy(), sl[:k].copy(), ro.copy(), rc[:W].copy(),
+                   int(grid.value))
+    return plan.to(device) if device is not None else plan
+
+
+def _spans_common(x: torch.Tensor, plan: ThdPlan):
+    _contig(x, "x")
+    if plan.span_start is None:
+        raise ValueError("the plan's tables are not on the device (thd_plan(..., device=...) or plan.to(device))")
+    return plan.total_tokens, plan.world_size
+
+
+def ulysses_seq_to_head_spans(x: torch.Tensor, plan: ThdPlan, B: int = 1,
+                              out: torch.Tensor | None = None) -> torch.Tensor:
+    """Planned rank-major slabs [B*T][H][D] -> [P][B][T][H/P][D]."""
+    T, P = _spans_common(x, plan)
+    if x.dim() != 3 or x.shape[0] != B * T:
+        raise ValueError("x must be [B*T][H][D]")
+    H, D = x.shape[1], x.shape[2]
+    if out is None:
+        out = torch.empty((P, B, T, H // P, D), dtype=x.dtype, device=x.device)
+    _contig(out, "out")
+    if out.numel() != x.numel() or out.dtype != x.dtype:
+        raise ValueError("out must match x in size and dtype")
+    _check(library().ulysses_seq_to_head_spans(
+        x.data_ptr(), out.data_ptr(), plan.span_start.data_ptr(), plan.span_rank.data_ptr(),
+        plan.span_local.data_ptr(), plan.rank_off.data_ptr(), plan.n_spans, T, P, B, H, D, _dt(x, True),
+        _stream(x)))
+    return out
+
+
+def ulysses_head_to_seq_spans(x: torch.Tensor, plan: ThdPlan, out: torch.Tensor | None = None) -> torch.Tensor:
+    """[P][B][T][H/P][D] -> planned rank-major slabs [B*T][H][D]."""
+    T, P = _spans_common(x, plan)
+    if x.dim() != 5 or x.shape[0] != P or x.shape[2] != T:
+        raise ValueError("x must be [P][B][T][H/P][D]")
+    B, D = x.shape[1], x.shape[4]
+    H = x.shape[3] * P
+    if out is None:
+        out = torch.empty((B * T, H, D), dtype=x.dtype, device=x.device)
+    _contig(out, "out")
+    if out.numel() != x.numel() or out.dtype != x.dtype:
+        raise ValueError("out must match x in size and dtype")
+    _check(library().ulysses_head_to_seq_spans(
+        x.data_ptr(), out.data_ptr(), plan.span_start.data_ptr(), plan.span_rank.data_ptr(),
+        plan.span_local.data_ptr(), plan.rank_off.data_ptr(), plan.n_spans, T, P, B, H, D, _dt(x, True),
+        _stream(x)))
     return out
 
 

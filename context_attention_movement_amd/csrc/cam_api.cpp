@@ -204,11 +204,17 @@ cam_status dense_relayout(const void* in, void* out, int64_t P, int64_t B, int64
     return launch_dense_relayout(a, stream);
 }
 
+// The per-sequence split (rank_cu, rank_off from ulysses_varlen_plan), or with
+// span_rank non-null a THD layout plan: cu = span starts, nseq = span count,
+// span_rank / span_local / rank_off from thd_plan.
 cam_status varlen_relayout(const void* in, void* out, const int32_t* cu, const int32_t* rank_cu,
                            const int64_t* rank_off, int64_t nseq, int64_t T, int64_t P, int64_t B,
-                           int64_t H, int64_t D, cam_dtype dt, void* stream, bool seq_to_head)
+                           int64_t H, int64_t D, cam_dtype dt, void* stream, bool seq_to_head,
+                           const int32_t* span_rank = nullptr, const int32_t* span_local = nullptr)
 {
-    const char* op = seq_to_head ? "ulysses_seq_to_head_varlen" : "ulysses_head_to_seq_varlen";
+    const bool spans = span_rank != nullptr || span_local != nullptr;
+    const char* op = spans ? (seq_to_head ? "ulysses_seq_to_head_spans" : "ulysses_head_to_seq_spans")
+                           : (seq_to_head ? "ulysses_seq_to_head_varlen" : "ulysses_head_to_seq_varlen");
     clear_error();
     if (P < 1 || B < 0 || T < 0 || H < 0 || D < 0 || nseq < 0)
         return set_error(CAM_ERR_SHAPE, "%s: need P >= 1 and nseq, total_tokens, B, H, D >= 0", op);
@@ -227,15 +233,30 @@ cam_status varlen_relayout(const void* in, void* out, const int32_t* cu, const i
         return set_error(CAM_ERR_SHAPE, "%s: B*T*H*D*esize overflows", op);
     if (bytes == 0)
         return CAM_OK;
-    if (!in || !out || !cu || !rank_cu || !rank_off)
-        return set_error(CAM_ERR_NULL, "%s: in, out, cu_seqlens, rank_cu and rank_off must be non-null", op);
-    if (!aligned(in, es) || !aligned(out, es) || !aligned(cu, 4) || !aligned(rank_cu, 4) || !aligned(rank_off, 8))
-        return set_error(CAM_ERR_ALIGNMENT, "%s: misaligned pointer", op);
-    if (overlaps(in, bytes, out, bytes))
-        return set_error(CAM_ERR_OVERLAP, "%s: in and out overlap", op);
-    if (overlaps(out, bytes, cu, 4 * (nseq + 1)) || overlaps(out, bytes, rank_cu, 4 * P * (nseq + 1)) ||
-        overlaps(out, bytes, rank_off, 8 * (P + 1)))
-        return set_error(CAM_ERR_OVERLAP, "%s: out overlaps the plan arrays", op);
+    if (spans) {
+        if (!in || !out || !cu || !span_rank || !span_local || !rank_off)
+            return set_error(CAM_ERR_NULL, "%s: in, out, span_start, span_rank, span_local and rank_off must be "
+                                           "non-null", op);
+        if (!aligned(in, es) || !aligned(out, es) || !aligned(cu, 4) || !aligned(span_rank, 4) ||
+            !aligned(span_local, 4) || !aligned(rank_off, 8))
+            return set_error(CAM_ERR_ALIGNMENT, "%s: misaligned pointer", op);
+        if (overlaps(in, bytes, out, bytes))
+            return set_error(CAM_ERR_OVERLAP, "%s: in and out overlap", op);
+        if (overlaps(out, bytes, cu, 4 * (nseq + 1)) || overlaps(out, bytes, span_rank, 4 * nseq) ||
+            overlaps(out, bytes, span_local, 4 * nseq) || overlaps(out, bytes, rank_off, 8 * (P + 1)))
+            return set_error(CAM_ERR_OVERLAP, "%s: out overlaps the plan arrays", op);
+    } else {
+        if (!in || !out || !cu || !rank_cu || !rank_off)
+            return set_error(CAM_ERR_NULL, "%s: in, out, cu_seqlens, rank_cu and rank_off must be non-null", op);
+        if (!aligned(in, es) || !aligned(out, es) || !aligned(cu, 4) || !aligned(rank_cu, 4) ||
+            !aligned(rank_off, 8))
+            return set_error(CAM_ERR_ALIGNMENT, "%s: misaligned pointer", op);
+        if (overlaps(in, bytes, out, bytes))
+            return set_error(CAM_ERR_OVERLAP, "%s: in and out overlap", op);
+        if (overlaps(out, bytes, cu, 4 * (nseq + 1)) || overlaps(out, bytes, rank_cu, 4 * P * (nseq + 1)) ||
+            overlaps(out, bytes, rank_off, 8 * (P + 1)))
+            return set_error(CAM_ERR_OVERLAP, "%s: out overlaps the plan arrays", op);
+    }
     if (P > UINT32_MAX || B > UINT32_MAX)
         return set_error(CAM_ERR_UNSUPPORTED, "%s: P and B must fit 32 bits", op);
 
@@ -247,6 +268,9 @@ cam_status varlen_relayout(const void* in, void* out, const int32_t* cu, const i
     a.cu = cu;
     a.rank_cu = rank_cu;
     a.rank_off = rank_off;
+    a.span_rank = span_rank;
+    a.span_local = span_local;
+    a.spans = spans;
     a.nseq = int32_t(nseq);
     a.P = uint32_t(P);
     a.B = uint32_t(B);
@@ -575,6 +599,28 @@ cam_status ulysses_head_to_seq(const void* in, void* out, int64_t P, int64_t B, 
                                int64_t D, cam_dtype dt, void* stream)
 {
     return dense_relayout(in, out, P, B, S, H, D, dt, stream, false);
+}
+
+cam_status ulysses_seq_to_head_spans(const void* in, void* out, const int32_t* span_start, const int32_t* span_rank,
+                                     const int32_t* span_local, const int64_t* rank_off, int64_t n_spans,
+                                     int64_t total_tokens, int64_t P, int64_t B, int64_t H, int64_t D, cam_dtype dt,
+                                     void* stream)
+{
+    if (total_tokens > 0 && (!span_rank || !span_local))
+        return set_error(CAM_ERR_NULL, "ulysses_seq_to_head_spans: span_rank and span_local must be non-null");
+    return varlen_relayout(in, out, span_start, nullptr, rank_off, n_spans, total_tokens, P, B, H, D, dt, stream,
+                           true, span_rank, span_local);
+}
+
+cam_status ulysses_head_to_seq_spans(const void* in, void* out, const int32_t* span_start, const int32_t* span_rank,
+                                     const int32_t* span_local, const int64_t* rank_off, int64_t n_spans,
+                                     int64_t total_tokens, int64_t P, int64_t B, int64_t H, int64_t D, cam_dtype dt,
+                                     void* stream)
+{
+    if (total_tokens > 0 && (!span_rank || !span_local))
+        return set_error(CAM_ERR_NULL, "ulysses_head_to_seq_spans: span_rank and span_local must be non-null");
+    return varlen_relayout(in, out, span_start, nullptr, rank_off, n_spans, total_tokens, P, B, H, D, dt, stream,
+                           false, span_rank, span_local);
 }
 
 cam_status ulysses_varlen_plan(const int32_t* cu, int64_t nseq, int64_t P, int32_t* rank_cu,

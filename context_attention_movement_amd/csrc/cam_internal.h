@@ -66,12 +66,19 @@ struct DenseRelayout {
 // Varlen relayout.  A plane is (r, b); the head side of plane (r, b) is rows
 // t < T of c vectors each, contiguous at vector (r*B + b)*T*c.  Token t's
 // sequence-side row is found per tile from cu_seqlens and the plan.
+// With spans set, cu holds the planned spans' first tokens (nseq = number of
+// spans, cu[nseq] = T) and token t of span s is row span_local[s] + t - cu[s]
+// of rank span_rank[s]'s slab (a THD layout plan) instead of a piece of the
+// per-sequence split.
 struct VarlenRelayout {
     const void* src;
     void* dst;
     const int32_t* cu;
     const int32_t* rank_cu;
     const int64_t* rank_off;
+    const int32_t* span_rank;
+    const int32_t* span_local;
+    bool spans;
     int32_t nseq;
     uint32_t P, B;
     FastDiv div_P, div_B;
@@ -267,15 +274,19 @@ constexpr int kTileVecs = kThreads * kVecsPerThread;
 #define CAM_NT_COPY 3
 #endif
 #ifndef CAM_NT_COMBINE_BWD
-#define CAM_NT_COMBINE_BWD 3
+#define CAM_NT_COMBINE_BWD 2
 #endif
 // Combine gradient tiling: rows per tile for rows of >= 512 bytes and shorter.
 #ifndef CAM_COMBINE_BWD_ROWS_WIDE
 #define CAM_COMBINE_BWD_ROWS_WIDE 8
 #endif
 #ifndef CAM_COMBINE_BWD_ROWS_NARROW
-#define CAM_COMBINE_BWD_ROWS_NARROW 32
+#define CAM_COMBINE_BWD_ROWS_NARROW 16
 #endif
+#ifndef CAM_COMBINE_BWD_BATCH
+#define CAM_COMBINE_BWD_BATCH 4
+#endif
+constexpr int kCombineBwdBatch = CAM_COMBINE_BWD_BATCH;
 // Combine tiling (measured on MI355X): rows per workgroup tile for rows of
 // >= 512 bytes and for shorter rows, and partial rows loaded per batch.
 #ifndef CAM_COMBINE_ROWS_WIDE

@@ -486,7 +486,7 @@ __global__ __launch_bounds__(kThreads) void k_combine_bwd(CombineBwd a)
 {
     typedef typename VecOf<W>::type V;
     constexpr int E = W / 2;
-    constexpr int CH = kCombineBatch;
+    constexpr int CH = kCombineBwdBatch;
     constexpr bool NTL = (CAM_NT_COMBINE_BWD & 1) != 0, NTS = (CAM_NT_COMBINE_BWD & 2) != 0;
     extern __shared__ float smem[];
     const uint32_t RB = a.rows_per_tile;

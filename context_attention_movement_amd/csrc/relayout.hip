@@ -97,6 +97,36 @@ __device__ __forceinline__ int64_t varlen_seq_row(const VarlenRelayout& a, const
     return row * int64_t(a.Pc) + int64_t(r) * a.c;
 }
 
+// The same for a THD layout plan: cu holds the spans' first tokens.
+__device__ __forceinline__ int64_t span_seq_row(const VarlenRelayout& a, const int32_t* cu, uint32_t t,
+                                                uint32_t r, uint32_t b)
+{
+    const int32_t s = seq_of_token(cu, a.nseq, t);
+    const int64_t c0 = cu[s];
+    const int64_t k = int64_t(t) - c0;
+    if (k < 0 || k >= int64_t(cu[s + 1]) - c0)
+        return -1;
+    const uint32_t p = uint32_t(a.span_rank[s]);
+    if (p >= a.P)
+        return -1;
+    const int64_t l = int64_t(a.span_local[s]) + k;
+    const int64_t R = a.rank_off[p];
+    const int64_t Tp = a.rank_off[p + 1] - R;
+    if (l < 0 || l >= Tp)
+        return -1;
+    const int64_t row = int64_t(a.B) * R + int64_t(b) * Tp + l;
+    if (row < 0 || row >= int64_t(a.B) * int64_t(a.T))
+        return -1;
+    return row * int64_t(a.Pc) + int64_t(r) * a.c;
+}
+
+template <bool SPANS>
+__device__ __forceinline__ int64_t seq_row(const VarlenRelayout& a, const int32_t* cu, uint32_t t, uint32_t r,
+                                           uint32_t b)
+{
+    return SPANS ? span_seq_row(a, cu, t, r, b) : varlen_seq_row(a, cu, t, r, b);
+}
+
 template <int W, bool S2H, bool GUARD, int NTP>
 __device__ __forceinline__ void varlen_tile(const VarlenRelayout& a, const int64_t* row_off, uint64_t head_base,
                                             uint32_t vb, uint32_t ve, uint32_t row0)
@@ -129,7 +159,7 @@ __device__ __forceinline__ void varlen_tile(const VarlenRelayout& a, const int64
             st<W, (NTP & 2) != 0>(a.dst, dst_off[u], x[u]);
 }
 
-template <int W, bool S2H>
+template <int W, bool S2H, bool SPANS>
 __global__ __launch_bounds__(kThreads) void k_varlen_relayout(VarlenRelayout a)
 {
     // sequence-side offset of every row the tile touches (a tile spans at most
@@ -157,8 +187,8 @@ __global__ __launch_bounds__(kThreads) void k_varlen_relayout(VarlenRelayout a)
         for (uint32_t i = threadIdx.x; i < nrows; i += kThreads) {
             // the two calls differ only in the address space of the table,
             // so each compiles to plain LDS or global loads
-            const int64_t off = cached ? varlen_seq_row(a, cu_lds, row0 + i, r, b)
-                                       : varlen_seq_row(a, a.cu, row0 + i, r, b);
+            const int64_t off = cached ? seq_row<SPANS>(a, cu_lds, row0 + i, r, b)
+                                       : seq_row<SPANS>(a, a.cu, row0 + i, r, b);
             row_off[i] = off;
             rows_ok = rows_ok && off >= 0;
         }
@@ -220,10 +250,12 @@ cam_status launch_dense_relayout(const DenseRelayout& a, void* stream)
 cam_status launch_varlen_relayout(const VarlenRelayout& a, void* stream)
 {
     const void* fn = nullptr;
-#define CAM_PICK(Wd)                                                                        \
-    if (a.width == Wd)                                                                      \
-        fn = a.seq_to_head ? reinterpret_cast<const void*>(&k_varlen_relayout<Wd, true>)  \
-                           : reinterpret_cast<const void*>(&k_varlen_relayout<Wd, false>);
+#define CAM_PICK(Wd)                                                                                    \
+    if (a.width == Wd)                                                                                  \
+        fn = a.spans ? (a.seq_to_head ? reinterpret_cast<const void*>(&k_varlen_relayout<Wd, true, true>)  \
+                                      : reinterpret_cast<const void*>(&k_varlen_relayout<Wd, false, true>)) \
+                     : (a.seq_to_head ? reinterpret_cast<const void*>(&k_varlen_relayout<Wd, true, false>) \
+                                      : reinterpret_cast<const void*>(&k_varlen_relayout<Wd, false, false>));
     CAM_PICK(16) CAM_PICK(8) CAM_PICK(4) CAM_PICK(2)
 #undef CAM_PICK
     return launch(fn, a, a.n_tiles, stream, "varlen relayout");

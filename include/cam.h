@@ -142,6 +142,70 @@ cam_status ulysses_head_to_seq_varlen(const void* in, void* out, const int32_t* 
                                       int64_t H, int64_t D, cam_dtype dt, void* stream);
 
 /* ------------------------------------------------------------------------- */
+/* THD layout planner and planned relayout  ([CU] "THD layout planner": token  */
+/* and causal work balanced over the ranks, short samples whole, alternating   */
+/* long-sequence direction, several grids with a contiguous fallback, exact    */
+/* balanced token capacity in aligned blocks, deterministic per-rank spans)    */
+/* ------------------------------------------------------------------------- */
+typedef struct cam_thd_planner_config {
+    int64_t block_size;          /* every length and min_split_tokens a multiple of it */
+    int64_t min_split_tokens;    /* shorter samples are short (kept whole when they fit) */
+    int64_t max_chunks_per_rank; /* planned candidates above it per rank are dropped */
+    double token_weight;         /* cost of a token at position k:               */
+    double causal_weight;        /*   token_weight + causal_weight * (k + 1)      */
+    int64_t mode;                /* 0: planned with contiguous fallback; 1: contiguous */
+} cam_thd_planner_config;
+
+/*
+ * thd_plan (host only, no HIP call): plan the packed batch cu_seqlens[nseq+1]
+ * over world_size ranks.  Rank r holds exactly floor((r+1)N/W) - floor(rN/W)
+ * of the N aligned blocks.  Candidates: the contiguous layout, and for
+ * g = 1..6 a grid that places the short samples whole (costliest first,
+ * cheapest rank with room), deals each long sequence's W * 2^(g-1) chunks along
+ * a snake whose direction alternates per round and per long sequence, then
+ * moves the highest-position blocks of overfull ranks to the cheapest ranks
+ * with room and lays shorts that fitted nowhere into the remaining room.  The
+ * least maximum rank cost wins (ties: fewer spans, then the lower candidate).
+ * Output, in packed token order: span_start[n+1] (first token of each span,
+ * span_start[n] = T), span_rank[n], span_local[n] (first row in the rank's
+ * slab, which lists the rank's spans in packed order), rank_off[W+1] (slab
+ * token offsets), rank_cost[W] and *chosen (0 = contiguous, else the grid).
+ * Tables are caller-owned host memory of max_spans (+1) entries; *n_spans is
+ * set even when they are too small (CAM_ERR_SHAPE, nothing else written).
+ * Errors: CAM_ERR_UNSUPPORTED (world_size < 1, non-positive sizes, weights
+ * negative, non-finite or both zero), CAM_ERR_ALIGNMENT (a length or
+ * min_split_tokens not a multiple of block_size), CAM_ERR_SHAPE (malformed
+ * cu_seqlens, fewer blocks than ranks), CAM_ERR_NULL.
+ */
+cam_status thd_plan(const int32_t* cu_seqlens, int64_t nseq, int64_t world_size,
+                    const cam_thd_planner_config* cfg, int64_t max_spans, int32_t* span_start,
+                    int32_t* span_rank, int32_t* span_local, int64_t* rank_off, double* rank_cost,
+                    int64_t* n_spans, int32_t* chosen);
+
+/*
+ * ulysses_seq_to_head_spans: the varlen relayout over a THD layout plan.  The
+ *   sequence side is rank-major: rank p's slab [B][T_p][H][D] at token row
+ *   B*rank_off[p], its rows being its spans in packed order; the head side is
+ *   [P][B][T][H/P][D] in packed token order.  Token t of span s is row
+ *   span_local[s] + t - span_start[s] of rank span_rank[s]'s slab.
+ * ulysses_head_to_seq_spans: the inverse.
+ *   span_start[n_spans+1], span_rank, span_local (int32) and rank_off[P+1]
+ *   (int64) are DEVICE copies of thd_plan's tables for world_size = P;
+ *   total_tokens = span_start[n_spans] is passed by the host.  Rows a
+ *   malformed table would place outside the buffers are skipped.  H % P == 0.
+ */
+cam_status ulysses_seq_to_head_spans(const void* in, void* out, const int32_t* span_start,
+                                     const int32_t* span_rank, const int32_t* span_local,
+                                     const int64_t* rank_off, int64_t n_spans, int64_t total_tokens,
+                                     int64_t P, int64_t B, int64_t H, int64_t D, cam_dtype dt,
+                                     void* stream);
+cam_status ulysses_head_to_seq_spans(const void* in, void* out, const int32_t* span_start,
+                                     const int32_t* span_rank, const int32_t* span_local,
+                                     const int64_t* rank_off, int64_t n_spans, int64_t total_tokens,
+                                     int64_t P, int64_t B, int64_t H, int64_t D, cam_dtype dt,
+                                     void* stream);
+
+/* ------------------------------------------------------------------------- */
 /* Max/sum-aware LSE pack  ([VA] "What this PR does": the pack forms the LSE    */
 /* while writing the packed layout, instead of materializing it first)        */
 /* ------------------------------------------------------------------------- */
