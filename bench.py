@@ -142,6 +142,16 @@ class Workload:
             ms["comb_seq"] = torch.empty((Tm, Hm, Dvm), dtype=bf, device=dev)
             ms["lse_seq"] = torch.empty((Tm, Hm), dtype=torch.float32, device=dev)
             ms["comb_h2s"] = torch.empty((Pm, 1, Tm // Pm, Hm, Dvm), dtype=bf, device=dev)
+        # THD layout plan over 8 ranks of the same 131072 tokens in 64-token
+        # blocks (the planned relayout reuses the THD Q/K/V and O buffers)
+        self.p_lens = synth.thd_lengths(20, 131072, seed=synth.BASE_SEED + 4, align=64)
+        self.p_cu = synth.cu_seqlens(self.p_lens)
+        t0 = time.perf_counter()
+        self.p_plan = cam.thd_plan(self.p_cu, self.tP, cam.ThdPlannerConfig(block_size=64, min_split_tokens=8192),
+                                   device=dev)
+        self.p_plan_ms = (time.perf_counter() - t0) * 1e3
+        self.p_contig = cam.thd_plan(self.p_cu, self.tP, cam.ThdPlannerConfig(block_size=64, min_split_tokens=8192,
+                                                                                contiguous=True))
         # training: gradient buffers of the relayout pair and of the THD combine
         P, S, H, D = self.vP, self.vS, self.vH, self.vD
         self.v_dqkv = torch.empty((P, 3, S // P, H, D), dtype=bf, device=dev)
@@ -260,7 +270,15 @@ class Workload:
         # read; every partial: its two gradients written
         bwd_bytes = self.t_admitted * H * (2 * D + 4) + rows * 2 * D + P * rows * (2 * D + 4)
 
+        def planned_s2h():
+            cam.ulysses_seq_to_head_spans(self.t_qkv, self.p_plan, 3, out=self.t_qkv_out)
+
+        def planned_h2s():
+            cam.ulysses_head_to_seq_spans(self.t_o, self.p_plan, out=self.t_o_out)
+
         return [
+            ("relayout_seq_to_head_planned_thd_qkv", 2 * 3 * T * H * D * 2, planned_s2h),
+            ("relayout_head_to_seq_planned_thd_o", 2 * T * H * D * 2, planned_h2s),
             ("lse_combine_varlen_backward_thd", bwd_bytes, thd_backward),
             ("relayout_training_pair_video_p4 (fwd + bwd)", pair_bytes, training_pair),
             ("ring_of_8_online_merges_thd (fp32 accumulator)", ring_bytes, ring),
@@ -268,6 +286,24 @@ class Workload:
             ("combine_then_head_to_seq_mla (unfused)", comb_bytes + 2 * out_bytes, unfused),
             ("combine_varlen_to_sequence_shards_thd (fused)", self.op_bytes()["lse_combine_varlen_thd"], thd_fused),
         ]
+
+
+def plan_summary(w):
+    """Balance of the THD layout plan used by the planned relayouts: maximum
+    over mean rank cost for the plan, the contiguous layout and the
+    per-sequence split, with the planner's host time."""
+    P = w.tP
+    split = [0.0] * P
+    for L in (int(x) for x in w.p_lens):
+        for p in range(P):
+            a, e = p * L // P, (p + 1) * L // P
+            split[p] += (e - a) + (e * (e + 1) // 2 - a * (a + 1) // 2)
+    ratio = lambda c: round(float(max(c)) / (float(sum(c)) / len(c)), 4)
+    return {"ranks": P, "block_size": 64, "grid": w.p_plan.grid, "spans": w.p_plan.n_spans,
+            "max_over_mean_cost": ratio(w.p_plan.rank_cost),
+            "contiguous_max_over_mean_cost": ratio(w.p_contig.rank_cost),
+            "sequence_split_max_over_mean_cost": ratio(split), "host_ms": round(w.p_plan_ms, 3),
+            "cost": "token_weight 1 + causal_weight 1 * (k + 1) per token at position k"}
 
 
 # ---------------------------------------------------------------------------
@@ -654,6 +690,7 @@ def main():
         },
         "ops": op_table,
         "extensions": ext,
+        "thd_plan": plan_summary(w),
         "copy_ceiling": {"GBps": round(copy_gbps, 1), "frac_of_hbm_peak": round(copy_gbps / HBM_PEAK_GBPS, 4),
                          "bytes": int(copy_bytes), "kernel": "k_copy16"},
         "device": {"name": props.name, "arch": getattr(props, "gcnArchName", ""),

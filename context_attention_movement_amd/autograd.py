@@ -5,7 +5,8 @@
   and the other way round, bit for bit (FastVideo "[perf] Probe H3 chunked
   all-to-all with direct output slices", benchmark_ulysses_a2a.py: the
   forward/backward training pair, whose gradients must equal the collective's
-  exactly).  The same holds for the cu_seqlens varlen relayout.
+  exactly).  The same holds for the cu_seqlens varlen relayout and for the
+  relayout over a THD layout plan's spans.
 - The stable combine's gradient is lse_combine_backward (cuLA PR "feat
   (distributed): add packed hybrid runtime and THD planner", Validation: the
   forward and backward of context parallelism compared against a reference).
@@ -18,12 +19,13 @@ from __future__ import annotations
 
 import torch
 
-from . import (VarlenPlan, lse_combine_backward, ulysses_head_to_seq, ulysses_head_to_seq_varlen,
-               ulysses_seq_to_head, ulysses_seq_to_head_varlen)
+from . import (ThdPlan, VarlenPlan, lse_combine_backward, ulysses_head_to_seq, ulysses_head_to_seq_spans,
+               ulysses_head_to_seq_varlen, ulysses_seq_to_head, ulysses_seq_to_head_spans, ulysses_seq_to_head_varlen)
 from . import lse_combine as _lse_combine
 from . import lse_combine_varlen as _lse_combine_varlen
 
-__all__ = ["seq_to_head", "head_to_seq", "seq_to_head_varlen", "head_to_seq_varlen", "lse_combine"]
+__all__ = ["seq_to_head", "head_to_seq", "seq_to_head_varlen", "head_to_seq_varlen", "seq_to_head_spans",
+           "head_to_seq_spans", "lse_combine"]
 
 
 class _SeqToHead(torch.autograd.Function):
@@ -71,6 +73,29 @@ class _HeadToSeqVarlen(torch.autograd.Function):
         return ulysses_seq_to_head_varlen(g.contiguous(), ctx.plan, ctx.B), None
 
 
+class _SeqToHeadSpans(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, x, plan, B):
+        ctx.plan = plan
+        return ulysses_seq_to_head_spans(x.contiguous(), plan, B)
+
+    @staticmethod
+    def backward(ctx, g):
+        return ulysses_head_to_seq_spans(g.contiguous(), ctx.plan), None, None
+
+
+class _HeadToSeqSpans(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, x, plan):
+        ctx.plan = plan
+        ctx.B = x.shape[1]
+        return ulysses_head_to_seq_spans(x.contiguous(), plan)
+
+    @staticmethod
+    def backward(ctx, g):
+        return ulysses_seq_to_head_spans(g.contiguous(), ctx.plan, ctx.B), None
+
+
 class _LseCombine(torch.autograd.Function):
     @staticmethod
     def forward(ctx, part_out, part_lse, cu_seqlens):
@@ -113,6 +138,16 @@ def seq_to_head_varlen(x: torch.Tensor, plan: VarlenPlan, B: int = 1) -> torch.T
 def head_to_seq_varlen(x: torch.Tensor, plan: VarlenPlan) -> torch.Tensor:
     """Differentiable ulysses_head_to_seq_varlen: [P][B][T][H/P][D] -> rank-major [B*T][H][D]."""
     return _HeadToSeqVarlen.apply(x, plan)
+
+
+def seq_to_head_spans(x: torch.Tensor, plan: ThdPlan, B: int = 1) -> torch.Tensor:
+    """Differentiable ulysses_seq_to_head_spans: planned slabs [B*T][H][D] -> [P][B][T][H/P][D]."""
+    return _SeqToHeadSpans.apply(x, plan, B)
+
+
+def head_to_seq_spans(x: torch.Tensor, plan: ThdPlan) -> torch.Tensor:
+    """Differentiable ulysses_head_to_seq_spans: [P][B][T][H/P][D] -> planned slabs [B*T][H][D]."""
+    return _HeadToSeqSpans.apply(x, plan)
 
 
 def lse_combine(part_out: torch.Tensor, part_lse: torch.Tensor, cu_seqlens: torch.Tensor | None = None):
