@@ -203,9 +203,9 @@ class Workload:
              lambda: cam.ulysses_head_to_seq(self.v_o, self.vP, out=self.v_o_out)),
             ("lse_pack_mla", "k_pack<16>", pack),
             ("lse_combine_mla", "k_combine<16, false, false, 1, true, 0>", combine),
-            ("relayout_seq_to_head_varlen_thd_qkv", "k_varlen_relayout<16, true>",
+            ("relayout_seq_to_head_varlen_thd_qkv", "k_varlen_relayout<16, true, false>",
              lambda: cam.ulysses_seq_to_head_varlen(self.t_qkv, self.t_plan, 3, out=self.t_qkv_out)),
-            ("relayout_head_to_seq_varlen_thd_o", "k_varlen_relayout<16, false>",
+            ("relayout_head_to_seq_varlen_thd_o", "k_varlen_relayout<16, false, false>",
              lambda: cam.ulysses_head_to_seq_varlen(self.t_o, self.t_plan, out=self.t_o_out)),
             ("lse_combine_varlen_thd", "k_combine<16, false, true, 1, false, 0>",
              lambda: cam.lse_combine_varlen(self.t_part, self.t_lse, self.t_cu_dev, out=self.t_comb,

@@ -399,8 +399,9 @@ __global__ __launch_bounds__(kThreads) void k_combine(Combine a)
 // Per row: La = accumulator LSE (-inf: empty), Lb = partial LSE; the valid ones
 // (finite) are combined with weights exp(L - max); the accumulator row is
 // rewritten in fp32 and, if asked, the rounded payload too.  A group of G lanes
-// covers a row, 4 elements per lane; an invalid partial's row is never read
-// (its lane re-reads the accumulator row, a valid address, and discards it).
+// covers a row, 4 elements per lane; an empty accumulator row is not read, and
+// an invalid partial's row is never read (its lane re-reads the accumulator
+// row, a valid address, and discards it).
 template <bool FP16, bool FINAL>
 __global__ __launch_bounds__(kThreads) void k_merge(Merge a)
 {
@@ -430,7 +431,10 @@ __global__ __launch_bounds__(kThreads) void k_merge(Merge a)
                               : reinterpret_cast<const char*>(arow);
         char* frow = FINAL ? static_cast<char*>(a.fin) + int64_t(t) * a.f_st_b + int64_t(h) * a.f_sh_b : nullptr;
         for (uint32_t k = gl; k < a.cv; k += G) {
-            const f32x4 x = *reinterpret_cast<const f32x4*>(arow + 4 * k);
+            // an empty accumulator (the first hop) is not read
+            f32x4 x = {0.0f, 0.0f, 0.0f, 0.0f};
+            if (va)
+                x = *reinterpret_cast<const f32x4*>(arow + 4 * k);
             const u32x2 y = *reinterpret_cast<const u32x2*>(prow + 8 * k);
             issue_fence();
             const float b0 = FP16 ? fp16_lo(y.x) : bf16_lo(y.x), b1 = FP16 ? fp16_hi(y.x) : bf16_hi(y.x);
