@@ -202,7 +202,7 @@ class Workload:
             ("relayout_head_to_seq_video_p4_o", "k_dense_relayout<16, false>",
              lambda: cam.ulysses_head_to_seq(self.v_o, self.vP, out=self.v_o_out)),
             ("lse_pack_mla", "k_pack<16>", pack),
-            ("lse_combine_mla", "k_combine<16, false, false, 1, true, 0>", combine),
+            ("lse_combine_mla", "k_combine_stream<16, false, false, 0>", combine),
             ("relayout_seq_to_head_varlen_thd_qkv", "k_varlen_relayout<16, true, false>",
              lambda: cam.ulysses_seq_to_head_varlen(self.t_qkv, self.t_plan, 3, out=self.t_qkv_out)),
             ("relayout_head_to_seq_varlen_thd_o", "k_varlen_relayout<16, false, false>",

@@ -313,6 +313,17 @@ constexpr int kCombineBatch = CAM_COMBINE_BATCH;
 #ifndef CAM_COMBINE_BATCH_WAVE
 #define CAM_COMBINE_BATCH_WAVE 8
 #endif
+// rows of >= 64 vectors by the LDS-free row-stream kernel (1) or the tiled
+// kernel (0); its workgroup size and rows per wave
+#ifndef CAM_COMBINE_STREAM
+#define CAM_COMBINE_STREAM 1
+#endif
+#ifndef CAM_COMBINE_STREAM_THREADS
+#define CAM_COMBINE_STREAM_THREADS 64
+#endif
+#ifndef CAM_COMBINE_STREAM_ROWS
+#define CAM_COMBINE_STREAM_ROWS 1
+#endif
 constexpr int kCombineInFlightWave = CAM_COMBINE_INFLIGHT_WAVE;
 constexpr int kCombineBatchWave = CAM_COMBINE_BATCH_WAVE;
 // XCD-aware tile order per kernel (1 = each XCD takes a contiguous range of

@@ -392,6 +392,131 @@ __global__ __launch_bounds__(kThreads) void k_combine(Combine a)
     }
 }
 
+// Rows of at least 64 vectors, without LDS or barriers: every wave owns a
+// stream of rows (row = wave, wave + n_waves, ...).  A row's P statistics sit
+// in lanes 0..P-1 and are reduced across the wave; each valid partial's weight
+// is read into a scalar register; the next row's LSEs are loaded while the
+// current row's payload streams, so a row costs one memory round trip.
+__device__ __forceinline__ float wave_max(float v)
+{
+    for (int off = 32; off > 0; off >>= 1)
+        v = fmaxf(v, __shfl_xor(v, off, 64));
+    return v;
+}
+__device__ __forceinline__ float wave_sum(float v)
+{
+    for (int off = 32; off > 0; off >>= 1)
+        v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+template <bool VARLEN>
+__device__ __forceinline__ float row_stat(const Combine& a, uint64_t row, uint32_t lane)
+{
+    if (row >= a.n_rows || lane >= a.P)
+        return -__builtin_inff();
+    const uint32_t t = fdiv(uint32_t(row), a.div_H);
+    const uint32_t h = uint32_t(row) - t * a.H;
+    if (VARLEN && !causal_piece_ok(a.cu, a.nseq, a.div_P, lane, t))
+        return -__builtin_inff();
+    return a.pl[int64_t(lane) * a.pl_sp + int64_t(t) * a.pl_st + int64_t(h) * a.pl_sh];
+}
+
+template <int W, bool FP16, bool VARLEN, int OM>
+__global__ __launch_bounds__(kThreads) void k_combine_stream(Combine a)
+{
+    typedef typename VecOf<W>::type V;
+    constexpr int E = W / 2;
+    constexpr int CH = kCombineBatchWave;
+    constexpr bool NTL = (CAM_NT_COMBINE & 1) != 0, NTS = (CAM_NT_COMBINE & 2) != 0;
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t wpb = blockDim.x >> 6;
+    const uint64_t blk = a.xcd ? xcd_first(blockIdx.x, gridDim.x) : blockIdx.x;
+    const uint64_t n_waves = uint64_t(gridDim.x) * wpb;
+    uint64_t row = blk * wpb + uniform32(threadIdx.x >> 6);
+    float L_next = row_stat<VARLEN>(a, row, lane);
+    for (; row < a.n_rows; row += n_waves) {
+        const float L = L_next;
+        L_next = row_stat<VARLEN>(a, row + n_waves, lane);  // in flight during this row
+        const uint32_t t = fdiv(uint32_t(row), a.div_H);
+        const uint32_t h = uint32_t(row) - t * a.H;
+        const bool valid = __builtin_isfinite(L);
+        const float M = wave_max(valid ? L : -__builtin_inff());
+        const float w = valid ? expf(L - M) : 0.0f;
+        const float Z = wave_sum(w);
+        const uint64_t vmask = __ballot(valid);
+        const float wn = w * (vmask ? 1.0f / Z : 0.0f);
+        int64_t o_off, l_off;
+        if (OM == 0) {
+            o_off = int64_t(t) * a.o_st_b + int64_t(h) * a.o_sh_b;
+            l_off = int64_t(t) * a.lo_st + int64_t(h) * a.lo_sh;
+        } else {
+            int64_t g;
+            if (OM == 1) {
+                const uint32_t tq = fdiv(h, a.div_Hp);
+                g = int64_t(tq) * a.Hq + int64_t(t) * a.Hp + (h - tq * a.Hp);
+            } else {
+                g = varlen_token_row(a.cu, a, t) * a.H + h;
+            }
+            const bool in = g >= 0 && uint64_t(g) < a.n_rows;
+            o_off = in ? g * int64_t(a.o_row_b) : -1;
+            l_off = in ? g : -1;
+        }
+        if (lane == 0 && a.lse_out && l_off >= 0)
+            a.lse_out[l_off] = vmask ? M + logf(Z) : -__builtin_inff();
+        const bool have = o_off >= 0;
+        char* orow = static_cast<char*>(a.out) + (have ? o_off : 0);
+        const char* prow = vmask ? static_cast<const char*>(a.po) + int64_t(t) * a.po_st_b + int64_t(h) * a.po_sh_b
+                                 : orow;
+        for (uint32_t kb = 0; kb < a.cv; kb += 64) {
+            const bool kin = kb + lane < a.cv;
+            const uint32_t k = kin ? kb + lane : a.cv - 1;
+            float acc[E];
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                acc[e] = 0.0f;
+            uint64_t m = vmask;
+            int last = vmask ? __builtin_ctzll(vmask) : 0;
+            do {
+                int idx[CH];
+                float wv[CH];
+                bool tk[CH];
+#pragma unroll
+                for (int u = 0; u < CH; ++u) {
+                    const bool take = m != 0;
+                    const int p = take ? __builtin_ctzll(m) : last;
+                    m = take ? (m & (m - 1)) : m;
+                    idx[u] = p;
+                    last = p;
+                    tk[u] = take;
+                    wv[u] = __uint_as_float(uint32_t(__builtin_amdgcn_readlane(int(__float_as_uint(wn)), p)));
+                }
+                V x[CH];
+#pragma unroll
+                for (int u = 0; u < CH; ++u)
+                    x[u] = ld_at<W, NTL>(prow + int64_t(k) * W + int64_t(idx[u]) * a.po_sp_b);
+                issue_fence();
+#pragma unroll
+                for (int u = 0; u < CH; ++u) {
+                    const Halves<W> xh = __builtin_bit_cast(Halves<W>, x[u]);
+#pragma unroll
+                    for (int e = 0; e < E; ++e) {
+                        const float v = fmaf(wv[u], half_to_f32<FP16>(xh.h[e]), acc[e]);
+                        acc[e] = tk[u] ? v : acc[e];
+                    }
+                }
+            } while (m);
+            if (have && kin) {
+                Halves<W> oh;
+#pragma unroll
+                for (int e = 0; e < E; ++e)
+                    oh.h[e] = f32_to_half<FP16>(vmask ? acc[e] : 0.0f);
+                st_at<W, NTS>(orow + int64_t(k) * W, __builtin_bit_cast(V, oh));
+            }
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Online two-way merge (ring / context-parallel accumulation)
 // ---------------------------------------------------------------------------
@@ -707,6 +832,28 @@ cam_status launch_combine(const Combine& a, void* stream)
     CAM_PICK(16, kCombineInFlightWave, true) CAM_PICK(8, kCombineInFlightWave, true)
     CAM_PICK(4, kCombineInFlightWave, true) CAM_PICK(2, kCombineInFlightWave, true)
 #undef CAM_PICK
+    if (wave && CAM_COMBINE_STREAM) {
+#define CAM_PICK_STREAM(Wd)                                                                                \
+        if (a.width == Wd) {                                                                               \
+            if (a.cu)                                                                                      \
+                fn = a.out_mode == 2                                                                       \
+                         ? (a.fp16 ? reinterpret_cast<const void*>(&k_combine_stream<Wd, true, true, 2>)    \
+                                   : reinterpret_cast<const void*>(&k_combine_stream<Wd, false, true, 2>))  \
+                         : (a.fp16 ? reinterpret_cast<const void*>(&k_combine_stream<Wd, true, true, 0>)    \
+                                   : reinterpret_cast<const void*>(&k_combine_stream<Wd, false, true, 0>)); \
+            else                                                                                           \
+                fn = a.out_mode == 1                                                                       \
+                         ? (a.fp16 ? reinterpret_cast<const void*>(&k_combine_stream<Wd, true, false, 1>)   \
+                                   : reinterpret_cast<const void*>(&k_combine_stream<Wd, false, false, 1>)) \
+                         : (a.fp16 ? reinterpret_cast<const void*>(&k_combine_stream<Wd, true, false, 0>)   \
+                                   : reinterpret_cast<const void*>(&k_combine_stream<Wd, false, false, 0>)); \
+        }
+        CAM_PICK_STREAM(16) CAM_PICK_STREAM(8) CAM_PICK_STREAM(4) CAM_PICK_STREAM(2)
+#undef CAM_PICK_STREAM
+        const uint64_t waves = (a.n_rows + CAM_COMBINE_STREAM_ROWS - 1) / CAM_COMBINE_STREAM_ROWS;
+        const uint32_t wpb = CAM_COMBINE_STREAM_THREADS / 64;
+        return launch(fn, a, (waves + wpb - 1) / wpb, stream, "lse_combine", 0, CAM_COMBINE_STREAM_THREADS);
+    }
     uint64_t lds = (uint64_t(a.rows_per_tile) * a.P + 2) * 4 + uint64_t(a.rows_per_tile) * 20;
     if (a.cu && a.nseq < kCuCache)
         lds += uint64_t(a.nseq + 1) * 4;
