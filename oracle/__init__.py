@@ -79,6 +79,13 @@ def _load():
                                    vp, vp, vp]),
         "orc_span_seq_to_head": (None, [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64]),
         "orc_span_head_to_seq": (None, [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64]),
+        "orc_plan_first_positions": (None, [vp, i64, i64, vp, vp, i64, vp]),
+        "orc_plan_piece_valid": (C.c_int, [vp, i64, vp, i64, i64]),
+        "orc_lse_combine_planned": (None, [vp, i64, i64, i64, vp, i64, i64, i64, i64, i64, i64, i64, i64,
+                                           C.c_int, vp, i64, i64, vp, i64, i64, vp, vp, i64]),
+        "orc_lse_combine_planned_backward": (None, [vp, i64, i64, i64, vp, i64, i64, i64, i64, i64, i64, i64,
+                                                    i64, C.c_int, vp, i64, i64, vp, i64, i64, vp, i64, i64, i64,
+                                                    vp, i64, i64, i64, vp, vp, i64]),
         "orc_combine_row_backward_f64": (None, [vp, vp, vp, i64, i64, vp, C.c_double, vp, vp]),
         "orc_lse_combine_backward": (None, [vp, i64, i64, i64, vp, i64, i64, i64, i64, i64, i64, i64, i64,
                                             C.c_int, vp, i64, i64, vp, i64, i64, vp, i64, i64, i64,
@@ -447,4 +454,74 @@ def span_head_to_seq(x: np.ndarray, plan: dict, P: int, B: int, H: int, D: int) 
                                  _p(plan["span_local"]), _p(plan["rank_off"]), plan["span_rank"].size,
                                  P, B, H, D, x.dtype.itemsize)
     return out.reshape(B * T, H, D)
+
+
+# -- causal combine over a THD layout plan ---------------------------------------
+
+def plan_first_positions(cu, plan: dict, W: int) -> np.ndarray:
+    """[W][nseq] int32: smallest position of sequence i held by rank p (INT32_MAX if none)."""
+    cu = np.ascontiguousarray(cu, dtype=np.int32)
+    nseq = cu.size - 1
+    first = np.empty((W, nseq), dtype=np.int32)
+    _load().orc_plan_first_positions(_p(cu), nseq, W, _p(plan["span_start"]), _p(plan["span_rank"]),
+                                     plan["span_rank"].size, _p(first))
+    return first
+
+
+def plan_piece_valid(cu, first: np.ndarray, p: int, t: int) -> bool:
+    cu = np.ascontiguousarray(cu, dtype=np.int32)
+    return bool(_load().orc_plan_piece_valid(_p(cu), cu.size - 1, _p(np.ascontiguousarray(first)), p, t))
+
+
+def plan_mask(cu, first: np.ndarray, P: int) -> np.ndarray:
+    """[P][T] bool: partial p valid for token t under the planned rule."""
+    T = int(cu[-1])
+    m = np.zeros((P, T), dtype=bool)
+    for p in range(P):
+        for t in range(T):
+            m[p, t] = plan_piece_valid(cu, first, p, t)
+    return m
+
+
+def lse_combine_planned(part_out: np.ndarray, part_lse: np.ndarray, cu, first: np.ndarray, dtype: str = "bf16",
+                        t_begin: int = 0):
+    """lse_combine with the planned validity rule; views as in lse_combine."""
+    P, Tw, H, D = part_out.shape
+
+    def ptr(view):
+        return view.__array_interface__["data"][0]
+
+    po = _strides_el(part_out)
+    pl = _strides_el(part_lse)
+    cu = np.ascontiguousarray(cu, dtype=np.int32)
+    first = np.ascontiguousarray(first, dtype=np.int32)
+    out = np.empty((Tw, H, D), dtype=np.uint16)
+    lse = np.empty((Tw, H), dtype=np.float32)
+    _load().orc_lse_combine_planned(ptr(part_out), po[0], po[1], po[2], ptr(part_lse), pl[0], pl[1], pl[2],
+                                    P, t_begin, t_begin + Tw, H, D, _dt(dtype), _p(out), H * D, D, _p(lse), H, 1,
+                                    _p(cu), _p(first), cu.size - 1)
+    return out, lse
+
+
+def lse_combine_planned_backward(part_out: np.ndarray, part_lse: np.ndarray, g_out: np.ndarray,
+                                 g_lse: np.ndarray | None, cu, first: np.ndarray, dtype: str = "bf16",
+                                 t_begin: int = 0):
+    P, Tw, H, D = part_out.shape
+
+    def ptr(view):
+        return view.__array_interface__["data"][0]
+
+    po = _strides_el(part_out)
+    pl = _strides_el(part_lse)
+    go = _strides_el(g_out)
+    gl = _strides_el(g_lse) if g_lse is not None else (0, 0)
+    cu = np.ascontiguousarray(cu, dtype=np.int32)
+    first = np.ascontiguousarray(first, dtype=np.int32)
+    d_po = np.empty((P, Tw, H, D), dtype=np.uint16)
+    d_pl = np.empty((P, Tw, H), dtype=np.float32)
+    _load().orc_lse_combine_planned_backward(
+        ptr(part_out), po[0], po[1], po[2], ptr(part_lse), pl[0], pl[1], pl[2], P, t_begin, t_begin + Tw, H, D,
+        _dt(dtype), ptr(g_out), go[0], go[1], ptr(g_lse) if g_lse is not None else None, gl[0], gl[1],
+        _p(d_po), Tw * H * D, H * D, D, _p(d_pl), Tw * H, H, 1, _p(cu), _p(first), cu.size - 1)
+    return d_po, d_pl
 

@@ -1279,3 +1279,127 @@ void orc_span_head_to_seq(const void* in, void* out, const int32_t* span_start, 
 {
     span_relayout(in, out, span_start, span_rank, span_local, rank_off, n_spans, P, B, H, D, es, 0);
 }
+
+/* ------------------------------------------------------------------------ */
+/* Causal combine over a THD layout plan                                      */
+/* ------------------------------------------------------------------------ */
+/*
+ * Reading (context parallelism over a planned layout, [CU]): every rank holds
+ * the queries and the keys of its spans; partial p of token (i, k) is the
+ * causal attention of that query over the keys rank p holds of sequence i,
+ * so it sees a key, and is valid, iff rank p holds a position <= k of
+ * sequence i.  first_pos[p * nseq + i] is the smallest position of sequence i
+ * that rank p holds (INT32_MAX if none).  For the per-sequence split this is
+ * the piece rule of orc_causal_piece_valid.
+ */
+void orc_plan_first_positions(const int32_t* cu, int64_t nseq, int64_t W, const int32_t* span_start,
+                              const int32_t* span_rank, int64_t n_spans, int32_t* first_pos)
+{
+    for (int64_t k = 0; k < W * nseq; ++k)
+        first_pos[k] = INT32_MAX;
+    for (int64_t s = 0; s < n_spans; ++s) {
+        /* the sequence that contains the span's first token (a span is
+         * non-empty and lies inside one sequence) */
+        int64_t i = 0;
+        while (!(span_start[s] >= cu[i] && span_start[s] < cu[i + 1]))
+            ++i;
+        int64_t pos = (int64_t)span_start[s] - cu[i];
+        int32_t* f = &first_pos[(int64_t)span_rank[s] * nseq + i];
+        if (pos < *f)
+            *f = (int32_t)pos;
+    }
+}
+
+int orc_plan_piece_valid(const int32_t* cu, int64_t nseq, const int32_t* first_pos, int64_t p, int64_t t)
+{
+    for (int64_t i = 0; i < nseq; ++i)
+        if (t >= cu[i] && t < cu[i + 1])
+            return (int64_t)first_pos[p * nseq + i] <= t - cu[i];
+    return 0;
+}
+
+/* orc_lse_combine with the planned validity rule (layouts as there). */
+void orc_lse_combine_planned(const void* part_out, int64_t po_sp, int64_t po_st, int64_t po_sh,
+                             const float* part_lse, int64_t pl_sp, int64_t pl_st, int64_t pl_sh, int64_t P,
+                             int64_t t_begin, int64_t t_end, int64_t H, int64_t D, int dtype, void* out,
+                             int64_t o_st, int64_t o_sh, float* lse_out, int64_t lo_st, int64_t lo_sh,
+                             const int32_t* cu_seqlens, const int32_t* first_pos, int64_t nseq)
+{
+    double* po = (double*)malloc(sizeof(double) * (size_t)(P * D + 1));
+    double* pl = (double*)malloc(sizeof(double) * (size_t)(P + 1));
+    int* valid = (int*)malloc(sizeof(int) * (size_t)(P + 1));
+    double* acc = (double*)malloc(sizeof(double) * (size_t)(D + 1));
+    for (int64_t t = t_begin; t < t_end; ++t)
+        for (int64_t h = 0; h < H; ++h) {
+            int64_t tr = t - t_begin;
+            for (int64_t p = 0; p < P; ++p) {
+                valid[p] = orc_plan_piece_valid(cu_seqlens, nseq, first_pos, p, t);
+                pl[p] = -INFINITY;
+                if (!valid[p])
+                    continue;
+                pl[p] = (double)part_lse[p * pl_sp + tr * pl_st + h * pl_sh];
+                if (!isfinite(pl[p]))
+                    continue;
+                for (int64_t d = 0; d < D; ++d)
+                    po[p * D + d] = load_half(part_out, p * po_sp + tr * po_st + h * po_sh + d, dtype);
+            }
+            double lse;
+            orc_combine_row_f64(po, pl, valid, P, D, acc, &lse);
+            for (int64_t d = 0; d < D; ++d)
+                store_half(out, tr * o_st + h * o_sh + d, dtype, acc[d]);
+            if (lse_out)
+                lse_out[tr * lo_st + h * lo_sh] = (float)lse;
+        }
+    free(po);
+    free(pl);
+    free(valid);
+    free(acc);
+}
+
+/* orc_lse_combine_backward with the planned validity rule. */
+void orc_lse_combine_planned_backward(const void* part_out, int64_t po_sp, int64_t po_st, int64_t po_sh,
+                                      const float* part_lse, int64_t pl_sp, int64_t pl_st, int64_t pl_sh,
+                                      int64_t P, int64_t t_begin, int64_t t_end, int64_t H, int64_t D,
+                                      int dtype, const void* g_out, int64_t go_st, int64_t go_sh,
+                                      const float* g_lse, int64_t gl_st, int64_t gl_sh, void* d_part_out,
+                                      int64_t dpo_sp, int64_t dpo_st, int64_t dpo_sh, float* d_part_lse,
+                                      int64_t dpl_sp, int64_t dpl_st, int64_t dpl_sh,
+                                      const int32_t* cu_seqlens, const int32_t* first_pos, int64_t nseq)
+{
+    double* po = (double*)malloc(sizeof(double) * (size_t)(P * D + 1));
+    double* pl = (double*)malloc(sizeof(double) * (size_t)(P + 1));
+    int* valid = (int*)malloc(sizeof(int) * (size_t)(P + 1));
+    double* g = (double*)malloc(sizeof(double) * (size_t)(D + 1));
+    double* d_o = (double*)malloc(sizeof(double) * (size_t)(P * D + 1));
+    double* d_l = (double*)malloc(sizeof(double) * (size_t)(P + 1));
+    for (int64_t t = t_begin; t < t_end; ++t)
+        for (int64_t h = 0; h < H; ++h) {
+            int64_t tr = t - t_begin;
+            for (int64_t p = 0; p < P; ++p) {
+                valid[p] = orc_plan_piece_valid(cu_seqlens, nseq, first_pos, p, t);
+                pl[p] = -INFINITY;
+                if (!valid[p])
+                    continue;
+                pl[p] = (double)part_lse[p * pl_sp + tr * pl_st + h * pl_sh];
+                if (!isfinite(pl[p]))
+                    continue;
+                for (int64_t d = 0; d < D; ++d)
+                    po[p * D + d] = load_half(part_out, p * po_sp + tr * po_st + h * po_sh + d, dtype);
+            }
+            for (int64_t d = 0; d < D; ++d)
+                g[d] = load_half(g_out, tr * go_st + h * go_sh + d, dtype);
+            double gl = g_lse ? (double)g_lse[tr * gl_st + h * gl_sh] : 0.0;
+            orc_combine_row_backward_f64(po, pl, valid, P, D, g, gl, d_o, d_l);
+            for (int64_t p = 0; p < P; ++p) {
+                for (int64_t d = 0; d < D; ++d)
+                    store_half(d_part_out, p * dpo_sp + tr * dpo_st + h * dpo_sh + d, dtype, d_o[p * D + d]);
+                d_part_lse[p * dpl_sp + tr * dpl_st + h * dpl_sh] = (float)d_l[p];
+            }
+        }
+    free(po);
+    free(pl);
+    free(valid);
+    free(g);
+    free(d_o);
+    free(d_l);
+}
