@@ -152,6 +152,9 @@ class Workload:
         self.p_plan_ms = (time.perf_counter() - t0) * 1e3
         self.p_contig = cam.thd_plan(self.p_cu, self.tP, cam.ThdPlannerConfig(block_size=64, min_split_tokens=8192,
                                                                                 contiguous=True))
+        first = self.p_plan.first_pos_host
+        self.p_admitted = sum(max(0, int(L) - int(first[p, i])) for i, L in enumerate(self.p_lens)
+                              for p in range(self.tP) if first[p, i] < int(L))
         # training: gradient buffers of the relayout pair and of the THD combine
         P, S, H, D = self.vP, self.vS, self.vH, self.vD
         self.v_dqkv = torch.empty((P, 3, S // P, H, D), dtype=bf, device=dev)
@@ -276,7 +279,13 @@ class Workload:
         def planned_h2s():
             cam.ulysses_head_to_seq_spans(self.t_o, self.p_plan, out=self.t_o_out)
 
+        def planned_combine():
+            cam.lse_combine_planned(self.t_part, self.t_lse, self.p_plan, out=self.t_comb, lse_out=self.t_comb_lse)
+
+        planned_comb_bytes = self.p_admitted * H * (2 * D + 4) + rows * (2 * D + 4)
+
         return [
+            ("lse_combine_planned_thd", planned_comb_bytes, planned_combine),
             ("relayout_seq_to_head_planned_thd_qkv", 2 * 3 * T * H * D * 2, planned_s2h),
             ("relayout_head_to_seq_planned_thd_o", 2 * T * H * D * 2, planned_h2s),
             ("lse_combine_varlen_backward_thd", bwd_bytes, thd_backward),

@@ -25,6 +25,7 @@ __all__ = [
     "ulysses_seq_to_head", "ulysses_head_to_seq",
     "VarlenPlan", "ulysses_varlen_plan", "ulysses_seq_to_head_varlen", "ulysses_head_to_seq_varlen",
     "ThdPlannerConfig", "ThdPlan", "thd_plan", "ulysses_seq_to_head_spans", "ulysses_head_to_seq_spans",
+    "lse_combine_planned",
     "lse_pack_bytes", "lse_pack", "lse_combine_packed", "lse_combine", "lse_combine_varlen",
     "lse_combine_packed_seq", "lse_combine_varlen_seq", "lse_merge", "lse_combine_backward",
     "copy", "last_launch",
@@ -69,6 +70,12 @@ _SIGNATURES = {
                                   _int, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _vp]),
     "cam_copy": (_int, [_vp, _vp, _i64, _vp]),
     "thd_plan": (_int, [_vp, _i64, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "thd_plan_first_positions": (_int, [_vp, _i64, _i64, _vp, _vp, _i64, _vp]),
+    "lse_combine_planned": (_int, [_vp, _i64, _i64, _i64, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _i64,
+                                   _int, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _vp, _i64, _vp]),
+    "lse_combine_planned_backward": (_int, [_vp, _i64, _i64, _i64, _vp, _i64, _i64, _i64, _i64, _i64, _i64,
+                                            _i64, _int, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64,
+                                            _i64, _vp, _i64, _i64, _i64, _vp, _vp, _i64, _vp]),
     "ulysses_seq_to_head_spans": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64,
                                          _int, _vp]),
     "ulysses_head_to_seq_spans": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64,
@@ -310,6 +317,21 @@ class ThdPlan:
     span_rank: torch.Tensor | None = None
     span_local: torch.Tensor | None = None
     rank_off: torch.Tensor | None = None
+    cu: torch.Tensor | None = None
+    first_pos: torch.Tensor | None = None
+
+    @property
+    def first_pos_host(self) -> np.ndarray:
+        """[W][nseq] int32: smallest position of sequence i held by rank p
+        (INT32_MAX if none) -- the admission table of the planned combine."""
+        if getattr(self, "_first", None) is None:
+            nseq = self.cu_host.size - 1
+            first = np.empty((self.world_size, nseq), dtype=np.int32)
+            _check(library().thd_plan_first_positions(
+                self.cu_host.ctypes.data, nseq, self.world_size, self.span_start_host.ctypes.data,
+                self.span_rank_host.ctypes.data, self.n_spans, first.ctypes.data))
+            self._first = first
+        return self._first
 
     @property
     def n_spans(self) -> int:
@@ -335,6 +357,8 @@ class ThdPlan:
         self.span_rank = torch.from_numpy(self.span_rank_host).to(dev)
         self.span_local = torch.from_numpy(self.span_local_host).to(dev)
         self.rank_off = torch.from_numpy(self.rank_off_host).to(dev)
+        self.cu = torch.from_numpy(np.ascontiguousarray(self.cu_host, dtype=np.int32)).to(dev)
+        self.first_pos = torch.from_numpy(self.first_pos_host).to(dev)
         return self
 
 
@@ -530,10 +554,29 @@ def lse_combine_varlen(part_out: torch.Tensor, part_lse: torch.Tensor, cu_seqlen
     return out, lse_out
 
 
+def lse_combine_planned(part_out: torch.Tensor, part_lse: torch.Tensor, plan: ThdPlan,
+                        out: torch.Tensor | None = None, lse_out: torch.Tensor | None | bool = True):
+    """Causal combine of a batch laid out by a THD layout plan: partial p of
+    a token is admitted iff rank p holds a position of the token's sequence at
+    or before it (the plan's device tables are used)."""
+    P, T, H, D, out, lse_out, lo = _combine_common(part_out, part_lse, out, lse_out)
+    if plan.first_pos is None:
+        raise ValueError("the plan's tables are not on the device (thd_plan(..., device=...) or plan.to(device))")
+    if P != plan.world_size or T != plan.total_tokens:
+        raise ValueError("part_out must be [world_size][total_tokens][H][D] for this plan")
+    _check(library().lse_combine_planned(part_out.data_ptr(), *part_out.stride()[:3], part_lse.data_ptr(),
+                                         *part_lse.stride(), P, T, H, D, _dt(part_out), out.data_ptr(),
+                                         *out.stride()[:2], _ptr(lse_out), *lo, plan.cu.data_ptr(),
+                                         plan.first_pos.data_ptr(), plan.cu_host.size - 1, _stream(part_out)))
+    return out, lse_out
+
+
 def lse_combine_backward(part_out: torch.Tensor, part_lse: torch.Tensor, g_out: torch.Tensor,
                          g_lse: torch.Tensor | None = None, cu_seqlens: torch.Tensor | None = None,
-                         d_part_out: torch.Tensor | None = None, d_part_lse: torch.Tensor | None = None):
-    """Gradient of lse_combine (or, with cu_seqlens, of lse_combine_varlen):
+                         d_part_out: torch.Tensor | None = None, d_part_lse: torch.Tensor | None = None,
+                         plan: ThdPlan | None = None):
+    """Gradient of lse_combine (with cu_seqlens, of lse_combine_varlen; with
+    plan, of lse_combine_planned):
     part_out [P][T][H][D], part_lse [P][T][H], g_out [T][H][D] (the upstream
     gradient of out, payload dtype), g_lse [T][H] fp32 or None (zero) ->
     (d_part_out [P][T][H][D], d_part_lse [P][T][H] fp32).  Any strides with D
@@ -561,7 +604,14 @@ def lse_combine_backward(part_out: torch.Tensor, part_lse: torch.Tensor, g_out: 
     args = [part_out.data_ptr(), *part_out.stride()[:3], part_lse.data_ptr(), *part_lse.stride(), P, T, H, D,
             _dt(part_out), g_out.data_ptr(), *g_out.stride()[:2], _ptr(g_lse), *gl, d_part_out.data_ptr(),
             *d_part_out.stride()[:3], d_part_lse.data_ptr(), *d_part_lse.stride()]
-    if cu_seqlens is None:
+    if plan is not None:
+        if plan.first_pos is None:
+            raise ValueError("the plan's tables are not on the device")
+        if P != plan.world_size or T != plan.total_tokens:
+            raise ValueError("part_out must be [world_size][total_tokens][H][D] for this plan")
+        _check(library().lse_combine_planned_backward(*args, plan.cu.data_ptr(), plan.first_pos.data_ptr(),
+                                                      plan.cu_host.size - 1, _stream(part_out)))
+    elif cu_seqlens is None:
         _check(library().lse_combine_backward(*args, _stream(part_out)))
     else:
         _contig(cu_seqlens, "cu_seqlens")

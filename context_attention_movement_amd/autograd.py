@@ -22,6 +22,7 @@ import torch
 from . import (ThdPlan, VarlenPlan, lse_combine_backward, ulysses_head_to_seq, ulysses_head_to_seq_spans,
                ulysses_head_to_seq_varlen, ulysses_seq_to_head, ulysses_seq_to_head_spans, ulysses_seq_to_head_varlen)
 from . import lse_combine as _lse_combine
+from . import lse_combine_planned as _lse_combine_planned
 from . import lse_combine_varlen as _lse_combine_varlen
 
 __all__ = ["seq_to_head", "head_to_seq", "seq_to_head_varlen", "head_to_seq_varlen", "seq_to_head_spans",
@@ -98,12 +99,15 @@ class _HeadToSeqSpans(torch.autograd.Function):
 
 class _LseCombine(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, part_out, part_lse, cu_seqlens):
-        if cu_seqlens is None:
+    def forward(ctx, part_out, part_lse, cu_seqlens, plan):
+        if plan is not None:
+            out, lse = _lse_combine_planned(part_out, part_lse, plan)
+        elif cu_seqlens is None:
             out, lse = _lse_combine(part_out, part_lse)
         else:
             out, lse = _lse_combine_varlen(part_out, part_lse, cu_seqlens)
         ctx.save_for_backward(part_out, part_lse, cu_seqlens)
+        ctx.plan = plan
         ctx.mark_non_differentiable(*(() if cu_seqlens is None else (cu_seqlens,)))
         return out, lse
 
@@ -116,8 +120,8 @@ class _LseCombine(torch.autograd.Function):
             g_out = g_out.to(part_out.dtype).contiguous()
         if g_lse is not None and g_lse.dtype != torch.float32:
             g_lse = g_lse.float()
-        d_po, d_pl = lse_combine_backward(part_out, part_lse, g_out, g_lse, cu_seqlens)
-        return d_po, d_pl, None
+        d_po, d_pl = lse_combine_backward(part_out, part_lse, g_out, g_lse, cu_seqlens, plan=ctx.plan)
+        return d_po, d_pl, None, None
 
 
 def seq_to_head(x: torch.Tensor, P: int) -> torch.Tensor:
@@ -150,7 +154,9 @@ def head_to_seq_spans(x: torch.Tensor, plan: ThdPlan) -> torch.Tensor:
     return _HeadToSeqSpans.apply(x, plan)
 
 
-def lse_combine(part_out: torch.Tensor, part_lse: torch.Tensor, cu_seqlens: torch.Tensor | None = None):
-    """Differentiable stable combine (causal varlen when cu_seqlens is given):
-    part_out [P][T][H][D], part_lse [P][T][H] -> (out [T][H][D], lse_out [T][H])."""
-    return _LseCombine.apply(part_out, part_lse, cu_seqlens)
+def lse_combine(part_out: torch.Tensor, part_lse: torch.Tensor, cu_seqlens: torch.Tensor | None = None,
+                plan: ThdPlan | None = None):
+    """Differentiable stable combine (causal varlen when cu_seqlens is given,
+    causal over a THD layout plan when plan is given): part_out [P][T][H][D],
+    part_lse [P][T][H] -> (out [T][H][D], lse_out [T][H])."""
+    return _LseCombine.apply(part_out, part_lse, cu_seqlens, plan)

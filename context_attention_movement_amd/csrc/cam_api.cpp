@@ -346,6 +346,7 @@ struct CombineIn {
     int64_t Hp = 0, Hq = 0;          // mode 1
     const int32_t* rank_cu = nullptr;  // mode 2
     const int64_t* rank_off = nullptr;
+    const int32_t* first = nullptr;    // a plan's first positions [P][nseq] (planned rule)
 };
 
 cam_status combine(const char* op, const CombineIn& c, void* stream)
@@ -387,6 +388,15 @@ cam_status combine(const char* op, const CombineIn& c, void* stream)
         return set_error(CAM_ERR_OVERLAP, "%s: an output overlaps an input or the other output", op);
     if (c.cu && (overlaps(c.out, ext_o, c.cu, 4 * (c.nseq + 1)) || overlaps(c.lse_out, ext_lo, c.cu, 4 * (c.nseq + 1))))
         return set_error(CAM_ERR_OVERLAP, "%s: an output overlaps cu_seqlens", op);
+    if (c.first) {
+        int64_t ext_f;
+        if (!c.cu || !prod_ok({c.P, c.nseq, 4}, &ext_f))
+            return set_error(CAM_ERR_SHAPE, "%s: the first-position table needs cu_seqlens", op);
+        if (!aligned(c.first, 4))
+            return set_error(CAM_ERR_ALIGNMENT, "%s: misaligned first-position table", op);
+        if (overlaps(c.out, ext_o, c.first, ext_f) || overlaps(c.lse_out, ext_lo, c.first, ext_f))
+            return set_error(CAM_ERR_OVERLAP, "%s: an output overlaps the first-position table", op);
+    }
 
     Combine a{};
     const uint64_t row_b = uint64_t(c.D) * 2;
@@ -437,6 +447,7 @@ cam_status combine(const char* op, const CombineIn& c, void* stream)
     a.o_row_b = uint64_t(c.D) * 2;
     a.rank_cu = c.rank_cu;
     a.rank_off = c.rank_off;
+    a.first = c.first;
     a.fp16 = c.dt == CAM_FP16;
     return launch_combine(a, stream);
 }
@@ -458,6 +469,7 @@ struct CombineBwdIn {
     int64_t dpl_sp, dpl_st, dpl_sh;
     const int32_t* cu;
     int64_t nseq;
+    const int32_t* first = nullptr;  // a plan's first positions [P][nseq] (planned rule)
 };
 
 cam_status combine_backward(const char* op, const CombineBwdIn& c, void* stream)
@@ -504,6 +516,15 @@ cam_status combine_backward(const char* op, const CombineBwdIn& c, void* stream)
             return set_error(CAM_ERR_OVERLAP, "%s: an output overlaps an input", op);
     if (overlaps(c.dpo, ext_dpo, c.dpl, ext_dpl))
         return set_error(CAM_ERR_OVERLAP, "%s: the two outputs overlap", op);
+    if (c.first) {
+        int64_t ext_f;
+        if (!c.cu || !prod_ok({c.P, c.nseq, 4}, &ext_f))
+            return set_error(CAM_ERR_SHAPE, "%s: the first-position table needs cu_seqlens", op);
+        if (!aligned(c.first, 4))
+            return set_error(CAM_ERR_ALIGNMENT, "%s: misaligned first-position table", op);
+        if (overlaps(c.dpo, ext_dpo, c.first, ext_f) || overlaps(c.dpl, ext_dpl, c.first, ext_f))
+            return set_error(CAM_ERR_OVERLAP, "%s: an output overlaps the first-position table", op);
+    }
 
     CombineBwd a{};
     const uint64_t row_b = uint64_t(c.D) * 2;
@@ -547,6 +568,7 @@ cam_status combine_backward(const char* op, const CombineBwdIn& c, void* stream)
     a.rows_per_tile = rows;
     a.n_tiles = (uint64_t(n_rows) + rows - 1) / rows;
     a.cu = c.cu;
+    a.first = c.first;
     a.nseq = int32_t(c.nseq);
     a.div_P = make_fastdiv(a.P);
     a.fp16 = c.dt == CAM_FP16;
@@ -852,6 +874,44 @@ cam_status lse_combine_varlen_backward(const void* part_out, int64_t po_sp, int6
                    g_out, go_st, go_sh, g_lse, gl_st, gl_sh, d_part_out, dpo_sp, dpo_st, dpo_sh,
                    d_part_lse, dpl_sp, dpl_st, dpl_sh, cu_seqlens, nseq};
     return combine_backward("lse_combine_varlen_backward", c, stream);
+}
+
+cam_status lse_combine_planned(const void* part_out, int64_t po_sp, int64_t po_st, int64_t po_sh,
+                               const float* part_lse, int64_t pl_sp, int64_t pl_st, int64_t pl_sh, int64_t P,
+                               int64_t T, int64_t H, int64_t D, cam_dtype dt, void* out, int64_t o_st, int64_t o_sh,
+                               float* lse_out, int64_t lo_st, int64_t lo_sh, const int32_t* cu_seqlens,
+                               const int32_t* first_pos, int64_t nseq, void* stream)
+{
+    clear_error();
+    if (T > 0 && (!cu_seqlens || !first_pos))
+        return set_error(CAM_ERR_NULL, "lse_combine_planned: cu_seqlens and first_pos must be non-null");
+    if (T > INT32_MAX)
+        return set_error(CAM_ERR_SHAPE, "lse_combine_planned: total_tokens must fit int32");
+    CombineIn c{part_out, po_sp, po_st, po_sh, part_lse, pl_sp, pl_st, pl_sh, P, T, H, D, dt,
+                out, o_st, o_sh, lse_out, lo_st, lo_sh, cu_seqlens, nseq};
+    c.first = first_pos;
+    return combine("lse_combine_planned", c, stream);
+}
+
+cam_status lse_combine_planned_backward(const void* part_out, int64_t po_sp, int64_t po_st, int64_t po_sh,
+                                        const float* part_lse, int64_t pl_sp, int64_t pl_st, int64_t pl_sh,
+                                        int64_t P, int64_t T, int64_t H, int64_t D, cam_dtype dt,
+                                        const void* g_out, int64_t go_st, int64_t go_sh, const float* g_lse,
+                                        int64_t gl_st, int64_t gl_sh, void* d_part_out, int64_t dpo_sp,
+                                        int64_t dpo_st, int64_t dpo_sh, float* d_part_lse, int64_t dpl_sp,
+                                        int64_t dpl_st, int64_t dpl_sh, const int32_t* cu_seqlens,
+                                        const int32_t* first_pos, int64_t nseq, void* stream)
+{
+    clear_error();
+    if (T > 0 && (!cu_seqlens || !first_pos))
+        return set_error(CAM_ERR_NULL, "lse_combine_planned_backward: cu_seqlens and first_pos must be non-null");
+    if (T > INT32_MAX)
+        return set_error(CAM_ERR_SHAPE, "lse_combine_planned_backward: total_tokens must fit int32");
+    CombineBwdIn c{part_out, po_sp, po_st, po_sh, part_lse, pl_sp, pl_st, pl_sh, P, T, H, D, dt,
+                   g_out, go_st, go_sh, g_lse, gl_st, gl_sh, d_part_out, dpo_sp, dpo_st, dpo_sh,
+                   d_part_lse, dpl_sp, dpl_st, dpl_sh, cu_seqlens, nseq};
+    c.first = first_pos;
+    return combine_backward("lse_combine_planned_backward", c, stream);
 }
 
 cam_status lse_combine_packed_seq(const void* packed, int64_t P, int64_t T, int64_t H, int64_t Dv, int scatter_dim,

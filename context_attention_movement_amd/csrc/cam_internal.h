@@ -157,7 +157,8 @@ struct Combine {
     uint64_t o_row_b;       // modes 1, 2: bytes per output row
     const int32_t* rank_cu; // mode 2: the varlen plan
     const int64_t* rank_off;
-    const int32_t* cu;      // non-null: causal piece gating (varlen)
+    const int32_t* cu;      // non-null: causal gating (varlen)
+    const int32_t* first;   // with cu: a plan's first positions [P][nseq]; null: piece rule
     int32_t nseq;
     FastDiv div_P;
     int width;
@@ -211,7 +212,8 @@ struct CombineBwd {
     uint32_t gp_log2;
     uint32_t rows_per_tile;
     uint64_t n_tiles;
-    const int32_t* cu;      // non-null: causal piece gating (varlen)
+    const int32_t* cu;      // non-null: causal gating (varlen)
+    const int32_t* first;   // with cu: a plan's first positions [P][nseq]; null: piece rule
     int32_t nseq;
     FastDiv div_P;
     int width;

@@ -386,3 +386,32 @@ extern "C" cam_status thd_plan(const int32_t* cu_seqlens, int64_t nseq, int64_t 
     *chosen = best_g;
     return CAM_OK;
 }
+
+// Smallest position of each sequence that each rank holds, from a plan's
+// span tables (the causal rule of the planned combine: partial p of a token
+// at position k of sequence i is admitted iff first_pos[p][i] <= k).
+extern "C" cam_status thd_plan_first_positions(const int32_t* cu_seqlens, int64_t nseq, int64_t world_size,
+                                               const int32_t* span_start, const int32_t* span_rank,
+                                               int64_t n_spans, int32_t* first_pos)
+{
+    const char* op = "thd_plan_first_positions";
+    clear_error();
+    if (nseq < 0 || world_size < 1 || n_spans < 0)
+        return set_error(CAM_ERR_SHAPE, "%s: need nseq >= 0, world_size >= 1, n_spans >= 0", op);
+    if (!cu_seqlens || !first_pos || (n_spans > 0 && (!span_start || !span_rank)))
+        return set_error(CAM_ERR_NULL, "%s: null table", op);
+    std::fill(first_pos, first_pos + world_size * nseq, INT32_MAX);
+    for (int64_t s = 0; s < n_spans; ++s) {
+        const int32_t t = span_start[s];
+        // the sequence whose token range holds the span's first token
+        const int32_t* hit = std::upper_bound(cu_seqlens, cu_seqlens + nseq + 1, t);
+        const int64_t i = int64_t(hit - cu_seqlens) - 1;
+        const int64_t r = span_rank[s];
+        if (i < 0 || i >= nseq || r < 0 || r >= world_size)
+            return set_error(CAM_ERR_SHAPE, "%s: span %lld lies outside the batch or the ranks", op, (long long)s);
+        int32_t& f = first_pos[r * nseq + i];
+        f = std::min(f, int32_t(t - cu_seqlens[i]));
+    }
+    return CAM_OK;
+}
+

@@ -194,6 +194,17 @@ cam_status thd_plan(const int32_t* cu_seqlens, int64_t nseq, int64_t world_size,
  *   total_tokens = span_start[n_spans] is passed by the host.  Rows a
  *   malformed table would place outside the buffers are skipped.  H % P == 0.
  */
+/*
+ * thd_plan_first_positions (host only): first_pos[p * nseq + i] = the
+ *   smallest position of sequence i held by rank p under the plan's spans
+ *   (INT32_MAX if none), for the planned combine.  first_pos has world_size *
+ *   nseq entries, caller-owned host memory.  CAM_ERR_SHAPE if a span lies
+ *   outside the batch or the ranks.
+ */
+cam_status thd_plan_first_positions(const int32_t* cu_seqlens, int64_t nseq, int64_t world_size,
+                                    const int32_t* span_start, const int32_t* span_rank,
+                                    int64_t n_spans, int32_t* first_pos);
+
 cam_status ulysses_seq_to_head_spans(const void* in, void* out, const int32_t* span_start,
                                      const int32_t* span_rank, const int32_t* span_local,
                                      const int64_t* rank_off, int64_t n_spans, int64_t total_tokens,
@@ -303,6 +314,22 @@ cam_status lse_combine_varlen(const void* part_out, int64_t po_sp, int64_t po_st
  *   rank_off are the DEVICE copies of ulysses_varlen_plan's tables for the same
  *   P (the P partials are the P KV pieces, as in lse_combine_varlen).
  */
+/*
+ * lse_combine_planned: lse_combine_varlen for a batch laid out by a THD layout
+ *   plan (context parallelism in which rank p holds the queries and keys of
+ *   its spans): partial p of the token at position k of sequence i is the
+ *   causal attention over the keys rank p holds of sequence i, admitted iff
+ *   first_pos[p * nseq + i] <= k (thd_plan_first_positions; DEVICE copy, P
+ *   = world_size); masked partials are not read.  For the per-sequence split
+ *   it gives what lse_combine_varlen gives.
+ */
+cam_status lse_combine_planned(const void* part_out, int64_t po_sp, int64_t po_st, int64_t po_sh,
+                               const float* part_lse, int64_t pl_sp, int64_t pl_st, int64_t pl_sh,
+                               int64_t P, int64_t T, int64_t H, int64_t D, cam_dtype dt, void* out,
+                               int64_t o_st, int64_t o_sh, float* lse_out, int64_t lo_st, int64_t lo_sh,
+                               const int32_t* cu_seqlens, const int32_t* first_pos, int64_t nseq,
+                               void* stream);
+
 cam_status lse_combine_packed_seq(const void* packed, int64_t P, int64_t T, int64_t H, int64_t Dv,
                                   int scatter_dim, cam_dtype dt, void* out, float* lse_out,
                                   void* stream);
@@ -382,6 +409,19 @@ cam_status lse_combine_varlen_backward(const void* part_out, int64_t po_sp, int6
                                        int64_t dpo_sh, float* d_part_lse, int64_t dpl_sp,
                                        int64_t dpl_st, int64_t dpl_sh, const int32_t* cu_seqlens,
                                        int64_t nseq, void* stream);
+
+/* lse_combine_planned_backward: the gradient of lse_combine_planned (layouts
+ * and rules of lse_combine_backward, admission of lse_combine_planned). */
+cam_status lse_combine_planned_backward(const void* part_out, int64_t po_sp, int64_t po_st,
+                                        int64_t po_sh, const float* part_lse, int64_t pl_sp,
+                                        int64_t pl_st, int64_t pl_sh, int64_t P, int64_t T, int64_t H,
+                                        int64_t D, cam_dtype dt, const void* g_out, int64_t go_st,
+                                        int64_t go_sh, const float* g_lse, int64_t gl_st,
+                                        int64_t gl_sh, void* d_part_out, int64_t dpo_sp,
+                                        int64_t dpo_st, int64_t dpo_sh, float* d_part_lse,
+                                        int64_t dpl_sp, int64_t dpl_st, int64_t dpl_sh,
+                                        const int32_t* cu_seqlens, const int32_t* first_pos,
+                                        int64_t nseq, void* stream);
 
 /* ------------------------------------------------------------------------- */
 /* Measurement helper                                                          */

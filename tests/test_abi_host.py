@@ -273,3 +273,14 @@ def test_combine_backward_rejections(lib):
     assert g(*args()[:-1], None, 3, None) == NULL
     assert g(*args()[:-1], A + 0x6000_0000, 0, None) == SHAPE
     assert g(*args(dl=A + 0x6000_0000)[:-1], A + 0x6000_0000, 3, None) == OVERLAP
+
+
+def test_planned_combine_rejections(lib):
+    f = lib.lse_combine_planned
+    L, O, LO, CU, FP = A + 0x1000_0000, A + 0x2000_0000, A + 0x3000_0000, A + 0x5000_0000, A + 0x6000_0000
+    args = lambda cu=CU, fp=FP, out=O: (A, 64 * 8 * 16, 8 * 16, 16, L, 64 * 8, 8, 1, 4, 64, 8, 16, BF16,
+                                        out, 8 * 16, 16, LO, 8, 1, cu, fp, 3, None)
+    assert f(*args(fp=None)) == NULL
+    assert f(*args(cu=None)) == NULL
+    assert f(*args(fp=FP + 2)) == ALIGN
+    assert f(*args(out=FP)) == OVERLAP

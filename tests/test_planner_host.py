@@ -110,3 +110,16 @@ def test_for_rank_lists_slab_order(cam):
         assert all(0 <= a and a + n <= lens[i] for i, a, n in spans)
         keys = [(i, a) for i, a, _ in spans]
         assert keys == sorted(keys)
+
+
+def test_first_positions_match_oracle(cam, orc):
+    for seed in range(10):
+        cu = _batch(seed, 4)
+        N = int(cu[-1]) // 4
+        for W in (1, 3, 8):
+            if N < W:
+                continue
+            q = orc.thd_plan(cu, W, 4, 64)
+            plan = cam.ThdPlan(W, int(cu[-1]), cu, q["span_start"], q["span_rank"], q["span_local"], q["rank_off"],
+                               q["rank_cost"], q["grid"])
+            assert np.array_equal(plan.first_pos_host, orc.plan_first_positions(cu, q, W))
