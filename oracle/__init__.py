@@ -86,6 +86,7 @@ def _load():
         "orc_lse_combine_planned_backward": (None, [vp, i64, i64, i64, vp, i64, i64, i64, i64, i64, i64, i64,
                                                     i64, C.c_int, vp, i64, i64, vp, i64, i64, vp, i64, i64, i64,
                                                     vp, i64, i64, i64, vp, vp, i64]),
+        "orc_qkv_projection": (None, [vp, vp, vp, i64, i64, i64, i64, i64, i64, C.c_int]),
         "orc_combine_row_backward_f64": (None, [vp, vp, vp, i64, i64, vp, C.c_double, vp, vp]),
         "orc_lse_combine_backward": (None, [vp, i64, i64, i64, vp, i64, i64, i64, i64, i64, i64, i64, i64,
                                             C.c_int, vp, i64, i64, vp, i64, i64, vp, i64, i64, i64,
@@ -524,4 +525,16 @@ def lse_combine_planned_backward(part_out: np.ndarray, part_lse: np.ndarray, g_o
         _dt(dtype), ptr(g_out), go[0], go[1], ptr(g_lse) if g_lse is not None else None, gl[0], gl[1],
         _p(d_po), Tw * H * D, H * D, D, _p(d_pl), Tw * H, H, 1, _p(cu), _p(first), cu.size - 1)
     return d_po, d_pl
+
+
+# -- Q/K/V projection into the head-sharded layout --------------------------------
+
+def qkv_projection(x_bits: np.ndarray, w_bits: np.ndarray, P: int, B: int, H: int, D: int, dtype: str = "bf16"):
+    """x [S][K], w [B*H*D][K] (payload bits) -> head-sharded [P][B][S][H/P][D] bits."""
+    x_bits = np.ascontiguousarray(x_bits)
+    w_bits = np.ascontiguousarray(w_bits)
+    S, K = x_bits.shape
+    out = np.empty((P, B, S, H // P, D), dtype=np.uint16)
+    _load().orc_qkv_projection(_p(x_bits), _p(w_bits), _p(out), S, K, P, B, H, D, _dt(dtype))
+    return out
 

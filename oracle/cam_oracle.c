@@ -1403,3 +1403,35 @@ void orc_lse_combine_planned_backward(const void* part_out, int64_t po_sp, int64
     free(d_o);
     free(d_l);
 }
+
+/* ------------------------------------------------------------------------ */
+/* Q/K/V projection into the head-sharded layout  ([FV] direct output slices) */
+/* ------------------------------------------------------------------------ */
+/*
+ * out[r][b][t][h'][d] = sum_k x[t][k] * w[(b*H + r*H/P + h')*D + d][k]: the
+ * projection of the stacked sequence shards x [S][K] by the fused weight
+ * w [B*H*D][K] (a linear layer's layout), written where the seq->head
+ * relayout of its result would put it.  Double accumulation, rounded once to
+ * the payload type (dtype 0 bf16, 1 fp16).
+ */
+void orc_qkv_projection(const void* x, const void* w, void* out, int64_t S, int64_t K, int64_t P, int64_t B,
+                        int64_t H, int64_t D, int dtype)
+{
+    const int64_t Hp = H / P;
+    double* xr = (double*)malloc(sizeof(double) * (size_t)(K + 1));
+    for (int64_t t = 0; t < S; ++t) {
+        for (int64_t k = 0; k < K; ++k)
+            xr[k] = load_half(x, t * K + k, dtype);
+        for (int64_t b = 0; b < B; ++b)
+            for (int64_t h = 0; h < H; ++h)
+                for (int64_t d = 0; d < D; ++d) {
+                    const int64_t n = (b * H + h) * D + d;
+                    double acc = 0.0;
+                    for (int64_t k = 0; k < K; ++k)
+                        acc += xr[k] * load_half(w, n * K + k, dtype);
+                    const int64_t r = h / Hp, hp = h % Hp;
+                    store_half(out, (((r * B + b) * S + t) * Hp + hp) * D + d, dtype, acc);
+                }
+    }
+    free(xr);
+}
