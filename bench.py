@@ -44,6 +44,7 @@ sys.path.insert(0, str(ROOT))
 
 METRIC = "achieved HBM GB/s (% of peak) and µs/call for relayout, LSE-pack, combine"
 HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix cores, published
 KERNEL_SOURCES = ["relayout.hip", "lse.hip", "cam_device.h", "cam_internal.h"]
 TRAFFIC_FILE = ROOT / "profiles" / "traffic.json"
 
@@ -155,6 +156,12 @@ class Workload:
         first = self.p_plan.first_pos_host
         self.p_admitted = sum(max(0, int(L) - int(first[p, i])) for i, L in enumerate(self.p_lens)
                               for p in range(self.tP) if first[p, i] < int(L))
+        # Q/K/V projection of the video shape into the head-sharded layout:
+        # x [S][3072] (hidden = 24 heads x 128), w [3 * 24 * 128][3072]
+        P, S, H, D = self.vP, self.vS, self.vH, self.vD
+        self.j_x = randn((S, H * D))
+        self.j_w = (torch.randn((3 * H * D, H * D), generator=g, device=dev, dtype=torch.float32) * 0.02).to(bf)
+        self.j_flops = 2 * S * (3 * H * D) * (H * D)
         # training: gradient buffers of the relayout pair and of the THD combine
         P, S, H, D = self.vP, self.vS, self.vH, self.vD
         self.v_dqkv = torch.empty((P, 3, S // P, H, D), dtype=bf, device=dev)
@@ -619,6 +626,40 @@ def main():
             ext[n] = {"us_per_call": round(us, 2), "algorithmic_bytes": int(nb_ext), "last_launch": cam.last_launch(),
                       "GBps": round(nb_ext / us / 1e3, 1), "frac_of_hbm_peak": round(nb_ext / us / 1e3 / HBM_PEAK_GBPS, 4)}
 
+    # ---- Q/K/V projection written into the head-sharded layout (MFMA); the
+    # library GEMM (torch.mm) of the same product is timed beside it as a
+    # reference, to be read with the seq->head relayout it would need
+    with torch.cuda.stream(stream):
+        P, S, H, D = w.vP, w.vS, w.vH, w.vD
+        j_out = w.v_qkv_out  # [P][3][S][H/P][D]
+        j_tmp = torch.empty((S, 3 * H * D), dtype=torch.bfloat16, device="cuda")
+
+        def timed(fn, n=10):
+            for _ in range(3):
+                fn()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(n):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) * 1000.0 / n
+
+        j_us = timed(lambda: cam.qkv_projection_head_sharded(w.j_x, w.j_w, P, 3, H, D, out=j_out))
+        j_launch = cam.last_launch()
+        lib_us = timed(lambda: torch.mm(w.j_x, w.j_w.t(), out=j_tmp))
+        del j_tmp
+    projection = {
+        "op": "qkv_projection_head_sharded_video_p4 (S=32760, K=3072, N=3x24x128)",
+        "kernel": "k_proj_direct<false>", "bound": "mfma", "us_per_call": round(j_us, 2),
+        "TFLOPs": round(w.j_flops / j_us / 1e6, 1), "peak_TFLOPs": MFMA_BF16_PEAK_TFLOPS,
+        "frac_of_mfma_peak": round(w.j_flops / j_us / 1e6 / MFMA_BF16_PEAK_TFLOPS, 4), "launch": j_launch,
+        "reference_library_gemm_us": round(lib_us, 2),
+        "reference_library_gemm_TFLOPs": round(w.j_flops / lib_us / 1e6, 1),
+        "reference_note": "torch.mm (the platform's GEMM library) of the same product into [S][N]; it still "
+                          "needs the seq->head relayout (relayout_seq_to_head_video_p4_qkv) to reach this layout",
+    }
+
     # ---- plain-copy ceiling on the video Q/K/V operand size
     with torch.cuda.stream(stream):
         src, dst = w.v_qkv, w.v_qkv_out
@@ -699,6 +740,7 @@ def main():
         },
         "ops": op_table,
         "extensions": ext,
+        "projection": projection,
         "thd_plan": plan_summary(w),
         "copy_ceiling": {"GBps": round(copy_gbps, 1), "frac_of_hbm_peak": round(copy_gbps / HBM_PEAK_GBPS, 4),
                          "bytes": int(copy_bytes), "kernel": "k_copy16"},

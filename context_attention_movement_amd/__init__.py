@@ -28,7 +28,7 @@ __all__ = [
     "lse_combine_planned",
     "lse_pack_bytes", "lse_pack", "lse_combine_packed", "lse_combine", "lse_combine_varlen",
     "lse_combine_packed_seq", "lse_combine_varlen_seq", "lse_merge", "lse_combine_backward",
-    "copy", "last_launch",
+    "qkv_projection_head_sharded", "copy", "last_launch",
 ]
 
 LIB_PATH = Path(__file__).resolve().parent / "libcam.so"
@@ -69,6 +69,7 @@ _SIGNATURES = {
     "lse_combine_varlen": (_int, [_vp, _i64, _i64, _i64, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _i64,
                                   _int, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _vp]),
     "cam_copy": (_int, [_vp, _vp, _i64, _vp]),
+    "qkv_projection_head_sharded": (_int, [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _int, _vp]),
     "thd_plan": (_int, [_vp, _i64, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "thd_plan_first_positions": (_int, [_vp, _i64, _i64, _vp, _vp, _i64, _vp]),
     "lse_combine_planned": (_int, [_vp, _i64, _i64, _i64, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _i64,
@@ -693,6 +694,27 @@ def lse_merge(acc_out: torch.Tensor, acc_lse: torch.Tensor, part_out: torch.Tens
                                part_out.data_ptr(), *part_out.stride()[:2], part_lse.data_ptr(), *part_lse.stride(),
                                T, H, D, _dt(part_out), _ptr(out_final), *fs, _stream(part_out)))
     return acc_out, acc_lse
+
+
+def qkv_projection_head_sharded(x: torch.Tensor, w: torch.Tensor, P: int, B: int, H: int, D: int,
+                                out: torch.Tensor | None = None) -> torch.Tensor:
+    """x [S][K] (stacked sequence shards) times w [B*H*D][K] (linear-layer
+    layout), written as the head-sharded [P][B][S][H/P][D] (MFMA)."""
+    _contig(x, "x")
+    _contig(w, "w")
+    if x.dim() != 2 or w.dim() != 2 or w.shape[1] != x.shape[1] or w.shape[0] != B * H * D:
+        raise ValueError("x must be [S][K] and w [B*H*D][K]")
+    if x.dtype != w.dtype or x.dtype not in (torch.bfloat16, torch.float16):
+        raise TypeError("x and w must share a bf16 or fp16 dtype")
+    S, K = x.shape
+    if out is None:
+        out = torch.empty((P, B, S, H // P, D), dtype=x.dtype, device=x.device)
+    _contig(out, "out")
+    if out.numel() != S * B * H * D or out.dtype != x.dtype:
+        raise ValueError("out must be [P][B][S][H/P][D] of the operands' dtype")
+    _check(library().qkv_projection_head_sharded(x.data_ptr(), w.data_ptr(), out.data_ptr(), S, K, P, B, H, D,
+                                                 _dt(x), _stream(x)))
+    return out
 
 
 def copy(src: torch.Tensor, dst: torch.Tensor) -> torch.Tensor:

@@ -17,7 +17,7 @@ from pathlib import Path
 PKG = Path(__file__).resolve().parent
 CSRC = PKG / "csrc"
 LIB = PKG / "libcam.so"
-SOURCES = ["cam_api.cpp", "thd_planner.cpp", "relayout.hip", "lse.hip"]
+SOURCES = ["cam_api.cpp", "thd_planner.cpp", "relayout.hip", "lse.hip", "proj.hip"]
 ARCH = "gfx950"
 
 

@@ -1053,6 +1053,56 @@ cam_status lse_merge(float* acc_out, int64_t a_st, int64_t a_sh, float* acc_lse,
     return launch_merge(a, stream);
 }
 
+cam_status qkv_projection_head_sharded(const void* x, const void* w, void* out, int64_t S, int64_t K, int64_t P,
+                                       int64_t B, int64_t H, int64_t D, cam_dtype dt, void* stream)
+{
+    const char* op = "qkv_projection_head_sharded";
+    clear_error();
+    if (S < 0 || K < 0 || P < 1 || B < 0 || H < 0 || D < 0)
+        return set_error(CAM_ERR_SHAPE, "%s: need P >= 1 and S, K, B, H, D >= 0", op);
+    if (dt != CAM_BF16 && dt != CAM_FP16)
+        return set_error(CAM_ERR_UNSUPPORTED, "%s: operands must be bf16 or fp16", op);
+    if (H % P)
+        return set_error(CAM_ERR_DIVISIBILITY, "%s: H (%lld) must be a multiple of P (%lld)", op, (long long)H,
+                         (long long)P);
+    int64_t N, xb, wb, ob;
+    if (!prod_ok({B, H, D}, &N) || !prod_ok({S, K, 2}, &xb) || !prod_ok({N, K, 2}, &wb) || !prod_ok({S, N, 2}, &ob))
+        return set_error(CAM_ERR_SHAPE, "%s: sizes overflow", op);
+    if (S == 0 || N == 0)
+        return CAM_OK;
+    if (K == 0 || K % 64 || N % 256)
+        return set_error(CAM_ERR_UNSUPPORTED, "%s: needs K a positive multiple of 64 and B*H*D a multiple of 256", op);
+    if (S > INT32_MAX || N > INT32_MAX || K > INT32_MAX)
+        return set_error(CAM_ERR_UNSUPPORTED, "%s: S, K and B*H*D must be below 2^31", op);
+    if (!x || !w || !out)
+        return set_error(CAM_ERR_NULL, "%s: x, w and out must be non-null", op);
+    if (!aligned(x, 16) || !aligned(w, 16) || !aligned(out, 2))
+        return set_error(CAM_ERR_ALIGNMENT, "%s: x and w must be 16-byte aligned, out 2-byte aligned", op);
+    if (overlaps(out, ob, x, xb) || overlaps(out, ob, w, wb))
+        return set_error(CAM_ERR_OVERLAP, "%s: out overlaps an operand", op);
+    Proj a{};
+    a.x = x;
+    a.w = w;
+    a.out = out;
+    a.M = uint32_t(S);
+    a.K = uint32_t(K);
+    a.S = uint32_t(S);
+    a.B = uint32_t(B);
+    a.HD = uint32_t(H * D);
+    a.HpD = uint32_t((H / P) * D);
+    if (a.HpD == 0)
+        return CAM_OK;
+    a.div_HD = make_fastdiv(a.HD);
+    a.div_HpD = make_fastdiv(a.HpD);
+    a.tiles_m = uint32_t((S + 255) / 256);
+    a.tiles_n = uint32_t(N / 256);
+    if (uint64_t(a.tiles_m) * a.tiles_n > (1u << 20))
+        return set_error(CAM_ERR_UNSUPPORTED, "%s: more than 2^20 output tiles", op);
+    a.group_m = CAM_PROJ_GROUP_M;
+    a.fp16 = dt == CAM_FP16;
+    return launch_proj(a, stream);
+}
+
 cam_status cam_copy(const void* src, void* dst, int64_t bytes, void* stream)
 {
     clear_error();

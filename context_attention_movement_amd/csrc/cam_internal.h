@@ -220,6 +220,20 @@ struct CombineBwd {
     int fp16;
 };
 
+// Q/K/V projection into the head-sharded layout: out[r][b][t][h'][d] =
+// sum_k x[t][k] w[(b*H + r*Hp + h')*D + d][k] (MFMA, 256 x 256 tiles).
+struct Proj {
+    const void* x;          // [M = S][K]
+    const void* w;          // [N = B*H*D][K]
+    void* out;              // [P][B][S][Hp][D]
+    uint32_t M, K;
+    uint32_t S, B;
+    uint32_t HD, HpD;       // H*D, (H/P)*D
+    FastDiv div_HD, div_HpD;
+    uint32_t tiles_m, tiles_n, group_m;
+    int fp16;
+};
+
 struct Copy {
     const void* src;
     void* dst;
@@ -235,6 +249,7 @@ cam_status launch_combine(const Combine& a, void* stream);
 cam_status launch_copy(const Copy& a, void* stream);
 cam_status launch_merge(const Merge& a, void* stream);
 cam_status launch_combine_bwd(const CombineBwd& a, void* stream);
+cam_status launch_proj(const Proj& a, void* stream);
 
 // Error reporting shared by the host layer and the launchers.
 cam_status set_error(cam_status s, const char* fmt, ...);
@@ -277,6 +292,11 @@ constexpr int kTileVecs = kThreads * kVecsPerThread;
 #endif
 #ifndef CAM_NT_COMBINE_BWD
 #define CAM_NT_COMBINE_BWD 2
+#endif
+// Projection: row tiles per group of the tile order (column tiles of a
+// group run close together in time and share their weight tiles in cache).
+#ifndef CAM_PROJ_GROUP_M
+#define CAM_PROJ_GROUP_M 8
 #endif
 // Combine gradient tiling: rows per tile for rows of >= 512 bytes and shorter.
 #ifndef CAM_COMBINE_BWD_ROWS_WIDE

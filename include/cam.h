@@ -424,6 +424,26 @@ cam_status lse_combine_planned_backward(const void* part_out, int64_t po_sp, int
                                         int64_t nseq, void* stream);
 
 /* ------------------------------------------------------------------------- */
+/* Q/K/V projection into the head-sharded layout  ([FV] "direct output        */
+/* slices": the producer of the scatter operand writes the destination slices) */
+/* ------------------------------------------------------------------------- */
+/*
+ * qkv_projection_head_sharded: out[r][b][t][h'][d] =
+ *   sum_k x[t][k] * w[(b*H + r*H/P + h')*D + d][k], i.e. the projection x w^T
+ *   written where ulysses_seq_to_head would put it, so that relayout's pass
+ *   over Q/K/V is not needed.
+ *   x [S][K]: the P ranks' sequence shards stacked in token order (rank j's
+ *   rows are j*S/P .. (j+1)*S/P - 1); w [B*H*D][K]: the fused weight in a
+ *   linear layer's layout (rows ordered b, h, d); out [P][B][S][H/P][D]; all
+ *   contiguous, payload dt (bf16 or fp16) for all three.  fp32 accumulation
+ *   on the matrix cores, rounded to dt (RNE).  Requires K a positive multiple
+ *   of 64, B*H*D a multiple of 256, H % P == 0; x and w 16-byte aligned.
+ */
+cam_status qkv_projection_head_sharded(const void* x, const void* w, void* out, int64_t S, int64_t K,
+                                       int64_t P, int64_t B, int64_t H, int64_t D, cam_dtype dt,
+                                       void* stream);
+
+/* ------------------------------------------------------------------------- */
 /* Measurement helper                                                          */
 /* ------------------------------------------------------------------------- */
 /*

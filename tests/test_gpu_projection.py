@@ -1,0 +1,72 @@
+"""GPU parity of the Q/K/V projection written into the head-sharded layout
+(MFMA) against the oracle's double-precision product: every element within
+one unit in the last place of the payload type plus the fp32 accumulation
+bound 2e-5 * sum_k |x_k w_k|; small shapes with a ragged row tile, fp16, and
+the video DiT P = 4 shape on sampled rows (the tail tile included)."""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from helpers import announce, to_host_bits
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def cam():
+    import context_attention_movement_amd as m
+    m.library()
+    assert torch.cuda.is_available()
+    return m
+
+
+def _check(orc, got_bits, x_bits, w_bits, P, B, H, D, dt, what):
+    want = orc.qkv_projection(x_bits, w_bits, P, B, H, D, dt)
+    g = orc.half_bits_to_double(got_bits, dt)
+    o = orc.half_bits_to_double(want, dt)
+    xa = np.abs(orc.half_bits_to_double(x_bits, dt))
+    wa = np.abs(orc.half_bits_to_double(w_bits, dt))
+    S = x_bits.shape[0]
+    sabs = (xa @ wa.T).reshape(S, B, P, H // P, D).transpose(2, 1, 0, 3, 4)
+    ulp = np.abs(o) * (2.0 ** -7 if dt == "bf16" else 2.0 ** -10)
+    err = np.abs(g - o)
+    bad = err > ulp + 2e-5 * sabs
+    assert not np.isnan(g).any(), f"{what}: NaN"
+    assert not bad.any(), f"{what}: {int(bad.sum())} elements out of tolerance, worst {float(err.max())}"
+
+
+CASES = [  # (S, K, P, B, H, D, dtype)
+    (300, 128, 2, 3, 4, 64, "bf16"),
+    (257, 64, 4, 1, 8, 32, "bf16"),      # ragged last row tile
+    (64, 192, 2, 2, 2, 64, "fp16"),
+    (512, 256, 8, 1, 16, 16, "bf16"),    # Hp*D = 32: a 256-column tile spans 8 head blocks
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "S{}K{}P{}B{}H{}D{}{}".format(*c))
+def test_projection(cam, orc, case):
+    S, K, P, B, H, D, dt = case
+    announce(f"projection {case}")
+    x = synth.normal((S, K), seed=S + K, dtype=dt)
+    w = synth.normal((B * H * D, K), seed=S + K + 1, std=0.05, dtype=dt)
+    out = cam.qkv_projection_head_sharded(x.cuda(), w.cuda(), P, B, H, D)
+    torch.cuda.synchronize()
+    _check(orc, to_host_bits(out), synth.bits(x), synth.bits(w), P, B, H, D, dt, str(case))
+
+
+def test_projection_video_shape_sampled_rows(cam, orc):
+    """Video DiT P = 4: S = 32760 (127 full row tiles and a ragged one),
+    K = 3072, Q/K/V of 24 heads x 128; sampled token rows."""
+    S, K, P, B, H, D = 32760, 3072, 4, 3, 24, 128
+    announce("projection video shape")
+    g = synth._gen(synth.BASE_SEED + 92, "cuda")
+    x = torch.randn((S, K), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    w = (torch.randn((B * H * D, K), generator=g, device="cuda", dtype=torch.float32) * 0.02).to(torch.bfloat16)
+    out = cam.qkv_projection_head_sharded(x, w, P, B, H, D)
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 255, 256, 8191, 8192, 16380, 24571, 32511, 32512, 32759])
+    xs = to_host_bits(x[torch.from_numpy(rows).cuda()])
+    got = to_host_bits(out[:, :, torch.from_numpy(rows).cuda()])
+    _check(orc, got, xs, to_host_bits(w), P, B, H, D, "bf16", "video rows")

@@ -32,7 +32,7 @@ def test_matches_library_product_and_closed_form(orc, S, K, P, B, H, D, dt):
         # the same values produced in the sequence-sharded layout, then relaid
         stacked = rounded.reshape(P, S // P, B, H, D).transpose(0, 2, 1, 3, 4)   # [P][B][S/P][H][D]
         relaid = orc.seq_to_head(np.ascontiguousarray(stacked), P, B, S, H, D)
-        assert np.array_equal(relaid, got)
+        assert np.array_equal(relaid, want)
 
 
 def test_brute_force_tiny(orc):
