@@ -1099,6 +1099,7 @@ cam_status qkv_projection_head_sharded(const void* x, const void* w, void* out, 
     if (uint64_t(a.tiles_m) * a.tiles_n > (1u << 20))
         return set_error(CAM_ERR_UNSUPPORTED, "%s: more than 2^20 output tiles", op);
     a.group_m = CAM_PROJ_GROUP_M;
+    a.vec_out = (CAM_PROJ_VEC_OUT && a.HpD % 8 == 0 && aligned(out, 16)) ? 1 : 0;
     a.fp16 = dt == CAM_FP16;
     return launch_proj(a, stream);
 }

@@ -231,6 +231,7 @@ struct Proj {
     uint32_t HD, HpD;       // H*D, (H/P)*D
     FastDiv div_HD, div_HpD;
     uint32_t tiles_m, tiles_n, group_m;
+    int vec_out;            // 1: 16-byte output segments through LDS ((H/P)*D % 8 == 0, out 16-byte aligned)
     int fp16;
 };
 
@@ -296,7 +297,16 @@ constexpr int kTileVecs = kThreads * kVecsPerThread;
 // Projection: row tiles per group of the tile order (column tiles of a
 // group run close together in time and share their weight tiles in cache).
 #ifndef CAM_PROJ_GROUP_M
-#define CAM_PROJ_GROUP_M 8
+#define CAM_PROJ_GROUP_M 32
+#endif
+// Projection epilogue: 16-byte output segments staged through LDS (1) or
+// one 2-byte store per accumulator element (0)
+// Projection LDS swizzle: chunk position XOR ((row >> shift) % 8)
+#ifndef CAM_PROJ_SWZ_SHIFT
+#define CAM_PROJ_SWZ_SHIFT 1
+#endif
+#ifndef CAM_PROJ_VEC_OUT
+#define CAM_PROJ_VEC_OUT 1
 #endif
 // Combine gradient tiling: rows per tile for rows of >= 512 bytes and shorter.
 #ifndef CAM_COMBINE_BWD_ROWS_WIDE
