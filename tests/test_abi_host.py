@@ -284,3 +284,16 @@ def test_planned_combine_rejections(lib):
     assert f(*args(cu=None)) == NULL
     assert f(*args(fp=FP + 2)) == ALIGN
     assert f(*args(out=FP)) == OVERLAP
+
+
+def test_projection_rejections(lib):
+    f = lib.qkv_projection_head_sharded
+    X, W, O = A, A + 0x1000_0000, A + 0x2000_0000
+    assert f(X, W, O, 100, 96, 2, 1, 4, 64, BF16, None) == UNSUP       # K not a multiple of 64
+    assert f(X, W, O, 100, 64, 2, 1, 3, 32, BF16, None) == DIV          # H % P
+    assert f(X, W, O, 100, 64, 2, 1, 2, 64, BF16, None) == UNSUP        # N = 128 not a multiple of 256
+    assert f(X, W, O, 100, 64, 2, 1, 4, 64, FP32, None) == UNSUP
+    assert f(X + 8, W, O, 100, 64, 2, 1, 4, 64, BF16, None) == ALIGN
+    assert f(None, W, O, 100, 64, 2, 1, 4, 64, BF16, None) == NULL
+    assert f(X, W, X + 64, 100, 64, 2, 1, 4, 64, BF16, None) == OVERLAP
+    assert f(X, W, O, 0, 64, 2, 1, 4, 64, BF16, None) == OK              # nothing to do
