@@ -34,6 +34,11 @@ constexpr int kCPitch = kPN + 8;
 constexpr int kPLds = (2 * kPStage > kPM * kCPitch * 2) ? 2 * kPStage : kPM * kCPitch * 2;
 // waves per workgroup along M and N: 2 x 4, each wave a 128 x 64 sub-tile
 // (4 x 2 measures the same within noise; 2 x 2, one wave per SIMD, slower)
+// interleave the next k slice's LDS reads with this slice's MFMAs in the
+// schedule (1) or leave the order to the compiler (0)
+#ifndef CAM_PROJ_INTERLEAVE
+#define CAM_PROJ_INTERLEAVE 1
+#endif
 #ifndef CAM_PROJ_WAVES_M
 #define CAM_PROJ_WAVES_M 2
 #endif
@@ -156,6 +161,16 @@ __global__ __launch_bounds__(kPThreads) void k_proj_direct(Proj a)
 #pragma unroll
                 for (int j = 0; j < kPTN; ++j)
                     acc[i][j] = mfma_32x32x16<FP16>(fa[set][i], fb[set][j], acc[i][j]);
+#if CAM_PROJ_INTERLEAVE
+            // spread the next slice's LDS reads between this slice's MFMAs
+            if (ks + 1 < kPK / 16) {
+#pragma unroll
+                for (int u = 0; u < kPTM + kPTN; ++u) {
+                    __builtin_amdgcn_sched_group_barrier(0x0008, (kPTM * kPTN) / (kPTM + kPTN) > 0 ? (kPTM * kPTN) / (kPTM + kPTN) : 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x0100, 1, 0);
+                }
+            }
+#endif
         }
         __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of the next stage have landed
         __syncthreads();                // and everyone's; the current stage is free
