@@ -157,6 +157,29 @@ __device__ __forceinline__ bool causal_piece_ok(const int32_t* cu, int32_t nseq,
     return start < end && int64_t(start) <= k;
 }
 
+// Causal admission under a THD layout plan: partial p (rank p's KV) is
+// admitted for the token at position k of sequence i iff rank p holds a
+// position of sequence i at or before k, first[p][i] <= k (INT32_MAX when it
+// holds none of the sequence).
+__device__ __forceinline__ bool causal_span_ok(const int32_t* cu, int32_t nseq, const int32_t* first, uint32_t p,
+                                               uint32_t t)
+{
+    const int32_t i = seq_of_token(cu, nseq, t);
+    const int64_t c0 = cu[i];
+    const int64_t k = int64_t(t) - c0;
+    if (k < 0 || k >= int64_t(cu[i + 1]) - c0)
+        return false;
+    return int64_t(first[int64_t(p) * nseq + i]) <= k;
+}
+
+// Causal admission of partial p for token t: the plan's rule when a first-
+// position table is given, else the per-sequence piece rule.
+template <typename Rec>
+__device__ __forceinline__ bool admitted_partial(const Rec& a, const int32_t* cu, uint32_t p, uint32_t t)
+{
+    return a.first ? causal_span_ok(cu, a.nseq, a.first, p, t) : causal_piece_ok(cu, a.nseq, a.div_P, p, t);
+}
+
 // Rank-major (sequence-sharded) row of token t of a packed THD batch: the
 // row of the varlen relayout's sequence side for B = 1.
 __device__ __forceinline__ int64_t varlen_token_row(const int32_t* cu, const Combine& a, uint32_t t)
@@ -248,8 +271,7 @@ __global__ __launch_bounds__(kThreads) void k_combine(Combine a)
                 bool admitted = true;
                 if (VARLEN)
                     // the two calls differ only in the address space of the table
-                    admitted = cached ? causal_piece_ok(cu_lds, a.nseq, a.div_P, sp, t)
-                                      : causal_piece_ok(a.cu, a.nseq, a.div_P, sp, t);
+                    admitted = cached ? admitted_partial(a, cu_lds, sp, t) : admitted_partial(a, a.cu, sp, t);
                 if (admitted) {
                     L = a.pl[int64_t(sp) * a.pl_sp + int64_t(t) * a.pl_st + int64_t(h) * a.pl_sh];
                     valid = __builtin_isfinite(L);
@@ -417,7 +439,7 @@ __device__ __forceinline__ float row_stat(const Combine& a, uint64_t row, uint32
         return -__builtin_inff();
     const uint32_t t = fdiv(uint32_t(row), a.div_H);
     const uint32_t h = uint32_t(row) - t * a.H;
-    if (VARLEN && !causal_piece_ok(a.cu, a.nseq, a.div_P, lane, t))
+    if (VARLEN && !admitted_partial(a, a.cu, lane, t))
         return -__builtin_inff();
     return a.pl[int64_t(lane) * a.pl_sp + int64_t(t) * a.pl_st + int64_t(h) * a.pl_sh];
 }
@@ -658,8 +680,7 @@ __global__ __launch_bounds__(kThreads) void k_combine_bwd(CombineBwd a)
             if (live && sp < a.P) {
                 bool admitted = true;
                 if (VARLEN)
-                    admitted = cached ? causal_piece_ok(cu_lds, a.nseq, a.div_P, sp, t)
-                                      : causal_piece_ok(a.cu, a.nseq, a.div_P, sp, t);
+                    admitted = cached ? admitted_partial(a, cu_lds, sp, t) : admitted_partial(a, a.cu, sp, t);
                 if (admitted) {
                     L = a.pl[int64_t(sp) * a.pl_sp + int64_t(t) * a.pl_st + int64_t(h) * a.pl_sh];
                     valid = __builtin_isfinite(L);
