@@ -212,12 +212,12 @@ class Workload:
             ("relayout_head_to_seq_video_p4_o", "k_dense_relayout<16, false>",
              lambda: cam.ulysses_head_to_seq(self.v_o, self.vP, out=self.v_o_out)),
             ("lse_pack_mla", "k_pack<16>", pack),
-            ("lse_combine_mla", "k_combine_stream<16, false, false, 0>", combine),
+            ("lse_combine_mla", "k_combine_stream<16, false, 0, 0>", combine),
             ("relayout_seq_to_head_varlen_thd_qkv", "k_varlen_relayout<16, true, false>",
              lambda: cam.ulysses_seq_to_head_varlen(self.t_qkv, self.t_plan, 3, out=self.t_qkv_out)),
             ("relayout_head_to_seq_varlen_thd_o", "k_varlen_relayout<16, false, false>",
              lambda: cam.ulysses_head_to_seq_varlen(self.t_o, self.t_plan, out=self.t_o_out)),
-            ("lse_combine_varlen_thd", "k_combine<16, false, true, 1, false, 0>",
+            ("lse_combine_varlen_thd", "k_combine<16, false, 1, 1, false, 0>",
              lambda: cam.lse_combine_varlen(self.t_part, self.t_lse, self.t_cu_dev, out=self.t_comb,
                                             lse_out=self.t_comb_lse)),
         ]

@@ -172,12 +172,17 @@ __device__ __forceinline__ bool causal_span_ok(const int32_t* cu, int32_t nseq, 
     return int64_t(first[int64_t(p) * nseq + i]) <= k;
 }
 
-// Causal admission of partial p for token t: the plan's rule when a first-
-// position table is given, else the per-sequence piece rule.
-template <typename Rec>
+// Which partials a token admits (a kernel template parameter, so each rule
+// is its own kernel): every partial, the per-sequence piece rule over
+// cu_seqlens, or a THD layout plan's first-position rule.
+enum Causal : int { kAll = 0, kPieces = 1, kPlan = 2 };
+
+template <int CZ, typename Rec>
 __device__ __forceinline__ bool admitted_partial(const Rec& a, const int32_t* cu, uint32_t p, uint32_t t)
 {
-    return a.first ? causal_span_ok(cu, a.nseq, a.first, p, t) : causal_piece_ok(cu, a.nseq, a.div_P, p, t);
+    if (CZ == kPlan)
+        return causal_span_ok(cu, a.nseq, a.first, p, t);
+    return causal_piece_ok(cu, a.nseq, a.div_P, p, t);
 }
 
 // Rank-major (sequence-sharded) row of token t of a packed THD batch: the
@@ -216,7 +221,7 @@ __device__ __forceinline__ uint64_t uniform64(uint64_t x)
 // per-row quantity of phase 2 is wave-uniform and is kept in scalar registers.
 // OM: where the combined rows go -- 0 at the caller's strides, 1 token-major
 // (head-scattered rows of the exchange), 2 rank-major (varlen sequence shards).
-template <int W, bool FP16, bool VARLEN, int RF, bool WAVE, int OM>
+template <int W, bool FP16, int CZ, int RF, bool WAVE, int OM>
 __global__ __launch_bounds__(kThreads) void k_combine(Combine a)
 {
     typedef typename VecOf<W>::type V;
@@ -231,7 +236,7 @@ __global__ __launch_bounds__(kThreads) void k_combine(Combine a)
     int64_t* o_lds = reinterpret_cast<int64_t*>(m_lds + RB);               // RB: output row offsets
     float* iz_lds = reinterpret_cast<float*>(o_lds + RB);                  // RB
     int32_t* cu_lds = reinterpret_cast<int32_t*>(iz_lds + RB);             // nseq + 1 (varlen)
-    const bool cached = VARLEN && a.nseq < kCuCache;
+    const bool cached = CZ != kAll && a.nseq < kCuCache;
     if (cached)  // visible after the barrier that opens every tile
         for (uint32_t i = threadIdx.x; i <= uint32_t(a.nseq); i += blockDim.x)
             cu_lds[i] = a.cu[i];
@@ -269,9 +274,9 @@ __global__ __launch_bounds__(kThreads) void k_combine(Combine a)
             float L = -__builtin_inff();
             if (live && sp < a.P) {
                 bool admitted = true;
-                if (VARLEN)
+                if (CZ != kAll)
                     // the two calls differ only in the address space of the table
-                    admitted = cached ? admitted_partial(a, cu_lds, sp, t) : admitted_partial(a, a.cu, sp, t);
+                    admitted = cached ? admitted_partial<CZ>(a, cu_lds, sp, t) : admitted_partial<CZ>(a, a.cu, sp, t);
                 if (admitted) {
                     L = a.pl[int64_t(sp) * a.pl_sp + int64_t(t) * a.pl_st + int64_t(h) * a.pl_sh];
                     valid = __builtin_isfinite(L);
@@ -432,19 +437,19 @@ __device__ __forceinline__ float wave_sum(float v)
     return v;
 }
 
-template <bool VARLEN>
+template <int CZ>
 __device__ __forceinline__ float row_stat(const Combine& a, uint64_t row, uint32_t lane)
 {
     if (row >= a.n_rows || lane >= a.P)
         return -__builtin_inff();
     const uint32_t t = fdiv(uint32_t(row), a.div_H);
     const uint32_t h = uint32_t(row) - t * a.H;
-    if (VARLEN && !admitted_partial(a, a.cu, lane, t))
+    if (CZ != kAll && !admitted_partial<CZ>(a, a.cu, lane, t))
         return -__builtin_inff();
     return a.pl[int64_t(lane) * a.pl_sp + int64_t(t) * a.pl_st + int64_t(h) * a.pl_sh];
 }
 
-template <int W, bool FP16, bool VARLEN, int OM>
+template <int W, bool FP16, int CZ, int OM>
 __global__ __launch_bounds__(kThreads) void k_combine_stream(Combine a)
 {
     typedef typename VecOf<W>::type V;
@@ -456,10 +461,10 @@ __global__ __launch_bounds__(kThreads) void k_combine_stream(Combine a)
     const uint64_t blk = a.xcd ? xcd_first(blockIdx.x, gridDim.x) : blockIdx.x;
     const uint64_t n_waves = uint64_t(gridDim.x) * wpb;
     uint64_t row = blk * wpb + uniform32(threadIdx.x >> 6);
-    float L_next = row_stat<VARLEN>(a, row, lane);
+    float L_next = row_stat<CZ>(a, row, lane);
     for (; row < a.n_rows; row += n_waves) {
         const float L = L_next;
-        L_next = row_stat<VARLEN>(a, row + n_waves, lane);  // in flight during this row
+        L_next = row_stat<CZ>(a, row + n_waves, lane);  // in flight during this row
         const uint32_t t = fdiv(uint32_t(row), a.div_H);
         const uint32_t h = uint32_t(row) - t * a.H;
         const bool valid = __builtin_isfinite(L);
@@ -632,7 +637,7 @@ cam_status launch_merge(const Merge& a, void* stream)
 // partial, zero for those outside the valid set.  Phase 3 forms
 // dL_p = w_p (<g, O_p> - sum_q w_q <g, O_q> + g_lse) on the statistics lanes.
 // As in the forward, an invalid or masked partial's O row is never read.
-template <int W, bool FP16, bool VARLEN>
+template <int W, bool FP16, int CZ>
 __global__ __launch_bounds__(kThreads) void k_combine_bwd(CombineBwd a)
 {
     typedef typename VecOf<W>::type V;
@@ -646,7 +651,7 @@ __global__ __launch_bounds__(kThreads) void k_combine_bwd(CombineBwd a)
     float* gl_lds = d_lds + RB * a.P;                                          // RB  g_lse
     uint64_t* m_lds = reinterpret_cast<uint64_t*>(gl_lds + ((RB + 1) & ~1u));  // RB  validity masks
     int32_t* cu_lds = reinterpret_cast<int32_t*>(m_lds + RB);                  // nseq + 1 (varlen)
-    const bool cached = VARLEN && a.nseq < kCuCache;
+    const bool cached = CZ != kAll && a.nseq < kCuCache;
     if (cached)
         for (uint32_t i = threadIdx.x; i <= uint32_t(a.nseq); i += kThreads)
             cu_lds[i] = a.cu[i];
@@ -679,8 +684,8 @@ __global__ __launch_bounds__(kThreads) void k_combine_bwd(CombineBwd a)
             float L = -__builtin_inff();
             if (live && sp < a.P) {
                 bool admitted = true;
-                if (VARLEN)
-                    admitted = cached ? admitted_partial(a, cu_lds, sp, t) : admitted_partial(a, a.cu, sp, t);
+                if (CZ != kAll)
+                    admitted = cached ? admitted_partial<CZ>(a, cu_lds, sp, t) : admitted_partial<CZ>(a, a.cu, sp, t);
                 if (admitted) {
                     L = a.pl[int64_t(sp) * a.pl_sp + int64_t(t) * a.pl_st + int64_t(h) * a.pl_sh];
                     valid = __builtin_isfinite(L);
@@ -806,15 +811,34 @@ __global__ __launch_bounds__(kThreads) void k_combine_bwd(CombineBwd a)
     }
 }
 
+template <typename K>
+const void* fn_ptr(K* k)
+{
+    return reinterpret_cast<const void*>(k);
+}
+
+// The admission rule of a launch record: none, the piece rule, or a plan's.
+template <typename Rec>
+int causal_rule(const Rec& a)
+{
+    return !a.cu ? kAll : a.first ? kPlan : kPieces;
+}
+
+template <int W, bool FP16>
+const void* pick_combine_bwd(int cz)
+{
+    return cz == kPlan ? fn_ptr(&k_combine_bwd<W, FP16, kPlan>)
+           : cz == kPieces ? fn_ptr(&k_combine_bwd<W, FP16, kPieces>)
+                           : fn_ptr(&k_combine_bwd<W, FP16, kAll>);
+}
+
 cam_status launch_combine_bwd(const CombineBwd& a, void* stream)
 {
+    const int cz = causal_rule(a);
     const void* fn = nullptr;
-#define CAM_PICK_BWD(Wd)                                                                               \
-    if (a.width == Wd)                                                                                 \
-        fn = a.cu ? (a.fp16 ? reinterpret_cast<const void*>(&k_combine_bwd<Wd, true, true>)           \
-                            : reinterpret_cast<const void*>(&k_combine_bwd<Wd, false, true>))         \
-                  : (a.fp16 ? reinterpret_cast<const void*>(&k_combine_bwd<Wd, true, false>)          \
-                            : reinterpret_cast<const void*>(&k_combine_bwd<Wd, false, false>));
+#define CAM_PICK_BWD(Wd)                                                                                \
+    if (a.width == Wd)                                                                                  \
+        fn = a.fp16 ? pick_combine_bwd<Wd, true>(cz) : pick_combine_bwd<Wd, false>(cz);
     CAM_PICK_BWD(16) CAM_PICK_BWD(8) CAM_PICK_BWD(4) CAM_PICK_BWD(2)
 #undef CAM_PICK_BWD
     uint64_t lds = (2ull * a.rows_per_tile * a.P + ((a.rows_per_tile + 1) & ~1u)) * 4 + uint64_t(a.rows_per_tile) * 8;
@@ -823,54 +847,61 @@ cam_status launch_combine_bwd(const CombineBwd& a, void* stream)
     return launch(fn, a, a.n_tiles, stream, "lse_combine_backward", lds, kThreads);
 }
 
+// The output modes each admission rule is built for: every rule writes at
+// the caller's strides; the token-major exchange layout (1) has no causal
+// rule; the rank-major varlen shards (2) follow the piece rule.
+template <int W, bool FP16, int RF, bool WV>
+const void* pick_combine_tiled(int cz, int om)
+{
+    if (cz == kAll)
+        return om == 1 ? fn_ptr(&k_combine<W, FP16, kAll, RF, WV, 1>)
+               : om == 0 ? fn_ptr(&k_combine<W, FP16, kAll, RF, WV, 0>) : nullptr;
+    if (cz == kPieces)
+        return om == 2 ? fn_ptr(&k_combine<W, FP16, kPieces, RF, WV, 2>)
+               : om == 0 ? fn_ptr(&k_combine<W, FP16, kPieces, RF, WV, 0>) : nullptr;
+    return om == 0 ? fn_ptr(&k_combine<W, FP16, kPlan, RF, WV, 0>) : nullptr;
+}
+
+template <int W, bool FP16>
+const void* pick_combine_stream(int cz, int om)
+{
+    if (cz == kAll)
+        return om == 1 ? fn_ptr(&k_combine_stream<W, FP16, kAll, 1>)
+               : om == 0 ? fn_ptr(&k_combine_stream<W, FP16, kAll, 0>) : nullptr;
+    if (cz == kPieces)
+        return om == 2 ? fn_ptr(&k_combine_stream<W, FP16, kPieces, 2>)
+               : om == 0 ? fn_ptr(&k_combine_stream<W, FP16, kPieces, 0>) : nullptr;
+    return om == 0 ? fn_ptr(&k_combine_stream<W, FP16, kPlan, 0>) : nullptr;
+}
+
+// Rows of at least 512 bytes (one or more full 64-lane passes) keep two rows
+// in flight per lane group; shorter rows, packed several per wave, keep one
+// (the lower register count buys occupancy) -- measured on MI355X.  Rows of
+// a whole wave or more take the LDS-free row-stream kernel.
+template <int W, bool FP16>
+const void* pick_combine(int cz, int om, bool wide, bool wave)
+{
+    if (wave)
+        return CAM_COMBINE_STREAM ? pick_combine_stream<W, FP16>(cz, om)
+                                  : pick_combine_tiled<W, FP16, kCombineInFlightWave, true>(cz, om);
+    return wide ? pick_combine_tiled<W, FP16, 2, false>(cz, om) : pick_combine_tiled<W, FP16, 1, false>(cz, om);
+}
+
 cam_status launch_combine(const Combine& a, void* stream)
 {
-    // Rows of at least 512 bytes (one or more full 64-lane passes) keep two
-    // rows in flight per lane group; shorter rows, packed several per wave,
-    // keep one (the lower register count buys occupancy) -- measured on MI355X.
     const bool wide = uint64_t(a.cv) * a.width >= 512;
     const bool wave = a.g_log2 == 6;  // a whole wave per row (implies wide)
+    const int cz = causal_rule(a);
     const void* fn = nullptr;
-#define CAM_PICK(Wd, RFv, WV)                                                                          \
-    if (a.width == Wd && wave == WV && (WV || wide == (RFv == 2))) {                                   \
-        if (a.cu)                                                                                      \
-            fn = a.out_mode == 2                                                                       \
-                     ? (a.fp16 ? reinterpret_cast<const void*>(&k_combine<Wd, true, true, RFv, WV, 2>)  \
-                               : reinterpret_cast<const void*>(&k_combine<Wd, false, true, RFv, WV, 2>)) \
-                     : (a.fp16 ? reinterpret_cast<const void*>(&k_combine<Wd, true, true, RFv, WV, 0>)  \
-                               : reinterpret_cast<const void*>(&k_combine<Wd, false, true, RFv, WV, 0>)); \
-        else                                                                                           \
-            fn = a.out_mode == 1                                                                       \
-                     ? (a.fp16 ? reinterpret_cast<const void*>(&k_combine<Wd, true, false, RFv, WV, 1>) \
-                               : reinterpret_cast<const void*>(&k_combine<Wd, false, false, RFv, WV, 1>)) \
-                     : (a.fp16 ? reinterpret_cast<const void*>(&k_combine<Wd, true, false, RFv, WV, 0>) \
-                               : reinterpret_cast<const void*>(&k_combine<Wd, false, false, RFv, WV, 0>)); \
-    }
-    if ((a.out_mode == 1 && a.cu) || (a.out_mode == 2 && !a.cu) || a.out_mode > 2)
-        return CAM_ERR_UNSUPPORTED;
-    CAM_PICK(16, 1, false) CAM_PICK(8, 1, false) CAM_PICK(4, 1, false) CAM_PICK(2, 1, false)
-    CAM_PICK(16, 2, false) CAM_PICK(8, 2, false) CAM_PICK(4, 2, false) CAM_PICK(2, 2, false)
-    CAM_PICK(16, kCombineInFlightWave, true) CAM_PICK(8, kCombineInFlightWave, true)
-    CAM_PICK(4, kCombineInFlightWave, true) CAM_PICK(2, kCombineInFlightWave, true)
+#define CAM_PICK(Wd)                                                                                   \
+    if (a.width == Wd)                                                                                 \
+        fn = a.fp16 ? pick_combine<Wd, true>(cz, a.out_mode, wide, wave)                               \
+                    : pick_combine<Wd, false>(cz, a.out_mode, wide, wave);
+    CAM_PICK(16) CAM_PICK(8) CAM_PICK(4) CAM_PICK(2)
 #undef CAM_PICK
+    if (!fn)
+        return CAM_ERR_UNSUPPORTED;
     if (wave && CAM_COMBINE_STREAM) {
-#define CAM_PICK_STREAM(Wd)                                                                                \
-        if (a.width == Wd) {                                                                               \
-            if (a.cu)                                                                                      \
-                fn = a.out_mode == 2                                                                       \
-                         ? (a.fp16 ? reinterpret_cast<const void*>(&k_combine_stream<Wd, true, true, 2>)    \
-                                   : reinterpret_cast<const void*>(&k_combine_stream<Wd, false, true, 2>))  \
-                         : (a.fp16 ? reinterpret_cast<const void*>(&k_combine_stream<Wd, true, true, 0>)    \
-                                   : reinterpret_cast<const void*>(&k_combine_stream<Wd, false, true, 0>)); \
-            else                                                                                           \
-                fn = a.out_mode == 1                                                                       \
-                         ? (a.fp16 ? reinterpret_cast<const void*>(&k_combine_stream<Wd, true, false, 1>)   \
-                                   : reinterpret_cast<const void*>(&k_combine_stream<Wd, false, false, 1>)) \
-                         : (a.fp16 ? reinterpret_cast<const void*>(&k_combine_stream<Wd, true, false, 0>)   \
-                                   : reinterpret_cast<const void*>(&k_combine_stream<Wd, false, false, 0>)); \
-        }
-        CAM_PICK_STREAM(16) CAM_PICK_STREAM(8) CAM_PICK_STREAM(4) CAM_PICK_STREAM(2)
-#undef CAM_PICK_STREAM
         const uint64_t waves = (a.n_rows + CAM_COMBINE_STREAM_ROWS - 1) / CAM_COMBINE_STREAM_ROWS;
         const uint32_t wpb = CAM_COMBINE_STREAM_THREADS / 64;
         return launch(fn, a, (waves + wpb - 1) / wpb, stream, "lse_combine", 0, CAM_COMBINE_STREAM_THREADS);

@@ -20,6 +20,8 @@
 // output row segment at its head-sharded address.
 #include "cam_device.h"
 
+#include <type_traits>
+
 namespace cam {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -126,7 +128,7 @@ __global__ __launch_bounds__(kPThreads) void k_proj_direct(Proj a)
             for (int e = 0; e < 16; ++e)
                 acc[i][j][e] = 0.0f;
 
-    const uint32_t nk = a.K / kPK;
+    const uint32_t nk = a.K / kPK;  // >= 1: the host admits K a positive multiple of 64
     issue(0, 0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -144,18 +146,30 @@ __global__ __launch_bounds__(kPThreads) void k_proj_direct(Proj a)
         for (int j = 0; j < kPTN; ++j)
             fb[set][j] = *reinterpret_cast<const u32x4*>(sb + swz(brow + j * 32, c));
     };
-    for (uint32_t kt = 0; kt < nk; ++kt) {
+    // One K step: the next step's operands are requested first; the barrier
+    // that hands the next stage over sits before the last slice's MFMAs, so
+    // the next stage's first fragments are read while those MFMAs run.  The
+    // last step (LAST) requests and reads nothing more; keeping it a separate
+    // copy of the body leaves no join in the loop where the compiler would
+    // wait for reads that are not needed yet.
+    auto step = [&](uint32_t kt, auto last_tag) {
+        constexpr bool LAST = decltype(last_tag)::value;
         const uint32_t cur = kt & 1u;
-        if (kt + 1 < nk)
+        if (!LAST)
             issue(kt + 1, cur ^ 1u);
         const char* sa = lds + cur * kPStage;
         const char* sb = sa + kPM * kPK * 2;
-        frag(sa, sb, 0, 0);
 #pragma unroll
         for (uint32_t ks = 0; ks < kPK / 16; ++ks) {
             const int set = int(ks & 1u);
-            if (ks + 1 < kPK / 16)
+            if (ks + 1 < kPK / 16) {
                 frag(sa, sb, ks + 1, set ^ 1);
+            } else if (!LAST) {
+                __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of the next stage have landed
+                __syncthreads();                // and everyone's; every read of this stage is done
+                const char* na = lds + (cur ^ 1u) * kPStage;
+                frag(na, na + kPM * kPK * 2, 0, set ^ 1);
+            }
 #pragma unroll
             for (int i = 0; i < kPTM; ++i)
 #pragma unroll
@@ -172,9 +186,12 @@ __global__ __launch_bounds__(kPThreads) void k_proj_direct(Proj a)
             }
 #endif
         }
-        __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of the next stage have landed
-        __syncthreads();                // and everyone's; the current stage is free
-    }
+    };
+    frag(lds, lds + kPM * kPK * 2, 0, 0);
+    for (uint32_t kt = 0; kt + 1 < nk; ++kt)
+        step(kt, std::false_type{});
+    step(nk - 1, std::true_type{});
+    __syncthreads();  // every wave's MFMAs are done with LDS before the epilogue reuses it
 
     uint16_t* out = static_cast<uint16_t*>(a.out);
     if (a.vec_out) {
