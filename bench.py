@@ -173,6 +173,27 @@ class Workload:
         self.step_index = 0
         torch.cuda.synchronize()
 
+    def input_digests(self):
+        """SHA-256 (first 16 hex digits) of every seeded input buffer's shape,
+        dtype and its first and last MiB, read back before the timed steps."""
+        torch = self.torch
+        bufs = {"video_qkv": self.v_qkv, "video_o": self.v_o, "thd_qkv": self.t_qkv, "thd_o": self.t_o,
+                "thd_partials": self.t_part, "thd_partial_lse": self.t_lse, "thd_grad_out": self.t_gout,
+                "proj_x": self.j_x, "proj_w": self.j_w}
+        for i, ms in enumerate(self.m_sets):
+            for key in ("out", "max", "sum"):
+                bufs[f"mla_{key}_set{i}"] = ms[key]
+        out = {"thd_cu_seqlens": hashlib.sha256(self.t_cu.tobytes()).hexdigest()[:16],
+               "planned_thd_cu_seqlens": hashlib.sha256(self.p_cu.tobytes()).hexdigest()[:16]}
+        mib = 1 << 20
+        for name, t in bufs.items():
+            b = t.contiguous().view(torch.uint8).reshape(-1)
+            h = hashlib.sha256(f"{tuple(t.shape)}{t.dtype}".encode())
+            h.update(b[:mib].cpu().numpy().tobytes())
+            h.update(b[max(0, b.numel() - mib):].cpu().numpy().tobytes())
+            out[name] = h.hexdigest()[:16]
+        return out
+
     # algorithmic bytes of each operation
     def op_bytes(self):
         vP, vS, vH, vD = self.vP, self.vS, self.vH, self.vD
@@ -564,6 +585,7 @@ def main():
     torch.cuda.set_device(0)
     props = torch.cuda.get_device_properties(0)
     w = Workload(torch, cam, synth)
+    digests = w.input_digests()
     nbytes = w.op_bytes()
     names = [n for n, _, _ in w.ops()]
     kern = {n: k for n, k, _ in w.ops()}
@@ -748,6 +770,7 @@ def main():
                    "compute_units": props.multi_processor_count,
                    "hbm_GiB": round(props.total_memory / 2**30, 1)},
         "kernel_source_hash": kernel_source_hash(),
+        "inputs_sha256_head_tail_MiB": digests,
         "timing": "value and ms_per_step: host clock around the K synchronized steps; ops[*].us_per_call: "
                   f"{args.calls} back-to-back calls of that operation alone between two HIP events; "
                   "ops[*].in_step_*: HIP events around the operation inside the steps",
