@@ -194,7 +194,7 @@ cam_status dense_relayout(const void* in, void* out, int64_t P, int64_t B, int64
     if (slab_vecs >= kU32Limit)
         return set_error(CAM_ERR_UNSUPPORTED, "%s: one (rank, plane, rank) slab exceeds 2^31 vectors", op);
     a.slab_vecs = uint32_t(slab_vecs);
-    a.tiles_per_slab = tiles(slab_vecs, kTileVecs);
+    a.tiles_per_slab = tiles(slab_vecs, kDenseTileVecs);
     a.div_tps = make_fastdiv(a.tiles_per_slab);
     const uint64_t n_tiles = uint64_t(P) * uint64_t(B) * uint64_t(P) * a.tiles_per_slab;
     if (n_tiles > UINT32_MAX)
@@ -283,7 +283,7 @@ cam_status varlen_relayout(const void* in, void* out, const int32_t* cu, const i
     a.plane_vecs = uint64_t(T) * a.c;
     if (a.plane_vecs >= kU32Limit)
         return set_error(CAM_ERR_UNSUPPORTED, "%s: one (rank, plane) exceeds 2^31 vectors", op);
-    a.tiles_per_plane = tiles(a.plane_vecs, kTileVecs);
+    a.tiles_per_plane = tiles(a.plane_vecs, kVarlenTileVecs);
     a.div_tpp = make_fastdiv(a.tiles_per_plane);
     const uint64_t n_tiles = uint64_t(P) * uint64_t(B) * a.tiles_per_plane;
     if (n_tiles > UINT32_MAX)

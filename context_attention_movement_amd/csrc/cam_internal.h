@@ -263,24 +263,38 @@ void clear_error();
 #define CAM_THREADS 256
 #endif
 constexpr int kThreads = CAM_THREADS;
+// 16-byte vectors each thread moves per tile (its loads all in flight before
+// its stores): the pack and the copy, the dense relayout, the varlen
+// relayout -- chosen per kernel by measurement on MI355X with inputs too
+// large for the Infinity Cache.
 #ifndef CAM_VECS_PER_THREAD
 #define CAM_VECS_PER_THREAD 4
 #endif
 constexpr int kVecsPerThread = CAM_VECS_PER_THREAD;
 constexpr int kTileVecs = kThreads * kVecsPerThread;
+#ifndef CAM_VECS_DENSE
+#define CAM_VECS_DENSE 2
+#endif
+constexpr int kDenseVecs = CAM_VECS_DENSE;
+constexpr int kDenseTileVecs = kThreads * kDenseVecs;
+#ifndef CAM_VECS_VARLEN
+#define CAM_VECS_VARLEN 4
+#endif
+constexpr int kVarlenVecs = CAM_VECS_VARLEN;
+constexpr int kVarlenTileVecs = kThreads * kVarlenVecs;
 // Non-temporal policy per kernel (bit 0: loads, bit 1: stores), chosen by
 // measurement on MI355X.
 #ifndef CAM_NT_SEQ_TO_HEAD
 #define CAM_NT_SEQ_TO_HEAD 3
 #endif
 #ifndef CAM_NT_HEAD_TO_SEQ
-#define CAM_NT_HEAD_TO_SEQ 2
+#define CAM_NT_HEAD_TO_SEQ 3
 #endif
 #ifndef CAM_NT_VARLEN_SEQ_TO_HEAD
 #define CAM_NT_VARLEN_SEQ_TO_HEAD 3
 #endif
 #ifndef CAM_NT_VARLEN_HEAD_TO_SEQ
-#define CAM_NT_VARLEN_HEAD_TO_SEQ 2
+#define CAM_NT_VARLEN_HEAD_TO_SEQ 3
 #endif
 #ifndef CAM_NT_PACK
 #define CAM_NT_PACK 3
@@ -366,8 +380,11 @@ constexpr int kCombineBatchWave = CAM_COMBINE_BATCH_WAVE;
 #ifndef CAM_XCD_HEAD_TO_SEQ
 #define CAM_XCD_HEAD_TO_SEQ 1
 #endif
-#ifndef CAM_XCD_VARLEN
-#define CAM_XCD_VARLEN 0
+#ifndef CAM_XCD_VARLEN_SEQ_TO_HEAD
+#define CAM_XCD_VARLEN_SEQ_TO_HEAD 0
+#endif
+#ifndef CAM_XCD_VARLEN_HEAD_TO_SEQ
+#define CAM_XCD_VARLEN_HEAD_TO_SEQ 1
 #endif
 #ifndef CAM_XCD_PACK
 #define CAM_XCD_PACK 0

@@ -9,28 +9,29 @@
 // (H/P)*D elements that are contiguous on both sides (>= 512 bytes at the
 // workloads here), so every wavefront access is already a coalesced run of
 // 64 x W bytes; nothing needs an LDS transpose.  Each thread moves
-// kVecsPerThread W-byte vectors: all loads are issued before any store so that
-// several 16-byte requests per lane are in flight, which is what keeps HBM3E
-// busy on a streaming kernel.  Work is cut into tiles of kTileVecs vectors
-// inside a slab (dense) or plane (varlen); one division by the run length per
-// vector (a multiply-high) recovers the row, everything else is per tile.
+// a few W-byte vectors (kDenseVecs, kVarlenVecs): all loads are issued before
+// any store so that several 16-byte requests per lane are in flight, which is
+// what keeps HBM3E busy on a streaming kernel.  Work is cut into tiles of
+// kThreads times that many vectors inside a slab (dense) or plane (varlen);
+// one division by the run length per vector (a multiply-high) recovers the
+// row, everything else is per tile.
 #include "cam_device.h"
 
 namespace cam {
 
-// Move one tile of a dense slab: vectors v0 + u*kThreads, u < kVecsPerThread.
+// Move one tile of a dense slab: vectors v0 + u*kThreads, u < kDenseVecs.
 // GUARD = false is the straight-line path for tiles that lie wholly inside the
 // slab: every load is issued before any store and no branch separates them,
-// so each lane keeps kVecsPerThread requests in flight.
+// so each lane keeps kDenseVecs requests in flight.
 template <int W, bool S2H, bool GUARD, int NTP>
 __device__ __forceinline__ void dense_tile(const DenseRelayout& a, uint64_t head_base, uint64_t seq_base,
                                            uint32_t v0)
 {
     typedef typename VecOf<W>::type V;
-    V x[kVecsPerThread];
-    uint64_t dst_off[kVecsPerThread];
+    V x[kDenseVecs];
+    uint64_t dst_off[kDenseVecs];
 #pragma unroll
-    for (int u = 0; u < kVecsPerThread; ++u) {
+    for (int u = 0; u < kDenseVecs; ++u) {
         const uint32_t v = v0 + uint32_t(u * kThreads);
         if (!GUARD || v < a.slab_vecs) {
             const uint32_t s = fdiv(v, a.div_c);
@@ -43,7 +44,7 @@ __device__ __forceinline__ void dense_tile(const DenseRelayout& a, uint64_t head
     }
     issue_fence();
 #pragma unroll
-    for (int u = 0; u < kVecsPerThread; ++u) {
+    for (int u = 0; u < kDenseVecs; ++u) {
         const uint32_t v = v0 + uint32_t(u * kThreads);
         if (!GUARD || v < a.slab_vecs)
             st<W, (NTP & 2) != 0>(a.dst, dst_off[u], x[u]);
@@ -64,9 +65,9 @@ __global__ __launch_bounds__(kThreads) void k_dense_relayout(DenseRelayout a)
         const uint32_t b = rb - r * a.B;
         const uint64_t head_base = uint64_t(slab) * a.slab_vecs;
         const uint64_t seq_base = (uint64_t(j * a.B + b) * a.Sp * a.P + r) * a.c;
-        const uint32_t vt = ti * uint32_t(kTileVecs);
+        const uint32_t vt = ti * uint32_t(kDenseTileVecs);
         constexpr int NTP = S2H ? CAM_NT_SEQ_TO_HEAD : CAM_NT_HEAD_TO_SEQ;
-        if (vt + uint32_t(kTileVecs) <= a.slab_vecs)
+        if (vt + uint32_t(kDenseTileVecs) <= a.slab_vecs)
             dense_tile<W, S2H, false, NTP>(a, head_base, seq_base, vt + threadIdx.x);
         else
             dense_tile<W, S2H, true, NTP>(a, head_base, seq_base, vt + threadIdx.x);
@@ -132,11 +133,11 @@ __device__ __forceinline__ void varlen_tile(const VarlenRelayout& a, const int64
                                             uint32_t vb, uint32_t ve, uint32_t row0)
 {
     typedef typename VecOf<W>::type V;
-    V x[kVecsPerThread];
-    uint64_t dst_off[kVecsPerThread];
-    bool live[kVecsPerThread];
+    V x[kVarlenVecs];
+    uint64_t dst_off[kVarlenVecs];
+    bool live[kVarlenVecs];
 #pragma unroll
-    for (int u = 0; u < kVecsPerThread; ++u) {
+    for (int u = 0; u < kVarlenVecs; ++u) {
         const uint32_t v = vb + threadIdx.x + uint32_t(u * kThreads);
         live[u] = !GUARD || v < ve;
         if (live[u]) {
@@ -154,7 +155,7 @@ __device__ __forceinline__ void varlen_tile(const VarlenRelayout& a, const int64
     }
     issue_fence();
 #pragma unroll
-    for (int u = 0; u < kVecsPerThread; ++u)
+    for (int u = 0; u < kVarlenVecs; ++u)
         if (live[u])
             st<W, (NTP & 2) != 0>(a.dst, dst_off[u], x[u]);
 }
@@ -163,22 +164,23 @@ template <int W, bool S2H, bool SPANS>
 __global__ __launch_bounds__(kThreads) void k_varlen_relayout(VarlenRelayout a)
 {
     // sequence-side offset of every row the tile touches (a tile spans at most
-    // kTileVecs + 1 rows when rows are one vector long)
-    __shared__ int64_t row_off[kTileVecs + 1];
+    // kVarlenTileVecs + 1 rows when rows are one vector long)
+    __shared__ int64_t row_off[kVarlenTileVecs + 1];
     __shared__ int32_t cu_lds[kCuCache];
     const bool cached = a.nseq < kCuCache;
     if (cached)  // visible after the barrier that opens every tile
         for (uint32_t i = threadIdx.x; i <= uint32_t(a.nseq); i += kThreads)
             cu_lds[i] = a.cu[i];
-    const uint32_t first = CAM_XCD_VARLEN ? xcd_first(blockIdx.x, gridDim.x) : blockIdx.x;
+    constexpr bool XCD = S2H ? CAM_XCD_VARLEN_SEQ_TO_HEAD : CAM_XCD_VARLEN_HEAD_TO_SEQ;
+    const uint32_t first = XCD ? xcd_first(blockIdx.x, gridDim.x) : blockIdx.x;
     for (uint32_t tile = first; tile < a.n_tiles; tile += gridDim.x) {
         const uint32_t plane = fdiv(tile, a.div_tpp);
         const uint32_t ti = tile - plane * a.tiles_per_plane;
         const uint32_t r = fdiv(plane, a.div_B);
         const uint32_t b = plane - r * a.B;
         const uint64_t head_base = uint64_t(plane) * a.plane_vecs;
-        const uint32_t vb = ti * uint32_t(kTileVecs);
-        const uint64_t ve64 = uint64_t(vb) + kTileVecs;
+        const uint32_t vb = ti * uint32_t(kVarlenTileVecs);
+        const uint64_t ve64 = uint64_t(vb) + kVarlenTileVecs;
         const uint32_t ve = uint32_t(ve64 < a.plane_vecs ? ve64 : a.plane_vecs);
         const uint32_t row0 = fdiv(vb, a.div_c);
         const uint32_t nrows = fdiv(ve - 1, a.div_c) - row0 + 1;
@@ -193,7 +195,7 @@ __global__ __launch_bounds__(kThreads) void k_varlen_relayout(VarlenRelayout a)
             rows_ok = rows_ok && off >= 0;
         }
         // full tile whose every row the plan places inside the buffer: no guards
-        const bool fast = __syncthreads_and(rows_ok && ve - vb == uint32_t(kTileVecs));
+        const bool fast = __syncthreads_and(rows_ok && ve - vb == uint32_t(kVarlenTileVecs));
         constexpr int NTP = S2H ? CAM_NT_VARLEN_SEQ_TO_HEAD : CAM_NT_VARLEN_HEAD_TO_SEQ;
         if (fast)
             varlen_tile<W, S2H, false, NTP>(a, row_off, head_base, vb, ve, row0);
