@@ -765,7 +765,7 @@ cam_status lse_pack(const void* out, int64_t o_sp, int64_t o_st, int64_t o_sh, c
     if (o_vecs >= kU32Limit)
         return set_error(CAM_ERR_UNSUPPORTED, "%s: one chunk exceeds 2^31 vectors", op);
     a.o_vecs = uint32_t(o_vecs);
-    a.o_tiles_per_chunk = tiles(o_vecs, kTileVecs);
+    a.o_tiles_per_chunk = tiles(o_vecs, kPackTileVecs);
     a.div_otpc = make_fastdiv(a.o_tiles_per_chunk ? a.o_tiles_per_chunk : 1);
     a.l_tiles_per_chunk = tiles(uint64_t(g.rows), kThreads);
     a.div_ltpc = make_fastdiv(a.l_tiles_per_chunk);

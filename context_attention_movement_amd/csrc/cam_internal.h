@@ -264,14 +264,19 @@ void clear_error();
 #endif
 constexpr int kThreads = CAM_THREADS;
 // 16-byte vectors each thread moves per tile (its loads all in flight before
-// its stores): the pack and the copy, the dense relayout, the varlen
-// relayout -- chosen per kernel by measurement on MI355X with inputs too
-// large for the Infinity Cache.
-#ifndef CAM_VECS_PER_THREAD
-#define CAM_VECS_PER_THREAD 4
+// its stores): the pack's payload, the plain copy, the dense relayout, the
+// varlen relayout -- chosen per kernel by measurement on MI355X with inputs
+// too large for the Infinity Cache.
+#ifndef CAM_VECS_PACK
+#define CAM_VECS_PACK 3
 #endif
-constexpr int kVecsPerThread = CAM_VECS_PER_THREAD;
-constexpr int kTileVecs = kThreads * kVecsPerThread;
+constexpr int kPackVecs = CAM_VECS_PACK;
+constexpr int kPackTileVecs = kThreads * kPackVecs;
+#ifndef CAM_VECS_COPY
+#define CAM_VECS_COPY 2
+#endif
+constexpr int kCopyVecs = CAM_VECS_COPY;
+constexpr int kCopyTileVecs = kThreads * kCopyVecs;
 #ifndef CAM_VECS_DENSE
 #define CAM_VECS_DENSE 2
 #endif

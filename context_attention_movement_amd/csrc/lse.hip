@@ -40,9 +40,9 @@ template <int W, bool GUARD>
 __device__ __forceinline__ void pack_o_tile(const Pack& a, uint32_t r, const char* src, char* dst, uint32_t v0)
 {
     typedef typename VecOf<W>::type V;
-    V x[kVecsPerThread];
+    V x[kPackVecs];
 #pragma unroll
-    for (int u = 0; u < kVecsPerThread; ++u) {
+    for (int u = 0; u < kPackVecs; ++u) {
         const uint32_t v = v0 + uint32_t(u * kThreads);
         if (!GUARD || v < a.o_vecs) {
             const uint32_t q = fdiv(v, a.div_cv);
@@ -55,7 +55,7 @@ __device__ __forceinline__ void pack_o_tile(const Pack& a, uint32_t r, const cha
     }
     issue_fence();
 #pragma unroll
-    for (int u = 0; u < kVecsPerThread; ++u) {
+    for (int u = 0; u < kPackVecs; ++u) {
         const uint32_t v = v0 + uint32_t(u * kThreads);
         if (!GUARD || v < a.o_vecs)
             st<W, (CAM_NT_PACK & 2) != 0>(dst, v, x[u]);
@@ -76,8 +76,8 @@ __global__ __launch_bounds__(kThreads) void k_pack(Pack a)
             const uint32_t r = chunk - p * a.P;
             const char* src = static_cast<const char*>(a.out) + int64_t(p) * a.o_sp_b;
             char* dst = static_cast<char*>(a.packed) + uint64_t(chunk) * a.chunk_b;
-            const uint32_t vt = ti * uint32_t(kTileVecs);
-            if (vt + uint32_t(kTileVecs) <= a.o_vecs)
+            const uint32_t vt = ti * uint32_t(kPackTileVecs);
+            if (vt + uint32_t(kPackTileVecs) <= a.o_vecs)
                 pack_o_tile<W, false>(a, r, src, dst, vt + threadIdx.x);
             else
                 pack_o_tile<W, true>(a, r, src, dst, vt + threadIdx.x);

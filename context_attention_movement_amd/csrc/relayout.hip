@@ -208,16 +208,16 @@ template <bool GUARD>
 __device__ __forceinline__ void copy_tile(const Copy& a, uint64_t v0)
 {
     typedef typename VecOf<16>::type V;
-    V x[kVecsPerThread];
+    V x[kCopyVecs];
 #pragma unroll
-    for (int u = 0; u < kVecsPerThread; ++u) {
+    for (int u = 0; u < kCopyVecs; ++u) {
         const uint64_t v = v0 + uint64_t(u * kThreads);
         if (!GUARD || v < a.n_vecs)
             x[u] = ld<16, (CAM_NT_COPY & 1) != 0>(a.src, v);
     }
     issue_fence();
 #pragma unroll
-    for (int u = 0; u < kVecsPerThread; ++u) {
+    for (int u = 0; u < kCopyVecs; ++u) {
         const uint64_t v = v0 + uint64_t(u * kThreads);
         if (!GUARD || v < a.n_vecs)
             st<16, (CAM_NT_COPY & 2) != 0>(a.dst, v, x[u]);
@@ -226,11 +226,11 @@ __device__ __forceinline__ void copy_tile(const Copy& a, uint64_t v0)
 
 __global__ __launch_bounds__(kThreads) void k_copy16(Copy a)
 {
-    const uint64_t n_tiles = (a.n_vecs + kTileVecs - 1) / kTileVecs;
+    const uint64_t n_tiles = (a.n_vecs + kCopyTileVecs - 1) / kCopyTileVecs;
     const uint64_t first = CAM_XCD_COPY ? xcd_first(blockIdx.x, gridDim.x) : blockIdx.x;
     for (uint64_t tile = first; tile < n_tiles; tile += gridDim.x) {
-        const uint64_t vt = tile * kTileVecs;
-        if (vt + kTileVecs <= a.n_vecs)
+        const uint64_t vt = tile * kCopyTileVecs;
+        if (vt + kCopyTileVecs <= a.n_vecs)
             copy_tile<false>(a, vt + threadIdx.x);
         else
             copy_tile<true>(a, vt + threadIdx.x);
@@ -265,7 +265,7 @@ cam_status launch_varlen_relayout(const VarlenRelayout& a, void* stream)
 
 cam_status launch_copy(const Copy& a, void* stream)
 {
-    const uint64_t n_tiles = (a.n_vecs + kTileVecs - 1) / kTileVecs;
+    const uint64_t n_tiles = (a.n_vecs + kCopyTileVecs - 1) / kCopyTileVecs;
     return launch(reinterpret_cast<const void*>(&k_copy16), a, n_tiles, stream, "copy");
 }
 
