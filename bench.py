@@ -480,6 +480,8 @@ def summarize_rocprof(trace_dir, fetch_dir, write_dir, bench_json, out_txt, comm
       duration and its HBM bytes per launch: FETCH_SIZE and WRITE_SIZE per
       dispatch, each scaled by what the same counter reads for the plain copy
       kernel of known size."""
+    while command.startswith("command: "):  # a header passed back in is not repeated
+        command = command[len("command: "):]
     lines = [f"command: {command}", ""]
     stats = _read_csvs(trace_dir, "kernel_stats.csv") if trace_dir else []
     if stats:
