@@ -75,3 +75,34 @@ def test_ring_of_merges_equals_one_shot_combine(cam, orc, P, T, H, D):
                       orc.half_bits_to_double(ro).reshape(-1, D), "ring result")
     err = assert_lse_close(acc_l.cpu().numpy(), rl, "ring lse")
     print(f"ring P={P} lse err {err:.2e}", flush=True)
+
+
+def test_ring_full_thd_size_sampled(cam, orc):
+    """The ring at the packed THD batch's full size (131072 tokens, H = 32,
+    D = 128, 8 hops, fp32 accumulator; the shape the benchmark times): the
+    final rounded rows and LSEs of token windows at the start, the end and
+    around sequence boundaries against the oracle's one-shot combine of the
+    same 8 partials; the whole result is checked for NaN."""
+    P, H, D = 8, 32, 128
+    lens = synth.thd_lengths(20, 131072, seed=synth.BASE_SEED + 4)
+    cu = synth.cu_seqlens(lens)
+    T = int(cu[-1])
+    announce("ring of 8 merges, full THD size")
+    g = synth._gen(synth.BASE_SEED + 78, "cuda")
+    po = torch.randn((P, T, H, D), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    pl = torch.randn((P, T, H), generator=g, device="cuda", dtype=torch.float32).mul_(2.0)
+    pl[3, 1000:1100, :] = float("-inf")   # a stretch where one hop brings nothing
+    acc = torch.empty((T, H, D), device="cuda")
+    acc_l = torch.full((T, H), float("-inf"), device="cuda")
+    fin = torch.empty((T, H, D), dtype=torch.bfloat16, device="cuda")
+    for hop in range(P):
+        cam.lse_merge(acc, acc_l, po[hop], pl[hop], out_final=fin if hop == P - 1 else None)
+    torch.cuda.synchronize()
+    assert not torch.isnan(fin).any() and not torch.isnan(acc_l).any()
+    for a in [0, 1000 - 40, T - 96] + [int(c) - 48 for c in cu[1:-1:4]]:
+        a = max(0, min(a, T - 96))
+        b = a + 96
+        ro, rl = orc.lse_combine(to_host_bits(po[:, a:b]), pl[:, a:b].cpu().numpy())
+        assert_rows_close(orc.half_bits_to_double(to_host_bits(fin[a:b])).reshape(-1, D),
+                          orc.half_bits_to_double(ro).reshape(-1, D), f"ring window {a}")
+        assert_lse_close(acc_l[a:b].cpu().numpy(), rl, f"ring lse window {a}")
