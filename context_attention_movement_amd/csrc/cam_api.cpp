@@ -3,9 +3,9 @@
 // Host-only: every argument is checked here before anything reaches the GPU
 // (this file makes no HIP call), then a launch record is built and handed to
 // one kernel launcher.  A rejected call launches nothing and writes nothing:
-// the "decline rather than half-run" rule of FastVideo's fused all-to-all
-// helper (commit message of "[perf] Probe H3 chunked all-to-all with direct
-// output slices"), applied per call.
+// FastVideo's fused all-to-all helper either declines before it starts or
+// runs to the end (commit message of "[perf] Probe H3 chunked all-to-all
+// with direct output slices"); the same rule, applied per call.
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>

@@ -5,8 +5,8 @@
  *
  * Sources (web pages, cited by title and section):
  *  [FV] FastVideo compare view "[perf] Probe H3 chunked all-to-all with direct
- *       output slices": ulysses_a2a.py (fused all-to-all, "same layout,
- *       byte-identical results, fewer passes over local memory"),
+ *       output slices": ulysses_a2a.py (fused all-to-all: output identical to
+ *       the collective's, with less traffic through local memory),
  *       benchmark_ulysses_a2a.py (all_to_all_4D(x, 2, 1) on the scatter
  *       operand [3, S/P, H, 128]; (1, 2) on the gather operand [1, S, H/P, 128]).
  *  [VA] vllm-ascend PR "[Performance][Attention] Fuse local SFA LSE formation
@@ -142,7 +142,7 @@ cam_status ulysses_head_to_seq_varlen(const void* in, void* out, const int32_t* 
                                       int64_t H, int64_t D, cam_dtype dt, void* stream);
 
 /* ------------------------------------------------------------------------- */
-/* THD layout planner and planned relayout  ([CU] "THD layout planner": token  */
+/* THD layout planner and planned relayout  ([CU] PR description: token       */
 /* and causal work balanced over the ranks, short samples whole, alternating   */
 /* long-sequence direction, several grids with a contiguous fallback, exact    */
 /* balanced token capacity in aligned blocks, deterministic per-rank spans)    */
@@ -251,8 +251,9 @@ cam_status lse_pack(const void* out, int64_t o_sp, int64_t o_st, int64_t o_sh,
                     void* packed, void* stream);
 
 /* ------------------------------------------------------------------------- */
-/* Stable LSE-weighted combine  ([VA] "existing stable combine", invalid (-inf) */
-/* contributions "handled by the existing combine semantics", all-invalid rows) */
+/* Stable LSE-weighted combine  ([VA] "What this PR does": the PR keeps its    */
+/* combine unchanged and feeds it -inf for invalid statistics; rows with no     */
+/* valid partial)                                                               */
 /* ------------------------------------------------------------------------- */
 /*
  * Per output row, over the partials p < P in ascending order:

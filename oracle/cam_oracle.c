@@ -306,8 +306,9 @@ double orc_lse_from_stats(float m, float s)
     return -INFINITY;
 }
 
-/* Packed exchange layout (reading: the pages keep "row/head/token mapping,
- * packed payload semantics" but print no byte layout).  For source rank p and
+/* Packed exchange layout (reading: the pages say the mapping of rows, heads
+ * and tokens and the meaning of the packed payload stay as they were, but
+ * print no byte layout).  For source rank p and
  * destination rank r, chunk (p, r) holds the rows rank r will combine:
  *   scatter_dim = 1 (heads):  rows (t, h') for t < T, h' < H/P, source head
  *                             r*H/P + h'; row index q = t*(H/P) + h'.
@@ -365,7 +366,7 @@ void orc_lse_pack(const void* out, int64_t o_sp, int64_t o_st, int64_t o_sh,
 }
 
 /* ------------------------------------------------------------------------ */
-/* Stable LSE-weighted combine  ([VA] "existing stable combine")               */
+/* Stable LSE-weighted combine  ([VA] "What this PR does": kept unchanged)    */
 /* ------------------------------------------------------------------------ */
 /*
  * For one output row: V = {p : L_p finite}; M = max_{p in V} L_p;
@@ -761,7 +762,7 @@ void orc_lse_combine_backward(const void* part_out, int64_t po_sp, int64_t po_st
 }
 
 /* ------------------------------------------------------------------------ */
-/* THD layout planner and planned-span relayout  ([CU] "THD layout planner")  */
+/* THD layout planner and planned-span relayout  ([CU] PR description)        */
 /* ------------------------------------------------------------------------ */
 /*
  * The page states the planner's contract, not its steps: balance token-linear

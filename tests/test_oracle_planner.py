@@ -62,7 +62,7 @@ def _check_invariants(plan, cu, W, b, min_split, max_chunks):
     assert ss[0] == 0 and ss[-1] == T and np.all(np.diff(ss) > 0)
     assert np.all(ss % b == 0), "spans must be block-aligned"
     cap = np.array([((r + 1) * N // W - r * N // W) * b for r in range(W)])
-    assert np.array_equal(np.diff(ro), cap) and ro[0] == 0, "exact balanced token capacity"
+    assert np.array_equal(np.diff(ro), cap) and ro[0] == 0, "rank capacities must be the exact balanced split"
     for s in range(sr.size):  # a span never crosses a sequence boundary
         i = int(np.searchsorted(cu, ss[s], side="right")) - 1
         assert ss[s + 1] <= cu[i + 1]
