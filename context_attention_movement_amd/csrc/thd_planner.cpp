@@ -1,11 +1,13 @@
 // thd_planner.cpp -- host-side THD layout planner for context parallelism over
 // packed sequences (cuLA PR "feat(distributed): add packed hybrid runtime and
-// THD planner": the planner balances token-linear and causal work of an
-// arbitrary packed THD batch over the ranks, keeps short samples whole,
-// alternates long-sequence shard direction, evaluates several grids with a
-// contiguous fallback, enforces exact balanced token capacity in aligned
-// blocks, and gives deterministic per-rank spans; its input rules are those
-// of the PR's planner tests).
+// THD planner", description and planner tests).  What the plan must do: keep
+// each rank's work even, both the part that grows with its token count and
+// the part that grows with causal position, for any packed batch; leave a
+// short sample on one rank; deal long sequences out in a direction that flips
+// from rank to rank; try several grids and keep the plain contiguous layout
+// as a candidate; give every rank the same number of aligned blocks; return
+// the same span list for the same input.  Input checks follow the PR's
+// planner tests.
 //
 // The page does not print the steps; this is the reading implemented:
 //   - capacity: rank r holds exactly floor((r+1)N/W) - floor(rN/W) of the

@@ -142,10 +142,11 @@ cam_status ulysses_head_to_seq_varlen(const void* in, void* out, const int32_t* 
                                       int64_t H, int64_t D, cam_dtype dt, void* stream);
 
 /* ------------------------------------------------------------------------- */
-/* THD layout planner and planned relayout  ([CU] PR description: token       */
-/* and causal work balanced over the ranks, short samples whole, alternating   */
-/* long-sequence direction, several grids with a contiguous fallback, exact    */
-/* balanced token capacity in aligned blocks, deterministic per-rank spans)    */
+/* THD layout planner and planned relayout  ([CU] PR description: per-rank    */
+/* work that grows with tokens and with causal position kept even; a short    */
+/* sample stays on one rank; long sequences are dealt out in a direction that */
+/* flips from rank to rank; several grids tried, the plain contiguous layout  */
+/* kept as a candidate; equal aligned blocks per rank; a repeatable span list) */
 /* ------------------------------------------------------------------------- */
 typedef struct cam_thd_planner_config {
     int64_t block_size;          /* every length and min_split_tokens a multiple of it */
@@ -153,7 +154,7 @@ typedef struct cam_thd_planner_config {
     int64_t max_chunks_per_rank; /* planned candidates above it per rank are dropped */
     double token_weight;         /* cost of a token at position k:               */
     double causal_weight;        /*   token_weight + causal_weight * (k + 1)      */
-    int64_t mode;                /* 0: planned with contiguous fallback; 1: contiguous */
+    int64_t mode;                /* 0: best of the grids and the contiguous layout; 1: contiguous */
 } cam_thd_planner_config;
 
 /*
@@ -217,8 +218,8 @@ cam_status ulysses_head_to_seq_spans(const void* in, void* out, const int32_t* s
                                      void* stream);
 
 /* ------------------------------------------------------------------------- */
-/* Max/sum-aware LSE pack  ([VA] "What this PR does": the pack forms the LSE    */
-/* while writing the packed layout, instead of materializing it first)        */
+/* Max/sum-aware LSE pack  ([VA] "What this PR does": the LSE is computed     */
+/* inside the pack, so no separate fp32 LSE tensor is written beforehand)     */
 /* ------------------------------------------------------------------------- */
 /*
  * Inputs, for each source rank p < P (decode context parallel: rank p holds the

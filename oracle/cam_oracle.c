@@ -765,14 +765,16 @@ void orc_lse_combine_backward(const void* part_out, int64_t po_sp, int64_t po_st
 /* THD layout planner and planned-span relayout  ([CU] PR description)        */
 /* ------------------------------------------------------------------------ */
 /*
- * The page states the planner's contract, not its steps: balance token-linear
- * and causal (position-dependent) work of an arbitrary packed THD batch over
- * the context-parallel ranks; block-aligned shards with exact balanced token
- * capacity (non-power-of-two rank counts allowed); short samples kept whole;
- * long sequences sharded with a direction that alternates across ranks;
- * several planning grids, each a greedy assignment plus token rebalancing,
- * with a contiguous fallback; deterministic per-rank spans; and its input
- * rules (positive block size, block-aligned min_split_tokens and lengths,
+ * The page states what the planner must achieve, not its steps: even
+ * per-rank work, counting both the part proportional to tokens and the
+ * causal part that grows with position, for any packed THD batch over the
+ * context-parallel ranks; shards made of aligned blocks, every rank holding
+ * the same number of blocks up to one (any rank count, not only powers of
+ * two); a short sample left on one rank; long sequences dealt out in a
+ * direction that flips from rank to rank; several grids tried, each a
+ * greedy assignment followed by moving tokens between ranks, with the plain
+ * contiguous layout kept as a candidate; the same spans for the same input;
+ * and its input rules (positive block size, block-aligned min_split_tokens and lengths,
  * positive max_chunks_per_rank, finite non-negative weights not both zero,
  * at least one block per rank).  Reading (the concrete algorithm):
  *

@@ -3,9 +3,10 @@
 Planner: the input rules the page lists; the hand-worked plan in
 tests/golden/thd_plan_small.json; on random packed batches (non-power-of-two
 rank counts included) the invariants the page states -- every token placed
-once, block-aligned spans, exact balanced token capacity per rank, short
-samples whole when they fit, at most max_chunks_per_rank spans per rank
-(except the contiguous fallback), deterministic output -- with rank costs
+once, block-aligned spans, every rank holding its balanced share of blocks,
+short samples on one rank when they fit, at most max_chunks_per_rank spans
+per rank (unless the contiguous layout wins), the same output for the same
+input -- with rank costs
 recomputed exactly from the spans, and never worse than the contiguous
 layout (computed here from the balanced-shard closed form); brute force over
 every capacity-respecting block assignment bounds the plan on tiny batches.
