@@ -100,6 +100,12 @@ class Workload:
         self.v_o_sets = [(self.v_o, self.v_o_out)] + [
             (randn((P, 1, S, H // P, D)), torch.empty((P, 1, S // P, H, D), dtype=bf, device=dev))
             for _ in range(self.VO_SETS - 1)]
+        # video DiT, P = 8 (timed beyond the step): Q/K/V [8][3][9450][48][128]
+        # and O [8][1][75600][6][128], 2.8 GB and 0.9 GB
+        self.v8_qkv = randn((8, 3, 75600 // 8, 48, D))
+        self.v8_qkv_out = torch.empty((8, 3, 75600, 48 // 8, D), dtype=bf, device=dev)
+        self.v8_o = randn((8, 1, 75600, 48 // 8, D))
+        self.v8_o_out = torch.empty((8, 1, 75600 // 8, 48, D), dtype=bf, device=dev)
         # MLA decode, P = 8; NSETS independent buffer sets (> 1 GiB together) so
         # that repeated calls never find their inputs in the 256 MB Infinity Cache
         self.mP, self.mT, self.mH, self.mDv = 8, 128, 128, 512
@@ -184,7 +190,8 @@ class Workload:
         """SHA-256 (first 16 hex digits) of every seeded input buffer's shape,
         dtype and its first and last MiB, read back before the timed steps."""
         torch = self.torch
-        bufs = {"video_qkv": self.v_qkv, "video_o": self.v_o, "thd_qkv": self.t_qkv, "thd_o": self.t_o,
+        bufs = {"video_qkv": self.v_qkv, "video_o": self.v_o, "video_p8_qkv": self.v8_qkv, "video_p8_o": self.v8_o,
+                "thd_qkv": self.t_qkv, "thd_o": self.t_o,
                 "thd_partials": self.t_part, "thd_partial_lse": self.t_lse, "thd_grad_out": self.t_gout,
                 "proj_x": self.j_x, "proj_w": self.j_w}
         for i, ms in enumerate(self.m_sets):
@@ -255,7 +262,8 @@ class Workload:
 
 
     def extension_ops(self, k=0):
-        """Operations beyond the step: the gradient of the THD combine, the
+        """Operations beyond the step: the video relayouts at P = 8, the
+        planned THD operations, the gradient of the THD combine, the
         relayout training pair (forward and backward), the ring of online
         merges, the combine epilogues that write the sequence-sharded layout
         directly and the unfused sequence they replace.
@@ -322,7 +330,15 @@ class Workload:
 
         planned_comb_bytes = self.p_admitted * H * (2 * D + 4) + rows * (2 * D + 4)
 
+        def p8_s2h():
+            cam.ulysses_seq_to_head(self.v8_qkv, 8, out=self.v8_qkv_out)
+
+        def p8_h2s():
+            cam.ulysses_head_to_seq(self.v8_o, 8, out=self.v8_o_out)
+
         return [
+            ("relayout_seq_to_head_video_p8_qkv", 2 * self.v8_qkv.numel() * 2, p8_s2h),
+            ("relayout_head_to_seq_video_p8_o", 2 * self.v8_o.numel() * 2, p8_h2s),
             ("lse_combine_planned_thd", planned_comb_bytes, planned_combine),
             ("relayout_seq_to_head_planned_thd_qkv", 2 * 3 * T * H * D * 2, planned_s2h),
             ("relayout_head_to_seq_planned_thd_o", 2 * T * H * D * 2, planned_h2s),

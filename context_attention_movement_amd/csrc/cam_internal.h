@@ -278,7 +278,7 @@ constexpr int kPackTileVecs = kThreads * kPackVecs;
 constexpr int kCopyVecs = CAM_VECS_COPY;
 constexpr int kCopyTileVecs = kThreads * kCopyVecs;
 #ifndef CAM_VECS_DENSE
-#define CAM_VECS_DENSE 2
+#define CAM_VECS_DENSE 1
 #endif
 constexpr int kDenseVecs = CAM_VECS_DENSE;
 constexpr int kDenseTileVecs = kThreads * kDenseVecs;
@@ -380,7 +380,7 @@ constexpr int kCombineBatchWave = CAM_COMBINE_BATCH_WAVE;
 // XCD-aware tile order per kernel (1 = each XCD takes a contiguous range of
 // tiles, 0 = hardware order), chosen by measurement on MI355X.
 #ifndef CAM_XCD_SEQ_TO_HEAD
-#define CAM_XCD_SEQ_TO_HEAD 0
+#define CAM_XCD_SEQ_TO_HEAD 1
 #endif
 #ifndef CAM_XCD_HEAD_TO_SEQ
 #define CAM_XCD_HEAD_TO_SEQ 1
