@@ -313,6 +313,9 @@ constexpr int kVarlenTileVecs = kThreads * kVarlenVecs;
 #ifndef CAM_NT_COMBINE_BWD
 #define CAM_NT_COMBINE_BWD 2
 #endif
+#ifndef CAM_NT_MERGE
+#define CAM_NT_MERGE 3
+#endif
 // Projection: row tiles per group of the tile order (column tiles of a
 // group run close together in time and share their weight tiles in cache).
 #ifndef CAM_PROJ_GROUP_M
@@ -390,6 +393,9 @@ constexpr int kCombineBatchWave = CAM_COMBINE_BATCH_WAVE;
 #endif
 #ifndef CAM_XCD_VARLEN_HEAD_TO_SEQ
 #define CAM_XCD_VARLEN_HEAD_TO_SEQ 1
+#endif
+#ifndef CAM_XCD_MERGE
+#define CAM_XCD_MERGE 0
 #endif
 #ifndef CAM_XCD_PACK
 #define CAM_XCD_PACK 0

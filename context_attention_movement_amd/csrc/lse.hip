@@ -562,8 +562,8 @@ __global__ __launch_bounds__(kThreads) void k_merge(Merge a)
     const uint32_t G = 1u << a.g_log2;
     const uint32_t gl = threadIdx.x & (G - 1u);
     const uint64_t rows_per_block = uint64_t(kThreads) >> a.g_log2;
-    for (uint64_t rb = uint64_t(blockIdx.x) * rows_per_block; rb < a.n_rows;
-         rb += uint64_t(gridDim.x) * rows_per_block) {
+    const uint64_t blk = CAM_XCD_MERGE ? xcd_first(blockIdx.x, gridDim.x) : blockIdx.x;
+    for (uint64_t rb = blk * rows_per_block; rb < a.n_rows; rb += uint64_t(gridDim.x) * rows_per_block) {
         const uint64_t row = rb + (threadIdx.x >> a.g_log2);
         if (row >= a.n_rows)
             continue;
@@ -584,10 +584,13 @@ __global__ __launch_bounds__(kThreads) void k_merge(Merge a)
         char* frow = FINAL ? static_cast<char*>(a.fin) + int64_t(t) * a.f_st_b + int64_t(h) * a.f_sh_b : nullptr;
         for (uint32_t k = gl; k < a.cv; k += G) {
             // an empty accumulator (the first hop) is not read
+            constexpr bool NTL = (CAM_NT_MERGE & 1) != 0, NTS = (CAM_NT_MERGE & 2) != 0;
             f32x4 x = {0.0f, 0.0f, 0.0f, 0.0f};
+            const f32x4* xa = reinterpret_cast<const f32x4*>(arow + 4 * k);
+            const u32x2* yp = reinterpret_cast<const u32x2*>(prow + 8 * k);
             if (va)
-                x = *reinterpret_cast<const f32x4*>(arow + 4 * k);
-            const u32x2 y = *reinterpret_cast<const u32x2*>(prow + 8 * k);
+                x = NTL ? __builtin_nontemporal_load(xa) : *xa;
+            const u32x2 y = NTL ? __builtin_nontemporal_load(yp) : *yp;
             issue_fence();
             const float b0 = FP16 ? fp16_lo(y.x) : bf16_lo(y.x), b1 = FP16 ? fp16_hi(y.x) : bf16_hi(y.x);
             const float b2 = FP16 ? fp16_lo(y.y) : bf16_lo(y.y), b3 = FP16 ? fp16_hi(y.y) : bf16_hi(y.y);
@@ -596,7 +599,10 @@ __global__ __launch_bounds__(kThreads) void k_merge(Merge a)
             r.y = (va ? sa * x.y : 0.0f) + (vb ? sb * b1 : 0.0f);
             r.z = (va ? sa * x.z : 0.0f) + (vb ? sb * b2 : 0.0f);
             r.w = (va ? sa * x.w : 0.0f) + (vb ? sb * b3 : 0.0f);
-            *reinterpret_cast<f32x4*>(arow + 4 * k) = r;
+            if (NTS)
+                __builtin_nontemporal_store(r, reinterpret_cast<f32x4*>(arow + 4 * k));
+            else
+                *reinterpret_cast<f32x4*>(arow + 4 * k) = r;
             if (FINAL) {
                 u32x2 o;
                 if (FP16) {
@@ -606,7 +612,10 @@ __global__ __launch_bounds__(kThreads) void k_merge(Merge a)
                     o.x = f32_to_bf16_bits(r.x) | (f32_to_bf16_bits(r.y) << 16);
                     o.y = f32_to_bf16_bits(r.z) | (f32_to_bf16_bits(r.w) << 16);
                 }
-                *reinterpret_cast<u32x2*>(frow + 8 * k) = o;
+                if (NTS)
+                    __builtin_nontemporal_store(o, reinterpret_cast<u32x2*>(frow + 8 * k));
+                else
+                    *reinterpret_cast<u32x2*>(frow + 8 * k) = o;
             }
         }
         if (gl == 0)
