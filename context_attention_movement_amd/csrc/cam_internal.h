@@ -273,7 +273,7 @@ constexpr int kThreads = CAM_THREADS;
 constexpr int kPackVecs = CAM_VECS_PACK;
 constexpr int kPackTileVecs = kThreads * kPackVecs;
 #ifndef CAM_VECS_COPY
-#define CAM_VECS_COPY 2
+#define CAM_VECS_COPY 1
 #endif
 constexpr int kCopyVecs = CAM_VECS_COPY;
 constexpr int kCopyTileVecs = kThreads * kCopyVecs;
@@ -407,7 +407,7 @@ constexpr int kCombineBatchWave = CAM_COMBINE_BATCH_WAVE;
 #define CAM_XCD_COMBINE_NARROW 0
 #endif
 #ifndef CAM_XCD_COPY
-#define CAM_XCD_COPY 0
+#define CAM_XCD_COPY 1
 #endif
 #ifndef CAM_MAX_GRID
 #define CAM_MAX_GRID (1u << 20)
