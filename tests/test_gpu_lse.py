@@ -251,3 +251,22 @@ def test_thd_combine_full_size_sampled(cam, orc):
         assert_rows_close(orc.half_bits_to_double(to_host_bits(out[a:b])).reshape(-1, D),
                           orc.half_bits_to_double(ro).reshape(-1, D), f"THD window {a}")
         assert_lse_close(lse[a:b].cpu().numpy(), rl, f"THD lse window {a}")
+
+
+def test_mla_pack_and_combine_full_size_fp16(cam, orc):
+    """The MLA decode shape with an fp16 producer (P = 8, T = 128, H = 128,
+    Dv = 512, 1% corrupted statistics, the fp16 seed): the packed buffer bit
+    for bit and its L-region within 1e-5, then the combine over the exchange
+    within the payload bar, invalid rows NaN-poisoned."""
+    P, T, H, Dv = 8, 128, 128, 512
+    announce("MLA pack + combine full size, fp16")
+    o, m, s, _ = synth.dcp_partials(P, T, H, Dv, seed=synth.FP16_SEED, dtype="fp16")
+    packed_ref, _, err = _pack_and_check(cam, orc, o, m, s, 1, "MLA pack fp16")
+    ob = synth.bits(o).copy()
+    mn, sn = m.numpy(), s.numpy()
+    with np.errstate(invalid="ignore"):
+        invalid = ~(np.isfinite(mn) & np.isfinite(sn) & (sn > 0))
+    ob[invalid] = 0x7E01  # fp16 NaN payload in every invalid partial row
+    poisoned = orc.lse_pack(ob, mn, sn, 1)
+    worst, lerr = _combine_check(cam, orc, poisoned, P, T, H, Dv, 1, "fp16", "MLA combine fp16")
+    print(f"MLA fp16: pack LSE err {err:.3e}, combine worst row {worst:.3e}, lse err {lerr:.3e}", flush=True)
