@@ -22,6 +22,7 @@ read) divided by the step time.  Per-operation figures are under "ops".
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
     python bench.py --summarize-rocprof TRACE FETCH WRITE BENCH_JSON --summary-out F --command TEXT
+    python bench.py --summarize-counters COUNTER_DIR KERNEL --summary-out F --command TEXT
 """
 
 from __future__ import annotations
@@ -582,6 +583,32 @@ def summarize_rocprof(trace_dir, fetch_dir, write_dir, bench_json, out_txt, comm
     Path(out_txt).write_text("\n".join(lines) + "\n")
 
 
+def summarize_counters(counter_dir, kernel, out_txt, command):
+    """Write the median per dispatch of every counter rocprofv3 --pmc collected
+    for the kernels whose name contains `kernel`, one line per counter."""
+    while command.startswith("command: "):
+        command = command[len("command: "):]
+    vals = {}
+    names = set()
+    for r in _read_csvs(counter_dir, "counter_collection.csv"):
+        name = r.get("Kernel_Name", "")
+        if kernel not in name:
+            continue
+        names.add(name)
+        key = (r.get("Dispatch_Id", ""), r["Counter_Name"])
+        vals.setdefault(r["Counter_Name"], {}).setdefault(key, 0.0)
+        vals[r["Counter_Name"]][key] += float(r["Counter_Value"])  # summed over the dispatch's instances
+    lines = [f"command: {command}", "", f"kernel: {', '.join(sorted(names))}",
+             "counter (median per dispatch over the run):"]
+    for c in sorted(vals):
+        v = sorted(vals[c].values())
+        lines.append(f"  {c:32s} {v[len(v) // 2]:>18.0f}   dispatches={len(v)}")
+    text = "\n".join(lines) + "\n"
+    if out_txt:
+        Path(out_txt).write_text(text)
+    print(text, end="")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -591,6 +618,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for the CPU baseline")
     ap.add_argument("--summarize-rocprof", nargs=4, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR", "BENCH_JSON"))
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("COUNTER_DIR", "KERNEL"))
     ap.add_argument("--summary-out", default=None)
     ap.add_argument("--command", default="")
     args = ap.parse_args()
@@ -598,6 +626,9 @@ def main():
     if args.summarize_rocprof:
         tr, fe, wr, bj = [None if x in ("-", "") else x for x in args.summarize_rocprof]
         summarize_rocprof(tr, fe, wr, bj, args.summary_out, args.command)
+        return
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters[0], args.summarize_counters[1], args.summary_out, args.command)
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
