@@ -70,3 +70,38 @@ def test_projection_video_shape_sampled_rows(cam, orc):
     xs = to_host_bits(x[torch.from_numpy(rows).cuda()])
     got = to_host_bits(out[:, :, torch.from_numpy(rows).cuda()])
     _check(orc, got, xs, to_host_bits(w), P, B, H, D, "bf16", "video rows")
+
+
+_CAPTURE_FIRST = r"""
+import sys, torch
+sys.path.insert(0, sys.argv[1])
+import context_attention_movement_amd as cam
+torch.cuda.set_device(0)
+S, K, P, B, H, D = 300, 128, 2, 3, 4, 64
+g = torch.Generator(device="cuda").manual_seed(5)
+x = torch.randn(S, K, device="cuda", generator=g).to(torch.bfloat16)
+w = (torch.randn(B * H * D, K, device="cuda", generator=g) * 0.1).to(torch.bfloat16)
+out = torch.empty((P, B, S, H // P, D), device="cuda", dtype=torch.bfloat16)
+graph = torch.cuda.CUDAGraph()
+with torch.cuda.graph(graph):   # the process's first call of the projection
+    cam.qkv_projection_head_sharded(x, w, P, B, H, D, out=out)
+torch.cuda.synchronize()
+out.zero_()
+graph.replay()
+ref = cam.qkv_projection_head_sharded(x, w, P, B, H, D)
+torch.cuda.synchronize()
+sys.exit(0 if torch.equal(out, ref) else 3)
+"""
+
+
+def test_projection_first_call_inside_graph_capture():
+    """A caller may capture the projection before ever calling it eagerly (the
+    kernel's large-LDS attribute is then set during the capture): in a fresh
+    process, the replay equals an eager call bit for bit."""
+    import subprocess
+    import sys
+    from pathlib import Path
+    announce("projection: first call inside a graph capture (child process)")
+    root = str(Path(__file__).resolve().parents[1])
+    r = subprocess.run([sys.executable, "-c", _CAPTURE_FIRST, root], capture_output=True, text=True, timeout=180)
+    assert r.returncode == 0, f"child exited {r.returncode}: {r.stderr[-2000:]}"
