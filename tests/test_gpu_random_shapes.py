@@ -144,3 +144,63 @@ def test_random_merge(cam, orc, case):
     den = np.max(np.abs(ref_o), axis=1)
     assert np.all(num[den == 0] == 0) and (np.max(num[den > 0] / den[den > 0]) if (den > 0).any() else 0) <= 1e-5
     assert_lse_close(al_d.cpu().numpy(), ref_l, "random merge lse")
+
+
+@pytest.mark.parametrize("case", range(16))
+def test_random_pack_and_packed_combine(cam, orc, case):
+    rng = np.random.default_rng(9800 + case)
+    P = int(rng.integers(1, 9))
+    sd = int(rng.integers(0, 2))
+    T = P * int(rng.integers(1, 9)) if sd == 0 else int(rng.integers(1, 30))
+    H = P * int(rng.integers(1, 4)) if sd == 1 else int(rng.integers(1, 6))
+    Dv = int(rng.choice([1, 4, 8, 40, 64, 128, 512]))
+    dt = str(rng.choice(["bf16", "fp16"]))
+    announce(f"random pack + combine #{case}: P={P} T={T} H={H} Dv={Dv} scatter_dim={sd} {dt}")
+    o, m, s, _ = synth.dcp_partials(P, T, H, Dv, seed=9900 + case, dtype=dt, corrupt_frac=0.2)
+    ref = orc.lse_pack(synth.bits(o), m.numpy(), s.numpy(), sd)
+    packed = cam.lse_pack(o.cuda(), m.cuda(), s.cuda(), sd)
+    torch.cuda.synchronize()
+    O1, L1 = orc.packed_regions(ref, P, T, H, Dv, sd)
+    O2, L2 = orc.packed_regions(to_host_bits(packed), P, T, H, Dv, sd)
+    assert_bits_equal(O2, O1, "packed O-region")
+    assert_lse_close(L2, L1, "packed L-region")
+    ro, rl = orc.lse_combine_packed(ref, P, T, H, Dv, sd, dtype=dt)
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float16
+    out, lse = cam.lse_combine_packed(torch.from_numpy(ref).cuda(), P, T, H, Dv, sd, dtype=tdt)
+    torch.cuda.synchronize()
+    assert_rows_close(orc.half_bits_to_double(to_host_bits(out), dt).reshape(-1, Dv),
+                      orc.half_bits_to_double(ro, dt).reshape(-1, Dv), "packed combine")
+    assert_lse_close(lse.cpu().numpy(), rl, "packed combine lse")
+
+
+@pytest.mark.parametrize("case", range(16))
+def test_random_planned_combine(cam, orc, case):
+    rng = np.random.default_rng(10000 + case)
+    W = int(rng.integers(1, 9))
+    b = int(rng.choice([1, 2, 4]))
+    nseq = int(rng.integers(1, 8))
+    blocks = [int(v) for v in rng.integers(0, 40, size=nseq)]
+    while sum(blocks) < W:              # the planner needs at least one block per rank
+        blocks[int(rng.integers(0, nseq))] += 1
+    H = int(rng.integers(1, 5))
+    D = int(rng.choice([8, 64, 128, 512]))
+    cu = synth.cu_seqlens([x * b for x in blocks])
+    T = int(cu[-1])
+    announce(f"random planned combine #{case}: W={W} block={b} blocks={blocks} H={H} D={D}")
+    q = orc.thd_plan(cu, W, block_size=b, min_split_tokens=8 * b)
+    plan = cam.ThdPlan(W, T, cu, q["span_start"], q["span_rank"], q["span_local"], q["rank_off"],
+                       q["rank_cost"], q["grid"]).to("cuda")
+    first = orc.plan_first_positions(cu, q, W)
+    mask = orc.plan_mask(cu, first, W)
+    o = synth.bits(synth.normal((W, T, H, D), seed=10100 + case)).copy()
+    l = synth.partial_lse((W, T, H), seed=10200 + case).numpy().copy()
+    l[rng.random((W, T, H)) < 0.1] = -np.inf
+    o[~mask] = 0x7FC0
+    l[~mask] = np.nan
+    o[~np.isfinite(l)] = 0x7FC0
+    ro, rl = orc.lse_combine_planned(o, l, cu, first)
+    out, lse = cam.lse_combine_planned(from_host_bits(o, torch.bfloat16), torch.from_numpy(l).cuda(), plan)
+    torch.cuda.synchronize()
+    assert_rows_close(orc.half_bits_to_double(to_host_bits(out)).reshape(-1, D),
+                      orc.half_bits_to_double(ro).reshape(-1, D), "planned combine")
+    assert_lse_close(lse.cpu().numpy(), rl, "planned combine lse")
