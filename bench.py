@@ -46,7 +46,8 @@ sys.path.insert(0, str(ROOT))
 METRIC = "achieved HBM GB/s (% of peak) and µs/call for relayout, LSE-pack, combine"
 HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix cores, published
-KERNEL_SOURCES = ["relayout.hip", "lse.hip", "cam_device.h", "cam_internal.h"]
+KERNEL_SOURCES = ["relayout.hip", "lse.hip", "proj.hip", "cam_device.h", "cam_internal.h", "cam_api.cpp",
+                  "thd_planner.cpp"]
 TRAFFIC_FILE = ROOT / "profiles" / "traffic.json"
 
 
@@ -374,10 +375,13 @@ def plan_summary(w):
 # CPU baseline: the oracle as it stands, on a bounded sample
 # ---------------------------------------------------------------------------
 
-def cpu_baseline(w, budget_s: float = 25.0):
+def _cpu_work_items(w):
+    """The step's seven operations at full size as independent oracle calls
+    on host copies of the same synthetic inputs: (label, algorithmic bytes,
+    callable).  The THD causal combine, the costly one, is cut into token
+    windows (the oracle's own window arguments); each window is one item."""
     import numpy as np
     import oracle
-    import synth
 
     torch = w.torch
 
@@ -385,83 +389,97 @@ def cpu_baseline(w, budget_s: float = 25.0):
         t = t.detach().contiguous().cpu()
         return t.view(torch.int16).numpy().view(np.uint16)
 
-    done_bytes = 0.0
-    secs = 0.0
-    parts = []
-    # 1) video P = 4 Q/K/V seq->head, whole operand
-    x = bits(w.v_qkv)
-    t0 = time.perf_counter()
-    oracle.seq_to_head(x, w.vP, 3, w.vS, w.vH, w.vD)
-    dt = time.perf_counter() - t0
-    nb = w.op_bytes()["relayout_seq_to_head_video_p4_qkv"]
-    done_bytes += nb
-    secs += dt
-    parts.append(f"video P=4 QKV seq->head (full, {dt:.2f} s)")
-    del x
-    # 2) MLA pack and combine, whole workload
+    nb = w.op_bytes()
+    items = []
+    vx, vo = bits(w.v_qkv), bits(w.v_o)
+    items.append(("video P=4 QKV seq->head", nb["relayout_seq_to_head_video_p4_qkv"],
+                  lambda: oracle.seq_to_head(vx, w.vP, 3, w.vS, w.vH, w.vD)))
+    items.append(("video P=4 O head->seq", nb["relayout_head_to_seq_video_p4_o"],
+                  lambda: oracle.head_to_seq(vo, w.vP, 1, w.vS, w.vH, w.vD)))
     ob = bits(w.m_sets[0]["out"])
     m = w.m_sets[0]["max"].cpu().numpy()
     s = w.m_sets[0]["sum"].cpu().numpy()
-    t0 = time.perf_counter()
-    packed = oracle.lse_pack(ob, m, s, 1)
-    dt = time.perf_counter() - t0
-    done_bytes += w.op_bytes()["lse_pack_mla"]
-    secs += dt
-    parts.append(f"MLA pack (full, {dt:.2f} s)")
-    t0 = time.perf_counter()
-    oracle.lse_combine_packed(packed, w.mP, w.mT, w.mH, w.mDv, 1)
-    dt = time.perf_counter() - t0
-    done_bytes += w.op_bytes()["lse_combine_mla"]
-    secs += dt
-    parts.append(f"MLA combine (full, {dt:.2f} s)")
-    # 3) THD Q/K/V varlen seq->head, whole operand
-    x = bits(w.t_qkv)
-    t0 = time.perf_counter()
-    oracle.varlen_seq_to_head(x, w.t_cu, w.tP, 3, w.tH, w.tD)
-    dt = time.perf_counter() - t0
-    done_bytes += w.op_bytes()["relayout_seq_to_head_varlen_thd_qkv"]
-    secs += dt
-    parts.append(f"THD QKV varlen seq->head (full, {dt:.2f} s)")
-    del x
-    # 4) THD causal combine on a token window sized to the remaining budget
-    a = int(w.t_cu[3])
-    probe = 256
-    po = bits(w.t_part[:, a:a + probe])
-    pl = w.t_lse[:, a:a + probe].cpu().numpy()
-    t0 = time.perf_counter()
-    oracle.lse_combine(po, pl, cu=w.t_cu, t_begin=a)
-    per_token = (time.perf_counter() - t0) / probe
-    remaining = max(1.0, budget_s - secs)
-    win = int(min(w.tT - a, max(probe, remaining / per_token)))
-    po = bits(w.t_part[:, a:a + win])
-    pl = w.t_lse[:, a:a + win].cpu().numpy()
-    t0 = time.perf_counter()
-    oracle.lse_combine(po, pl, cu=w.t_cu, t_begin=a)
-    dt = time.perf_counter() - t0
-    frac = win / w.tT
-    done_bytes += w.op_bytes()["lse_combine_varlen_thd"] * frac
-    secs += dt
-    parts.append(f"THD causal combine on tokens [{a}, {a + win}) ({dt:.2f} s, {frac:.2%} of the batch)")
+    packed = oracle.lse_pack(ob, m, s, 1)  # the combine's input (not timed here)
+    items.append(("MLA pack", nb["lse_pack_mla"], lambda: oracle.lse_pack(ob, m, s, 1)))
+    items.append(("MLA combine", nb["lse_combine_mla"],
+                  lambda: oracle.lse_combine_packed(packed, w.mP, w.mT, w.mH, w.mDv, 1)))
+    tx, to = bits(w.t_qkv), bits(w.t_o)
+    items.append(("THD QKV varlen seq->head", nb["relayout_seq_to_head_varlen_thd_qkv"],
+                  lambda: oracle.varlen_seq_to_head(tx, w.t_cu, w.tP, 3, w.tH, w.tD)))
+    items.append(("THD O varlen head->seq", nb["relayout_head_to_seq_varlen_thd_o"],
+                  lambda: oracle.varlen_head_to_seq(to, w.t_cu, w.tP, 1, w.tH, w.tD)))
+    po, pl = bits(w.t_part), w.t_lse.cpu().numpy()
+    T, n_win = w.tT, 64
+    for k in range(n_win):
+        a, e = k * T // n_win, (k + 1) * T // n_win
+        items.append((f"THD causal combine [{a}, {e})", nb["lse_combine_varlen_thd"] * (e - a) / T,
+                      lambda a=a, e=e: oracle.lse_combine(po[:, a:e], pl[:, a:e], cu=w.t_cu, t_begin=a)))
+    return items
+
+
+def cpu_baseline(w, max_threads: int = 16):
+    """The oracle as it stands, timed on the host cores over the whole step's
+    workload (every operation at full size): once on one core, then with the
+    same independent calls spread over N threads (ctypes releases the GIL
+    during each oracle call).  The median of 3 runs is taken for each leg."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    items = _cpu_work_items(w)
+    total = sum(b for _, b, _ in items)
+    n_threads = max(1, min(max_threads, len(os.sched_getaffinity(0))))
+
+    def serial():
+        t0 = time.perf_counter()
+        for _, _, fn in items:
+            fn()
+        return time.perf_counter() - t0
+
+    def threaded():
+        t0 = time.perf_counter()
+        # costliest first so that the pool's tail is short
+        with ThreadPoolExecutor(max_workers=n_threads) as ex:
+            for f in [ex.submit(fn) for _, _, fn in sorted(items, key=lambda x: -x[1])]:
+                f.result()
+        return time.perf_counter() - t0
+
+    t1 = serial()
+    if t1 < 10.0:  # one run of a leg over 10 s, else the median of 3
+        t1 = statistics.median([t1, serial(), serial()])
+    tn = statistics.median(threaded() for _ in range(3))
+    sample = ("the whole step at full size: video P=4 QKV seq->head and O head->seq, MLA pack and combine, THD "
+              "QKV varlen seq->head and O head->seq, THD causal combine of all 131072 tokens (64 token windows); "
+              "C oracle (fp64, rounded once) on the same synthetic inputs downloaded from the GPU; GB/s = the "
+              "step's algorithmic bytes / oracle wall time (median of 3 runs, or one run of a leg over 10 s)")
     return {
-        "value": round(done_bytes / secs / 1e9, 4),
+        "value": round(total / tn / 1e9, 4),
         "unit": "GB/s",
-        "cores": 1,
+        "cores": n_threads,
         "kind": "oracle",
-        "seconds": round(secs, 2),
-        "sample": "; ".join(parts) + ". Single-threaded C oracle (fp64), same synthetic inputs "
-                  "downloaded from the GPU; GB/s = the sample's algorithmic bytes / oracle time.",
+        "seconds": round(tn, 2),
+        "sample": sample + f"; the same {len(items)} independent oracle calls on a pool of {n_threads} threads",
+        "single_core": {"value": round(total / t1 / 1e9, 4), "unit": "GB/s", "cores": 1, "seconds": round(t1, 2),
+                        "sample": sample + "; the calls one after another on one thread"},
         "cpu": _cpu_model(),
+        "affinity_cores": len(os.sched_getaffinity(0)),
     }
 
 
 def _cpu_model():
+    """Model name from /proc/cpuinfo, with the family, model and stepping
+    numbers (some hosts report only a generic brand string)."""
+    info = {}
     try:
         for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                return line.split(":", 1)[1].strip()
+            if ":" in line:
+                k, v = (x.strip() for x in line.split(":", 1))
+                info.setdefault(k, v)
+            if not line.strip() and info:
+                break
     except OSError:
-        pass
-    return "unknown"
+        return "unknown"
+    name = info.get("model name", "unknown")
+    extra = [f"{k} {info[k]}" for k in ("cpu family", "model", "stepping") if k in info]
+    return f"{name} ({', '.join(extra)})" if extra else name
 
 
 # ---------------------------------------------------------------------------
@@ -609,6 +627,36 @@ def summarize_counters(counter_dir, kernel, out_txt, command):
     print(text, end="")
 
 
+def profile_op(w, torch, name, calls):
+    """Run one operation of the step or beyond it `calls` times after 3
+    warmup calls (each on its own rotating buffer set where it has them),
+    printing its launch geometry and µs per call; for rocprofv3 runs."""
+    table = {n: fn for n, _, fn in w.ops()}
+    table.update({n: fn for n, _, fn in w.extension_ops()})
+    if name not in table:
+        raise SystemExit(f"unknown operation {name!r}; one of: {', '.join(table)}")
+    is_step = name in [n for n, _, _ in w.ops()]
+
+    def call(k):
+        if is_step:
+            return [fn for n, _, fn in w.ops(k=k) if n == name][0]()
+        return [fn for n, _, fn in w.extension_ops(k=k) if n == name][0]()
+
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        for k in range(3):
+            call(k)
+        torch.cuda.synchronize()
+        print(f"[profile-op] {name}: {calls} calls, launch {w.cam.last_launch()}", flush=True)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for k in range(calls):
+            call(k)
+        e1.record(stream)
+        torch.cuda.synchronize()
+    print(f"[profile-op] {name}: {e0.elapsed_time(e1) * 1000.0 / max(1, calls):.2f} us/call", flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -616,7 +664,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--calls", type=int, default=20, help="back-to-back calls per operation for µs/call")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for the CPU baseline")
+    ap.add_argument("--cpu-threads", type=int, default=16, help="most threads of the N-core CPU baseline leg")
+    ap.add_argument("--profile-op", default=None,
+                    help="run only this operation (a step or extension name) --calls times and exit (for rocprofv3)")
+    ap.add_argument("--digests-out", default=None, help="write the per-buffer input digests to this JSON file")
     ap.add_argument("--summarize-rocprof", nargs=4, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR", "BENCH_JSON"))
     ap.add_argument("--summarize-counters", nargs=2, metavar=("COUNTER_DIR", "KERNEL"))
     ap.add_argument("--summary-out", default=None)
@@ -644,7 +695,12 @@ def main():
     torch.cuda.set_device(0)
     props = torch.cuda.get_device_properties(0)
     w = Workload(torch, cam, synth)
+    if args.profile_op:
+        profile_op(w, torch, args.profile_op, args.calls)
+        return
     digests = w.input_digests()
+    if args.digests_out:
+        Path(args.digests_out).write_text(json.dumps(digests, indent=1) + "\n")
     nbytes = w.op_bytes()
     names = [n for n, _, _ in w.ops()]
     kern = {n: k for n, k, _ in w.ops()}
@@ -847,7 +903,6 @@ def main():
             "avg_launch_us": round(dom_us, 2),
             "algorithmic_bytes_per_launch": int(nbytes[dom]),
         },
-        "ops": op_table,
         "extensions": ext,
         "projection": projection,
         "thd_plan": plan_summary(w),
@@ -857,12 +912,22 @@ def main():
                    "compute_units": props.multi_processor_count,
                    "hbm_GiB": round(props.total_memory / 2**30, 1)},
         "kernel_source_hash": kernel_source_hash(),
-        "inputs_sha256_head_tail_MiB": digests,
+        "inputs_sha256": hashlib.sha256(json.dumps(digests, sort_keys=True).encode()).hexdigest()[:16],
+        "inputs_sha256_note": "SHA-256 over the per-buffer digests (shape, dtype, first and last MiB of every "
+                              "seeded input buffer); --digests-out writes them one by one",
         "timing": "value and ms_per_step: host clock around the K synchronized steps; ops[*].us_per_call: "
                   f"{args.calls} back-to-back calls of that operation alone between two HIP events; "
                   "ops[*].in_step_*: HIP events around the operation inside the steps",
     }
-    result["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(w, args.cpu_budget)
+    result["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(w, args.cpu_threads)
+    # the gated figures and the per-operation table last, so that the end of
+    # the line carries them
+    result["gates"] = {n: {"us_per_call": op_table[n]["us_per_call"],
+                           "frac_of_hbm_peak": op_table[n]["frac_of_hbm_peak"],
+                           "in_step_us_mean": op_table[n]["in_step_us_mean"]}
+                       for n in ("relayout_seq_to_head_video_p4_qkv", "relayout_head_to_seq_video_p4_o",
+                                 "lse_combine_mla")}
+    result["ops"] = op_table
     print(json.dumps(result), flush=True)
 
 

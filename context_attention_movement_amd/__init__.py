@@ -149,6 +149,35 @@ def _ptr(t: torch.Tensor | None) -> int | None:
     return None if t is None else t.data_ptr()
 
 
+def _check_buffer(t: torch.Tensor, name: str, shape, dtype: torch.dtype, contiguous: bool = True,
+                  inner_contiguous: bool = False) -> None:
+    """A caller-supplied output or input buffer: its shape and dtype must be
+    exactly what the call writes or reads, checked before any device check
+    or launch (the C ABI derives every extent from the sizes it is given, so
+    a short buffer would be written out of bounds)."""
+    if tuple(t.shape) != tuple(int(x) for x in shape):
+        raise ValueError(f"{name} must have shape {tuple(int(x) for x in shape)}, got {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if inner_contiguous and t.dim() and t.shape[-1] > 1 and t.stride(-1) != 1:
+        raise ValueError(f"{name} must have its last dimension contiguous")
+
+
+def _check_packed(packed: torch.Tensor, P: int, T: int, H: int, Dv: int, scatter_dim: int,
+                  dtype: torch.dtype) -> None:
+    """The packed exchange buffer must be contiguous and hold at least
+    lse_pack_bytes(P, T, H, Dv, scatter_dim) bytes."""
+    if dtype not in (torch.bfloat16, torch.float16):
+        raise TypeError(f"payload dtype must be bfloat16 or float16, got {dtype}")
+    n = lse_pack_bytes(P, T, H, Dv, scatter_dim, dtype)
+    if not packed.is_contiguous():
+        raise ValueError("packed must be contiguous")
+    if packed.numel() * packed.element_size() < n:
+        raise ValueError(f"packed needs {n} bytes, got {packed.numel() * packed.element_size()}")
+
+
 # ---------------------------------------------------------------------------
 # Dense relayout
 # ---------------------------------------------------------------------------
@@ -486,8 +515,13 @@ def lse_combine_packed(packed: torch.Tensor, P: int, T: int, H: int, Dv: int, sc
     """Combine, for every destination rank r, the chunks (p, r) of all sources
     (the exchange is a strided view of the packed buffer).  Returns
     (out [P*rows][Dv], lse_out [P*rows] or None)."""
-    _contig(packed, "packed")
+    _check_packed(packed, P, T, H, Dv, scatter_dim, dtype)
     rows = T * (H // P) if scatter_dim == 1 else (T // P) * H
+    if out is not None:
+        _check_buffer(out, "out", (P * rows, Dv), dtype)
+    if lse_out is not None and not isinstance(lse_out, bool):
+        _check_buffer(lse_out, "lse_out", (P * rows,), torch.float32)
+    _contig(packed, "packed")
     if out is None:
         out = torch.empty((P * rows, Dv), dtype=dtype, device=packed.device)
     _contig(out, "out")
@@ -503,21 +537,26 @@ def lse_combine_packed(packed: torch.Tensor, P: int, T: int, H: int, Dv: int, sc
     return out, lse_out
 
 
-def _combine_common(part_out, part_lse, out, lse_out):
-    _dev(part_out, "part_out")
-    _dev(part_lse, "part_lse")
+def _combine_common(part_out, part_lse, out, lse_out, out_name="out"):
     if part_out.dim() != 4 or part_out.stride(3) != 1:
         raise ValueError("part_out must be [P][T][H][D] with D contiguous")
+    _dt(part_out)
     if part_lse.dtype != torch.float32:
         raise TypeError("part_lse must be float32")
     P, T, H, D = part_out.shape
     if tuple(part_lse.shape) != (P, T, H):
         raise ValueError("part_lse must be [P][T][H]")
+    if out is not None:
+        _check_buffer(out, out_name, (T, H, D), part_out.dtype, contiguous=False, inner_contiguous=True)
+    if lse_out is not None and not isinstance(lse_out, bool):
+        _check_buffer(lse_out, "lse_out", (T, H), torch.float32, contiguous=False)
+    _dev(part_out, "part_out")
+    _dev(part_lse, "part_lse")
     if out is None:
         out = torch.empty((T, H, D), dtype=part_out.dtype, device=part_out.device)
-    _dev(out, "out")
+    _dev(out, out_name)
     if out.dim() != 3 or out.stride(2) != 1:
-        raise ValueError("out must be [T][H][D] with D contiguous")
+        raise ValueError(f"{out_name} must be [T][H][D] with D contiguous")
     if lse_out is True:
         lse_out = torch.empty((T, H), dtype=torch.float32, device=part_out.device)
     elif lse_out is False:
@@ -582,11 +621,7 @@ def lse_combine_backward(part_out: torch.Tensor, part_lse: torch.Tensor, g_out: 
     gradient of out, payload dtype), g_lse [T][H] fp32 or None (zero) ->
     (d_part_out [P][T][H][D], d_part_lse [P][T][H] fp32).  Any strides with D
     contiguous."""
-    P, T, H, D, _, _, _ = _combine_common(part_out, part_lse, g_out, None)
-    if g_out.dtype != part_out.dtype:
-        raise TypeError("g_out must have the payload dtype of part_out")
-    if tuple(g_out.shape) != (T, H, D):
-        raise ValueError("g_out must be [T][H][D]")
+    P, T, H, D, _, _, _ = _combine_common(part_out, part_lse, g_out, None, out_name="g_out")
     if g_lse is not None:
         _dev(g_lse, "g_lse")
         if g_lse.dtype != torch.float32 or tuple(g_lse.shape) != (T, H):
@@ -627,6 +662,11 @@ def lse_combine_packed_seq(packed: torch.Tensor, P: int, T: int, H: int, Dv: int
                            dtype=torch.bfloat16, out: torch.Tensor | None = None,
                            lse_out: torch.Tensor | None | bool = True):
     """lse_combine_packed with token-major output: (out [T][H][Dv], lse_out [T][H])."""
+    _check_packed(packed, P, T, H, Dv, scatter_dim, dtype)
+    if out is not None:
+        _check_buffer(out, "out", (T, H, Dv), dtype)
+    if lse_out is not None and not isinstance(lse_out, bool):
+        _check_buffer(lse_out, "lse_out", (T, H), torch.float32)
     _contig(packed, "packed")
     if out is None:
         out = torch.empty((T, H, Dv), dtype=dtype, device=packed.device)
@@ -647,13 +687,20 @@ def lse_combine_varlen_seq(part_out: torch.Tensor, part_lse: torch.Tensor, plan:
                            out: torch.Tensor | None = None, lse_out: torch.Tensor | None | bool = True):
     """lse_combine_varlen whose token rows go to the rank-major (sequence-
     sharded) order of the varlen relayout: (out [T][H][D], lse_out [T][H])."""
-    _dev(part_out, "part_out")
-    _dev(part_lse, "part_lse")
     if part_out.dim() != 4 or part_out.stride(3) != 1 or part_lse.dtype != torch.float32:
         raise ValueError("part_out must be [P][T][H][D] (D contiguous), part_lse float32 [P][T][H]")
+    _dt(part_out)
     P, T, H, D = part_out.shape
+    if tuple(part_lse.shape) != (P, T, H):
+        raise ValueError("part_lse must be [P][T][H]")
     if P != plan.P or T != plan.total_tokens:
         raise ValueError("the plan must match the partials' P and T")
+    if out is not None:
+        _check_buffer(out, "out", (T, H, D), part_out.dtype)
+    if lse_out is not None and not isinstance(lse_out, bool):
+        _check_buffer(lse_out, "lse_out", (T, H), torch.float32)
+    _dev(part_out, "part_out")
+    _dev(part_lse, "part_lse")
     if out is None:
         out = torch.empty((T, H, D), dtype=part_out.dtype, device=part_out.device)
     _contig(out, "out")

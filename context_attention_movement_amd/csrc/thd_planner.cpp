@@ -379,6 +379,12 @@ extern "C" cam_status thd_plan(const int32_t* cu_seqlens, int64_t nseq, int64_t 
         next[s.rank] += (s.hi - s.lo) * b;
         led.add(s.rank, s.lo, s.hi, +1);
     }
+    // every rank must hold exactly its capacity: the relayouts place rank r's
+    // slab at rank_off[r] and would leave rows unwritten otherwise
+    for (int64_t r = 0; r < world_size; ++r)
+        if (next[r] != B.cap[r] * b)
+            return set_error(CAM_ERR_SHAPE, "%s: rank %lld holds %lld tokens, its capacity is %lld", op,
+                             (long long)r, (long long)next[r], (long long)(B.cap[r] * b));
     span_start[best.size()] = cu_seqlens[nseq];
     rank_off[0] = 0;
     for (int64_t r = 0; r < world_size; ++r) {

@@ -242,6 +242,10 @@ cam_status ulysses_head_to_seq_spans(const void* in, void* out, const int32_t* s
  *
  * lse_pack_bytes returns the packed buffer size in bytes, or -1 for invalid
  * arguments (the reason is in cam_last_error()).
+ *
+ * Limits (CAM_ERR_UNSUPPORTED beyond them): P < 65536; rows per chunk below
+ * 2^31; one chunk's O-region below 2^31 access vectors; P*P chunks of tiles
+ * below 2^32 tiles.
  */
 int64_t lse_pack_bytes(int64_t P, int64_t T, int64_t H, int64_t Dv, int scatter_dim,
                        cam_dtype dt);
@@ -282,6 +286,12 @@ cam_status lse_pack(const void* out, int64_t o_sp, int64_t o_st, int64_t o_sh,
  *   t (position k of its sequence) is admitted only if piece p is non-empty and
  *   starts at or before k; otherwise neither its LSE nor its O row is read.
  *   cu_seqlens is a DEVICE array of nseq+1 int32; total_tokens = T.
+ *
+ * Limits of every combine entry point (lse_combine*, and their _seq, _planned
+ * and _backward forms): 1 <= P <= 64 (a row's partials are reduced across
+ * one wave; CAM_ERR_UNSUPPORTED above); T*H below 2^31 rows
+ * (CAM_ERR_UNSUPPORTED); strides non-negative; the varlen and planned forms
+ * need nseq >= 1 and T < 2^31.
  */
 cam_status lse_combine_packed(const void* packed, int64_t P, int64_t T, int64_t H, int64_t Dv,
                               int scatter_dim, cam_dtype dt, void* out, float* lse_out,
@@ -360,7 +370,8 @@ cam_status lse_combine_varlen_seq(const void* part_out, int64_t po_sp, int64_t p
  *   hops.  out_final (nullable, payload dt [T][H][D]) also receives the
  *   rounded result, for the last hop.  All strides are in elements (D
  *   contiguous); D % 4 == 0; accumulator rows 16-byte and payload rows 8-byte
- *   aligned.  Updates in place; no buffer may overlap another.
+ *   aligned.  Updates in place; no buffer may overlap another.  T*H must be
+ *   below 2^31 rows and every stride non-negative (CAM_ERR_UNSUPPORTED).
  */
 cam_status lse_merge(float* acc_out, int64_t a_st, int64_t a_sh, float* acc_lse, int64_t al_st,
                      int64_t al_sh, const void* part_out, int64_t p_st, int64_t p_sh,

@@ -77,6 +77,8 @@ def _load():
         "orc_lse_combine_packed_seq": (None, [vp, i64, i64, i64, i64, C.c_int, C.c_int, vp, vp]),
         "orc_thd_plan": (C.c_int, [vp, i64, i64, i64, i64, i64, C.c_double, C.c_double, i64, vp, vp, vp, vp,
                                    vp, vp, vp]),
+        "orc_thd_plan_candidate_trace": (C.c_int, [vp, i64, i64, i64, i64, C.c_double, C.c_double, C.c_int,
+                                                   vp, i64, vp, vp, i64, vp]),
         "orc_span_seq_to_head": (None, [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64]),
         "orc_span_head_to_seq": (None, [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64]),
         "orc_plan_first_positions": (None, [vp, i64, i64, vp, vp, i64, vp]),
@@ -431,6 +433,49 @@ def thd_plan(cu, world_size: int, block_size: int = 64, min_split_tokens: int = 
         k = int(n[0])
         return {"span_start": ss[:k + 1].copy(), "span_rank": sr[:k].copy(), "span_local": sl[:k].copy(),
                 "rank_off": ro.copy(), "rank_cost": rc[:world_size].copy(), "grid": int(g[0])}
+
+
+TRACE_MAX_W = 16
+
+
+class _PlanTrace(C.Structure):
+    _fields_ = [(n, C.c_int64) for n in ("step", "over", "to", "amount", "top_seq", "top_a", "top_e",
+                                        "bot_seq", "bot_a", "bot_e", "chose_bottom", "moved_seq", "moved_a",
+                                        "moved_e")] + [("blk", C.c_int64 * TRACE_MAX_W),
+                                                       ("caus", C.c_int64 * TRACE_MAX_W)]
+
+
+def thd_plan_candidate_trace(cu, world_size: int, g: int, block_size: int = 64, min_split_tokens: int = 8192,
+                             token_weight: float = 1.0, causal_weight: float = 1.0):
+    """One planner candidate (g = 0 contiguous, g >= 1 a grid) with the record
+    of its rebalancing steps: (spans [(seq, first block, end block, rank)],
+    records [dict per C1 move (step 1) and C2 piece (step 2)], each with the
+    ranks' blocks and causal work just before).  world_size <= 16."""
+    cu = np.ascontiguousarray(np.asarray(cu, dtype=np.int32))
+    nseq = cu.size - 1
+    assert 1 <= world_size <= TRACE_MAX_W
+    cap_t, cap_s = 256, 4 * (nseq + 8 * world_size) + 64
+    while True:
+        rec = (_PlanTrace * cap_t)()
+        spans = np.empty((cap_s, 4), dtype=np.int64)
+        nt = np.zeros(1, dtype=np.int64)
+        ns = np.zeros(1, dtype=np.int64)
+        code = _load().orc_thd_plan_candidate_trace(_p(cu), nseq, world_size, block_size, min_split_tokens,
+                                                    token_weight, causal_weight, g, C.addressof(rec), cap_t,
+                                                    _p(nt), _p(spans), cap_s, _p(ns))
+        if code != 0:
+            raise ValueError(PLAN_ERRORS.get(code, str(code)))
+        if nt[0] <= cap_t and ns[0] <= cap_s:
+            break
+        cap_t, cap_s = int(max(cap_t, nt[0])), int(max(cap_s, ns[0]))
+    out = []
+    for k in range(int(nt[0])):
+        r = rec[k]
+        d = {n: int(getattr(r, n)) for n, _ in _PlanTrace._fields_[:14]}
+        d["blk"] = [int(r.blk[i]) for i in range(world_size)]
+        d["caus"] = [int(r.caus[i]) for i in range(world_size)]
+        out.append(d)
+    return [tuple(int(v) for v in spans[k]) for k in range(int(ns[0]))], out
 
 
 def span_seq_to_head(x: np.ndarray, plan: dict, P: int, B: int, H: int, D: int) -> np.ndarray:

@@ -834,6 +834,27 @@ typedef struct {
     int64_t n, cap;
 } orc_spans;
 
+/* Optional record of the rebalancing steps C1 and C2 (test instrumentation;
+ * it changes no decision): per C1 move and per C2 piece, the ranks, the
+ * candidate spans, the blocks moved or placed, and every rank's blocks and
+ * causal work just before. */
+#define ORC_TRACE_MAX_W 16
+typedef struct {
+    int64_t step;                   /* 1: C1 move, 2: C2 piece */
+    int64_t over, to;               /* C1: overfull and receiving rank; C2: -1 and receiving rank */
+    int64_t amount;                 /* C1: min(excess of over, room of to); C2: blocks placed */
+    int64_t top_seq, top_a, top_e;  /* C1: o's long span ending highest, before the move */
+    int64_t bot_seq, bot_a, bot_e;  /* C1: o's long span starting lowest, before the move */
+    int64_t chose_bottom;           /* C1 */
+    int64_t moved_seq, moved_a, moved_e;
+    int64_t blk[ORC_TRACE_MAX_W], caus[ORC_TRACE_MAX_W];
+} orc_plan_trace;
+
+typedef struct {
+    orc_plan_trace* rec;
+    int64_t cap, n;
+} orc_trace_buf;
+
 static void spans_add(orc_spans* v, int64_t seq, int64_t a, int64_t e, int64_t rank)
 {
     if (a >= e)
@@ -914,8 +935,24 @@ static void spans_normalize(orc_spans* v)
 }
 
 /* grid g >= 1, or the contiguous layout for g = 0 */
+static orc_plan_trace* trace_next(orc_trace_buf* tb, const orc_loads* L)
+{
+    if (!tb || L->W > ORC_TRACE_MAX_W)
+        return NULL;
+    orc_plan_trace* t = tb->n < tb->cap ? &tb->rec[tb->n] : NULL;
+    tb->n++;
+    if (t) {
+        memset(t, 0, sizeof(*t));
+        for (int64_t r = 0; r < L->W; ++r) {
+            t->blk[r] = L->blk[r];
+            t->caus[r] = L->caus[r];
+        }
+    }
+    return t;
+}
+
 static void plan_candidate(int g, const int64_t* nb, int64_t nseq, int64_t W, int64_t b, int64_t min_split,
-                           double wt, double wc, const int64_t* capb, orc_spans* out)
+                           double wt, double wc, const int64_t* capb, orc_spans* out, orc_trace_buf* tb)
 {
     int64_t* blk = (int64_t*)calloc((size_t)W, sizeof(int64_t));
     int64_t* caus = (int64_t*)calloc((size_t)W, sizeof(int64_t));
@@ -1024,6 +1061,23 @@ static void plan_candidate(int g, const int64_t* nb, int64_t nseq, int64_t W, in
             double ml = co > cu ? co : cu;
             loads_add(&L, u, al, al + xl, -1);
             loads_add(&L, o, al, al + xl, +1);
+            orc_plan_trace* tr = trace_next(tb, &L);
+            if (tr) {
+                tr->step = 1;
+                tr->over = o;
+                tr->to = u;
+                tr->amount = x;
+                tr->top_seq = out->s[dh].seq;
+                tr->top_a = out->s[dh].a;
+                tr->top_e = out->s[dh].e;
+                tr->bot_seq = out->s[dl].seq;
+                tr->bot_a = out->s[dl].a;
+                tr->bot_e = out->s[dl].e;
+                tr->chose_bottom = ml < mh;
+                tr->moved_seq = ml < mh ? out->s[dl].seq : out->s[dh].seq;
+                tr->moved_a = ml < mh ? al : eh - xh;
+                tr->moved_e = ml < mh ? al + xl : eh;
+            }
             if (ml < mh) {
                 int64_t seq = out->s[dl].seq;
                 out->s[dl].a = al + xl;
@@ -1047,6 +1101,16 @@ static void plan_candidate(int g, const int64_t* nb, int64_t nseq, int64_t W, in
                 int64_t k = capb[u] - blk[u];
                 if (nb[i] - a < k)
                     k = nb[i] - a;
+                orc_plan_trace* tr = trace_next(tb, &L);
+                if (tr) {
+                    tr->step = 2;
+                    tr->over = -1;
+                    tr->to = u;
+                    tr->amount = k;
+                    tr->moved_seq = i;
+                    tr->moved_a = a;
+                    tr->moved_e = a + k;
+                }
                 spans_add(out, i, a, a + k, u);
                 loads_add(&L, u, a, a + k, +1);
                 a += k;
@@ -1169,7 +1233,7 @@ int orc_thd_plan(const int32_t* cu, int64_t nseq, int64_t W, int64_t block_size,
     int64_t* caus = (int64_t*)malloc(sizeof(int64_t) * (size_t)W);
     int64_t* cnt = (int64_t*)malloc(sizeof(int64_t) * (size_t)W);
     for (int g = 0; g <= 6; ++g) {
-        plan_candidate(g, nb, nseq, W, b, min_split_tokens, token_weight, causal_weight, capb, &cand);
+        plan_candidate(g, nb, nseq, W, b, min_split_tokens, token_weight, causal_weight, capb, &cand, NULL);
         for (int64_t r = 0; r < W; ++r)
             blk[r] = caus[r] = cnt[r] = 0;
         for (int64_t k = 0; k < cand.n; ++k) {
@@ -1231,6 +1295,60 @@ int orc_thd_plan(const int32_t* cu, int64_t nseq, int64_t W, int64_t block_size,
     free(caus);
     free(cnt);
     return rc;
+}
+
+/*
+ * One candidate of orc_thd_plan (g = 0 contiguous, g >= 1 a grid) with the
+ * record of its rebalancing steps C1 and C2 (test instrumentation: the tests
+ * recompute each decision from the recorded loads).  Writes up to max_trace
+ * records and sets *n_trace to the number made (W <= 16 for records), and
+ * the candidate's spans (sequence, first block, end block, rank) up to
+ * max_spans, *n_spans to their number.  Returns 0, or -1 .. -3 as
+ * orc_thd_plan.
+ */
+int orc_thd_plan_candidate_trace(const int32_t* cu, int64_t nseq, int64_t W, int64_t block_size,
+                                 int64_t min_split_tokens, double token_weight, double causal_weight, int g,
+                                 orc_plan_trace* trace, int64_t max_trace, int64_t* n_trace, int64_t* spans,
+                                 int64_t max_spans, int64_t* n_spans)
+{
+    const int64_t b = block_size;
+    if (W < 1 || b < 1 || min_split_tokens < 1 || min_split_tokens % b != 0 || g < 0 || g > 6)
+        return -1;
+    if (nseq < 0 || cu[0] != 0)
+        return -2;
+    int64_t* nb = (int64_t*)malloc(sizeof(int64_t) * (size_t)(nseq + 1));
+    int64_t N = 0;
+    for (int64_t i = 0; i < nseq; ++i) {
+        int64_t L = (int64_t)cu[i + 1] - cu[i];
+        if (L < 0 || L % b != 0) {
+            free(nb);
+            return -2;
+        }
+        nb[i] = L / b;
+        N += nb[i];
+    }
+    if (N < W) {
+        free(nb);
+        return -3;
+    }
+    int64_t* capb = (int64_t*)malloc(sizeof(int64_t) * (size_t)W);
+    for (int64_t r = 0; r < W; ++r)
+        capb[r] = (r + 1) * N / W - r * N / W;
+    orc_spans cand = {0, 0, 0};
+    orc_trace_buf tb = {trace, max_trace, 0};
+    plan_candidate(g, nb, nseq, W, b, min_split_tokens, token_weight, causal_weight, capb, &cand, &tb);
+    *n_trace = tb.n;
+    *n_spans = cand.n;
+    for (int64_t k = 0; k < cand.n && k < max_spans; ++k) {
+        spans[4 * k + 0] = cand.s[k].seq;
+        spans[4 * k + 1] = cand.s[k].a;
+        spans[4 * k + 2] = cand.s[k].e;
+        spans[4 * k + 3] = cand.s[k].rank;
+    }
+    free(cand.s);
+    free(nb);
+    free(capb);
+    return 0;
 }
 
 /*

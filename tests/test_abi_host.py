@@ -297,3 +297,80 @@ def test_projection_rejections(lib):
     assert f(None, W, O, 100, 64, 2, 1, 4, 64, BF16, None) == NULL
     assert f(X, W, X + 64, 100, 64, 2, 1, 4, 64, BF16, None) == OVERLAP
     assert f(X, W, O, 0, 64, 2, 1, 4, 64, BF16, None) == OK              # nothing to do
+
+
+# --- the binding rejects caller buffers that do not fit the call, before any
+# device check or launch (host tensors reach the shape check first) ----------
+
+def test_binding_rejects_wrong_combine_buffers(cam):
+    import torch
+    P, T, H, D = 2, 5, 4, 8
+    po = torch.zeros((P, T, H, D), dtype=torch.bfloat16)
+    pl = torch.zeros((P, T, H), dtype=torch.float32)
+    with pytest.raises(ValueError, match="out must have shape"):
+        cam.lse_combine(po, pl, out=torch.zeros((T, H, D - 1), dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="out must have shape"):
+        cam.lse_combine(po, pl, out=torch.zeros((T - 1, H, D), dtype=torch.bfloat16))
+    with pytest.raises(TypeError, match="out must be torch.bfloat16"):
+        cam.lse_combine(po, pl, out=torch.zeros((T, H, D), dtype=torch.float16))
+    with pytest.raises(ValueError, match="lse_out must have shape"):
+        cam.lse_combine(po, pl, lse_out=torch.zeros((T, H - 1), dtype=torch.float32))
+    with pytest.raises(TypeError, match="lse_out must be torch.float32"):
+        cam.lse_combine(po, pl, lse_out=torch.zeros((T, H), dtype=torch.float16))
+    with pytest.raises(ValueError, match="g_out must have shape"):
+        cam.lse_combine_backward(po, pl, torch.zeros((T, H, D + 1), dtype=torch.bfloat16))
+    with pytest.raises(TypeError, match="g_out must be torch.bfloat16"):
+        cam.lse_combine_backward(po, pl, torch.zeros((T, H, D), dtype=torch.float16))
+    cu = torch.tensor([0, T], dtype=torch.int32)
+    with pytest.raises(ValueError, match="out must have shape"):
+        cam.lse_combine_varlen(po, pl, cu, out=torch.zeros((T, H, 2 * D), dtype=torch.bfloat16))
+    # a correctly shaped host buffer passes the shape check and then fails the device check
+    with pytest.raises(ValueError, match="device tensor"):
+        cam.lse_combine(po, pl, out=torch.zeros((T, H, D), dtype=torch.bfloat16))
+
+
+def test_binding_rejects_short_packed_and_wrong_outputs(cam):
+    import torch
+    P, T, H, Dv = 2, 4, 4, 8
+    n = cam.lse_pack_bytes(P, T, H, Dv, 1)
+    rows = T * (H // P)
+    with pytest.raises(ValueError, match=f"packed needs {n} bytes"):
+        cam.lse_combine_packed(torch.zeros(n - 16, dtype=torch.uint8), P, T, H, Dv, 1)
+    with pytest.raises(ValueError, match=f"packed needs {n} bytes"):
+        cam.lse_combine_packed_seq(torch.zeros(n - 1, dtype=torch.uint8), P, T, H, Dv, 1)
+    packed = torch.zeros(n, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="out must have shape"):
+        cam.lse_combine_packed(packed, P, T, H, Dv, 1, out=torch.zeros((P * rows - 1, Dv), dtype=torch.bfloat16))
+    with pytest.raises(TypeError, match="out must be torch.bfloat16"):
+        cam.lse_combine_packed(packed, P, T, H, Dv, 1, out=torch.zeros((P * rows, Dv), dtype=torch.float32))
+    with pytest.raises(ValueError, match="lse_out must have shape"):
+        cam.lse_combine_packed(packed, P, T, H, Dv, 1, lse_out=torch.zeros(P * rows - 1, dtype=torch.float32))
+    with pytest.raises(ValueError, match="out must have shape"):
+        cam.lse_combine_packed_seq(packed, P, T, H, Dv, 1, out=torch.zeros((T, H, Dv - 8), dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="lse_out must have shape"):
+        cam.lse_combine_packed_seq(packed, P, T, H, Dv, 1, lse_out=torch.zeros((T, H + 1), dtype=torch.float32))
+    with pytest.raises(TypeError, match="payload dtype"):
+        cam.lse_combine_packed(packed, P, T, H, Dv, 1, dtype=torch.float32)
+    with pytest.raises(ValueError, match="device tensor"):
+        cam.lse_combine_packed(packed, P, T, H, Dv, 1)
+
+
+def test_binding_rejects_wrong_varlen_seq_outputs(cam):
+    import torch
+    P, H, D = 2, 4, 8
+    lens = [3, 6]
+    cu = synth.cu_seqlens(lens)
+    T = int(cu[-1])
+    rank_cu = np.empty((P, len(lens) + 1), dtype=np.int32)
+    rank_off = np.empty(P + 1, dtype=np.int64)
+    plan = cam.VarlenPlan(P, len(lens), T, cu, rank_cu, rank_off, None, None, None)
+    po = torch.zeros((P, T, H, D), dtype=torch.bfloat16)
+    pl = torch.zeros((P, T, H), dtype=torch.float32)
+    with pytest.raises(ValueError, match="out must have shape"):
+        cam.lse_combine_varlen_seq(po, pl, plan, out=torch.zeros((T, H, D - 1), dtype=torch.bfloat16))
+    with pytest.raises(TypeError, match="out must be torch.bfloat16"):
+        cam.lse_combine_varlen_seq(po, pl, plan, out=torch.zeros((T, H, D), dtype=torch.float16))
+    with pytest.raises(ValueError, match="lse_out must have shape"):
+        cam.lse_combine_varlen_seq(po, pl, plan, lse_out=torch.zeros((T + 1, H), dtype=torch.float32))
+    with pytest.raises(ValueError, match="part_lse must be"):
+        cam.lse_combine_varlen_seq(po, pl[:, :-1], plan)

@@ -82,16 +82,69 @@ def _check_invariants(plan, cu, W, b, min_split, max_chunks):
     assert plan["rank_cost"].max() <= _contiguous_max(cu, W, b) + 1e-9
 
 
-def test_golden_hand_plan(orc):
-    g = json.loads((GOLDEN / "thd_plan_small.json").read_text())
-    i, e = g["input"], g["expected"]
+GOLDEN_PLANS = sorted(p.name for p in GOLDEN.glob("thd_plan_*.json"))
+
+
+def _golden_plan(orc_mod, name):
+    g = json.loads((GOLDEN / name).read_text())
+    i = g["input"]
     cu = synth.cu_seqlens(i["lengths"])
-    p = orc.thd_plan(cu, i["world_size"], i["block_size"], i["min_split_tokens"], i["max_chunks_per_rank"],
-                     i["token_weight"], i["causal_weight"])
+    return g["expected"], orc_mod.thd_plan(cu, i["world_size"], i["block_size"], i["min_split_tokens"],
+                                           i["max_chunks_per_rank"], i["token_weight"], i["causal_weight"])
+
+
+def _matches(e, p):
+    return (p["grid"] == e["grid"] and all(p[k].tolist() == e[k] for k in
+                                           ("span_start", "span_rank", "span_local", "rank_off"))
+            and p["rank_cost"].tolist() == e["rank_cost"])
+
+
+@pytest.mark.parametrize("name", GOLDEN_PLANS)
+def test_golden_hand_plan(orc, name):
+    e, p = _golden_plan(orc, name)
     assert p["grid"] == e["grid"]
     for k in ("span_start", "span_rank", "span_local", "rank_off"):
         assert p[k].tolist() == e[k], k
     assert p["rank_cost"].tolist() == e["rank_cost"]
+
+
+# Planted mistakes (in a copy of the oracle built here, never in the product):
+# each hand-worked plan must catch the rebalancing step it reaches taking the
+# other choice.
+MUTANTS = {
+    # C1 takes the top blocks where the bottom ones are cheaper and vice versa
+    "c1_flipped": ("            if (ml < mh) {", "            if (!(ml < mh)) {"),
+    # C2 lays a short's pieces into the lowest rank with room, not the cheapest
+    "c2_lowest_rank": ("                int64_t u = cheapest_with_room(&L, 1);\n                int64_t k = capb[u] - blk[u];",
+                       "                int64_t u = 0;\n                while (capb[u] - blk[u] < 1)\n                    ++u;\n"
+                       "                int64_t k = capb[u] - blk[u];"),
+}
+CAUGHT_BY = {"c1_flipped": ["thd_plan_c1_bottom.json", "thd_plan_c1_top.json"],
+             "c2_lowest_rank": ["thd_plan_c2_split_short.json"]}
+
+
+@pytest.mark.parametrize("mutant", sorted(MUTANTS))
+def test_golden_plans_catch_planted_rebalancing_mistakes(orc, tmp_path, mutant):
+    import importlib.util
+    import shutil
+    import subprocess
+
+    src = (Path(orc.__file__).parent / "cam_oracle.c").read_text()
+    old, new = MUTANTS[mutant]
+    assert src.count(old) == 1, "the planted mistake must replace exactly one statement"
+    d = tmp_path / "oracle"
+    d.mkdir()
+    (d / "cam_oracle.c").write_text(src.replace(old, new))
+    shutil.copy(Path(orc.__file__), d / "__init__.py")
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off", "-o", str(d / "liboracle.so"),
+                    str(d / "cam_oracle.c"), "-lm"], check=True)
+    spec = importlib.util.spec_from_file_location("oracle_mutant_" + mutant, d / "__init__.py")
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    for name in GOLDEN_PLANS:
+        e, p = _golden_plan(mod, name)
+        if name in CAUGHT_BY[mutant]:
+            assert not _matches(e, p), f"{name} does not catch {mutant}"
 
 
 @pytest.mark.parametrize("kw,W,kind", [
@@ -264,3 +317,105 @@ def test_span_relayout_brute_force(orc):
             row = B * int(ro[p]) + bb * Tp + l
             for r in range(W):
                 assert np.array_equal(y[r, bb, t], x[row, r * Hp:(r + 1) * Hp])
+
+
+def _trace_batch(seed):
+    """Random packed batches shaped to reach the rebalancing steps.  Seeds
+    below 12: one to three long sequences and small shorts, so that the snake
+    overfills ranks (C1).  Seeds from 12: mostly shorts near a rank's share,
+    so that some fit nowhere whole (C2)."""
+    rng = np.random.default_rng(7000 + seed)
+    W = int(rng.integers(2, 9))
+    b = int(rng.choice([1, 2, 4]))
+    min_split = 16 * b
+    if seed < 12:
+        longs = [int(x) for x in rng.integers(16, 80, size=int(rng.integers(1, 4)))]
+        share = max(2, (sum(longs) + 12 * W) // W)
+        shorts = [int(x) for x in rng.integers(1, min(16, share + 2), size=int(rng.integers(W, 3 * W + 1)))]
+    else:
+        longs = [int(rng.integers(16, 60))] if rng.integers(0, 2) else []
+        shorts = [int(x) for x in rng.integers(4, 16, size=int(rng.integers(W + 1, 2 * W + 3)))]
+    lens = longs + shorts
+    rng.shuffle(lens)
+    return synth.cu_seqlens([x * b for x in lens]), W, b, min_split
+
+
+def _range_cost(a, e, b, wt, wc):
+    """Cost of blocks [a, e) of a sequence in exact integers: wt per token plus
+    wc * (k + 1) for each token position k."""
+    return wt * (e - a) * b + wc * sum(range(a * b + 1, e * b + 1))
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_rebalancing_decisions_recomputed_in_integers(orc, seed):
+    """Every C1 move and C2 piece of every grid candidate, recomputed from the
+    recorded loads in Python integers: C1 takes the overfull rank with the
+    lowest index, sends min(its excess, the room of the cheapest rank with
+    room) blocks to that rank, and of the two candidate moves (the top of the
+    highest long span, the bottom of the lowest) takes the one whose larger
+    cost of the pair is smaller (ties: the top); C2 lays a short's next piece
+    into the cheapest rank with room (ties: the lowest), as far as its room
+    allows; each record's loads are the previous record's after its move."""
+    cu, W, b, min_split = _trace_batch(seed)
+    lens = np.diff(cu) // b
+    N = int(lens.sum())
+    cap = [(r + 1) * N // W - r * N // W for r in range(W)]
+    n_c1 = n_c1_distinct = n_c2 = 0
+    for wt, wc in ((1, 1), (3, 1), (1, 4), (0, 1), (2, 0)):
+        for g in range(1, 7):
+            _, recs = orc.thd_plan_candidate_trace(cu, W, g, b, min_split, float(wt), float(wc))
+            prev = None
+            for t in recs:
+                blk, caus = list(t["blk"]), list(t["caus"])
+                if prev is not None:
+                    assert (blk, caus) == prev, "a record's loads must follow from the previous move"
+                cost = [wt * blk[r] * b + wc * caus[r] for r in range(W)]
+                room = [cap[r] - blk[r] for r in range(W)]
+                with_room = [r for r in range(W) if room[r] >= 1]
+                to = min(with_room, key=lambda r: (cost[r], r))
+                assert t["to"] == to
+                a, e = t["moved_a"], t["moved_e"]
+                moved_caus = sum(range(a * b + 1, e * b + 1))
+                if t["step"] == 1:
+                    over = [r for r in range(W) if blk[r] > cap[r]][0]
+                    assert t["over"] == over
+                    amount = min(blk[over] - cap[over], room[to])
+                    assert t["amount"] == amount
+                    n_top = min(amount, t["top_e"] - t["top_a"])
+                    n_bot = min(amount, t["bot_e"] - t["bot_a"])
+                    c_top = _range_cost(t["top_e"] - n_top, t["top_e"], b, wt, wc)
+                    c_bot = _range_cost(t["bot_a"], t["bot_a"] + n_bot, b, wt, wc)
+                    via_top = max(cost[over] - c_top, cost[to] + c_top)
+                    via_bot = max(cost[over] - c_bot, cost[to] + c_bot)
+                    take_bottom = via_bot < via_top
+                    assert bool(t["chose_bottom"]) == take_bottom, (t, via_top, via_bot)
+                    if take_bottom:
+                        assert (t["moved_seq"], a, e) == (t["bot_seq"], t["bot_a"], t["bot_a"] + n_bot)
+                    else:
+                        assert (t["moved_seq"], a, e) == (t["top_seq"], t["top_e"] - n_top, t["top_e"])
+                    n_c1 += 1
+                    n_c1_distinct += via_top != via_bot
+                    blk[over] -= e - a
+                    caus[over] -= moved_caus
+                else:
+                    assert t["step"] == 2
+                    assert t["amount"] == e - a == min(room[to], int(lens[t["moved_seq"]]) - a)
+                    n_c2 += 1
+                blk[to] += e - a
+                caus[to] += moved_caus
+                prev = (blk, caus)
+    if seed < 12:
+        assert n_c1 > 0 and n_c1_distinct > 0, "the batch must reach C1 with two different candidate costs"
+    if seed % 3 == 0:
+        print(f"seed {seed}: W={W} b={b}: {n_c1} C1 moves ({n_c1_distinct} with distinct costs), {n_c2} C2 pieces")
+
+
+def test_rebalancing_traces_reach_c2(orc):
+    """Across the traced batches, shorts that fit nowhere whole occur (C2)."""
+    total = 0
+    for seed in range(12, 24):
+        cu, W, b, min_split = _trace_batch(seed)
+        for g in range(1, 7):
+            _, recs = orc.thd_plan_candidate_trace(cu, W, g, b, min_split)
+            total += sum(t["step"] == 2 for t in recs)
+    assert total >= 50, total

@@ -123,3 +123,24 @@ def test_first_positions_match_oracle(cam, orc):
             plan = cam.ThdPlan(W, int(cu[-1]), cu, q["span_start"], q["span_rank"], q["span_local"], q["rank_off"],
                                q["rank_cost"], q["grid"])
             assert np.array_equal(plan.first_pos_host, orc.plan_first_positions(cu, q, W))
+
+
+@pytest.mark.parametrize("name", sorted(p.name for p in (__import__("pathlib").Path(__file__).resolve().parent
+                                                          / "golden").glob("thd_plan_*.json")))
+def test_planner_equals_hand_worked_plans(cam, name):
+    """The library's planner gives each hand-worked plan exactly (the plans
+    that reach the rebalancing steps included)."""
+    import json
+    from pathlib import Path
+    g = json.loads((Path(__file__).resolve().parent / "golden" / name).read_text())
+    i, e = g["input"], g["expected"]
+    cfg = cam.ThdPlannerConfig(block_size=i["block_size"], min_split_tokens=i["min_split_tokens"],
+                               max_chunks_per_rank=i["max_chunks_per_rank"], token_weight=i["token_weight"],
+                               causal_weight=i["causal_weight"])
+    p = cam.thd_plan(synth.cu_seqlens(i["lengths"]), i["world_size"], cfg)
+    assert p.grid == e["grid"]
+    assert p.span_start_host.tolist() == e["span_start"]
+    assert p.span_rank_host.tolist() == e["span_rank"]
+    assert p.span_local_host.tolist() == e["span_local"]
+    assert p.rank_off_host.tolist() == e["rank_off"]
+    assert p.rank_cost.tolist() == e["rank_cost"]
