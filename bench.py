@@ -335,6 +335,9 @@ class Workload:
         def p8_s2h():
             cam.ulysses_seq_to_head(self.v8_qkv, 8, out=self.v8_qkv_out)
 
+        def lds_s2h():
+            cam.ablation_seq_to_head_lds(self.v_qkv, self.vP, LDS_ROWS_PER_TILE, out=self.v_qkv_out)
+
         def p8_h2s():
             cam.ulysses_head_to_seq(self.v8_o, 8, out=self.v8_o_out)
 
@@ -350,7 +353,75 @@ class Workload:
             ("combine_to_sequence_shards_mla (fused)", comb_bytes, fused),
             ("combine_then_head_to_seq_mla (unfused)", comb_bytes + 2 * out_bytes, unfused),
             ("combine_varlen_to_sequence_shards_thd (fused)", self.op_bytes()["lse_combine_varlen_thd"], thd_fused),
+            ("relayout_seq_to_head_video_p4_qkv_lds_staged (ablation)",
+             self.op_bytes()["relayout_seq_to_head_video_p4_qkv"], lds_s2h),
         ]
+
+
+LDS_ROWS_PER_TILE = 4  # rows staged per workgroup by the LDS-staged relayout ablation
+
+
+def paired_ab(torch, stream, fa, fb, pairs=8, calls=10):
+    """Paired A/B timing: `pairs` pairs of (calls back-to-back calls of A, the
+    same of B) between HIP events, the order alternating from pair to pair.
+    Returns the per-pair relative differences (B - A) / A."""
+    def t(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(calls):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1000.0 / calls
+
+    with torch.cuda.stream(stream):
+        for _ in range(2):
+            fa()
+            fb()
+        torch.cuda.synchronize()
+        out = []
+        for i in range(pairs):
+            if i % 2 == 0:
+                ta, tb = t(fa), t(fb)
+            else:
+                tb, ta = t(fb), t(fa)
+            out.append((ta, tb))
+    return out
+
+
+def ab_decision(torch, stream, name, fa, fb, pairs=8, calls=10):
+    """A paired comparison with a null control (A against itself, same
+    protocol): the noise floor is the largest per-pair |difference| of the
+    null control, the threshold twice that; B is called faster or slower only
+    if its median difference exceeds the threshold and every pair agrees in
+    sign, otherwise neutral."""
+    null = paired_ab(torch, stream, fa, fa, pairs, calls)
+    res = paired_ab(torch, stream, fa, fb, pairs, calls)
+    out = ab_verdict(null, res)
+    out.update({"comparison": name,
+                "protocol": f"{pairs} pairs x {calls} back-to-back calls per side, order alternating; null control "
+                            "A against A; noise floor = largest per-pair |difference| of the null control; threshold "
+                            "= twice the floor, with every pair in the same direction"})
+    return out
+
+
+def ab_verdict(null, res):
+    """The decision rule of ab_decision on per-pair (A, B) timings."""
+    dn = [(b - a) / a for a, b in null]
+    d = [(b - a) / a for a, b in res]
+    floor = max(abs(x) for x in dn)
+    med = statistics.median(d)
+    faster = sum(1 for x in d if x < 0)
+    if med < -2 * floor and faster == len(d):
+        verdict = "B faster"
+    elif med > 2 * floor and faster == 0:
+        verdict = "B slower"
+    else:
+        verdict = "neutral"
+    return {"A_us_median": round(statistics.median(a for a, _ in res), 2),
+            "B_us_median": round(statistics.median(b for _, b in res), 2),
+            "B_minus_A_median_pct": round(100 * med, 3), "B_faster_pairs": f"{faster}/{len(d)}",
+            "noise_floor_pct": round(100 * floor, 3), "threshold_pct": round(200 * floor, 3), "verdict": verdict}
 
 
 def plan_summary(w):
@@ -631,13 +702,15 @@ def profile_op(w, torch, name, calls):
     """Run one operation of the step or beyond it `calls` times after 3
     warmup calls (each on its own rotating buffer set where it has them),
     printing its launch geometry and µs per call; for rocprofv3 runs."""
-    table = {n: fn for n, _, fn in w.ops()}
-    table.update({n: fn for n, _, fn in w.extension_ops()})
+    copy_ref = "copy_video_qkv"  # the plain copy of the video Q/K/V operand (the ceiling reference)
+    table = [n for n, _, _ in w.ops()] + [n for n, _, _ in w.extension_ops()] + [copy_ref]
     if name not in table:
         raise SystemExit(f"unknown operation {name!r}; one of: {', '.join(table)}")
     is_step = name in [n for n, _, _ in w.ops()]
 
     def call(k):
+        if name == copy_ref:
+            return w.cam.copy(w.v_qkv, w.v_qkv_out)
         if is_step:
             return [fn for n, _, fn in w.ops(k=k) if n == name][0]()
         return [fn for n, _, fn in w.extension_ops(k=k) if n == name][0]()
@@ -812,6 +885,15 @@ def main():
     copy_bytes = 2 * src.numel() * src.element_size()
     copy_gbps = copy_bytes / (e0.elapsed_time(e1) * 100.0) / 1e3
 
+    # ---- kernel-choice evidence: the direct seq->head kernel (A) against the
+    # LDS-staged one (B) on the video P = 4 Q/K/V operand, paired A/B with a
+    # null control
+    ablations = [ab_decision(torch, stream, "relayout seq->head video P=4 QKV: direct 16-byte moves (A) vs "
+                             f"LDS-staged, {LDS_ROWS_PER_TILE} rows per tile (B)",
+                             lambda: cam.ulysses_seq_to_head(w.v_qkv, w.vP, out=w.v_qkv_out),
+                             lambda: cam.ablation_seq_to_head_lds(w.v_qkv, w.vP, LDS_ROWS_PER_TILE,
+                                                                  out=w.v_qkv_out))]
+
     # ---- plain-copy ceiling at each operation's own size: half its
     # algorithmic bytes each way; small sizes rotate over up to 8 disjoint
     # regions of one large pair so that repeated copies start cold, as the
@@ -906,6 +988,7 @@ def main():
         "extensions": ext,
         "projection": projection,
         "thd_plan": plan_summary(w),
+        "ablations": ablations,
         "copy_ceiling": {"GBps": round(copy_gbps, 1), "frac_of_hbm_peak": round(copy_gbps / HBM_PEAK_GBPS, 4),
                          "bytes": int(copy_bytes), "kernel": "k_copy16"},
         "device": {"name": props.name, "arch": getattr(props, "gcnArchName", ""),

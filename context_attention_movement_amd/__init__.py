@@ -28,7 +28,7 @@ __all__ = [
     "lse_combine_planned",
     "lse_pack_bytes", "lse_pack", "lse_combine_packed", "lse_combine", "lse_combine_varlen",
     "lse_combine_packed_seq", "lse_combine_varlen_seq", "lse_merge", "lse_combine_backward",
-    "qkv_projection_head_sharded", "copy", "last_launch",
+    "qkv_projection_head_sharded", "ablation_seq_to_head_lds", "copy", "last_launch",
 ]
 
 LIB_PATH = Path(__file__).resolve().parent / "libcam.so"
@@ -69,6 +69,7 @@ _SIGNATURES = {
     "lse_combine_varlen": (_int, [_vp, _i64, _i64, _i64, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _i64,
                                   _int, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _vp]),
     "cam_copy": (_int, [_vp, _vp, _i64, _vp]),
+    "cam_ablation_seq_to_head_lds": (_int, [_vp, _vp, _i64, _i64, _i64, _i64, _i64, _int, _i64, _vp]),
     "qkv_projection_head_sharded": (_int, [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _int, _vp]),
     "thd_plan": (_int, [_vp, _i64, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "thd_plan_first_positions": (_int, [_vp, _i64, _i64, _vp, _vp, _i64, _vp]),
@@ -761,6 +762,26 @@ def qkv_projection_head_sharded(x: torch.Tensor, w: torch.Tensor, P: int, B: int
         raise ValueError("out must be [P][B][S][H/P][D] of the operands' dtype")
     _check(library().qkv_projection_head_sharded(x.data_ptr(), w.data_ptr(), out.data_ptr(), S, K, P, B, H, D,
                                                  _dt(x), _stream(x)))
+    return out
+
+
+def ablation_seq_to_head_lds(x: torch.Tensor, P: int, rows_per_tile: int = 4,
+                             out: torch.Tensor | None = None) -> torch.Tensor:
+    """ulysses_seq_to_head by the LDS-staged kernel (kept to measure that
+    choice against the direct kernel; the API does not use it)."""
+    _contig(x, "x")
+    if x.dim() != 5 or x.shape[0] != P:
+        raise ValueError("x must be [P][B][S/P][H][D]")
+    _, B, Sp, H, D = x.shape
+    if H % P:
+        raise ValueError("H must be a multiple of P")
+    if out is None:
+        out = torch.empty((P, B, Sp * P, H // P, D), dtype=x.dtype, device=x.device)
+    _contig(out, "out")
+    if out.numel() != x.numel() or out.dtype != x.dtype:
+        raise ValueError("out must match x in size and dtype")
+    _check(library().cam_ablation_seq_to_head_lds(x.data_ptr(), out.data_ptr(), P, B, Sp * P, H, D, _dt(x, True),
+                                                  rows_per_tile, _stream(x)))
     return out
 
 

@@ -6,6 +6,7 @@
 // FastVideo's fused all-to-all helper either declines before it starts or
 // runs to the end (commit message of "[perf] Probe H3 chunked all-to-all
 // with direct output slices"); the same rule, applied per call.
+#include <algorithm>
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
@@ -202,6 +203,58 @@ cam_status dense_relayout(const void* in, void* out, int64_t P, int64_t B, int64
     a.n_tiles = uint32_t(n_tiles);
     a.seq_to_head = seq_to_head;
     return launch_dense_relayout(a, stream);
+}
+
+// LDS-staged seq->head (ablation): 16-byte accesses only, R rows per tile
+// staged whole in LDS (at most 64 KiB and 256 * 24 vectors per tile).
+cam_status ablation_seq_to_head_lds(const void* in, void* out, int64_t P, int64_t B, int64_t S, int64_t H,
+                                    int64_t D, cam_dtype dt, int64_t R, void* stream)
+{
+    const char* op = "cam_ablation_seq_to_head_lds";
+    clear_error();
+    if (P < 1 || B < 0 || S < 0 || H < 0 || D < 0)
+        return set_error(CAM_ERR_SHAPE, "%s: need P >= 1 and B, S, H, D >= 0", op);
+    const int es = elem_size(dt);
+    if (!es)
+        return set_error(CAM_ERR_UNSUPPORTED, "%s: unknown dtype code %d", op, int(dt));
+    if (S % P || H % P)
+        return set_error(CAM_ERR_DIVISIBILITY, "%s: S and H must be multiples of P", op);
+    int64_t bytes;
+    if (!prod_ok({B, S, H, D, es}, &bytes))
+        return set_error(CAM_ERR_SHAPE, "%s: B*S*H*D*esize overflows", op);
+    if (bytes == 0)
+        return CAM_OK;
+    if (!in || !out)
+        return set_error(CAM_ERR_NULL, "%s: in and out must be non-null", op);
+    const uint64_t run = uint64_t(H / P) * uint64_t(D) * es;
+    if (run % 16 || !aligned(in, 16) || !aligned(out, 16))
+        return set_error(CAM_ERR_ALIGNMENT, "%s: 16-byte accesses only: runs and pointers must be 16-byte multiples",
+                         op);
+    if (overlaps(in, bytes, out, bytes))
+        return set_error(CAM_ERR_OVERLAP, "%s: in and out overlap", op);
+    const uint64_t c = run / 16;
+    if (R < 1 || uint64_t(R) * uint64_t(P) * c > 4096)
+        return set_error(CAM_ERR_UNSUPPORTED, "%s: rows_per_tile * H * D * esize must be within 64 KiB of LDS", op);
+    DenseLds a{};
+    a.src = in;
+    a.dst = out;
+    a.P = uint32_t(P);
+    a.B = uint32_t(B);
+    a.c = uint32_t(c);
+    a.div_c = make_fastdiv(a.c);
+    a.R = uint32_t(R);
+    a.Rc = uint32_t(R * c);
+    a.div_Rc = make_fastdiv(a.Rc);
+    a.Sp = uint64_t(S / P);
+    const uint64_t tps = (a.Sp + a.R - 1) / a.R;
+    const uint64_t n_tiles = uint64_t(P) * uint64_t(B) * tps;
+    if (n_tiles > UINT32_MAX || a.Sp * uint64_t(P) * c * uint64_t(B) * uint64_t(P) >= (uint64_t(1) << 40))
+        return set_error(CAM_ERR_UNSUPPORTED, "%s: too many tiles", op);
+    a.tiles_per_slab = uint32_t(tps);
+    a.div_tps = make_fastdiv(a.tiles_per_slab);
+    a.div_B = make_fastdiv(a.B);
+    a.n_tiles = uint32_t(n_tiles);
+    return launch_dense_lds(a, stream);
 }
 
 // The per-sequence split (rank_cu, rank_off from ulysses_varlen_plan), or with
@@ -423,15 +476,21 @@ cam_status combine(const char* op, const CombineIn& c, void* stream)
     a.n_rows = uint64_t(n_rows);
     a.cv = uint32_t(row_b / a.width);
     a.g_log2 = log2u(pow2ceil(a.cv < 64 ? (a.cv ? a.cv : 1) : 64));
+    if (a.g_log2 < 6 && kCombineNarrowVpl == 2 && a.g_log2 > 0)
+        a.g_log2 -= 1;  // narrow rows: each lane moves two vectors of the row per pass
     a.gp_log2 = log2u(pow2ceil(a.P));
     // tile geometry (measured per row width): rows per tile, workgroup size,
     // tile order; at least one row per payload group
     const bool wave = a.g_log2 == 6;
-    a.threads = wave ? CAM_COMBINE_THREADS_WAVE : kThreads;
     a.xcd = wave ? CAM_XCD_COMBINE_WAVE : CAM_XCD_COMBINE_NARROW;
     uint32_t rows = wave                                   ? CAM_COMBINE_ROWS_WAVE
                     : uint64_t(a.cv) * a.width >= 512 ? CAM_COMBINE_ROWS_WIDE
                                                       : CAM_COMBINE_ROWS_NARROW;
+    // a workgroup holds one lane group per row of its tile (64 to 256
+    // threads), so very short rows take a smaller workgroup rather than a
+    // larger tile: the tile's per-row tables in LDS stay within 64 KiB
+    a.threads = wave ? CAM_COMBINE_THREADS_WAVE
+                     : std::min<uint32_t>(kThreads, std::max<uint32_t>(64u, rows << a.g_log2));
     const uint32_t groups = a.threads >> a.g_log2;
     if (rows < groups)
         rows = groups;
@@ -560,6 +619,8 @@ cam_status combine_backward(const char* op, const CombineBwdIn& c, void* stream)
     a.n_rows = uint64_t(n_rows);
     a.cv = uint32_t(row_b / a.width);
     a.g_log2 = log2u(pow2ceil(a.cv < 64 ? (a.cv ? a.cv : 1) : 64));
+    if (a.g_log2 < 6 && kCombineNarrowVpl == 2 && a.g_log2 > 0)
+        a.g_log2 -= 1;  // narrow rows: each lane moves two vectors of the row per pass
     a.gp_log2 = log2u(pow2ceil(a.P));
     uint32_t rows = uint64_t(a.cv) * a.width >= 512 ? CAM_COMBINE_BWD_ROWS_WIDE : CAM_COMBINE_BWD_ROWS_NARROW;
     const uint32_t groups = uint32_t(kThreads) >> a.g_log2;
@@ -621,6 +682,12 @@ cam_status ulysses_head_to_seq(const void* in, void* out, int64_t P, int64_t B, 
                                int64_t D, cam_dtype dt, void* stream)
 {
     return dense_relayout(in, out, P, B, S, H, D, dt, stream, false);
+}
+
+cam_status cam_ablation_seq_to_head_lds(const void* in, void* out, int64_t P, int64_t B, int64_t S, int64_t H,
+                                        int64_t D, cam_dtype dt, int64_t rows_per_tile, void* stream)
+{
+    return ablation_seq_to_head_lds(in, out, P, B, S, H, D, dt, rows_per_tile, stream);
 }
 
 cam_status ulysses_seq_to_head_spans(const void* in, void* out, const int32_t* span_start, const int32_t* span_rank,
@@ -1049,6 +1116,8 @@ cam_status lse_merge(float* acc_out, int64_t a_st, int64_t a_sh, float* acc_lse,
     a.n_rows = uint64_t(n_rows);
     a.cv = uint32_t(D / 4);
     a.g_log2 = log2u(pow2ceil(a.cv < 64 ? (a.cv ? a.cv : 1) : 64));
+    if (a.g_log2 < 6 && kCombineNarrowVpl == 2 && a.g_log2 > 0)
+        a.g_log2 -= 1;  // narrow rows: each lane moves two vectors of the row per pass
     a.fp16 = dt == CAM_FP16;
     return launch_merge(a, stream);
 }

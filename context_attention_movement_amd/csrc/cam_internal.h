@@ -241,6 +241,26 @@ struct Copy {
     uint64_t n_vecs;        // 16-byte vectors
 };
 
+// LDS-staged seq->head relayout (an ablation measured against the direct
+// kernel; ulysses_seq_to_head does not use it).  A tile is R consecutive
+// sequence-side rows (all H heads, R*P*c contiguous vectors) of one (j, b)
+// slab, staged whole in LDS and written as P contiguous runs of R*c vectors.
+struct DenseLds {
+    const void* src;
+    void* dst;
+    uint32_t P, B;
+    uint32_t c;             // vectors per head-block run
+    FastDiv div_c;
+    uint32_t R;             // rows per tile
+    uint32_t Rc;            // R*c
+    FastDiv div_Rc;
+    uint64_t Sp;            // rows per source slab (S/P)
+    uint32_t tiles_per_slab;  // ceil(Sp / R)
+    FastDiv div_tps;
+    FastDiv div_B;
+    uint32_t n_tiles;       // P*B*tiles_per_slab
+};
+
 // Kernel launchers (defined in the .hip sources).  They only launch; the
 // records have been validated.  Return CAM_OK or CAM_ERR_HIP (message set).
 cam_status launch_dense_relayout(const DenseRelayout& a, void* stream);
@@ -248,6 +268,7 @@ cam_status launch_varlen_relayout(const VarlenRelayout& a, void* stream);
 cam_status launch_pack(const Pack& a, void* stream);
 cam_status launch_combine(const Combine& a, void* stream);
 cam_status launch_copy(const Copy& a, void* stream);
+cam_status launch_dense_lds(const DenseLds& a, void* stream);
 cam_status launch_merge(const Merge& a, void* stream);
 cam_status launch_combine_bwd(const CombineBwd& a, void* stream);
 cam_status launch_proj(const Proj& a, void* stream);
@@ -353,6 +374,24 @@ constexpr int kCombineBwdBatch = CAM_COMBINE_BWD_BATCH;
 #define CAM_COMBINE_BATCH 4
 #endif
 constexpr int kCombineBatch = CAM_COMBINE_BATCH;
+// rows of < 64 vectors: most valid partial rows loaded at once per lane
+#ifndef CAM_COMBINE_NARROW_BATCH
+#define CAM_COMBINE_NARROW_BATCH 1
+#endif
+constexpr int kCombineNarrowBatch = CAM_COMBINE_NARROW_BATCH;
+static_assert(kCombineNarrowBatch >= 1 && kCombineNarrowBatch <= 8, "narrow combine batch must be 1..8");
+// rows of < 64 vectors: vectors of a row each lane moves per pass (1 or 2);
+// a row then takes pow2ceil(ceil(vectors / VPL)) lanes
+#ifndef CAM_COMBINE_NARROW_VPL
+#define CAM_COMBINE_NARROW_VPL 2
+#endif
+constexpr int kCombineNarrowVpl = CAM_COMBINE_NARROW_VPL;
+static_assert(kCombineNarrowVpl == 1 || kCombineNarrowVpl == 2, "vectors per lane must be 1 or 2");
+// rows of < 64 vectors: 1 = the valid partials one at a time, the next one's
+// payload requested before the current one is accumulated (software pipeline)
+#ifndef CAM_COMBINE_NARROW_PIPE
+#define CAM_COMBINE_NARROW_PIPE 0
+#endif
 // rows of >= 64 vectors (a whole wave per row): rows per tile, rows in flight
 // per wave, partial rows per batch
 #ifndef CAM_COMBINE_THREADS_WAVE

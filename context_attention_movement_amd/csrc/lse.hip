@@ -197,6 +197,25 @@ __device__ __forceinline__ int64_t varlen_token_row(const int32_t* cu, const Com
     return a.rank_off[p] + int64_t(a.rank_cu[int64_t(p) * (a.nseq + 1) + i]) + (k - piece_start(p, L, a.div_P));
 }
 
+// Partial weights exp(L - M) <= 1 and their normaliser 1/Z.  The fast forms
+// (hardware exp2 and reciprocal, about 1 ulp) are an option measured against
+// the correctly rounded library calls.
+#ifndef CAM_COMBINE_FAST_WEIGHTS
+#define CAM_COMBINE_FAST_WEIGHTS 0
+#endif
+__device__ __forceinline__ float weight_exp(float x)
+{
+    if (CAM_COMBINE_FAST_WEIGHTS)
+        return __expf(x);
+    return expf(x);
+}
+__device__ __forceinline__ float recip(float z)
+{
+    if (CAM_COMBINE_FAST_WEIGHTS)
+        return __builtin_amdgcn_rcpf(z);
+    return 1.0f / z;
+}
+
 // The combine works on tiles of kCombineRows consecutive rows per workgroup.
 // Phase 1 turns the tile's partial LSEs into weights in LDS: thread
 // (row, p) loads one LSE (consecutive rows are consecutive addresses), a group
@@ -217,24 +236,97 @@ __device__ __forceinline__ uint64_t uniform64(uint64_t x)
     return uint64_t(uniform32(uint32_t(x))) | (uint64_t(uniform32(uint32_t(x >> 32))) << 32);
 }
 
+// The payload rows of a row's valid partials, in ascending order, as a
+// compacted list built in phase 1: byte offsets from the partials' base and
+// normalised weights.  N rows are loaded at once (N is exact, so no lane
+// loads or accumulates a row it does not need), then accumulated in order.
+template <int N, int W, bool FP16, bool NTL, int VPL>
+__device__ __forceinline__ void combine_rows(const char* po, const int64_t* offs, const float* wks,
+                                             const uint32_t (&kbyte)[VPL], float (&acc)[VPL][W / 2])
+{
+    typedef typename VecOf<W>::type V;
+    constexpr int E = W / 2;
+    int64_t o[N];
+#pragma unroll
+    for (int u = 0; u < N; ++u)
+        o[u] = offs[u];
+    V x[N][VPL];
+#pragma unroll
+    for (int u = 0; u < N; ++u)
+#pragma unroll
+        for (int v = 0; v < VPL; ++v)
+            x[u][v] = ld_at<W, NTL>(po + o[u] + kbyte[v]);
+    issue_fence();
+    float w[N];
+#pragma unroll
+    for (int u = 0; u < N; ++u)
+        w[u] = wks[u];
+#pragma unroll
+    for (int u = 0; u < N; ++u)
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) {
+            const Halves<W> xh = __builtin_bit_cast(Halves<W>, x[u][v]);
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                acc[v][e] = fmaf(w[u], half_to_f32<FP16>(xh.h[e]), acc[v][e]);
+        }
+}
+
+// E fp32 values rounded to the payload type (round to nearest even), packed
+// as one access vector; bf16 pairs use the hardware's packed conversion.
+template <int W, bool FP16>
+__device__ __forceinline__ typename VecOf<W>::type round_payload(const float (&acc)[W / 2])
+{
+    constexpr int E = W / 2;
+    Halves<W> oh;
+    if constexpr (!FP16 && E % 2 == 0) {
+        typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+        typedef float f2 __attribute__((ext_vector_type(2)));
+        struct Words {
+            uint32_t w[E / 2];
+        } words;
+#pragma unroll
+        for (int e = 0; e < E; e += 2) {
+            const f2 v = {acc[e], acc[e + 1]};
+            words.w[e / 2] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf2));
+        }
+        return __builtin_bit_cast(typename VecOf<W>::type, words);
+    } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            oh.h[e] = f32_to_half<FP16>(acc[e]);
+        return __builtin_bit_cast(typename VecOf<W>::type, oh);
+    }
+}
+
 // WAVE: one row group is a whole wave (rows of >= 64 vectors), so every
 // per-row quantity of phase 2 is wave-uniform and is kept in scalar registers.
 // OM: where the combined rows go -- 0 at the caller's strides, 1 token-major
 // (head-scattered rows of the exchange), 2 rank-major (varlen sequence shards).
+#ifdef CAM_COMBINE_WAVES_PER_EU
+#define CAM_COMBINE_OCC __attribute__((amdgpu_waves_per_eu(CAM_COMBINE_WAVES_PER_EU)))
+#else
+#define CAM_COMBINE_OCC
+#endif
 template <int W, bool FP16, int CZ, int RF, bool WAVE, int OM>
-__global__ __launch_bounds__(kThreads) void k_combine(Combine a)
+__global__ __launch_bounds__(kThreads) CAM_COMBINE_OCC void k_combine(Combine a)
 {
     typedef typename VecOf<W>::type V;
     constexpr int E = W / 2;  // payload elements per vector
     constexpr int CH = WAVE ? kCombineBatchWave : kCombineBatch;
     constexpr bool NTL = (CAM_NT_COMBINE & 1) != 0, NTS = (CAM_NT_COMBINE & 2) != 0;
-    // per tile: weights [rows][P], validity masks, 1/Z
+    // per tile.  WAVE: weights [rows][P] by partial, validity masks, 1/Z.
+    // Otherwise: each row's valid partials as a compacted list -- weights and
+    // payload-row byte offsets [rows][P] (the first n of a row used) -- and
+    // the row's count n.
     extern __shared__ float smem[];
     const uint32_t RB = a.rows_per_tile;
     float* w_lds = smem;                                                   // RB * P
-    uint64_t* m_lds = reinterpret_cast<uint64_t*>(w_lds + ((RB * a.P + 1) & ~1u));  // RB
-    int64_t* o_lds = reinterpret_cast<int64_t*>(m_lds + RB);               // RB: output row offsets
-    float* iz_lds = reinterpret_cast<float*>(o_lds + RB);                  // RB
+    uint64_t* m_lds = reinterpret_cast<uint64_t*>(w_lds + ((RB * a.P + 1) & ~1u));  // WAVE: RB; else RB * P
+    int64_t* q_lds = reinterpret_cast<int64_t*>(m_lds);                    // !WAVE: compacted offsets
+    int64_t* o_lds = reinterpret_cast<int64_t*>(m_lds + (WAVE ? RB : RB * a.P));  // RB: output row offsets
+    float* iz_lds = reinterpret_cast<float*>(o_lds + RB);                  // RB (WAVE: 1/Z; else the count)
+    uint32_t* nv_lds = reinterpret_cast<uint32_t*>(iz_lds);
     int32_t* cu_lds = reinterpret_cast<int32_t*>(iz_lds + RB);             // nseq + 1 (varlen)
     const bool cached = CZ != kAll && a.nseq < kCuCache;
     if (cached)  // visible after the barrier that opens every tile
@@ -286,14 +378,21 @@ __global__ __launch_bounds__(kThreads) void k_combine(Combine a)
             for (uint32_t off = GP >> 1; off > 0; off >>= 1)
                 M = fmaxf(M, __shfl_xor(M, int(off), int(GP)));
             const uint64_t vmask = (__ballot(valid) >> sbase) & spmask;
-            const float w = valid ? expf(L - M) : 0.0f;
+            const float w = valid ? weight_exp(L - M) : 0.0f;
             float Z = w;
             for (uint32_t off = GP >> 1; off > 0; off >>= 1)
                 Z += __shfl_xor(Z, int(off), int(GP));
             if (live) {
-                const float iz = vmask ? 1.0f / Z : 0.0f;
-                if (sp < a.P)
-                    w_lds[rl * a.P + sp] = w * iz;
+                const float iz = vmask ? recip(Z) : 0.0f;
+                if (WAVE) {
+                    if (sp < a.P)
+                        w_lds[rl * a.P + sp] = w * iz;
+                } else if (valid) {
+                    const uint32_t slot = uint32_t(__builtin_popcountll(vmask & ((1ull << sp) - 1ull)));
+                    w_lds[rl * a.P + slot] = w * iz;
+                    q_lds[rl * a.P + slot] =
+                        int64_t(sp) * a.po_sp_b + int64_t(t) * a.po_st_b + int64_t(h) * a.po_sh_b;
+                }
                 if (sp == 0) {
                     int64_t o_off, l_off;
                     if (OM == 0) {
@@ -312,9 +411,13 @@ __global__ __launch_bounds__(kThreads) void k_combine(Combine a)
                         o_off = in ? g * int64_t(a.o_row_b) : -1;
                         l_off = in ? g : -1;
                     }
-                    m_lds[rl] = vmask;
+                    if (WAVE) {
+                        m_lds[rl] = vmask;
+                        iz_lds[rl] = iz;
+                    } else {
+                        nv_lds[rl] = uint32_t(__builtin_popcountll(vmask));
+                    }
                     o_lds[rl] = o_off;
-                    iz_lds[rl] = iz;
                     if (a.lse_out && l_off >= 0)
                         a.lse_out[l_off] = vmask ? M + logf(Z) : -__builtin_inff();
                 }
@@ -322,9 +425,101 @@ __global__ __launch_bounds__(kThreads) void k_combine(Combine a)
         }
         __syncthreads();
 
-        // ---- phase 2: stream the payload rows, RF rows per group in flight
+        // ---- phase 2: stream the payload rows
         const uint64_t left = a.n_rows - row0;
         const uint32_t nr = left < RB ? uint32_t(left) : RB;  // rows of this tile
+        if constexpr (!WAVE) {
+            // a lane group per row; its valid partials' rows up to 8 at a time
+            const char* po = static_cast<const char*>(a.po);
+            for (uint32_t rl = group; rl < nr; rl += groups) {
+                const uint32_t n = nv_lds[rl];
+                const int64_t ooff = o_lds[rl];
+                const bool have = ooff >= 0;
+                char* orow = static_cast<char*>(a.out) + (have ? ooff : 0);
+                const int64_t* offs = q_lds + rl * a.P;
+                const float* wks = w_lds + rl * a.P;
+                constexpr int VPL = kCombineNarrowVpl;
+                for (uint32_t kb = 0; kb < a.cv; kb += G * VPL) {
+                    bool kin[VPL];
+                    uint32_t kbyte[VPL];
+                    float acc[VPL][E];
+#pragma unroll
+                    for (int v = 0; v < VPL; ++v) {
+                        const uint32_t idx = kb + gl + uint32_t(v) * G;
+                        kin[v] = idx < a.cv;
+                        kbyte[v] = (kin[v] ? idx : a.cv - 1) * uint32_t(W);
+#pragma unroll
+                        for (int e = 0; e < E; ++e)
+                            acc[v][e] = 0.0f;
+                    }
+                    constexpr uint32_t NB = kCombineNarrowBatch;
+                    if constexpr (CAM_COMBINE_NARROW_PIPE) {
+                        // two register sets take turns: partial kk + 1's payload
+                        // is requested before partial kk is accumulated, so one
+                        // request stays in flight while the other is consumed
+                        typedef typename VecOf<W>::type V;
+                        V xa[VPL], xb[VPL];
+                        auto fetch = [&](V (&x)[VPL], uint32_t kk) {
+                            const int64_t o1 = offs[kk];
+#pragma unroll
+                            for (int v = 0; v < VPL; ++v)
+                                x[v] = ld_at<W, NTL>(po + o1 + kbyte[v]);
+                        };
+                        auto take = [&](const V (&x)[VPL], uint32_t kk) {
+                            const float wv = wks[kk];
+#pragma unroll
+                            for (int v = 0; v < VPL; ++v) {
+                                const Halves<W> xh = __builtin_bit_cast(Halves<W>, x[v]);
+#pragma unroll
+                                for (int e = 0; e < E; ++e)
+                                    acc[v][e] = fmaf(wv, half_to_f32<FP16>(xh.h[e]), acc[v][e]);
+                            }
+                        };
+                        if (n > 0) {
+                            fetch(xa, 0);
+                            uint32_t kk = 0;
+                            for (; kk + 2 < n; kk += 2) {
+                                fetch(xb, kk + 1);
+                                issue_fence();
+                                take(xa, kk);
+                                issue_fence();
+                                fetch(xa, kk + 2);
+                                issue_fence();
+                                take(xb, kk + 1);
+                                issue_fence();
+                            }
+                            if (kk + 1 < n) {
+                                fetch(xb, kk + 1);
+                                take(xa, kk);
+                                take(xb, kk + 1);
+                            } else {
+                                take(xa, kk);
+                            }
+                        }
+                    } else
+                    for (uint32_t k0 = 0; k0 < n; k0 += NB) {
+                        const uint32_t cnt = n - k0 < NB ? n - k0 : NB;
+                        const int64_t* o = offs + k0;
+                        const float* wk = wks + k0;
+                        switch (cnt) {
+                        case 8: if constexpr (NB >= 8) combine_rows<8, W, FP16, NTL, VPL>(po, o, wk, kbyte, acc); break;
+                        case 7: if constexpr (NB >= 7) combine_rows<7, W, FP16, NTL, VPL>(po, o, wk, kbyte, acc); break;
+                        case 6: if constexpr (NB >= 6) combine_rows<6, W, FP16, NTL, VPL>(po, o, wk, kbyte, acc); break;
+                        case 5: if constexpr (NB >= 5) combine_rows<5, W, FP16, NTL, VPL>(po, o, wk, kbyte, acc); break;
+                        case 4: if constexpr (NB >= 4) combine_rows<4, W, FP16, NTL, VPL>(po, o, wk, kbyte, acc); break;
+                        case 3: if constexpr (NB >= 3) combine_rows<3, W, FP16, NTL, VPL>(po, o, wk, kbyte, acc); break;
+                        case 2: if constexpr (NB >= 2) combine_rows<2, W, FP16, NTL, VPL>(po, o, wk, kbyte, acc); break;
+                        default: combine_rows<1, W, FP16, NTL, VPL>(po, o, wk, kbyte, acc); break;
+                        }
+                    }
+#pragma unroll
+                    for (int v = 0; v < VPL; ++v)
+                        if (have && kin[v])
+                            st_at<W, NTS>(orow + kbyte[v], round_payload<W, FP16>(acc[v]));
+                }
+            }
+            continue;
+        }
         const uint32_t first = WAVE ? uniform32(group * RF) : group * RF;
         for (uint32_t rl0 = first; rl0 < nr; rl0 += groups * RF) {
             uint32_t rl[RF];
@@ -437,6 +632,38 @@ __device__ __forceinline__ float wave_sum(float v)
     return v;
 }
 
+// The next N valid partials of a row whose statistics sit in the wave's lanes:
+// their indices come off the wave-uniform mask m (lowest first), their
+// normalised weights are read from the owning lanes, then all N payload
+// vectors are loaded before any is accumulated.
+template <int N, int W, bool FP16, bool NTL>
+__device__ __forceinline__ void stream_rows(const char* prow, int64_t sp_b, uint32_t kbyte, uint64_t& m, float wn,
+                                            float (&acc)[W / 2])
+{
+    typedef typename VecOf<W>::type V;
+    constexpr int E = W / 2;
+    int idx[N];
+    float w[N];
+#pragma unroll
+    for (int u = 0; u < N; ++u) {
+        idx[u] = __builtin_ctzll(m);
+        m &= m - 1;
+        w[u] = __uint_as_float(uint32_t(__builtin_amdgcn_readlane(int(__float_as_uint(wn)), idx[u])));
+    }
+    V x[N];
+#pragma unroll
+    for (int u = 0; u < N; ++u)
+        x[u] = ld_at<W, NTL>(prow + kbyte + int64_t(idx[u]) * sp_b);
+    issue_fence();
+#pragma unroll
+    for (int u = 0; u < N; ++u) {
+        const Halves<W> xh = __builtin_bit_cast(Halves<W>, x[u]);
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            acc[e] = fmaf(w[u], half_to_f32<FP16>(xh.h[e]), acc[e]);
+    }
+}
+
 template <int CZ>
 __device__ __forceinline__ float row_stat(const Combine& a, uint64_t row, uint32_t lane)
 {
@@ -469,10 +696,10 @@ __global__ __launch_bounds__(kThreads) void k_combine_stream(Combine a)
         const uint32_t h = uint32_t(row) - t * a.H;
         const bool valid = __builtin_isfinite(L);
         const float M = wave_max(valid ? L : -__builtin_inff());
-        const float w = valid ? expf(L - M) : 0.0f;
+        const float w = valid ? weight_exp(L - M) : 0.0f;
         const float Z = wave_sum(w);
         const uint64_t vmask = __ballot(valid);
-        const float wn = w * (vmask ? 1.0f / Z : 0.0f);
+        const float wn = w * (vmask ? recip(Z) : 0.0f);
         int64_t o_off, l_off;
         if (OM == 0) {
             o_off = int64_t(t) * a.o_st_b + int64_t(h) * a.o_sh_b;
@@ -495,51 +722,30 @@ __global__ __launch_bounds__(kThreads) void k_combine_stream(Combine a)
         char* orow = static_cast<char*>(a.out) + (have ? o_off : 0);
         const char* prow = vmask ? static_cast<const char*>(a.po) + int64_t(t) * a.po_st_b + int64_t(h) * a.po_sh_b
                                  : orow;
+        const uint32_t n = uint32_t(__builtin_popcountll(vmask));
         for (uint32_t kb = 0; kb < a.cv; kb += 64) {
             const bool kin = kb + lane < a.cv;
-            const uint32_t k = kin ? kb + lane : a.cv - 1;
+            const uint32_t kbyte = (kin ? kb + lane : a.cv - 1) * uint32_t(W);
             float acc[E];
 #pragma unroll
             for (int e = 0; e < E; ++e)
                 acc[e] = 0.0f;
-            uint64_t m = vmask;
-            int last = vmask ? __builtin_ctzll(vmask) : 0;
-            do {
-                int idx[CH];
-                float wv[CH];
-                bool tk[CH];
-#pragma unroll
-                for (int u = 0; u < CH; ++u) {
-                    const bool take = m != 0;
-                    const int p = take ? __builtin_ctzll(m) : last;
-                    m = take ? (m & (m - 1)) : m;
-                    idx[u] = p;
-                    last = p;
-                    tk[u] = take;
-                    wv[u] = __uint_as_float(uint32_t(__builtin_amdgcn_readlane(int(__float_as_uint(wn)), p)));
+            uint64_t m = vmask;  // wave-uniform: the valid partials not yet taken
+            for (uint32_t k0 = 0; k0 < n; k0 += CH) {
+                const uint32_t cnt = n - k0 < uint32_t(CH) ? n - k0 : uint32_t(CH);
+                switch (cnt) {
+                case 8: if constexpr (CH >= 8) stream_rows<8, W, FP16, NTL>(prow, a.po_sp_b, kbyte, m, wn, acc); break;
+                case 7: if constexpr (CH >= 7) stream_rows<7, W, FP16, NTL>(prow, a.po_sp_b, kbyte, m, wn, acc); break;
+                case 6: if constexpr (CH >= 6) stream_rows<6, W, FP16, NTL>(prow, a.po_sp_b, kbyte, m, wn, acc); break;
+                case 5: if constexpr (CH >= 5) stream_rows<5, W, FP16, NTL>(prow, a.po_sp_b, kbyte, m, wn, acc); break;
+                case 4: if constexpr (CH >= 4) stream_rows<4, W, FP16, NTL>(prow, a.po_sp_b, kbyte, m, wn, acc); break;
+                case 3: if constexpr (CH >= 3) stream_rows<3, W, FP16, NTL>(prow, a.po_sp_b, kbyte, m, wn, acc); break;
+                case 2: if constexpr (CH >= 2) stream_rows<2, W, FP16, NTL>(prow, a.po_sp_b, kbyte, m, wn, acc); break;
+                default: stream_rows<1, W, FP16, NTL>(prow, a.po_sp_b, kbyte, m, wn, acc); break;
                 }
-                V x[CH];
-#pragma unroll
-                for (int u = 0; u < CH; ++u)
-                    x[u] = ld_at<W, NTL>(prow + int64_t(k) * W + int64_t(idx[u]) * a.po_sp_b);
-                issue_fence();
-#pragma unroll
-                for (int u = 0; u < CH; ++u) {
-                    const Halves<W> xh = __builtin_bit_cast(Halves<W>, x[u]);
-#pragma unroll
-                    for (int e = 0; e < E; ++e) {
-                        const float v = fmaf(wv[u], half_to_f32<FP16>(xh.h[e]), acc[e]);
-                        acc[e] = tk[u] ? v : acc[e];
-                    }
-                }
-            } while (m);
-            if (have && kin) {
-                Halves<W> oh;
-#pragma unroll
-                for (int e = 0; e < E; ++e)
-                    oh.h[e] = f32_to_half<FP16>(vmask ? acc[e] : 0.0f);
-                st_at<W, NTS>(orow + int64_t(k) * W, __builtin_bit_cast(V, oh));
             }
+            if (have && kin)
+                st_at<W, NTS>(orow + kbyte, round_payload<W, FP16>(acc));
         }
     }
 }
@@ -915,10 +1121,21 @@ cam_status launch_combine(const Combine& a, void* stream)
         const uint32_t wpb = CAM_COMBINE_STREAM_THREADS / 64;
         return launch(fn, a, (waves + wpb - 1) / wpb, stream, "lse_combine", 0, CAM_COMBINE_STREAM_THREADS);
     }
-    uint64_t lds = (uint64_t(a.rows_per_tile) * a.P + 2) * 4 + uint64_t(a.rows_per_tile) * 20;
+    // weights [rows][P] (padded to 8 bytes); WAVE: masks [rows], else the
+    // compacted offsets [rows][P]; output offsets [rows]; 1/Z or counts [rows]
+    const uint64_t RB = a.rows_per_tile;
+    uint64_t lds = ((RB * a.P + 1) & ~1ull) * 4 + (wave ? RB : RB * a.P) * 8 + RB * 8 + RB * 4;
     if (a.cu && a.nseq < kCuCache)
         lds += uint64_t(a.nseq + 1) * 4;
-    return launch(fn, a, a.n_tiles, stream, "lse_combine", lds, a.threads);
+    if (lds > 65536)
+        return set_error(CAM_ERR_UNSUPPORTED, "lse_combine: a tile's tables need %llu bytes of LDS (at most 65536)",
+                         (unsigned long long)lds);
+#ifdef CAM_COMBINE_GRID_CAP
+    const uint64_t grid = a.n_tiles < CAM_COMBINE_GRID_CAP ? a.n_tiles : CAM_COMBINE_GRID_CAP;
+#else
+    const uint64_t grid = a.n_tiles;
+#endif
+    return launch(fn, a, grid, stream, "lse_combine", lds, a.threads);
 }
 
 }  // namespace cam

@@ -237,6 +237,75 @@ __global__ __launch_bounds__(kThreads) void k_copy16(Copy a)
     }
 }
 
+// LDS-staged seq->head (ablation).  Loads: the tile's R*P*c vectors are one
+// contiguous range of the source slab; each thread loads its share into
+// registers (all loads issued first), writes them to LDS, and after the
+// barrier every thread reads the vectors of its output positions from LDS:
+// output position v = r*(R*c) + s*c + k (head block r, row s, vector k) is
+// contiguous per r in the destination, and sits at LDS index s*P*c + r*c + k.
+constexpr int kLdsVecsPerThread = 24;  // R*P*c <= 256 * 24 (checked on the host)
+
+template <bool FULL>
+__device__ __forceinline__ void lds_tile(const DenseLds& a, const u32x4* src, u32x4* lds, uint32_t rows,
+                                         uint64_t dst_row0)
+{
+    constexpr bool NTL = (CAM_NT_SEQ_TO_HEAD & 1) != 0, NTS = (CAM_NT_SEQ_TO_HEAD & 2) != 0;
+    const uint32_t n = rows * a.P * a.c;
+    u32x4 x[kLdsVecsPerThread];
+#pragma unroll
+    for (int u = 0; u < kLdsVecsPerThread; ++u) {
+        const uint32_t v = threadIdx.x + uint32_t(u) * kThreads;
+        if (v < n)
+            x[u] = ld_at<16, NTL>(src + v);
+    }
+    issue_fence();
+#pragma unroll
+    for (int u = 0; u < kLdsVecsPerThread; ++u) {
+        const uint32_t v = threadIdx.x + uint32_t(u) * kThreads;
+        if (v < n)
+            lds[v] = x[u];
+    }
+    __syncthreads();
+    const uint32_t rc = rows * a.c;
+    for (uint32_t v = threadIdx.x; v < n; v += kThreads) {
+        const uint32_t r = FULL ? fdiv(v, a.div_Rc) : v / rc;
+        const uint32_t w = v - r * rc;
+        const uint32_t srow = fdiv(w, a.div_c);
+        const uint32_t k = w - srow * a.c;
+        const u32x4 y = lds[srow * a.P * a.c + r * a.c + k];
+        // head side: [P][B][S][c], row j*Sp + s0 + srow of head block r
+        const uint64_t o = (uint64_t(r) * a.B * (a.Sp * a.P) + dst_row0 + srow) * a.c + k;
+        st<16, NTS>(a.dst, o, y);
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void k_dense_s2h_lds(DenseLds a)
+{
+    extern __shared__ u32x4 lds[];
+    for (uint32_t tile = blockIdx.x; tile < a.n_tiles; tile += gridDim.x) {
+        const uint32_t slab = fdiv(tile, a.div_tps);     // (j, b): source rank j, plane b
+        const uint32_t ti = tile - slab * a.tiles_per_slab;
+        const uint32_t j = fdiv(slab, a.div_B);
+        const uint32_t b = slab - j * a.B;
+        const uint64_t s0 = uint64_t(ti) * a.R;
+        const uint32_t rows = uint32_t(a.Sp - s0 < a.R ? a.Sp - s0 : a.R);
+        const u32x4* src = static_cast<const u32x4*>(a.src) + (uint64_t(slab) * a.Sp + s0) * a.P * a.c;
+        // destination row of (b, j*Sp + s0) in head block 0: [P][B][S] rows
+        const uint64_t dst_row0 = uint64_t(b) * (a.Sp * a.P) + uint64_t(j) * a.Sp + s0;
+        __syncthreads();  // the previous tile's readers are done with LDS
+        if (rows == a.R)
+            lds_tile<true>(a, src, lds, rows, dst_row0);
+        else
+            lds_tile<false>(a, src, lds, rows, dst_row0);
+    }
+}
+
+cam_status launch_dense_lds(const DenseLds& a, void* stream)
+{
+    return launch(reinterpret_cast<const void*>(&k_dense_s2h_lds), a, a.n_tiles, stream, "LDS-staged relayout",
+                  uint64_t(a.R) * a.P * a.c * 16);
+}
+
 cam_status launch_dense_relayout(const DenseRelayout& a, void* stream)
 {
     const void* fn = nullptr;

@@ -460,6 +460,21 @@ cam_status qkv_projection_head_sharded(const void* x, const void* w, void* out, 
 /* Measurement helper                                                          */
 /* ------------------------------------------------------------------------- */
 /*
+ * cam_ablation_seq_to_head_lds: what ulysses_seq_to_head computes (same
+ *   arguments and layouts), by a different kernel kept only to measure the
+ *   choice against it: each workgroup stages rows_per_tile whole
+ *   sequence-side rows (all H heads) in LDS and writes every head block's rows
+ *   as one contiguous run (the "LDS-staged transpose" of the head/sequence
+ *   swap).  ulysses_seq_to_head does not call it.  16-byte accesses only: (H/P)*D*esize and both pointers must be
+ *   multiples of 16 bytes (CAM_ERR_ALIGNMENT); rows_per_tile >= 1 with
+ *   rows_per_tile*H*D*esize <= 64 KiB (CAM_ERR_UNSUPPORTED).  Other errors as
+ *   ulysses_seq_to_head.
+ */
+cam_status cam_ablation_seq_to_head_lds(const void* in, void* out, int64_t P, int64_t B, int64_t S,
+                                        int64_t H, int64_t D, cam_dtype dt, int64_t rows_per_tile,
+                                        void* stream);
+
+/*
  * cam_copy: plain 16-byte-vector device copy of `bytes` bytes (src and dst
  * 16-byte aligned, bytes % 16 == 0, no overlap) with the same launch shape as
  * the relayout kernels.  It is the achievable-copy ceiling measured beside

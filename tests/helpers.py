@@ -97,3 +97,18 @@ def assert_grad_lse_close(got: np.ndarray, want: np.ndarray, scale: np.ndarray, 
     assert not bad.any(), f"{what}: {int(bad.sum())} LSE-gradient entries out of tolerance, worst " \
                           f"{float(np.max(err / np.maximum(tol, 1e-300)))} x tol"
     return float(np.max(err / np.maximum(scale[None, :], 1e-30)))
+
+
+def window_pool(T: int, fn, n_windows: int = 64, threads: int | None = None) -> list:
+    """Call fn(a, e) on token windows [a, e) that cover [0, T), from a pool of
+    threads (the oracle's C calls and numpy's large array operations release
+    the GIL); returns the results in window order.  Used to compare a whole
+    full-size result with the oracle in seconds."""
+    import os
+    from concurrent.futures import ThreadPoolExecutor
+
+    threads = threads or max(1, min(16, len(os.sched_getaffinity(0))))
+    n = max(1, min(n_windows, T))
+    bounds = [(k * T // n, (k + 1) * T // n) for k in range(n)]
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        return list(ex.map(lambda ae: fn(*ae), bounds))

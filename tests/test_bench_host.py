@@ -37,3 +37,19 @@ def test_counter_summary_median_per_dispatch(tmp_path):
     assert lines["SQ_LDS_BANK_CONFLICT"][1] == "20" and lines["SQ_LDS_BANK_CONFLICT"][2] == "dispatches=3"
     assert lines["SQ_INSTS_LDS"][1] == "2000"
     assert "k_pack" not in text
+
+
+def test_ab_verdict_rule():
+    """Paired A/B decision: faster or slower only beyond twice the null
+    control's largest per-pair difference and with every pair agreeing."""
+    sys.path.insert(0, str(ROOT))
+    import bench
+    null = [(100.0, 101.0), (100.0, 99.5), (100.0, 100.2)]           # floor 1%
+    faster = [(100.0, 97.0), (100.0, 96.5), (100.0, 97.5)]           # -3%, all pairs
+    assert bench.ab_verdict(null, faster)["verdict"] == "B faster"
+    assert bench.ab_verdict(null, faster)["noise_floor_pct"] == 1.0
+    assert bench.ab_verdict(null, [(100.0, 98.5), (100.0, 98.6), (100.0, 98.4)])["verdict"] == "neutral"  # < 2%
+    mixed = [(100.0, 96.0), (100.0, 101.0), (100.0, 96.0)]
+    assert bench.ab_verdict(null, mixed)["verdict"] == "neutral"     # a pair disagrees
+    slower = [(100.0, 104.0), (100.0, 103.0), (100.0, 105.0)]
+    assert bench.ab_verdict(null, slower)["verdict"] == "B slower"

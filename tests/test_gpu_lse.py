@@ -2,7 +2,8 @@
 against the oracle: packed O-region bit-exact, LSE within 1e-5 absolute with
 identical -inf positions, combined payload within 8e-3 per-row relative
 error; invalid partials never read; MLA decode and packed-THD workloads at
-full size (THD on sampled token windows)."""
+full size, every row (the THD oracle runs over token windows on the host's
+cores)."""
 
 import math
 
@@ -11,7 +12,7 @@ import pytest
 import torch
 
 import synth
-from helpers import (announce, assert_bits_equal, assert_lse_close, assert_rows_close, from_host_bits,
+from helpers import (window_pool, announce, assert_bits_equal, assert_lse_close, assert_rows_close, from_host_bits,
                      to_host_bits)
 
 pytestmark = pytest.mark.gpu
@@ -224,33 +225,35 @@ def test_combine_varlen_masked_partials_not_read(cam, orc):
     assert_lse_close(lse.cpu().numpy(), rl, "varlen lse")
 
 
-def test_thd_combine_full_size_sampled(cam, orc):
+def test_thd_combine_full_size(cam, orc):
     """Packed THD at full size (131072 tokens, H = 32, D = 128, 8 KV-piece
-    partials): the whole batch is combined on the GPU; token windows at the
-    start, the end and around sequence boundaries are compared with the
-    oracle row by row; the whole output is checked for NaN."""
+    partials, the launch the benchmark times): every row of the combined
+    output and every LSE against the oracle, computed over token windows on
+    the host's cores."""
     P, H, D = 8, 32, 128
     lens = synth.thd_lengths(20, 131072, seed=synth.BASE_SEED + 4)
     cu = synth.cu_seqlens(lens)
     T = int(cu[-1])
-    announce("THD combine full size")
+    announce("THD combine full size, every row")
     g = synth._gen(synth.BASE_SEED + 77, "cuda")
     po = torch.randn((P, T, H, D), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
     pl = torch.randn((P, T, H), generator=g, device="cuda", dtype=torch.float32).mul_(2.0)
     cu_d = torch.from_numpy(cu).cuda()
     out, lse = cam.lse_combine_varlen(po, pl, cu_d)
     torch.cuda.synchronize()
-    assert not torch.isnan(out).any() and not torch.isnan(lse).any()
-    starts = [0, T - 96] + [int(c) - 48 for c in cu[1:-1:3]] + [int(cu[5]) + 1000]
-    for a in starts:
-        a = max(0, min(a, T - 96))
-        b = a + 96
-        ow = to_host_bits(po[:, a:b])
-        lw = pl[:, a:b].cpu().numpy()
-        ro, rl = orc.lse_combine(ow, lw, cu=cu, t_begin=a)
-        assert_rows_close(orc.half_bits_to_double(to_host_bits(out[a:b])).reshape(-1, D),
-                          orc.half_bits_to_double(ro).reshape(-1, D), f"THD window {a}")
-        assert_lse_close(lse[a:b].cpu().numpy(), rl, f"THD lse window {a}")
+    po_h, pl_h = to_host_bits(po), pl.cpu().numpy()
+    out_h, lse_h = to_host_bits(out), lse.cpu().numpy()
+    del po
+
+    def check(a, e):
+        ro, rl = orc.lse_combine(po_h[:, a:e], pl_h[:, a:e], cu=cu, t_begin=a)
+        w = assert_rows_close(orc.half_bits_to_double(out_h[a:e]).reshape(-1, D),
+                              orc.half_bits_to_double(ro).reshape(-1, D), f"THD rows [{a}, {e})")
+        return w, assert_lse_close(lse_h[a:e], rl, f"THD lse [{a}, {e})")
+
+    res = window_pool(T, check)
+    print(f"THD combine, all {T * H} rows: worst row {max(r[0] for r in res):.3e}, "
+          f"lse err {max(r[1] for r in res):.3e}", flush=True)
 
 
 def test_mla_pack_and_combine_full_size_fp16(cam, orc):
