@@ -618,15 +618,33 @@ cam_status combine_backward(const char* op, const CombineBwdIn& c, void* stream)
     a.div_H = make_fastdiv(a.H);
     a.n_rows = uint64_t(n_rows);
     a.cv = uint32_t(row_b / a.width);
-    a.g_log2 = log2u(pow2ceil(a.cv < 64 ? (a.cv ? a.cv : 1) : 64));
-    if (a.g_log2 < 6 && kCombineNarrowVpl == 2 && a.g_log2 > 0)
-        a.g_log2 -= 1;  // narrow rows: each lane moves two vectors of the row per pass
     a.gp_log2 = log2u(pow2ceil(a.P));
-    uint32_t rows = uint64_t(a.cv) * a.width >= 512 ? CAM_COMBINE_BWD_ROWS_WIDE : CAM_COMBINE_BWD_ROWS_NARROW;
-    const uint32_t groups = uint32_t(kThreads) >> a.g_log2;
-    if (rows < groups)
-        rows = groups;
-    a.rows_per_tile = rows;
+    const uint32_t g_full = log2u(pow2ceil(a.cv < 64 ? (a.cv ? a.cv : 1) : 64));
+    const uint32_t rows0 = uint64_t(a.cv) * a.width >= 512 ? CAM_COMBINE_BWD_ROWS_WIDE : CAM_COMBINE_BWD_ROWS_NARROW;
+    // compacted form: each lane moves kCombineBwdVpl vectors of a row per
+    // pass, the workgroup holds one lane group per row of its tile, and the
+    // per-lane dot products of every (row, valid partial) are reduced in LDS;
+    // used when those tables fit 64 KiB, otherwise the row groups reduce with
+    // cross-lane shuffles
+    {
+        const uint32_t g = (kCombineBwdVpl == 2 && g_full > 0 && g_full < 6) ? g_full - 1 : g_full;
+        const uint32_t threads = std::min<uint32_t>(kThreads, std::max<uint32_t>(64u, rows0 << g));
+        const uint32_t rows = std::max(rows0, threads >> g);
+        const uint64_t lds = uint64_t(rows) * a.P * (4 + 8 + 4 * (uint64_t(1) << g)) + uint64_t(rows) * (8 + 4 + 4) +
+                             (c.cu && c.nseq < kCuCache ? uint64_t(c.nseq + 1) * 4 : 0) + 16;
+        a.compact = g_full < 6 && lds <= 65536;
+        if (a.compact) {
+            a.g_log2 = g;
+            a.threads = threads;
+            a.rows_per_tile = rows;
+        }
+    }
+    if (!a.compact) {
+        a.g_log2 = g_full;
+        a.threads = kThreads;
+        a.rows_per_tile = std::max(rows0, uint32_t(kThreads) >> g_full);
+    }
+    const uint32_t rows = a.rows_per_tile;
     a.n_tiles = (uint64_t(n_rows) + rows - 1) / rows;
     a.cu = c.cu;
     a.first = c.first;

@@ -70,9 +70,6 @@ __device__ __forceinline__ int32_t seq_of_token(const int32_t* cu, int32_t nseq,
     return lo;
 }
 
-// cu_seqlens entries staged in LDS by the varlen kernels (larger tables are
-// searched in global memory).
-constexpr int32_t kCuCache = 1024;
 
 // Keep a batch of independent loads together: no instruction is scheduled
 // across this point, so every load above it is issued before anything below

@@ -218,6 +218,8 @@ struct CombineBwd {
     FastDiv div_P;
     int width;
     int fp16;
+    uint32_t threads;       // workgroup size
+    uint32_t compact;       // 1: compacted partial lists and LDS-reduced dot products (see lse.hip)
 };
 
 // Q/K/V projection into the head-sharded layout: out[r][b][t][h'][d] =
@@ -278,6 +280,10 @@ cam_status set_error(cam_status s, const char* fmt, ...);
 // records the geometry of this thread's latest launch (cam_last_launch)
 void note_launch(uint64_t workgroups, uint32_t threads, uint64_t lds_bytes);
 void clear_error();
+
+// cu_seqlens entries staged in LDS by the varlen kernels (larger tables are
+// searched in global memory).
+constexpr int32_t kCuCache = 1024;
 
 // Launch shape shared by all streaming kernels.
 #ifndef CAM_THREADS
@@ -362,6 +368,18 @@ constexpr int kVarlenTileVecs = kThreads * kVarlenVecs;
 #define CAM_COMBINE_BWD_BATCH 4
 #endif
 constexpr int kCombineBwdBatch = CAM_COMBINE_BWD_BATCH;
+// gradient, compacted form: valid partial rows loaded at once per lane (1..8)
+// and vectors of a row per lane per pass (1 or 2)
+#ifndef CAM_COMBINE_BWD_NARROW_BATCH
+#define CAM_COMBINE_BWD_NARROW_BATCH 1
+#endif
+#ifndef CAM_COMBINE_BWD_VPL
+#define CAM_COMBINE_BWD_VPL 1
+#endif
+constexpr int kCombineBwdNarrowBatch = CAM_COMBINE_BWD_NARROW_BATCH;
+constexpr int kCombineBwdVpl = CAM_COMBINE_BWD_VPL;
+static_assert(kCombineBwdNarrowBatch >= 1 && kCombineBwdNarrowBatch <= 8, "gradient batch must be 1..8");
+static_assert(kCombineBwdVpl == 1 || kCombineBwdVpl == 2, "gradient vectors per lane must be 1 or 2");
 // Combine tiling (measured on MI355X): rows per workgroup tile for rows of
 // >= 512 bytes and for shorter rows, and partial rows loaded per batch.
 #ifndef CAM_COMBINE_ROWS_WIDE

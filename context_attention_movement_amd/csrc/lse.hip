@@ -852,7 +852,78 @@ cam_status launch_merge(const Merge& a, void* stream)
 // partial, zero for those outside the valid set.  Phase 3 forms
 // dL_p = w_p (<g, O_p> - sum_q w_q <g, O_q> + g_lse) on the statistics lanes.
 // As in the forward, an invalid or masked partial's O row is never read.
-template <int W, bool FP16, int CZ>
+// Dot product of two payload vectors in fp32: pairs of bf16/fp16 elements
+// through the packed dot instruction (products exact, fp32 accumulation),
+// single elements through fma.
+template <int W, bool FP16>
+__device__ __forceinline__ float payload_dot(typename VecOf<W>::type a, typename VecOf<W>::type b, float d)
+{
+    constexpr int E = W / 2;
+    if constexpr (E % 2 == 0) {
+        struct Words {
+            uint32_t w[E / 2];
+        };
+        const Words aw = __builtin_bit_cast(Words, a), bw = __builtin_bit_cast(Words, b);
+#pragma unroll
+        for (int i = 0; i < E / 2; ++i) {
+            if constexpr (FP16) {
+                typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+                d = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, aw.w[i]), __builtin_bit_cast(h2, bw.w[i]), d, false);
+            } else {
+                typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+                d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2, aw.w[i]), __builtin_bit_cast(b2, bw.w[i]), d,
+                                                    false);
+            }
+        }
+        return d;
+    } else {
+        const Halves<W> ah = __builtin_bit_cast(Halves<W>, a), bh = __builtin_bit_cast(Halves<W>, b);
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            d = fmaf(half_to_f32<FP16>(ah.h[e]), half_to_f32<FP16>(bh.h[e]), d);
+        return d;
+    }
+}
+
+// Gradient, compacted form: the next N valid partials of a row, <g, O_p> of
+// this lane's vectors added to the lane's slot of each partial in LDS (a
+// clamped tail vector contributes nothing).
+template <int N, int W, bool FP16, bool NTL, int VPL>
+__device__ __forceinline__ void bwd_dots(const char* po, const int64_t* offs, const uint32_t (&kbyte)[VPL],
+                                         const bool (&kin)[VPL], const typename VecOf<W>::type (&gv)[VPL],
+                                         float* dd, uint32_t G)
+{
+    typedef typename VecOf<W>::type V;
+    int64_t o[N];
+#pragma unroll
+    for (int u = 0; u < N; ++u)
+        o[u] = offs[u];
+    V x[N][VPL];
+#pragma unroll
+    for (int u = 0; u < N; ++u)
+#pragma unroll
+        for (int v = 0; v < VPL; ++v)
+            x[u][v] = ld_at<W, NTL>(po + o[u] + kbyte[v]);
+    issue_fence();
+#pragma unroll
+    for (int u = 0; u < N; ++u) {
+        float d = 0.0f;
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) {
+            const float dv = payload_dot<W, FP16>(x[u][v], gv[v], 0.0f);
+            d += kin[v] ? dv : 0.0f;
+        }
+        dd[u * G] += d;
+    }
+}
+
+// COMPACT: each row's valid partials as a compacted list (byte offsets) in
+// LDS, loaded with exact counts; every lane adds its share of <g, O_p> to its
+// own slot of a per-(row, valid partial) table, reduced in phase 3 (no
+// cross-lane shuffles in the payload loop); the workgroup holds one lane
+// group per row.  Otherwise a lane group reduces each dot product with
+// shuffles and accumulates it per partial.
+template <int W, bool FP16, int CZ, bool COMPACT>
 __global__ __launch_bounds__(kThreads) void k_combine_bwd(CombineBwd a)
 {
     typedef typename VecOf<W>::type V;
@@ -861,11 +932,22 @@ __global__ __launch_bounds__(kThreads) void k_combine_bwd(CombineBwd a)
     constexpr bool NTL = (CAM_NT_COMBINE_BWD & 1) != 0, NTS = (CAM_NT_COMBINE_BWD & 2) != 0;
     extern __shared__ float smem[];
     const uint32_t RB = a.rows_per_tile;
-    float* w_lds = smem;                                                       // RB * P weights
+    const uint32_t G = 1u << a.g_log2;
+    // COMPACT: offsets [RB*P] int64, masks [RB], weights [RB*P], per-lane dot
+    // products [RB*P*G], g_lse [RB], counts [RB], cu
+    int64_t* q_lds = reinterpret_cast<int64_t*>(smem);
+    uint64_t* mc_lds = reinterpret_cast<uint64_t*>(q_lds + RB * a.P);
+    float* wc_lds = reinterpret_cast<float*>(mc_lds + RB);
+    float* dd_lds = wc_lds + RB * a.P;
+    float* glc_lds = dd_lds + RB * a.P * G;
+    uint32_t* nv_lds = reinterpret_cast<uint32_t*>(glc_lds + RB);
+    // otherwise: weights [RB*P], <g, O_p> [RB*P], g_lse [RB], masks [RB], cu
+    float* w_lds = COMPACT ? wc_lds : smem;                                    // RB * P weights
     float* d_lds = w_lds + RB * a.P;                                           // RB * P  <g, O_p>
-    float* gl_lds = d_lds + RB * a.P;                                          // RB  g_lse
-    uint64_t* m_lds = reinterpret_cast<uint64_t*>(gl_lds + ((RB + 1) & ~1u));  // RB  validity masks
-    int32_t* cu_lds = reinterpret_cast<int32_t*>(m_lds + RB);                  // nseq + 1 (varlen)
+    float* gl_lds = COMPACT ? glc_lds : d_lds + RB * a.P;                      // RB  g_lse
+    uint64_t* m_lds = COMPACT ? mc_lds : reinterpret_cast<uint64_t*>(gl_lds + ((RB + 1) & ~1u));  // RB masks
+    int32_t* cu_lds = COMPACT ? reinterpret_cast<int32_t*>(nv_lds + RB)
+                              : reinterpret_cast<int32_t*>(m_lds + RB);        // nseq + 1 (varlen)
     const bool cached = CZ != kAll && a.nseq < kCuCache;
     if (cached)
         for (uint32_t i = threadIdx.x; i <= uint32_t(a.nseq); i += kThreads)
@@ -876,16 +958,19 @@ __global__ __launch_bounds__(kThreads) void k_combine_bwd(CombineBwd a)
     const uint32_t sp = lane & (GP - 1u);
     const uint32_t sbase = lane & ~(GP - 1u);
     const uint64_t spmask = GP == 64u ? ~0ull : ((1ull << GP) - 1ull);
-    const uint32_t G = 1u << a.g_log2;
     const uint32_t gl = lane & (G - 1u);
-    const uint32_t groups = uint32_t(kThreads) >> a.g_log2;
+    const uint32_t nthr = blockDim.x;
+    const uint32_t groups = nthr >> a.g_log2;
     const uint32_t group = threadIdx.x >> a.g_log2;
 
     for (uint64_t tile = blockIdx.x; tile < a.n_tiles; tile += gridDim.x) {
         const uint64_t row0 = tile * RB;
         // ---- phase 1: weights of the tile's rows
         __syncthreads();
-        for (uint32_t base = 0; base < RB * GP; base += kThreads) {
+        if (COMPACT)
+            for (uint32_t i = threadIdx.x; i < RB * a.P * G; i += nthr)
+                dd_lds[i] = 0.0f;
+        for (uint32_t base = 0; base < RB * GP; base += nthr) {
             const uint32_t tau = base + threadIdx.x;
             const uint32_t rl = tau >> a.gp_log2;
             const uint64_t row = row0 + rl;
@@ -918,11 +1003,19 @@ __global__ __launch_bounds__(kThreads) void k_combine_bwd(CombineBwd a)
                 const float iz = vmask ? 1.0f / Z : 0.0f;
                 if (sp < a.P) {
                     w_lds[rl * a.P + sp] = w * iz;
-                    d_lds[rl * a.P + sp] = 0.0f;
+                    if (!COMPACT)
+                        d_lds[rl * a.P + sp] = 0.0f;
+                }
+                if (COMPACT && valid) {
+                    const uint32_t slot = uint32_t(__builtin_popcountll(vmask & ((1ull << sp) - 1ull)));
+                    q_lds[rl * a.P + slot] =
+                        int64_t(sp) * a.po_sp_b + int64_t(t) * a.po_st_b + int64_t(h) * a.po_sh_b;
                 }
                 if (sp == 0) {
                     m_lds[rl] = vmask;
                     gl_lds[rl] = a.gl ? a.gl[int64_t(t) * a.gl_st + int64_t(h) * a.gl_sh] : 0.0f;
+                    if (COMPACT)
+                        nv_lds[rl] = uint32_t(__builtin_popcountll(vmask));
                 }
             }
         }
@@ -931,6 +1024,77 @@ __global__ __launch_bounds__(kThreads) void k_combine_bwd(CombineBwd a)
         // ---- phase 2: one pass over each row's payload
         const uint64_t left = a.n_rows - row0;
         const uint32_t nr = left < RB ? uint32_t(left) : RB;
+        if constexpr (COMPACT) {
+            constexpr int VPL = kCombineBwdVpl;
+            constexpr uint32_t NB = kCombineBwdNarrowBatch;
+            const char* po = static_cast<const char*>(a.po);
+            for (uint32_t rl = group; rl < nr; rl += groups) {
+                const uint64_t row = row0 + rl;
+                const uint32_t t = fdiv(uint32_t(row), a.div_H);
+                const uint32_t h = uint32_t(row) - t * a.H;
+                const uint64_t msk = m_lds[rl];
+                const uint32_t n = nv_lds[rl];
+                const char* grow = static_cast<const char*>(a.go) + int64_t(t) * a.go_st_b + int64_t(h) * a.go_sh_b;
+                char* drow = static_cast<char*>(a.dpo) + int64_t(t) * a.dpo_st_b + int64_t(h) * a.dpo_sh_b;
+                const int64_t* offs = q_lds + rl * a.P;
+                float* ddr = dd_lds + rl * a.P * G + gl;
+                for (uint32_t kb = 0; kb < a.cv; kb += G * VPL) {
+                    bool kin[VPL];
+                    uint32_t kbyte[VPL];
+                    V gv[VPL];
+#pragma unroll
+                    for (int v = 0; v < VPL; ++v) {
+                        const uint32_t idx = kb + gl + uint32_t(v) * G;
+                        kin[v] = idx < a.cv;
+                        kbyte[v] = (kin[v] ? idx : a.cv - 1) * uint32_t(W);
+                        gv[v] = V{};
+                    }
+                    if (n) {  // the upstream gradient is read only where some partial is valid
+#pragma unroll
+                        for (int v = 0; v < VPL; ++v)
+                            gv[v] = ld_at<W, NTL>(grow + kbyte[v]);
+                    }
+                    for (uint32_t k0 = 0; k0 < n; k0 += NB) {
+                        const uint32_t cnt = n - k0 < NB ? n - k0 : NB;
+                        const int64_t* o = offs + k0;
+                        float* dd = ddr + k0 * G;
+                        switch (cnt) {
+                        case 8: if constexpr (NB >= 8) bwd_dots<8, W, FP16, NTL, VPL>(po, o, kbyte, kin, gv, dd, G); break;
+                        case 7: if constexpr (NB >= 7) bwd_dots<7, W, FP16, NTL, VPL>(po, o, kbyte, kin, gv, dd, G); break;
+                        case 6: if constexpr (NB >= 6) bwd_dots<6, W, FP16, NTL, VPL>(po, o, kbyte, kin, gv, dd, G); break;
+                        case 5: if constexpr (NB >= 5) bwd_dots<5, W, FP16, NTL, VPL>(po, o, kbyte, kin, gv, dd, G); break;
+                        case 4: if constexpr (NB >= 4) bwd_dots<4, W, FP16, NTL, VPL>(po, o, kbyte, kin, gv, dd, G); break;
+                        case 3: if constexpr (NB >= 3) bwd_dots<3, W, FP16, NTL, VPL>(po, o, kbyte, kin, gv, dd, G); break;
+                        case 2: if constexpr (NB >= 2) bwd_dots<2, W, FP16, NTL, VPL>(po, o, kbyte, kin, gv, dd, G); break;
+                        default: bwd_dots<1, W, FP16, NTL, VPL>(po, o, kbyte, kin, gv, dd, G); break;
+                        }
+                    }
+                    // dO_p = w_p g for every partial (exact zero outside the valid set)
+                    float gf[VPL][E];
+#pragma unroll
+                    for (int v = 0; v < VPL; ++v) {
+                        const Halves<W> gh = __builtin_bit_cast(Halves<W>, gv[v]);
+#pragma unroll
+                        for (int e = 0; e < E; ++e)
+                            gf[v][e] = half_to_f32<FP16>(gh.h[e]);
+                    }
+                    for (uint32_t p = 0; p < a.P; ++p) {
+                        const bool vp = ((msk >> p) & 1ull) != 0;
+                        const float wp = w_lds[rl * a.P + p];
+#pragma unroll
+                        for (int v = 0; v < VPL; ++v) {
+                            float y[E];
+#pragma unroll
+                            for (int e = 0; e < E; ++e)
+                                y[e] = wp * gf[v][e];
+                            const V out = vp ? round_payload<W, FP16>(y) : V{};
+                            if (kin[v])
+                                st_at<W, NTS>(drow + int64_t(kbyte[v]) + int64_t(p) * a.dpo_sp_b, out);
+                        }
+                    }
+                }
+            }
+        } else
         for (uint32_t rl = group; rl < nr; rl += groups) {
             const uint64_t row = row0 + rl;
             const uint32_t t = fdiv(uint32_t(row), a.div_H);
@@ -1004,14 +1168,25 @@ __global__ __launch_bounds__(kThreads) void k_combine_bwd(CombineBwd a)
         __syncthreads();
 
         // ---- phase 3: gradient of the partial LSEs
-        for (uint32_t base = 0; base < RB * GP; base += kThreads) {
+        for (uint32_t base = 0; base < RB * GP; base += nthr) {
             const uint32_t tau = base + threadIdx.x;
             const uint32_t rl = tau >> a.gp_log2;
             const uint64_t row = row0 + rl;
             const bool live = rl < RB && row < a.n_rows;
             const bool mine = live && sp < a.P;
             const float w = mine ? w_lds[rl * a.P + sp] : 0.0f;
-            const float d = mine ? d_lds[rl * a.P + sp] : 0.0f;
+            float d = 0.0f;
+            if (COMPACT) {
+                const uint64_t vm = mine ? m_lds[rl] : 0ull;
+                if (((vm >> sp) & 1ull) != 0) {
+                    const uint32_t slot = uint32_t(__builtin_popcountll(vm & ((1ull << sp) - 1ull)));
+                    const float* q = dd_lds + (rl * a.P + slot) * G;
+                    for (uint32_t j = 0; j < G; ++j)
+                        d += q[j];
+                }
+            } else {
+                d = mine ? d_lds[rl * a.P + sp] : 0.0f;
+            }
             float s = w * d;
             for (uint32_t off = GP >> 1; off > 0; off >>= 1)
                 s += __shfl_xor(s, int(off), int(GP));
@@ -1039,12 +1214,12 @@ int causal_rule(const Rec& a)
     return !a.cu ? kAll : a.first ? kPlan : kPieces;
 }
 
-template <int W, bool FP16>
+template <int W, bool FP16, bool COMPACT>
 const void* pick_combine_bwd(int cz)
 {
-    return cz == kPlan ? fn_ptr(&k_combine_bwd<W, FP16, kPlan>)
-           : cz == kPieces ? fn_ptr(&k_combine_bwd<W, FP16, kPieces>)
-                           : fn_ptr(&k_combine_bwd<W, FP16, kAll>);
+    return cz == kPlan ? fn_ptr(&k_combine_bwd<W, FP16, kPlan, COMPACT>)
+           : cz == kPieces ? fn_ptr(&k_combine_bwd<W, FP16, kPieces, COMPACT>)
+                           : fn_ptr(&k_combine_bwd<W, FP16, kAll, COMPACT>);
 }
 
 cam_status launch_combine_bwd(const CombineBwd& a, void* stream)
@@ -1053,13 +1228,19 @@ cam_status launch_combine_bwd(const CombineBwd& a, void* stream)
     const void* fn = nullptr;
 #define CAM_PICK_BWD(Wd)                                                                                \
     if (a.width == Wd)                                                                                  \
-        fn = a.fp16 ? pick_combine_bwd<Wd, true>(cz) : pick_combine_bwd<Wd, false>(cz);
+        fn = a.compact ? (a.fp16 ? pick_combine_bwd<Wd, true, true>(cz) : pick_combine_bwd<Wd, false, true>(cz)) \
+                       : (a.fp16 ? pick_combine_bwd<Wd, true, false>(cz) : pick_combine_bwd<Wd, false, false>(cz));
     CAM_PICK_BWD(16) CAM_PICK_BWD(8) CAM_PICK_BWD(4) CAM_PICK_BWD(2)
 #undef CAM_PICK_BWD
-    uint64_t lds = (2ull * a.rows_per_tile * a.P + ((a.rows_per_tile + 1) & ~1u)) * 4 + uint64_t(a.rows_per_tile) * 8;
+    const uint64_t RB = a.rows_per_tile, G = uint64_t(1) << a.g_log2;
+    uint64_t lds = a.compact ? RB * a.P * (8 + 4 + 4 * G) + RB * (8 + 4 + 4)
+                             : (2ull * RB * a.P + ((RB + 1) & ~1ull)) * 4 + RB * 8;
     if (a.cu && a.nseq < kCuCache)
         lds += uint64_t(a.nseq + 1) * 4;
-    return launch(fn, a, a.n_tiles, stream, "lse_combine_backward", lds, kThreads);
+    if (lds > 65536)
+        return set_error(CAM_ERR_UNSUPPORTED, "lse_combine_backward: a tile's tables need %llu bytes of LDS (at most "
+                         "65536)", (unsigned long long)lds);
+    return launch(fn, a, a.n_tiles, stream, "lse_combine_backward", lds, a.threads);
 }
 
 // The output modes each admission rule is built for: every rule writes at
