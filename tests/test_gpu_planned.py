@@ -35,6 +35,8 @@ CASES = [  # (lengths in blocks, block size, W, B, H, D, dtype)
     ([0, 12, 5, 33, 1, 0, 64], 1, 8, 2, 16, 8, torch.float16),     # 16-byte runs of 8 elements x 2 heads
     ([6, 1, 1], 1, 2, 1, 4, 3, torch.bfloat16),                    # 6-byte runs: 2-byte accesses
     ([9, 27, 4], 2, 5, 2, 10, 2, torch.float32),                   # 8-byte runs, 5 ranks
+    ([3, 40, 1, 7, 90, 2], 4, 4, 2, 16, 128, torch.bfloat16),      # 1 KB runs: the wave-uniform row map
+    ([20, 1, 9], 8, 3, 1, 6, 256, torch.bfloat16),                 # 1 KB runs over 3 ranks
 ]
 
 

@@ -97,6 +97,10 @@ VARLEN = [  # (lengths, P, B, H, D, dtype)
     (list(range(1, 60)), 8, 1, 8, 7, torch.float16),              # odd D, many tiny sequences
     ([4096, 17, 2048, 333], 8, 2, 32, 128, torch.bfloat16),
     ([1000, 999], 4, 1, 4, 32, torch.float32),
+    # rows of a multiple of 64 16-byte vectors: the wave-uniform row-map kernel
+    ([1, 2, 3, 129, 64, 700, 0], 2, 3, 4, 256, torch.bfloat16),   # 1 KB runs, sub-P and empty sequences
+    ([5, 1000, 0, 33], 2, 1, 16, 128, torch.bfloat16),            # 2 KB runs
+    ([77, 3, 500], 4, 2, 8, 128, torch.float32),                  # 1 KB runs of 4-byte elements
 ]
 
 
