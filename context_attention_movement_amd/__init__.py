@@ -150,6 +150,15 @@ def _ptr(t: torch.Tensor | None) -> int | None:
     return None if t is None else t.data_ptr()
 
 
+def _tables_on(ref: torch.Tensor, *tables: torch.Tensor) -> None:
+    """A plan's device tables must live on the device of the data they index
+    (a host table's address handed to a kernel would be read as device memory)."""
+    for t in tables:
+        if t.device != ref.device:
+            raise ValueError(f"the plan's tables are on {t.device}, the data on {ref.device}: "
+                             "build the plan for that device (device=...) or move it there")
+
+
 def _check_buffer(t: torch.Tensor, name: str, shape, dtype: torch.dtype, contiguous: bool = True,
                   inner_contiguous: bool = False) -> None:
     """A caller-supplied output or input buffer: its shape and dtype must be
@@ -271,6 +280,7 @@ def ulysses_seq_to_head_varlen(x: torch.Tensor, plan: VarlenPlan, B: int = 1,
     _contig(out, "out")
     if out.numel() != x.numel() or out.dtype != x.dtype:
         raise ValueError("out must match x in size and dtype")
+    _tables_on(x, plan.cu, plan.rank_cu, plan.rank_off)
     _check(library().ulysses_seq_to_head_varlen(
         x.data_ptr(), out.data_ptr(), plan.cu.data_ptr(), plan.rank_cu.data_ptr(), plan.rank_off.data_ptr(),
         plan.nseq, T, P, B, H, D, _dt(x, True), _stream(x)))
@@ -290,6 +300,7 @@ def ulysses_head_to_seq_varlen(x: torch.Tensor, plan: VarlenPlan, out: torch.Ten
     _contig(out, "out")
     if out.numel() != x.numel() or out.dtype != x.dtype:
         raise ValueError("out must match x in size and dtype")
+    _tables_on(x, plan.cu, plan.rank_cu, plan.rank_off)
     _check(library().ulysses_head_to_seq_varlen(
         x.data_ptr(), out.data_ptr(), plan.cu.data_ptr(), plan.rank_cu.data_ptr(), plan.rank_off.data_ptr(),
         plan.nseq, T, P, B, H, D, _dt(x, True), _stream(x)))
@@ -446,6 +457,7 @@ def ulysses_seq_to_head_spans(x: torch.Tensor, plan: ThdPlan, B: int = 1,
     _contig(out, "out")
     if out.numel() != x.numel() or out.dtype != x.dtype:
         raise ValueError("out must match x in size and dtype")
+    _tables_on(x, plan.span_start, plan.span_rank, plan.span_local, plan.rank_off)
     _check(library().ulysses_seq_to_head_spans(
         x.data_ptr(), out.data_ptr(), plan.span_start.data_ptr(), plan.span_rank.data_ptr(),
         plan.span_local.data_ptr(), plan.rank_off.data_ptr(), plan.n_spans, T, P, B, H, D, _dt(x, True),
@@ -465,6 +477,7 @@ def ulysses_head_to_seq_spans(x: torch.Tensor, plan: ThdPlan, out: torch.Tensor 
     _contig(out, "out")
     if out.numel() != x.numel() or out.dtype != x.dtype:
         raise ValueError("out must match x in size and dtype")
+    _tables_on(x, plan.span_start, plan.span_rank, plan.span_local, plan.rank_off)
     _check(library().ulysses_head_to_seq_spans(
         x.data_ptr(), out.data_ptr(), plan.span_start.data_ptr(), plan.span_rank.data_ptr(),
         plan.span_local.data_ptr(), plan.rank_off.data_ptr(), plan.n_spans, T, P, B, H, D, _dt(x, True),
@@ -605,6 +618,7 @@ def lse_combine_planned(part_out: torch.Tensor, part_lse: torch.Tensor, plan: Th
         raise ValueError("the plan's tables are not on the device (thd_plan(..., device=...) or plan.to(device))")
     if P != plan.world_size or T != plan.total_tokens:
         raise ValueError("part_out must be [world_size][total_tokens][H][D] for this plan")
+    _tables_on(part_out, plan.cu, plan.first_pos)
     _check(library().lse_combine_planned(part_out.data_ptr(), *part_out.stride()[:3], part_lse.data_ptr(),
                                          *part_lse.stride(), P, T, H, D, _dt(part_out), out.data_ptr(),
                                          *out.stride()[:2], _ptr(lse_out), *lo, plan.cu.data_ptr(),
@@ -646,6 +660,7 @@ def lse_combine_backward(part_out: torch.Tensor, part_lse: torch.Tensor, g_out: 
             raise ValueError("the plan's tables are not on the device")
         if P != plan.world_size or T != plan.total_tokens:
             raise ValueError("part_out must be [world_size][total_tokens][H][D] for this plan")
+        _tables_on(part_out, plan.cu, plan.first_pos)
         _check(library().lse_combine_planned_backward(*args, plan.cu.data_ptr(), plan.first_pos.data_ptr(),
                                                       plan.cu_host.size - 1, _stream(part_out)))
     elif cu_seqlens is None:
@@ -711,6 +726,7 @@ def lse_combine_varlen_seq(part_out: torch.Tensor, part_lse: torch.Tensor, plan:
         lse_out = None
     if lse_out is not None:
         _contig(lse_out, "lse_out")
+    _tables_on(part_out, plan.cu, plan.rank_cu, plan.rank_off)
     _check(library().lse_combine_varlen_seq(part_out.data_ptr(), *part_out.stride()[:3], part_lse.data_ptr(),
                                             *part_lse.stride(), P, T, H, D, _dt(part_out), out.data_ptr(),
                                             _ptr(lse_out), plan.cu.data_ptr(), plan.rank_cu.data_ptr(),

@@ -374,3 +374,14 @@ def test_binding_rejects_wrong_varlen_seq_outputs(cam):
         cam.lse_combine_varlen_seq(po, pl, plan, lse_out=torch.zeros((T + 1, H), dtype=torch.float32))
     with pytest.raises(ValueError, match="part_lse must be"):
         cam.lse_combine_varlen_seq(po, pl[:, :-1], plan)
+
+
+def test_binding_rejects_plan_tables_on_another_device(cam):
+    # a plan whose tables sit on the host must not reach a kernel that runs
+    # on the device (its host addresses would be read as device memory);
+    # meta tensors stand in for device data on a machine without a GPU
+    import torch
+    data = torch.empty((2, 3), device="meta")
+    with pytest.raises(ValueError, match="the plan's tables are on cpu"):
+        cam._tables_on(data, torch.zeros(3, dtype=torch.int32))
+    cam._tables_on(data, torch.empty(3, dtype=torch.int32, device="meta"))  # same device: accepted

@@ -175,3 +175,18 @@ def test_empty_inputs(cam):
     plan = cam.ulysses_varlen_plan([0], 2)
     y = torch.empty((0, 4, 8), dtype=torch.bfloat16, device="cuda")
     assert cam.ulysses_seq_to_head_varlen(y, plan, 1).numel() == 0
+
+
+def test_host_plan_rejected_before_launch(cam):
+    # a plan built with its tables on the host is refused for device data
+    # (the check runs in the binding; no kernel is launched)
+    announce("host plan with device data")
+    T, H, D, P = 64, 8, 16, 2
+    plan = cam.ulysses_varlen_plan([0, 20, T], P, device="cpu")
+    x = torch.zeros((T, H, D), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError, match="the plan's tables are on cpu"):
+        cam.ulysses_seq_to_head_varlen(x, plan, 1)
+    po = torch.zeros((P, T, H, D), dtype=torch.bfloat16, device="cuda")
+    pl = torch.zeros((P, T, H), dtype=torch.float32, device="cuda")
+    with pytest.raises(ValueError, match="the plan's tables are on cpu"):
+        cam.lse_combine_varlen_seq(po, pl, plan)
