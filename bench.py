@@ -29,6 +29,7 @@ from __future__ import annotations
 
 import argparse
 import csv
+import gc
 import glob
 import hashlib
 import json
@@ -779,24 +780,33 @@ def main():
     kern = {n: k for n, k, _ in w.ops()}
     stream = torch.cuda.Stream()
 
-    # ---- timed region: K steps, every operation once per step, events around each
+    # ---- timed region: K steps, every operation once per step, events around each.
+    # The steps' callables are built beforehand and Python's cyclic garbage
+    # collector is paused, so that the host keeps ahead of the GPU: a host
+    # pause while the queue is empty would show up as GPU time between events.
     with torch.cuda.stream(stream):
         for _ in range(args.warmup):
             for _, _, fn in w.ops():
                 fn()
             w.step_index += 1
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for k in range(args.steps):
-            ev = evs[k]
-            ev[0].record(stream)
-            for i, (_, _, fn) in enumerate(w.ops()):
-                fn()
-                ev[i + 1].record(stream)
-            w.step_index += 1
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
+        step_fns = [[fn for _, _, fn in w.ops(k=w.step_index + k)] for k in range(args.steps)]
+        gc.collect()
+        gc.disable()
+        try:
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for k in range(args.steps):
+                ev = evs[k]
+                ev[0].record(stream)
+                for i, fn in enumerate(step_fns[k]):
+                    fn()
+                    ev[i + 1].record(stream)
+            torch.cuda.synchronize()
+            wall = time.perf_counter() - t0
+        finally:
+            gc.enable()
+        w.step_index += args.steps
     in_step = {n: [evs[k][i].elapsed_time(evs[k][i + 1]) * 1000.0 for k in range(args.steps)]
                for i, n in enumerate(names)}
     step_ms = wall * 1000.0 / args.steps
@@ -936,11 +946,18 @@ def main():
             "in_step_us_mean": round(mean_step, 2),
             "in_step_us_median": round(statistics.median(in_step[n]), 2),
             "in_step_us_p95": round(sorted(in_step[n])[int(0.95 * (len(in_step[n]) - 1))], 2),
+            "in_step_us_max": round(max(in_step[n]), 2),
             "in_step_GBps": round(nbytes[n] / mean_step / 1e3, 1),
             "launch": launches[n],
         }
-    dom = max(names, key=lambda n: statistics.mean(in_step[n]))
+    # the dominant kernel: the largest typical (median) share of the step; its
+    # achieved rate uses the mean launch duration over the timed region
+    dom = max(names, key=lambda n: statistics.median(in_step[n]))
     dom_us = statistics.mean(in_step[dom])
+    for n in names:
+        if max(in_step[n]) > 3.0 * statistics.median(in_step[n]):
+            print(f"warning: {n} took {max(in_step[n]):.1f} us in one step (median {statistics.median(in_step[n]):.1f} us)",
+                  file=sys.stderr, flush=True)
     dom_gbps = nbytes[dom] / dom_us / 1e3
     traffic = None
     if TRAFFIC_FILE.exists():
@@ -983,6 +1000,7 @@ def main():
             "frac": round(dom_gbps / HBM_PEAK_GBPS, 4),
             "traffic": traffic,
             "avg_launch_us": round(dom_us, 2),
+            "median_launch_us": round(statistics.median(in_step[dom]), 2),
             "algorithmic_bytes_per_launch": int(nbytes[dom]),
         },
         "extensions": ext,
