@@ -782,8 +782,9 @@ def main():
 
     # ---- timed region: K steps, every operation once per step, events around each.
     # The steps' callables are built beforehand and Python's cyclic garbage
-    # collector is paused, so that the host keeps ahead of the GPU: a host
-    # pause while the queue is empty would show up as GPU time between events.
+    # collector is paused (here and in every GPU timing after it), so that the
+    # host keeps ahead of the GPU: a host pause while the queue is empty would
+    # show up as GPU time between events.
     with torch.cuda.stream(stream):
         for _ in range(args.warmup):
             for _, _, fn in w.ops():
@@ -792,20 +793,17 @@ def main():
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
         step_fns = [[fn for _, _, fn in w.ops(k=w.step_index + k)] for k in range(args.steps)]
         gc.collect()
-        gc.disable()
-        try:
-            torch.cuda.synchronize()
-            t0 = time.perf_counter()
-            for k in range(args.steps):
-                ev = evs[k]
-                ev[0].record(stream)
-                for i, fn in enumerate(step_fns[k]):
-                    fn()
-                    ev[i + 1].record(stream)
-            torch.cuda.synchronize()
-            wall = time.perf_counter() - t0
-        finally:
-            gc.enable()
+        gc.disable()  # until every GPU timing below is taken
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(args.steps):
+            ev = evs[k]
+            ev[0].record(stream)
+            for i, fn in enumerate(step_fns[k]):
+                fn()
+                ev[i + 1].record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
         w.step_index += args.steps
     in_step = {n: [evs[k][i].elapsed_time(evs[k][i + 1]) * 1000.0 for k in range(args.steps)]
                for i, n in enumerate(names)}
@@ -929,6 +927,7 @@ def main():
             torch.cuda.synchronize()
             copy_same[n] = 2 * half / (e0.elapsed_time(e1) * 1000.0 / calls) / 1e3
     del c_src, c_dst
+    gc.enable()
 
     op_table = {}
     for n in names:
