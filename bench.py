@@ -360,6 +360,9 @@ class Workload:
 
 
 LDS_ROWS_PER_TILE = 4  # rows staged per workgroup by the LDS-staged relayout ablation
+# µs/call of each operation alone: warm-up calls, then blocks of back-to-back
+# calls between two HIP events (median and 95th percentile over the blocks)
+WARM_CALLS, BLOCKS, PER_BLOCK = 10, 8, 5
 
 
 def paired_ab(torch, stream, fa, fb, pairs=8, calls=10):
@@ -736,7 +739,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--calls", type=int, default=20, help="back-to-back calls per operation for µs/call")
+    ap.add_argument("--calls", type=int, default=20, help="calls of the operation under --profile-op")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-threads", type=int, default=16, help="most threads of the N-core CPU baseline leg")
     ap.add_argument("--profile-op", default=None,
@@ -785,15 +788,17 @@ def main():
     # collector is paused (here and in every GPU timing after it), so that the
     # host keeps ahead of the GPU: a host pause while the queue is empty would
     # show up as GPU time between events.
+    # The host work comes before the warm-up steps, so that the GPU does not
+    # sit idle (and clock down) between the warm-up and the timed steps.
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
+    step_fns = [[fn for _, _, fn in w.ops(k=w.step_index + args.warmup + k)] for k in range(args.steps)]
+    gc.collect()
+    gc.disable()  # until every GPU timing below is taken
     with torch.cuda.stream(stream):
         for _ in range(args.warmup):
             for _, _, fn in w.ops():
                 fn()
             w.step_index += 1
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
-        step_fns = [[fn for _, _, fn in w.ops(k=w.step_index + k)] for k in range(args.steps)]
-        gc.collect()
-        gc.disable()  # until every GPU timing below is taken
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for k in range(args.steps):
@@ -810,40 +815,39 @@ def main():
     step_ms = wall * 1000.0 / args.steps
     step_bytes = sum(nbytes.values())
 
-    # ---- µs per call, each operation alone: back-to-back calls between two
-    # events on the launch stream (the MLA and video-O calls rotate over
-    # their buffer sets)
-    iso_us, launches = {}, {}
-    with torch.cuda.stream(stream):
-        for i, n in enumerate(names):
-            for j in range(3):
-                w.ops(k=j)[i][2]()
-            launches[n] = cam.last_launch()
-            fns = [w.ops(k=j)[i][2] for j in range(args.calls)]
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # ---- µs per call, each operation alone: after WARM_CALLS warm-up calls,
+    # BLOCKS blocks of PER_BLOCK back-to-back calls, each block between two
+    # events on the launch stream; the median block gives µs/call, beside its
+    # 95th percentile (the MLA and video-O calls rotate over their buffer sets)
+    def blocks_us(get_fn):
+        for j in range(WARM_CALLS):
+            get_fn(j)()
+        fns = [get_fn(WARM_CALLS + j) for j in range(BLOCKS * PER_BLOCK)]
+        evb = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(BLOCKS)]
+        torch.cuda.synchronize()
+        for b, (e0, e1) in enumerate(evb):
             e0.record(stream)
-            for fn in fns:
+            for fn in fns[b * PER_BLOCK:(b + 1) * PER_BLOCK]:
                 fn()
             e1.record(stream)
-            torch.cuda.synchronize()
-            iso_us[n] = e0.elapsed_time(e1) * 1000.0 / args.calls
+        torch.cuda.synchronize()
+        per = sorted(e0.elapsed_time(e1) * 1000.0 / PER_BLOCK for e0, e1 in evb)
+        return statistics.median(per), per[int(0.95 * (len(per) - 1))]
+
+    iso_us, iso_p95, launches = {}, {}, {}
+    with torch.cuda.stream(stream):
+        for i, n in enumerate(names):
+            iso_us[n], iso_p95[n] = blocks_us(lambda j, i=i: w.ops(k=j)[i][2])
+            launches[n] = cam.last_launch()
 
     # ---- operations beyond the step (same µs/call method)
     ext = {}
     with torch.cuda.stream(stream):
         for i, (n, nb_ext, _) in enumerate(w.extension_ops()):
-            for j in range(3):
-                w.extension_ops(k=j)[i][2]()
-            fns = [w.extension_ops(k=j)[i][2] for j in range(args.calls)]
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for fn in fns:
-                fn()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            us = e0.elapsed_time(e1) * 1000.0 / args.calls
-            ext[n] = {"us_per_call": round(us, 2), "algorithmic_bytes": int(nb_ext), "last_launch": cam.last_launch(),
-                      "GBps": round(nb_ext / us / 1e3, 1), "frac_of_hbm_peak": round(nb_ext / us / 1e3 / HBM_PEAK_GBPS, 4)}
+            us, p95 = blocks_us(lambda j, i=i: w.extension_ops(k=j)[i][2])
+            ext[n] = {"us_per_call": round(us, 2), "us_per_call_p95": round(p95, 2), "algorithmic_bytes": int(nb_ext),
+                      "last_launch": cam.last_launch(), "GBps": round(nb_ext / us / 1e3, 1),
+                      "frac_of_hbm_peak": round(nb_ext / us / 1e3 / HBM_PEAK_GBPS, 4)}
 
     # ---- Q/K/V projection written into the head-sharded layout (MFMA); the
     # library GEMM (torch.mm) of the same product is timed beside it as a
@@ -938,6 +942,7 @@ def main():
             "kernel": kern[n],
             "algorithmic_bytes": int(nbytes[n]),
             "us_per_call": round(us, 2),
+            "us_per_call_p95": round(iso_p95[n], 2),
             "GBps": round(gbps, 1),
             "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
             "copy_same_bytes_GBps": round(copy_same[n], 1),
@@ -1016,8 +1021,9 @@ def main():
         "inputs_sha256_note": "SHA-256 over the per-buffer digests (shape, dtype, first and last MiB of every "
                               "seeded input buffer); --digests-out writes them one by one",
         "timing": "value and ms_per_step: host clock around the K synchronized steps; ops[*].us_per_call: "
-                  f"{args.calls} back-to-back calls of that operation alone between two HIP events; "
-                  "ops[*].in_step_*: HIP events around the operation inside the steps",
+                  f"after {WARM_CALLS} warm-up calls, {BLOCKS} blocks of {PER_BLOCK} back-to-back calls of that "
+                  "operation alone, each block between two HIP events: the median block (us_per_call_p95: its "
+                  "95th percentile); ops[*].in_step_*: HIP events around the operation inside the steps",
     }
     result["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(w, args.cpu_threads)
     # the gated figures and the per-operation table last, so that the end of
