@@ -181,6 +181,8 @@ cam_status dense_relayout(const void* in, void* out, int64_t P, int64_t B, int64
     const uint64_t run = uint64_t(H / P) * uint64_t(D) * es;
     DenseRelayout a{};
     a.width = pick_width({run, reinterpret_cast<uintptr_t>(in), reinterpret_cast<uintptr_t>(out)});
+    if (run / a.width >= kU32Limit)
+        return set_error(CAM_ERR_UNSUPPORTED, "%s: one head block of one row exceeds 2^31 vectors", op);
     a.src = in;
     a.dst = out;
     a.P = uint32_t(P);
@@ -316,6 +318,8 @@ cam_status varlen_relayout(const void* in, void* out, const int32_t* cu, const i
     const uint64_t run = uint64_t(H / P) * uint64_t(D) * es;
     VarlenRelayout a{};
     a.width = pick_width({run, reinterpret_cast<uintptr_t>(in), reinterpret_cast<uintptr_t>(out)});
+    if (run / a.width >= kU32Limit)
+        return set_error(CAM_ERR_UNSUPPORTED, "%s: one head block of one row exceeds 2^31 vectors", op);
     a.src = in;
     a.dst = out;
     a.cu = cu;
@@ -474,6 +478,8 @@ cam_status combine(const char* op, const CombineIn& c, void* stream)
     a.H = uint32_t(c.H);
     a.div_H = make_fastdiv(a.H);
     a.n_rows = uint64_t(n_rows);
+    if (row_b / a.width >= kU32Limit)
+        return set_error(CAM_ERR_UNSUPPORTED, "%s: one row exceeds 2^31 vectors", op);
     a.cv = uint32_t(row_b / a.width);
     a.g_log2 = log2u(pow2ceil(a.cv < 64 ? (a.cv ? a.cv : 1) : 64));
     if (a.g_log2 < 6 && kCombineNarrowVpl == 2 && a.g_log2 > 0)
@@ -617,6 +623,8 @@ cam_status combine_backward(const char* op, const CombineBwdIn& c, void* stream)
     a.H = uint32_t(c.H);
     a.div_H = make_fastdiv(a.H);
     a.n_rows = uint64_t(n_rows);
+    if (row_b / a.width >= kU32Limit)
+        return set_error(CAM_ERR_UNSUPPORTED, "%s: one row exceeds 2^31 vectors", op);
     a.cv = uint32_t(row_b / a.width);
     a.gp_log2 = log2u(pow2ceil(a.P));
     const uint32_t g_full = log2u(pow2ceil(a.cv < 64 ? (a.cv ? a.cv : 1) : 64));
@@ -842,6 +850,8 @@ cam_status lse_pack(const void* out, int64_t o_sp, int64_t o_st, int64_t o_sh, c
     a.Tp = uint64_t(T / P);
     a.Hp = uint32_t(H / P);
     a.rows = uint32_t(g.rows);
+    if (row_b / a.width >= kU32Limit)
+        return set_error(CAM_ERR_UNSUPPORTED, "%s: one row exceeds 2^31 vectors", op);
     a.cv = uint32_t(row_b / a.width);
     a.div_cv = make_fastdiv(a.cv ? a.cv : 1);
     a.chunk_b = uint64_t(g.chunk);
@@ -1132,6 +1142,8 @@ cam_status lse_merge(float* acc_out, int64_t a_st, int64_t a_sh, float* acc_lse,
     a.H = uint32_t(H);
     a.div_H = make_fastdiv(a.H);
     a.n_rows = uint64_t(n_rows);
+    if (uint64_t(D / 4) >= kU32Limit)
+        return set_error(CAM_ERR_UNSUPPORTED, "%s: one row exceeds 2^31 vectors", op);
     a.cv = uint32_t(D / 4);
     a.g_log2 = log2u(pow2ceil(a.cv < 64 ? (a.cv ? a.cv : 1) : 64));
     if (a.g_log2 < 6 && kCombineNarrowVpl == 2 && a.g_log2 > 0)

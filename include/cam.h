@@ -96,6 +96,9 @@ cam_status cam_last_launch(uint64_t* workgroups, uint32_t* threads, uint64_t* ld
  * CAM_BF16 / CAM_FP16, 4 for CAM_FP32).  Requires P >= 1, S % P == 0,
  * H % P == 0 (CAM_ERR_DIVISIBILITY).  Any of B, S, H, D may be 0 (no work).
  * `in` and `out` are device buffers of B*S*H*D elements each.
+ * Limits (CAM_ERR_UNSUPPORTED beyond them): P and B below 2^32; one head block
+ * of one row ((H/P)*D elements) and one (source rank, plane, destination
+ * rank) slab below 2^31 access vectors; at most 2^32 tiles.
  */
 cam_status ulysses_seq_to_head(const void* in, void* out, int64_t P, int64_t B, int64_t S,
                                int64_t H, int64_t D, cam_dtype dt, void* stream);
@@ -128,7 +131,10 @@ cam_status ulysses_head_to_seq(const void* in, void* out, int64_t P, int64_t B, 
  *   does not match cu_seqlens is not detected on the device; rows whose
  *   computed source or destination falls outside the buffers are skipped, so
  *   a malformed plan cannot make the kernel access out of bounds.
- *   Requires H % P == 0.
+ *   Requires H % P == 0; T and nseq must fit int32 (CAM_ERR_SHAPE).  Limits
+ *   (CAM_ERR_UNSUPPORTED beyond them): P and B below 2^32; one head block of
+ *   one row and one (rank, plane) below 2^31 access vectors; at most 2^32
+ *   tiles.
  */
 cam_status ulysses_varlen_plan(const int32_t* cu_seqlens_host, int64_t nseq, int64_t P,
                                int32_t* rank_cu_host, int64_t* rank_off_host);
@@ -244,8 +250,8 @@ cam_status ulysses_head_to_seq_spans(const void* in, void* out, const int32_t* s
  * arguments (the reason is in cam_last_error()).
  *
  * Limits (CAM_ERR_UNSUPPORTED beyond them): P < 65536; rows per chunk below
- * 2^31; one chunk's O-region below 2^31 access vectors; P*P chunks of tiles
- * below 2^32 tiles.
+ * 2^31; one row, and one chunk's O-region, below 2^31 access vectors; P*P
+ * chunks of tiles below 2^32 tiles.
  */
 int64_t lse_pack_bytes(int64_t P, int64_t T, int64_t H, int64_t Dv, int scatter_dim,
                        cam_dtype dt);
@@ -289,9 +295,9 @@ cam_status lse_pack(const void* out, int64_t o_sp, int64_t o_st, int64_t o_sh,
  *
  * Limits of every combine entry point (lse_combine*, and their _seq, _planned
  * and _backward forms): 1 <= P <= 64 (a row's partials are reduced across
- * one wave; CAM_ERR_UNSUPPORTED above); T*H below 2^31 rows
- * (CAM_ERR_UNSUPPORTED); strides non-negative; the varlen and planned forms
- * need nseq >= 1 and T < 2^31.
+ * one wave; CAM_ERR_UNSUPPORTED above); T*H below 2^31 rows and one row
+ * below 2^31 access vectors (CAM_ERR_UNSUPPORTED); strides non-negative; the
+ * varlen and planned forms need nseq >= 1 and T < 2^31.
  */
 cam_status lse_combine_packed(const void* packed, int64_t P, int64_t T, int64_t H, int64_t Dv,
                               int scatter_dim, cam_dtype dt, void* out, float* lse_out,
@@ -371,7 +377,8 @@ cam_status lse_combine_varlen_seq(const void* part_out, int64_t po_sp, int64_t p
  *   rounded result, for the last hop.  All strides are in elements (D
  *   contiguous); D % 4 == 0; accumulator rows 16-byte and payload rows 8-byte
  *   aligned.  Updates in place; no buffer may overlap another.  T*H must be
- *   below 2^31 rows and every stride non-negative (CAM_ERR_UNSUPPORTED).
+ *   below 2^31 rows, D/4 below 2^31 and every stride non-negative
+ *   (CAM_ERR_UNSUPPORTED).
  */
 cam_status lse_merge(float* acc_out, int64_t a_st, int64_t a_sh, float* acc_lse, int64_t al_st,
                      int64_t al_sh, const void* part_out, int64_t p_st, int64_t p_sh,

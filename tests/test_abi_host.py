@@ -385,3 +385,31 @@ def test_binding_rejects_plan_tables_on_another_device(cam):
     with pytest.raises(ValueError, match="the plan's tables are on cpu"):
         cam._tables_on(data, torch.zeros(3, dtype=torch.int32))
     cam._tables_on(data, torch.empty(3, dtype=torch.int32, device="meta"))  # same device: accepted
+
+
+def test_rows_beyond_32bit_vector_counts_rejected(lib):
+    # one row (or one head block of a row) of 2^31 or more 16-byte vectors
+    # would not fit the kernels' 32-bit vector counters: refused before any
+    # launch (the fake addresses are far enough apart that nothing overlaps)
+    G = 1 << 40
+    f = lib.ulysses_seq_to_head
+    assert f(A, A + G, 1, 1, 1, 1, 1 << 35, BF16, None) == UNSUP
+    assert b"2^31 vectors" in lib.cam_last_error()
+    assert lib.ulysses_head_to_seq(A, A + G, 1, 1, 1, 1, 1 << 35, BF16, None) == UNSUP
+    v = lib.ulysses_seq_to_head_varlen
+    assert v(A, A + G, A + 2 * G, A + 3 * G, A + 4 * G, 1, 1, 1, 1, 1, 1 << 35, BF16, None) == UNSUP
+    D = 1 << 34                                   # 2^35-byte bf16 rows: 2^31 vectors
+    c = lib.lse_combine
+    assert c(A, D, D, D, A + 2 * G, 1, 1, 1, 1, 1, 1, D, BF16, A + G, D, D, A + 3 * G, 1, 1, None) == UNSUP
+    assert b"one row exceeds" in lib.cam_last_error()
+    b = lib.lse_combine_backward
+    assert b(A, D, D, D, A + 2 * G, 1, 1, 1, 1, 1, 1, D, BF16, A + G, D, D, None, 1, 1,
+             A + 3 * G, D, D, D, A + 4 * G, 1, 1, 1, None) == UNSUP
+    assert b"one row exceeds" in lib.cam_last_error()
+    p = lib.lse_pack
+    assert p(A, D, D, D, A + 2 * G, 1, 1, 1, A + 3 * G, 1, 1, 1, 1, 1, 1, D, 1, BF16, A + G, None) == UNSUP
+    assert b"one row exceeds" in lib.cam_last_error()
+    m = lib.lse_merge
+    Dm = 1 << 33                                  # 2^33 fp32 accumulator elements: 2^31 four-element vectors
+    assert m(A, Dm, Dm, A + G, 1, 1, A + 2 * G, Dm, Dm, A + 3 * G, 1, 1, 1, 1, Dm, BF16, None, 0, 0, None) == UNSUP
+    assert b"one row exceeds" in lib.cam_last_error()
