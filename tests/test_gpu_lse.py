@@ -143,6 +143,45 @@ def test_mla_combine_full_size_poisoned(cam, orc):
     print(f"MLA combine worst row rel err {worst:.3e}, lse err {err:.3e}", flush=True)
 
 
+def test_pack_and_combine_beyond_4gib(cam, orc):
+    """The MLA shape at T = 4096: the packed exchange buffer and the partials
+    each exceed 2^32 bytes, so chunk, row and byte offsets pass 32 bits.  The
+    whole O-region is compared bit for bit and every LSE with the oracle's;
+    every combined row against the oracle's combine of its own packed buffer."""
+    P, T, H, Dv = 8, 4096, 128, 512
+    announce("pack and combine with buffers over 4 GiB")
+    o, m, s, _ = synth.dcp_partials(P, T, H, Dv, seed=synth.BASE_SEED + 7, device="cuda")
+    packed = cam.lse_pack(o, m, s, 1)
+    out, lse = cam.lse_combine_packed(packed, P, T, H, Dv, 1)
+    torch.cuda.synchronize()
+    assert packed.numel() > 2**32 and o.numel() * 2 >= 2**32
+    ob = to_host_bits(o)
+    del o
+    mh, sh = m.cpu().numpy(), s.cpu().numpy()
+    ref = orc.lse_pack(ob, mh, sh, 1)
+    got = to_host_bits(packed)
+    del packed
+    rows = orc.pack_rows(P, T, H, 1)
+    chunk = orc.pack_chunk_bytes(P, T, H, Dv, 1)
+    o_bytes = (rows * Dv * 2 + 15) // 16 * 16
+    rc, gc = ref.reshape(P, P, chunk), got.reshape(P, P, chunk)
+    for p in range(P):  # chunk by chunk, to keep the host temporaries small
+        for r in range(P):
+            assert np.array_equal(gc[p, r, :rows * Dv * 2], rc[p, r, :rows * Dv * 2]), f"O-region ({p}, {r})"
+            assert_lse_close(gc[p, r, o_bytes:o_bytes + 4 * rows].view(np.float32),
+                             rc[p, r, o_bytes:o_bytes + 4 * rows].view(np.float32), f"L-region ({p}, {r})")
+    del got, gc
+    out_ref, lse_ref = orc.lse_combine_packed(ref, P, T, H, Dv, 1)
+    outh, lseh = to_host_bits(out), lse.cpu().numpy()
+    worst = 0.0
+    for r in range(P):
+        sl = slice(r * rows, (r + 1) * rows)
+        worst = max(worst, assert_rows_close(orc.half_bits_to_double(outh[sl]), orc.half_bits_to_double(out_ref[sl]),
+                                             f"combine beyond 4 GiB, rank {r}"))
+    err = assert_lse_close(lseh, lse_ref, "combine beyond 4 GiB: lse_out")
+    print(f"beyond 4 GiB: worst row {worst:.3e}, lse err {err:.3e}", flush=True)
+
+
 def test_combine_all_invalid_rows_and_p1(cam, orc):
     announce("combine all-invalid rows and P=1 identity")
     T, H, D = 33, 4, 64
