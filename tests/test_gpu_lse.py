@@ -264,18 +264,20 @@ def test_combine_varlen_masked_partials_not_read(cam, orc):
     assert_lse_close(lse.cpu().numpy(), rl, "varlen lse")
 
 
-def test_thd_combine_full_size(cam, orc):
+@pytest.mark.parametrize("dt", ["bf16", "fp16"])
+def test_thd_combine_full_size(cam, orc, dt):
     """Packed THD at full size (131072 tokens, H = 32, D = 128, 8 KV-piece
-    partials, the launch the benchmark times): every row of the combined
-    output and every LSE against the oracle, computed over token windows on
-    the host's cores."""
+    partials; bf16 is the launch the benchmark times): every row of the
+    combined output and every LSE against the oracle, computed over token
+    windows on the host's cores."""
     P, H, D = 8, 32, 128
     lens = synth.thd_lengths(20, 131072, seed=synth.BASE_SEED + 4)
     cu = synth.cu_seqlens(lens)
     T = int(cu[-1])
-    announce("THD combine full size, every row")
-    g = synth._gen(synth.BASE_SEED + 77, "cuda")
-    po = torch.randn((P, T, H, D), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    announce(f"THD combine full size, every row, {dt}")
+    g = synth._gen((synth.BASE_SEED if dt == "bf16" else synth.FP16_SEED) + 77, "cuda")
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float16
+    po = torch.randn((P, T, H, D), generator=g, device="cuda", dtype=torch.float32).to(tdt)
     pl = torch.randn((P, T, H), generator=g, device="cuda", dtype=torch.float32).mul_(2.0)
     cu_d = torch.from_numpy(cu).cuda()
     out, lse = cam.lse_combine_varlen(po, pl, cu_d)
@@ -285,13 +287,13 @@ def test_thd_combine_full_size(cam, orc):
     del po
 
     def check(a, e):
-        ro, rl = orc.lse_combine(po_h[:, a:e], pl_h[:, a:e], cu=cu, t_begin=a)
-        w = assert_rows_close(orc.half_bits_to_double(out_h[a:e]).reshape(-1, D),
-                              orc.half_bits_to_double(ro).reshape(-1, D), f"THD rows [{a}, {e})")
+        ro, rl = orc.lse_combine(po_h[:, a:e], pl_h[:, a:e], dtype=dt, cu=cu, t_begin=a)
+        w = assert_rows_close(orc.half_bits_to_double(out_h[a:e], dt).reshape(-1, D),
+                              orc.half_bits_to_double(ro, dt).reshape(-1, D), f"THD rows [{a}, {e})")
         return w, assert_lse_close(lse_h[a:e], rl, f"THD lse [{a}, {e})")
 
     res = window_pool(T, check)
-    print(f"THD combine, all {T * H} rows: worst row {max(r[0] for r in res):.3e}, "
+    print(f"THD combine ({dt}), all {T * H} rows: worst row {max(r[0] for r in res):.3e}, "
           f"lse err {max(r[1] for r in res):.3e}", flush=True)
 
 

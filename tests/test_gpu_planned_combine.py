@@ -130,6 +130,46 @@ def test_planned_thd_combine_full_size(cam, orc):
           f"lse err {max(r[1] for r in res):.3e}", flush=True)
 
 
+def test_planned_thd_backward_full_size(cam, orc):
+    """The gradient of the combine over the 8-rank plan of the full THD batch:
+    every row of both gradients against the oracle's planned gradient."""
+    P, H, D = 8, 32, 128
+    lens = synth.thd_lengths(20, 131072, seed=synth.BASE_SEED + 4, align=64)
+    cu = synth.cu_seqlens(lens)
+    T = int(cu[-1])
+    announce("planned THD combine backward full size, every row")
+    q, first, plan = _plan(cam, orc, cu, P, block_size=64, min_split_tokens=8192)
+    g = synth._gen(synth.BASE_SEED + 92, "cuda")
+    po = torch.randn((P, T, H, D), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    pl = torch.randn((P, T, H), generator=g, device="cuda", dtype=torch.float32).mul_(2.0)
+    go = torch.randn((T, H, D), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    gl = torch.randn((T, H), generator=g, device="cuda", dtype=torch.float32)
+    d_po, d_pl = cam.lse_combine_backward(po, pl, go, gl, plan=plan)
+    torch.cuda.synchronize()
+    po_h, pl_h, go_h, gl_h = to_host_bits(po), pl.cpu().numpy(), to_host_bits(go), gl.cpu().numpy()
+    dpo_h, dpl_h = to_host_bits(d_po), d_pl.cpu().numpy()
+    del po, d_po
+
+    def check(a, e):
+        ro, rl = orc.lse_combine_planned_backward(po_h[:, a:e], pl_h[:, a:e], go_h[a:e], gl_h[a:e], cu, first,
+                                                  t_begin=a)
+        n = (e - a) * H
+        got_o = orc.half_bits_to_double(np.ascontiguousarray(dpo_h[:, a:e])).reshape(P, n, D)
+        want_o = orc.half_bits_to_double(ro).reshape(P, n, D)
+        w = assert_rows_close(got_o.reshape(-1, D), want_o.reshape(-1, D), f"planned d_part_out [{a}, {e})")
+        assert np.all(got_o[want_o == 0] == 0), f"planned d_part_out [{a}, {e}) not exactly zero outside the valid set"
+        scale = grad_lse_scale(orc.half_bits_to_double(np.ascontiguousarray(po_h[:, a:e])).reshape(P, n, D),
+                               orc.half_bits_to_double(go_h[a:e]).reshape(n, D),
+                               gl_h[a:e].reshape(-1).astype(np.float64))
+        le = assert_grad_lse_close(np.ascontiguousarray(dpl_h[:, a:e]).reshape(P, -1), rl.reshape(P, -1), scale,
+                                   f"planned d_part_lse [{a}, {e})")
+        return w, le
+
+    res = window_pool(T, check, n_windows=128)
+    print(f"planned THD backward, all {T * H} rows: worst d_part_out row {max(r[0] for r in res):.3e}, "
+          f"worst d_part_lse / scale {max(r[1] for r in res):.3e}", flush=True)
+
+
 def test_planned_combine_autograd(cam, orc):
     from context_attention_movement_amd import autograd as ag
     W, H, D = 3, 2, 64
