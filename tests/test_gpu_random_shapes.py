@@ -2,8 +2,10 @@
 widths and rank counts the hand-picked cases do not: dense relayouts (both
 directions, every element, bf16/fp16/fp32 bits), varlen relayouts over
 ragged batches with empty sequences, the generic strided combine with
-invalid partials, the causal varlen combine, and one merge.  Each case is
-printed before it runs."""
+invalid partials, the causal varlen combine, merges, the pack and the
+combine over the exchange, the combine over random THD plans, and the
+combine's gradient under each admission rule.  Each case is printed before
+it runs."""
 
 import numpy as np
 import pytest
@@ -204,3 +206,74 @@ def test_random_planned_combine(cam, orc, case):
     assert_rows_close(orc.half_bits_to_double(to_host_bits(out)).reshape(-1, D),
                       orc.half_bits_to_double(ro).reshape(-1, D), "planned combine")
     assert_lse_close(lse.cpu().numpy(), rl, "planned combine lse")
+
+
+@pytest.mark.parametrize("case", range(16))
+def test_random_backward(cam, orc, case):
+    """The combine's gradient on seeded random shapes, under each admission
+    rule (every partial, the causal piece rule, a THD plan's rule): rank
+    counts up to 64, row lengths reaching every access width and both the
+    compacted and the wide-row forms, invalid and masked partials
+    NaN-poisoned (never read)."""
+    from helpers import assert_grad_lse_close, grad_lse_scale
+    rng = np.random.default_rng(11000 + case)
+    rule = ["all", "pieces", "plan"][case % 3]
+    dt = str(rng.choice(["bf16", "fp16"]))
+    H = int(rng.integers(1, 5))
+    D = int(rng.choice([2, 5, 8, 24, 64, 128, 200, 512]))
+    first = plan = cu = None
+    if rule == "plan":
+        P = int(rng.integers(1, 9))
+        b = int(rng.choice([1, 2, 4]))
+        blocks = [int(v) for v in rng.integers(0, 20, size=int(rng.integers(1, 6)))]
+        while sum(blocks) < P:
+            blocks[int(rng.integers(0, len(blocks)))] += 1
+        cu = synth.cu_seqlens([x * b for x in blocks])
+        T = int(cu[-1])
+        q = orc.thd_plan(cu, P, block_size=b, min_split_tokens=8 * b)
+        plan = cam.ThdPlan(P, T, cu, q["span_start"], q["span_rank"], q["span_local"], q["rank_off"],
+                           q["rank_cost"], q["grid"]).to("cuda")
+        first = orc.plan_first_positions(cu, q, P)
+        mask = orc.plan_mask(cu, first, P)
+    else:
+        P = int(rng.choice([1, 2, 3, 8, 16, 33, 64]))
+        T = int(rng.integers(1, 30))
+        if rule == "pieces":
+            cuts = np.sort(rng.choice(np.arange(1, T), size=min(3, T - 1), replace=False)) if T > 1 else []
+            cu = np.concatenate([[0], cuts, [T]]).astype(np.int32)
+            mask = orc.causal_mask(cu, P)
+        else:
+            mask = np.ones((P, T), dtype=bool)
+    announce(f"random backward #{case}: rule={rule} P={P} T={T} H={H} D={D} {dt}")
+    nan_bits = 0x7FC0 if dt == "bf16" else 0x7E00
+    o = synth.bits(synth.normal((P, T, H, D), seed=11100 + case, dtype=dt)).copy()
+    l = synth.partial_lse((P, T, H), seed=11200 + case).numpy().copy()
+    bad = rng.random((P, T, H)) < 0.1
+    l[bad] = rng.choice([-np.inf, np.inf, np.nan], size=int(bad.sum()))
+    o[~mask] = nan_bits
+    l[~mask] = np.nan
+    o[~np.isfinite(l)] = nan_bits
+    g = synth.bits(synth.normal((T, H, D), seed=11300 + case, dtype=dt))
+    gl = synth.normal((T, H), seed=11400 + case, dtype="fp32").numpy() if case % 2 else None
+    if rule == "plan":
+        ro, rl = orc.lse_combine_planned_backward(o, l, g, gl, cu, first, dtype=dt)
+    else:
+        ro, rl = orc.lse_combine_backward(o, l, g, gl, dtype=dt, cu=cu)
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float16
+    args = (from_host_bits(o, tdt), torch.from_numpy(l).cuda(), from_host_bits(g, tdt),
+            None if gl is None else torch.from_numpy(gl).cuda())
+    if rule == "plan":
+        d_po, d_pl = cam.lse_combine_backward(*args, plan=plan)
+    elif rule == "pieces":
+        d_po, d_pl = cam.lse_combine_backward(*args, cu_seqlens=torch.from_numpy(cu).cuda())
+    else:
+        d_po, d_pl = cam.lse_combine_backward(*args)
+    torch.cuda.synchronize()
+    got_o = orc.half_bits_to_double(to_host_bits(d_po), dt).reshape(P, T * H, D)
+    want_o = orc.half_bits_to_double(ro, dt).reshape(P, T * H, D)
+    assert_rows_close(got_o.reshape(-1, D), want_o.reshape(-1, D), "random backward d_part_out")
+    assert np.all(got_o[want_o == 0] == 0), "d_part_out not exactly zero outside the valid set"
+    scale = grad_lse_scale(np.where(np.isfinite(l)[..., None], orc.half_bits_to_double(o, dt), 0.0).reshape(P, T * H, D),
+                           orc.half_bits_to_double(g, dt).reshape(T * H, D),
+                           None if gl is None else gl.reshape(-1).astype(np.float64))
+    assert_grad_lse_close(d_pl.cpu().numpy().reshape(P, -1), rl.reshape(P, -1), scale, "random backward d_part_lse")
