@@ -184,6 +184,8 @@ class Workload:
         self.v_do = torch.empty((P, 1, S, H // P, D), dtype=bf, device=dev)
         P, T, H, D = self.tP, self.tT, self.tH, self.tD
         self.t_dpart = torch.empty((P, T, H, D), dtype=bf, device=dev)
+        # the same gradient into the library's partial-stack layout (partials 1 MiB apart)
+        self.t_dpart_gap = cam.empty_partials(P, T, H, D, dtype=bf, device=dev)
         self.t_dlse = torch.empty((P, T, H), dtype=torch.float32, device=dev)
         self.t_gout = randn((T, H, D))
         self.step_index = 0
@@ -318,6 +320,10 @@ class Workload:
             cam.lse_combine_backward(self.t_part, self.t_lse, self.t_gout, None, cu_seqlens=self.t_cu_dev,
                                      d_part_out=self.t_dpart, d_part_lse=self.t_dlse)
 
+        def thd_backward_gap():
+            cam.lse_combine_backward(self.t_part, self.t_lse, self.t_gout, None, cu_seqlens=self.t_cu_dev,
+                                     d_part_out=self.t_dpart_gap, d_part_lse=self.t_dlse)
+
         # admitted partials: O row and LSE read; every row: upstream gradient
         # read; every partial: its two gradients written
         bwd_bytes = self.t_admitted * H * (2 * D + 4) + rows * 2 * D + P * rows * (2 * D + 4)
@@ -349,6 +355,7 @@ class Workload:
             ("relayout_seq_to_head_planned_thd_qkv", 2 * 3 * T * H * D * 2, planned_s2h),
             ("relayout_head_to_seq_planned_thd_o", 2 * T * H * D * 2, planned_h2s),
             ("lse_combine_varlen_backward_thd", bwd_bytes, thd_backward),
+            ("lse_combine_varlen_backward_thd (gradient into empty_partials)", bwd_bytes, thd_backward_gap),
             ("relayout_training_pair_video_p4 (fwd + bwd)", pair_bytes, training_pair),
             ("ring_of_8_online_merges_thd (fp32 accumulator)", ring_bytes, ring),
             ("combine_to_sequence_shards_mla (fused)", comb_bytes, fused),

@@ -413,3 +413,19 @@ def test_rows_beyond_32bit_vector_counts_rejected(lib):
     Dm = 1 << 33                                  # 2^33 fp32 accumulator elements: 2^31 four-element vectors
     assert m(A, Dm, Dm, A + G, 1, 1, A + 2 * G, Dm, Dm, A + 3 * G, 1, 1, 1, 1, Dm, BF16, None, 0, 0, None) == UNSUP
     assert b"one row exceeds" in lib.cam_last_error()
+
+
+def test_empty_partials_layout(cam):
+    # the partial-stack layout: each partial contiguous, a 1 MiB gap after
+    # each one from 64 MiB per partial on, none below (meta tensors: no memory)
+    import torch
+    x = cam.empty_partials(8, 131072, 32, 128, device="meta")
+    assert tuple(x.shape) == (8, 131072, 32, 128)
+    assert x.stride() == (131072 * 32 * 128 + (1 << 19), 32 * 128, 128, 1)   # 2^19 bf16 elements = 1 MiB
+    assert x[0].is_contiguous() and not x.is_contiguous()
+    y = cam.empty_partials(8, 8191, 32, 128, device="meta")                  # just under 64 MiB per partial
+    assert y.is_contiguous()
+    z = cam.empty_partials(4, 8192, 32, 128, dtype=torch.float16, device="meta")
+    assert z.stride(0) == 8192 * 32 * 128 + (1 << 19)
+    f = cam.empty_partials(2, 1 << 20, 8, 4, dtype=torch.float32, device="meta")  # 128 MiB fp32 partials
+    assert f.stride(0) == (1 << 20) * 32 + (1 << 18)

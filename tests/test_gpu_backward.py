@@ -176,6 +176,31 @@ def test_thd_backward_full_size(cam, orc):
           f"worst d_part_lse / scale {max(r[1] for r in res):.3e}", flush=True)
 
 
+def test_backward_into_empty_partials(cam, orc):
+    """The gradient written into the library's partial-stack layout (64 MiB
+    partials, so 1 MiB gaps): every row against the oracle, and the gaps
+    between the partials untouched."""
+    P, H, D = 8, 32, 128
+    lens = synth.thd_lengths(6, 8192, seed=synth.BASE_SEED + 5, lo=64, hi=1024)
+    cu = synth.cu_seqlens(lens)
+    T = int(cu[-1])
+    announce(f"combine backward into empty_partials, T={T}")
+    g = synth._gen(synth.BASE_SEED + 79, "cuda")
+    po = torch.randn((P, T, H, D), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    pl = torch.randn((P, T, H), generator=g, device="cuda", dtype=torch.float32).mul_(2.0)
+    go = torch.randn((T, H, D), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    d_po = cam.empty_partials(P, T, H, D)
+    n = T * H * D
+    gap = d_po.stride(0) - n
+    assert gap == (1 << 19)
+    base = torch.full((P * d_po.stride(0),), 7.0, dtype=torch.bfloat16, device="cuda")
+    d_po = base.as_strided((P, T, H, D), d_po.stride())
+    _, d_pl = cam.lse_combine_backward(po, pl, go, None, cu_seqlens=torch.from_numpy(cu).cuda(), d_part_out=d_po)
+    torch.cuda.synchronize()
+    assert torch.all(base.view(P, n + gap)[:, n:] == 7.0), "wrote into the gaps between the partials"
+    _check_backward(orc, po, pl, go, None, d_po, d_pl, cu=cu, tag="into empty_partials")
+
+
 # -- autograd -------------------------------------------------------------------
 
 def test_relayout_training_pair_gradients_exact(cam, orc):
