@@ -59,6 +59,7 @@ CASES = [  # (P, T, H, D, dtype)
     (1, 13, 3, 16, "bf16"),      # P = 1: dO = g, dL = g_lse
     (16, 6, 4, 64, "bf16"),
     (64, 3, 2, 32, "bf16"),      # the largest P
+    (64, 3, 2, 512, "bf16"),     # the largest P with 1 KB rows (the wide-row form)
 ]
 
 

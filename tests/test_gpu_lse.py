@@ -222,7 +222,7 @@ def test_combine_all_invalid_rows_and_p1(cam, orc):
 @pytest.mark.parametrize("P,T,H,D,dt", [(2, 100, 3, 8, "bf16"), (5, 64, 4, 128, "bf16"), (8, 37, 2, 24, "fp16"),
                                         (16, 20, 4, 64, "bf16"), (64, 9, 2, 16, "bf16"), (3, 50, 2, 5, "bf16"),
                                         (3, 21, 2, 300, "bf16"), (2, 10, 3, 1000, "fp16"), (8, 13, 5, 512, "bf16"),
-                                        (33, 7, 3, 256, "bf16")])
+                                        (33, 7, 3, 256, "bf16"), (64, 5, 3, 512, "bf16"), (64, 6, 2, 1024, "fp16")])
 def test_combine_generic_strided(cam, orc, P, T, H, D, dt):
     announce(f"combine strided P={P} T={T} H={H} D={D} {dt}")
     o = synth.normal((P, H, T, D), seed=P * 100 + D, dtype=dt)          # stored [P][H][T][D]
