@@ -125,22 +125,10 @@ CAUGHT_BY = {"c1_flipped": ["thd_plan_c1_bottom.json", "thd_plan_c1_top.json"],
 
 @pytest.mark.parametrize("mutant", sorted(MUTANTS))
 def test_golden_plans_catch_planted_rebalancing_mistakes(orc, tmp_path, mutant):
-    import importlib.util
-    import shutil
-    import subprocess
+    from oracle_mutant import build_oracle_mutant
 
-    src = (Path(orc.__file__).parent / "cam_oracle.c").read_text()
     old, new = MUTANTS[mutant]
-    assert src.count(old) == 1, "the planted mistake must replace exactly one statement"
-    d = tmp_path / "oracle"
-    d.mkdir()
-    (d / "cam_oracle.c").write_text(src.replace(old, new))
-    shutil.copy(Path(orc.__file__), d / "__init__.py")
-    subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off", "-o", str(d / "liboracle.so"),
-                    str(d / "cam_oracle.c"), "-lm"], check=True)
-    spec = importlib.util.spec_from_file_location("oracle_mutant_" + mutant, d / "__init__.py")
-    mod = importlib.util.module_from_spec(spec)
-    spec.loader.exec_module(mod)
+    mod = build_oracle_mutant(orc, tmp_path, old, new, mutant)
     for name in GOLDEN_PLANS:
         e, p = _golden_plan(mod, name)
         if name in CAUGHT_BY[mutant]:
