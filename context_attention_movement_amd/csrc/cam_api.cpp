@@ -42,6 +42,9 @@ void note_launch(uint64_t workgroups, uint32_t threads, uint64_t lds_bytes)
 namespace {
 
 constexpr int64_t kI64Max = INT64_MAX;
+// Element strides beyond 2^48 address no real buffer; bounding them keeps every
+// byte-stride and offset product of the launch records inside 64 bits.
+constexpr int64_t kMaxStride = int64_t(1) << 48;
 
 bool mul_ok(int64_t a, int64_t b, int64_t* out)
 {
@@ -125,6 +128,8 @@ bool extent(std::initializer_list<int64_t> dims, std::initializer_list<int64_t> 
         last += term;
         ++s;
     }
+    if (last == kI64Max)
+        return false;
     return mul_ok(last + 1, esize, out);
 }
 
@@ -235,7 +240,7 @@ cam_status ablation_seq_to_head_lds(const void* in, void* out, int64_t P, int64_
     if (overlaps(in, bytes, out, bytes))
         return set_error(CAM_ERR_OVERLAP, "%s: in and out overlap", op);
     const uint64_t c = run / 16;
-    if (R < 1 || uint64_t(R) * uint64_t(P) * c > 4096)
+    if (R < 1 || R > 4096 || P > 4096 || B > int64_t(UINT32_MAX) || uint64_t(R) * uint64_t(P) * c > 4096)
         return set_error(CAM_ERR_UNSUPPORTED, "%s: rows_per_tile * H * D * esize must be within 64 KiB of LDS", op);
     DenseLds a{};
     a.src = in;
@@ -371,12 +376,13 @@ cam_status pack_geometry(const char* op, int64_t P, int64_t T, int64_t H, int64_
     if (scatter_dim == 0 && T % P)
         return set_error(CAM_ERR_DIVISIBILITY, "%s: scatter_dim 0 needs T %% P == 0 (T=%lld P=%lld)", op,
                          (long long)T, (long long)P);
-    int64_t rows, obytes, chunk, total;
+    int64_t rows, obytes, lbytes, chunk, total;
     if (!prod_ok({scatter_dim == 1 ? T : T / P, scatter_dim == 1 ? H / P : H}, &rows) ||
-        !prod_ok({rows, Dv, 2}, &obytes) || obytes > kI64Max / 2)
+        !prod_ok({rows, Dv, 2}, &obytes) || obytes > kI64Max / 4 || !prod_ok({rows, 4}, &lbytes) ||
+        lbytes > kI64Max / 4)
         return set_error(CAM_ERR_SHAPE, "%s: sizes overflow", op);
     obytes = (obytes + 15) / 16 * 16;
-    chunk = obytes + (rows * 4 + 15) / 16 * 16;
+    chunk = obytes + (lbytes + 15) / 16 * 16;  // each term below 2^61: no overflow
     if (!prod_ok({P, P, chunk}, &total))
         return set_error(CAM_ERR_SHAPE, "%s: packed size overflows", op);
     g->rows = rows;
@@ -415,8 +421,8 @@ cam_status combine(const char* op, const CombineIn& c, void* stream)
     if (c.dt != CAM_BF16 && c.dt != CAM_FP16)
         return set_error(CAM_ERR_UNSUPPORTED, "%s: payload dtype must be bf16 or fp16", op);
     for (int64_t s : {c.po_sp, c.po_st, c.po_sh, c.pl_sp, c.pl_st, c.pl_sh, c.o_st, c.o_sh, c.lo_st, c.lo_sh})
-        if (s < 0)
-            return set_error(CAM_ERR_UNSUPPORTED, "%s: strides must be non-negative", op);
+        if (s < 0 || s > kMaxStride)
+            return set_error(CAM_ERR_UNSUPPORTED, "%s: strides must be non-negative and below 2^48", op);
     int64_t n_rows;
     if (!prod_ok({c.T, c.H}, &n_rows))
         return set_error(CAM_ERR_SHAPE, "%s: T*H overflows", op);
@@ -547,8 +553,8 @@ cam_status combine_backward(const char* op, const CombineBwdIn& c, void* stream)
         return set_error(CAM_ERR_UNSUPPORTED, "%s: payload dtype must be bf16 or fp16", op);
     for (int64_t s : {c.po_sp, c.po_st, c.po_sh, c.pl_sp, c.pl_st, c.pl_sh, c.go_st, c.go_sh, c.gl_st, c.gl_sh,
                       c.dpo_sp, c.dpo_st, c.dpo_sh, c.dpl_sp, c.dpl_st, c.dpl_sh})
-        if (s < 0)
-            return set_error(CAM_ERR_UNSUPPORTED, "%s: strides must be non-negative", op);
+        if (s < 0 || s > kMaxStride)
+            return set_error(CAM_ERR_UNSUPPORTED, "%s: strides must be non-negative and below 2^48", op);
     int64_t n_rows;
     if (!prod_ok({c.T, c.H}, &n_rows))
         return set_error(CAM_ERR_SHAPE, "%s: T*H overflows", op);
@@ -803,8 +809,8 @@ cam_status lse_pack(const void* out, int64_t o_sp, int64_t o_st, int64_t o_sh, c
     if (st != CAM_OK)
         return st;
     for (int64_t s : {o_sp, o_st, o_sh, m_sp, m_st, m_sh, s_sp, s_st, s_sh})
-        if (s < 0)
-            return set_error(CAM_ERR_UNSUPPORTED, "%s: strides must be non-negative", op);
+        if (s < 0 || s > kMaxStride)
+            return set_error(CAM_ERR_UNSUPPORTED, "%s: strides must be non-negative and below 2^48", op);
     if (g.total == 0 || g.rows == 0)
         return CAM_OK;
     if (!out || !smax || !ssum || !packed)
@@ -1069,14 +1075,18 @@ cam_status lse_combine_varlen_seq(const void* part_out, int64_t po_sp, int64_t p
         return set_error(CAM_ERR_NULL, "%s: cu_seqlens, rank_cu and rank_off must be non-null", op);
     if ((rank_cu && !aligned(rank_cu, 4)) || (rank_off && !aligned(rank_off, 8)))
         return set_error(CAM_ERR_ALIGNMENT, "%s: misaligned plan array", op);
+    int64_t hd = 0;
     if (P > 0 && nseq >= 0 && T > 0 && D >= 0 && H >= 0) {
-        const int64_t ob = T * H * D * 2, lb = lse_out ? T * H * 4 : 0;
-        if (overlaps(out, ob, rank_cu, 4 * P * (nseq + 1)) || overlaps(out, ob, rank_off, 8 * (P + 1)) ||
-            overlaps(lse_out, lb, rank_cu, 4 * P * (nseq + 1)) || overlaps(lse_out, lb, rank_off, 8 * (P + 1)))
+        int64_t ob, lb = 0, rcb, rob;
+        if (!prod_ok({T, H, D, 2}, &ob) || (lse_out && !prod_ok({T, H, 4}, &lb)) || nseq == kI64Max ||
+            !prod_ok({P, nseq + 1, 4}, &rcb) || P == kI64Max || !prod_ok({P + 1, 8}, &rob) || !prod_ok({H, D}, &hd))
+            return set_error(CAM_ERR_SHAPE, "%s: sizes overflow", op);
+        if (overlaps(out, ob, rank_cu, rcb) || overlaps(out, ob, rank_off, rob) || overlaps(lse_out, lb, rank_cu, rcb) ||
+            overlaps(lse_out, lb, rank_off, rob))
             return set_error(CAM_ERR_OVERLAP, "%s: an output overlaps the plan arrays", op);
     }
     CombineIn c{part_out, po_sp, po_st, po_sh, part_lse, pl_sp, pl_st, pl_sh, P, T, H, D, dt,
-                out, H * D, D, lse_out, H, 1, cu_seqlens, nseq};
+                out, hd, D, lse_out, H, 1, cu_seqlens, nseq};
     c.out_mode = 2;
     c.rank_cu = rank_cu;
     c.rank_off = rank_off;
@@ -1095,8 +1105,8 @@ cam_status lse_merge(float* acc_out, int64_t a_st, int64_t a_sh, float* acc_lse,
     if (dt != CAM_BF16 && dt != CAM_FP16)
         return set_error(CAM_ERR_UNSUPPORTED, "%s: payload dtype must be bf16 or fp16", op);
     for (int64_t s : {a_st, a_sh, al_st, al_sh, p_st, p_sh, pl_st, pl_sh, f_st, f_sh})
-        if (s < 0)
-            return set_error(CAM_ERR_UNSUPPORTED, "%s: strides must be non-negative", op);
+        if (s < 0 || s > kMaxStride)
+            return set_error(CAM_ERR_UNSUPPORTED, "%s: strides must be non-negative and below 2^48", op);
     int64_t n_rows;
     if (!prod_ok({T, H}, &n_rows))
         return set_error(CAM_ERR_SHAPE, "%s: T*H overflows", op);

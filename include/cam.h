@@ -48,7 +48,12 @@ extern "C" {
 typedef enum cam_dtype {
     CAM_BF16 = 0, /* bfloat16 payload */
     CAM_FP16 = 1, /* IEEE binary16 payload */
-    CAM_FP32 = 2  /* 4-byte words (relayouts only; used for index payloads) */
+    CAM_FP32 = 2, /* 4-byte words (relayouts only; used for index payloads) */
+    /* Not dtypes: they widen the enumeration to every 32-bit code a caller
+     * can pass, so that an unknown code is a well-defined value that the
+     * validation rejects (CAM_ERR_UNSUPPORTED). */
+    CAM_DTYPE_RANGE_MIN_ = INT32_MIN,
+    CAM_DTYPE_RANGE_MAX_ = INT32_MAX
 } cam_dtype;
 
 typedef enum cam_status {
