@@ -479,8 +479,8 @@ cam_status qkv_projection_head_sharded(const void* x, const void* w, void* out, 
  *   as one contiguous run (the "LDS-staged transpose" of the head/sequence
  *   swap).  ulysses_seq_to_head does not call it.  16-byte accesses only: (H/P)*D*esize and both pointers must be
  *   multiples of 16 bytes (CAM_ERR_ALIGNMENT); rows_per_tile >= 1 with
- *   rows_per_tile*H*D*esize <= 64 KiB (CAM_ERR_UNSUPPORTED).  Other errors as
- *   ulysses_seq_to_head.
+ *   rows_per_tile*H*D*esize <= 64 KiB, and B below 2^32 (CAM_ERR_UNSUPPORTED).
+ *   Other errors as ulysses_seq_to_head.
  */
 cam_status cam_ablation_seq_to_head_lds(const void* in, void* out, int64_t P, int64_t B, int64_t S,
                                         int64_t H, int64_t D, cam_dtype dt, int64_t rows_per_tile,
