@@ -53,3 +53,12 @@ def test_ab_verdict_rule():
     assert bench.ab_verdict(null, mixed)["verdict"] == "neutral"     # a pair disagrees
     slower = [(100.0, 104.0), (100.0, 103.0), (100.0, 105.0)]
     assert bench.ab_verdict(null, slower)["verdict"] == "B slower"
+
+
+def test_kernel_source_hash_covers_every_library_source():
+    """Every source compiled into libcam.so takes part in the hash that keys
+    the stored hardware counters, so a change to any of them retires them."""
+    import bench
+    from context_attention_movement_amd import build as cam_build
+    headers = {p.name for p in cam_build.CSRC.glob("*.h")}
+    assert set(cam_build.SOURCES) | headers <= set(bench.KERNEL_SOURCES)
