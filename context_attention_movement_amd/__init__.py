@@ -763,8 +763,6 @@ def lse_merge(acc_out: torch.Tensor, acc_lse: torch.Tensor, part_out: torch.Tens
     """In place: (acc_out fp32 [T][H][D], acc_lse fp32 [T][H]) <- stable combine of
     the accumulator and one partial (part_out [T][H][D] bf16/fp16, part_lse
     [T][H]); optionally also writes the rounded result to out_final."""
-    for t_, n in ((acc_out, "acc_out"), (acc_lse, "acc_lse"), (part_out, "part_out"), (part_lse, "part_lse")):
-        _dev(t_, n)
     if acc_out.dtype != torch.float32 or acc_lse.dtype != torch.float32 or part_lse.dtype != torch.float32:
         raise TypeError("accumulator and LSEs must be float32")
     if acc_out.dim() != 3 or part_out.dim() != 3 or acc_out.stride(2) != 1 or part_out.stride(2) != 1:
@@ -774,10 +772,12 @@ def lse_merge(acc_out: torch.Tensor, acc_lse: torch.Tensor, part_out: torch.Tens
         raise ValueError("shape mismatch")
     fs = (0, 0)
     if out_final is not None:
-        _dev(out_final, "out_final")
-        if out_final.dim() != 3 or out_final.stride(2) != 1 or out_final.dtype != part_out.dtype:
-            raise ValueError("out_final must be [T][H][D] like part_out")
+        _check_buffer(out_final, "out_final", (T, H, D), part_out.dtype, contiguous=False, inner_contiguous=True)
         fs = out_final.stride()[:2]
+    for t_, n in ((acc_out, "acc_out"), (acc_lse, "acc_lse"), (part_out, "part_out"), (part_lse, "part_lse")):
+        _dev(t_, n)
+    if out_final is not None:
+        _dev(out_final, "out_final")
     _check(library().lse_merge(acc_out.data_ptr(), *acc_out.stride()[:2], acc_lse.data_ptr(), *acc_lse.stride(),
                                part_out.data_ptr(), *part_out.stride()[:2], part_lse.data_ptr(), *part_lse.stride(),
                                T, H, D, _dt(part_out), _ptr(out_final), *fs, _stream(part_out)))

@@ -376,6 +376,30 @@ def test_binding_rejects_wrong_varlen_seq_outputs(cam):
         cam.lse_combine_varlen_seq(po, pl[:, :-1], plan)
 
 
+def test_binding_rejects_wrong_merge_outputs(cam):
+    """A caller's out_final must be exactly [T][H][D] of the payload dtype with
+    D contiguous: a short one would be written out of bounds."""
+    import torch
+    T, H, D = 5, 3, 8
+    acc = torch.zeros((T, H, D), dtype=torch.float32)
+    acc_l = torch.zeros((T, H), dtype=torch.float32)
+    po = torch.zeros((T, H, D), dtype=torch.bfloat16)
+    pl = torch.zeros((T, H), dtype=torch.float32)
+    with pytest.raises(ValueError, match="out_final must have shape"):
+        cam.lse_merge(acc, acc_l, po, pl, out_final=torch.zeros((T - 1, H, D), dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="out_final must have shape"):
+        cam.lse_merge(acc, acc_l, po, pl, out_final=torch.zeros((T, H, D + 1), dtype=torch.bfloat16))
+    with pytest.raises(TypeError, match="out_final must be torch.bfloat16"):
+        cam.lse_merge(acc, acc_l, po, pl, out_final=torch.zeros((T, H, D), dtype=torch.float16))
+    with pytest.raises(ValueError, match="last dimension contiguous"):
+        cam.lse_merge(acc, acc_l, po, pl, out_final=torch.zeros((T, H, 2 * D), dtype=torch.bfloat16)[:, :, ::2])
+    with pytest.raises(ValueError, match="shape mismatch"):
+        cam.lse_merge(acc, acc_l[:-1], po, pl)
+    # shapes right: the device check comes next
+    with pytest.raises(ValueError, match="must be a device tensor"):
+        cam.lse_merge(acc, acc_l, po, pl, out_final=torch.zeros((T, H, D), dtype=torch.bfloat16))
+
+
 def test_binding_rejects_plan_tables_on_another_device(cam):
     # a plan whose tables sit on the host must not reach a kernel that runs
     # on the device (its host addresses would be read as device memory);
