@@ -108,7 +108,6 @@ class _LseCombine(torch.autograd.Function):
             out, lse = _lse_combine_varlen(part_out, part_lse, cu_seqlens)
         ctx.save_for_backward(part_out, part_lse, cu_seqlens)
         ctx.plan = plan
-        ctx.mark_non_differentiable(*(() if cu_seqlens is None else (cu_seqlens,)))
         return out, lse
 
     @staticmethod
