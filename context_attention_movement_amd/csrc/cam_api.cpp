@@ -74,8 +74,9 @@ int elem_size(cam_dtype dt)
         return 2;
     case CAM_FP32:
         return 4;
+    default:  // any other code the enum's range admits
+        return 0;
     }
-    return 0;
 }
 
 const char* dt_name(cam_dtype dt)
@@ -84,8 +85,8 @@ const char* dt_name(cam_dtype dt)
     case CAM_BF16: return "bf16";
     case CAM_FP16: return "fp16";
     case CAM_FP32: return "fp32";
+    default: return "unknown";
     }
-    return "unknown";
 }
 
 bool aligned(const void* p, int64_t n) { return (reinterpret_cast<uintptr_t>(p) % uint64_t(n)) == 0; }

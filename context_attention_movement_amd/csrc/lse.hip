@@ -334,7 +334,6 @@ __global__ __launch_bounds__(kThreads) CAM_COMBINE_OCC void k_combine(Combine a)
             cu_lds[i] = a.cu[i];
 
     const uint32_t lane = threadIdx.x & 63u;
-    const uint32_t wave = threadIdx.x >> 6;
     // phase-1 geometry: GP lanes per row
     const uint32_t GP = 1u << a.gp_log2;
     const uint32_t sp = lane & (GP - 1u);
@@ -679,7 +678,6 @@ __device__ __forceinline__ float row_stat(const Combine& a, uint64_t row, uint32
 template <int W, bool FP16, int CZ, int OM>
 __global__ __launch_bounds__(kThreads) void k_combine_stream(Combine a)
 {
-    typedef typename VecOf<W>::type V;
     constexpr int E = W / 2;
     constexpr int CH = kCombineBatchWave;
     constexpr bool NTL = (CAM_NT_COMBINE & 1) != 0, NTS = (CAM_NT_COMBINE & 2) != 0;
