@@ -155,10 +155,16 @@ class Workload:
         self.t_comb_seq = torch.empty((T, H, D), dtype=bf, device=dev)
         self.t_comb_seq_lse = torch.empty((T, H), dtype=torch.float32, device=dev)
         Pm, Tm, Hm, Dvm = self.mP, self.mT, self.mH, self.mDv
-        for ms in self.m_sets:
+        for i, ms in enumerate(self.m_sets):
             ms["comb_seq"] = torch.empty((Tm, Hm, Dvm), dtype=bf, device=dev)
             ms["lse_seq"] = torch.empty((Tm, Hm), dtype=torch.float32, device=dev)
             ms["comb_h2s"] = torch.empty((Pm, 1, Tm // Pm, Hm, Dvm), dtype=bf, device=dev)
+            # the combine's gradient at this shape (rows of 1 KB): the partials
+            # above, their LSEs and an upstream gradient
+            ms["bwd_lse"] = synth.partial_lse((Pm, Tm, Hm), seed=synth.BASE_SEED + 6 + 1000 * i, device=dev)
+            ms["bwd_g"] = synth.normal((Tm, Hm, Dvm), seed=synth.BASE_SEED + 7 + 1000 * i, device=dev)
+            ms["bwd_dpo"] = torch.empty((Pm, Tm, Hm, Dvm), dtype=bf, device=dev)
+            ms["bwd_dpl"] = torch.empty((Pm, Tm, Hm), dtype=torch.float32, device=dev)
         # THD layout plan over 8 ranks of the same 131072 tokens in 64-token
         # blocks (the planned relayout reuses the THD Q/K/V and O buffers)
         self.p_lens = synth.thd_lengths(20, 131072, seed=synth.BASE_SEED + 4, align=64)
@@ -200,7 +206,7 @@ class Workload:
                 "thd_partials": self.t_part, "thd_partial_lse": self.t_lse, "thd_grad_out": self.t_gout,
                 "proj_x": self.j_x, "proj_w": self.j_w}
         for i, ms in enumerate(self.m_sets):
-            for key in ("out", "max", "sum"):
+            for key in ("out", "max", "sum", "bwd_lse", "bwd_g"):
                 bufs[f"mla_{key}_set{i}"] = ms[key]
         for i, (vo, _) in enumerate(self.v_o_sets[1:], start=1):
             bufs[f"video_o_set{i}"] = vo
@@ -268,7 +274,8 @@ class Workload:
 
     def extension_ops(self, k=0):
         """Operations beyond the step: the video relayouts at P = 8, the
-        planned THD operations, the gradient of the THD combine, the
+        planned THD operations, the gradient of the combine (THD, and at the
+        MLA shape), the
         relayout training pair (forward and backward), the ring of online
         merges, the combine epilogues that write the sequence-sharded layout
         directly and the unfused sequence they replace.
@@ -285,6 +292,15 @@ class Workload:
         def unfused():
             cam.lse_combine_packed(ms["packed_in"], Pm, Tm, Hm, Dvm, 1, out=ms["comb"], lse_out=ms["lse"])
             cam.ulysses_head_to_seq(ms["comb"].view(Pm, 1, Tm, Hm // Pm, Dvm), Pm, out=ms["comb_h2s"])
+
+        def mla_backward():
+            cam.lse_combine_backward(ms["out"], ms["bwd_lse"], ms["bwd_g"], None, d_part_out=ms["bwd_dpo"],
+                                     d_part_lse=ms["bwd_dpl"])
+
+        # every partial valid: each partial's row and LSE read, the upstream
+        # gradient row read, each partial's two gradients written
+        m_rows = Tm * Hm
+        mla_bwd_bytes = 2 * Pm * m_rows * (2 * Dvm + 4) + m_rows * 2 * Dvm
 
         def thd_fused():
             cam.lse_combine_varlen_seq(self.t_part, self.t_lse, self.t_plan, out=self.t_comb_seq,
@@ -356,6 +372,7 @@ class Workload:
             ("relayout_head_to_seq_planned_thd_o", 2 * T * H * D * 2, planned_h2s),
             ("lse_combine_varlen_backward_thd", bwd_bytes, thd_backward),
             ("lse_combine_varlen_backward_thd (gradient into empty_partials)", bwd_bytes, thd_backward_gap),
+            ("lse_combine_backward_mla (rows of 1 KB)", mla_bwd_bytes, mla_backward),
             ("relayout_training_pair_video_p4 (fwd + bwd)", pair_bytes, training_pair),
             ("ring_of_8_online_merges_thd (fp32 accumulator)", ring_bytes, ring),
             ("combine_to_sequence_shards_mla (fused)", comb_bytes, fused),

@@ -663,8 +663,8 @@ __device__ __forceinline__ void stream_rows(const char* prow, int64_t sp_b, uint
     }
 }
 
-template <int CZ>
-__device__ __forceinline__ float row_stat(const Combine& a, uint64_t row, uint32_t lane)
+template <int CZ, typename Rec>
+__device__ __forceinline__ float row_stat(const Rec& a, uint64_t row, uint32_t lane)
 {
     if (row >= a.n_rows || lane >= a.P)
         return -__builtin_inff();
@@ -1199,6 +1199,110 @@ __global__ __launch_bounds__(kThreads) void k_combine_bwd(CombineBwd a)
     }
 }
 
+// Gradient for rows of at least 64 vectors, without LDS or barriers (the
+// forward's row-stream layout): one wave per row.  The row's P statistics sit
+// in lanes 0..P-1 and give the forward's normalised weights; the upstream
+// gradient g is read once; each valid partial's <g, O_p> is formed per lane
+// with the packed dot instruction and summed across the wave into lane p;
+// every partial's dO_p = w_p g is written (exact zero outside the valid set);
+// lane p then writes dL_p = w_p (<g, O_p> - sum_q w_q <g, O_q> + g_lse).
+template <int N, int W, bool FP16, bool NTL>
+__device__ __forceinline__ void stream_dots(const char* prow, int64_t sp_b, uint32_t kbyte, bool kin, uint64_t& m,
+                                            typename VecOf<W>::type gv, uint32_t lane, float& dsum)
+{
+    typedef typename VecOf<W>::type V;
+    int idx[N];
+#pragma unroll
+    for (int u = 0; u < N; ++u) {
+        idx[u] = __builtin_ctzll(m);
+        m &= m - 1;
+    }
+    V x[N];
+#pragma unroll
+    for (int u = 0; u < N; ++u)
+        x[u] = ld_at<W, NTL>(prow + kbyte + int64_t(idx[u]) * sp_b);
+    issue_fence();
+#pragma unroll
+    for (int u = 0; u < N; ++u) {
+        const float d = wave_sum(kin ? payload_dot<W, FP16>(gv, x[u], 0.0f) : 0.0f);  // a clamped tail lane adds 0
+        dsum += lane == uint32_t(idx[u]) ? d : 0.0f;
+    }
+}
+
+template <int W, bool FP16, int CZ>
+__global__ __launch_bounds__(kThreads) void k_combine_bwd_stream(CombineBwd a)
+{
+    typedef typename VecOf<W>::type V;
+    constexpr int E = W / 2;
+    constexpr int CH = kCombineBatchWave;
+    constexpr bool NTL = (CAM_NT_COMBINE_BWD & 1) != 0, NTS = (CAM_NT_COMBINE_BWD & 2) != 0;
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t wpb = blockDim.x >> 6;
+    const uint64_t blk = CAM_XCD_COMBINE_BWD_STREAM ? xcd_first(blockIdx.x, gridDim.x) : blockIdx.x;
+    const uint64_t n_waves = uint64_t(gridDim.x) * wpb;
+    uint64_t row = blk * wpb + uniform32(threadIdx.x >> 6);
+    float L_next = row_stat<CZ>(a, row, lane);
+    for (; row < a.n_rows; row += n_waves) {
+        const float L = L_next;
+        L_next = row_stat<CZ>(a, row + n_waves, lane);  // in flight during this row
+        const uint32_t t = fdiv(uint32_t(row), a.div_H);
+        const uint32_t h = uint32_t(row) - t * a.H;
+        const bool valid = __builtin_isfinite(L);
+        const float M = wave_max(valid ? L : -__builtin_inff());
+        const float w = valid ? expf(L - M) : 0.0f;
+        const float Z = wave_sum(w);
+        const uint64_t vmask = __ballot(valid);
+        const float wn = w * (vmask ? 1.0f / Z : 0.0f);
+        const uint32_t n = uint32_t(__builtin_popcountll(vmask));
+        const float glv = a.gl ? a.gl[int64_t(t) * a.gl_st + int64_t(h) * a.gl_sh] : 0.0f;
+        const char* prow = static_cast<const char*>(a.po) + int64_t(t) * a.po_st_b + int64_t(h) * a.po_sh_b;
+        const char* grow = static_cast<const char*>(a.go) + int64_t(t) * a.go_st_b + int64_t(h) * a.go_sh_b;
+        char* drow = static_cast<char*>(a.dpo) + int64_t(t) * a.dpo_st_b + int64_t(h) * a.dpo_sh_b;
+        float dsum = 0.0f;  // lane p: <g, O_p>
+        for (uint32_t kb = 0; kb < a.cv; kb += 64) {
+            const bool kin = kb + lane < a.cv;
+            const uint32_t kbyte = (kin ? kb + lane : a.cv - 1) * uint32_t(W);
+            // the upstream gradient is read only where some partial is valid
+            const V gv = n ? ld_at<W, NTL>(grow + kbyte) : V{};
+            uint64_t m = vmask;  // wave-uniform: the valid partials not yet taken
+            for (uint32_t k0 = 0; k0 < n; k0 += CH) {
+                const uint32_t cnt = n - k0 < uint32_t(CH) ? n - k0 : uint32_t(CH);
+                switch (cnt) {
+                case 8: if constexpr (CH >= 8) stream_dots<8, W, FP16, NTL>(prow, a.po_sp_b, kbyte, kin, m, gv, lane, dsum); break;
+                case 7: if constexpr (CH >= 7) stream_dots<7, W, FP16, NTL>(prow, a.po_sp_b, kbyte, kin, m, gv, lane, dsum); break;
+                case 6: if constexpr (CH >= 6) stream_dots<6, W, FP16, NTL>(prow, a.po_sp_b, kbyte, kin, m, gv, lane, dsum); break;
+                case 5: if constexpr (CH >= 5) stream_dots<5, W, FP16, NTL>(prow, a.po_sp_b, kbyte, kin, m, gv, lane, dsum); break;
+                case 4: if constexpr (CH >= 4) stream_dots<4, W, FP16, NTL>(prow, a.po_sp_b, kbyte, kin, m, gv, lane, dsum); break;
+                case 3: if constexpr (CH >= 3) stream_dots<3, W, FP16, NTL>(prow, a.po_sp_b, kbyte, kin, m, gv, lane, dsum); break;
+                case 2: if constexpr (CH >= 2) stream_dots<2, W, FP16, NTL>(prow, a.po_sp_b, kbyte, kin, m, gv, lane, dsum); break;
+                default: stream_dots<1, W, FP16, NTL>(prow, a.po_sp_b, kbyte, kin, m, gv, lane, dsum); break;
+                }
+            }
+            // dO_p = w_p g for every partial (exact zero outside the valid set)
+            float gf[E];
+            const Halves<W> gh = __builtin_bit_cast(Halves<W>, gv);
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                gf[e] = half_to_f32<FP16>(gh.h[e]);
+            for (uint32_t p = 0; p < a.P; ++p) {
+                const float wp = __uint_as_float(uint32_t(__builtin_amdgcn_readlane(int(__float_as_uint(wn)), int(p))));
+                const bool vp = ((vmask >> p) & 1ull) != 0;
+                float y[E];
+#pragma unroll
+                for (int e = 0; e < E; ++e)
+                    y[e] = wp * gf[e];
+                const V out = vp ? round_payload<W, FP16>(y) : V{};
+                if (kin)
+                    st_at<W, NTS>(drow + kbyte + int64_t(p) * a.dpo_sp_b, out);
+            }
+        }
+        const float sw = wave_sum(wn * dsum);  // sum_q w_q <g, O_q>
+        if (lane < a.P)
+            a.dpl[int64_t(lane) * a.dpl_sp + int64_t(t) * a.dpl_st + int64_t(h) * a.dpl_sh] =
+                valid ? wn * (dsum - sw + glv) : 0.0f;
+    }
+}
+
 template <typename K>
 const void* fn_ptr(K* k)
 {
@@ -1220,10 +1324,29 @@ const void* pick_combine_bwd(int cz)
                            : fn_ptr(&k_combine_bwd<W, FP16, kAll, COMPACT>);
 }
 
+template <int W, bool FP16>
+const void* pick_combine_bwd_stream(int cz)
+{
+    return cz == kPlan ? fn_ptr(&k_combine_bwd_stream<W, FP16, kPlan>)
+           : cz == kPieces ? fn_ptr(&k_combine_bwd_stream<W, FP16, kPieces>)
+                           : fn_ptr(&k_combine_bwd_stream<W, FP16, kAll>);
+}
+
 cam_status launch_combine_bwd(const CombineBwd& a, void* stream)
 {
     const int cz = causal_rule(a);
     const void* fn = nullptr;
+    if (CAM_COMBINE_BWD_STREAM && !a.compact && a.g_log2 == 6) {
+        // rows of a whole wave or more: one wave per row, no LDS
+#define CAM_PICK_BWD_STREAM(Wd)                                                                          \
+    if (a.width == Wd)                                                                                   \
+        fn = a.fp16 ? pick_combine_bwd_stream<Wd, true>(cz) : pick_combine_bwd_stream<Wd, false>(cz);
+        CAM_PICK_BWD_STREAM(16) CAM_PICK_BWD_STREAM(8) CAM_PICK_BWD_STREAM(4) CAM_PICK_BWD_STREAM(2)
+#undef CAM_PICK_BWD_STREAM
+        const uint32_t wpb = CAM_COMBINE_STREAM_THREADS / 64;
+        return launch(fn, a, (a.n_rows + wpb - 1) / wpb, stream, "lse_combine_backward", 0,
+                      CAM_COMBINE_STREAM_THREADS);
+    }
 #define CAM_PICK_BWD(Wd)                                                                                \
     if (a.width == Wd)                                                                                  \
         fn = a.compact ? (a.fp16 ? pick_combine_bwd<Wd, true, true>(cz) : pick_combine_bwd<Wd, false, true>(cz)) \

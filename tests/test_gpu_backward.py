@@ -60,6 +60,12 @@ CASES = [  # (P, T, H, D, dtype)
     (16, 6, 4, 64, "bf16"),
     (64, 3, 2, 32, "bf16"),      # the largest P
     (64, 3, 2, 512, "bf16"),     # the largest P with 1 KB rows (the wide-row form)
+    # rows of a wave or more (the row-stream form): a ragged second pass, two
+    # full passes, 8-byte accesses, a rank count that is not a power of two
+    (8, 9, 3, 520, "bf16"),      # 1040-byte rows: 65 vectors
+    (4, 6, 2, 1024, "fp16"),     # 2 KB rows
+    (8, 5, 3, 516, "bf16"),      # 1032-byte rows: 8-byte accesses, 129 vectors
+    (33, 4, 2, 512, "fp16"),
 ]
 
 
@@ -93,10 +99,12 @@ def test_combine_backward(cam, orc, case, with_g_lse):
         assert torch.equal(d_po[0].cpu()[valid], go[valid])
 
 
-def test_combine_backward_strided(cam, orc):
-    """LSE [P][H][T] and partials inside a wider buffer; gradients into strided views."""
-    P, T, H, D = 4, 21, 6, 64
-    announce("combine backward strided")
+@pytest.mark.parametrize("D", [64, 512])
+def test_combine_backward_strided(cam, orc, D):
+    """LSE [P][H][T] and partials inside a wider buffer; gradients into strided
+    views (rows under a wave and rows of a whole wave)."""
+    P, T, H = 4, 21, 6
+    announce(f"combine backward strided D={D}")
     po = synth.normal((P, T, H, D + 32), seed=61).cuda()[..., 16:16 + D]
     pl = synth.partial_lse((P, H, T), seed=62).cuda().transpose(1, 2)
     go = synth.normal((T, H, D), seed=63).cuda()
@@ -111,15 +119,17 @@ def test_combine_backward_strided(cam, orc):
     _check_backward(orc, po, pl, go, gl, d_po, d_pl, tag="strided")
 
 
+@pytest.mark.parametrize("D", [128, 520])
 @pytest.mark.parametrize("P", [2, 4, 8])
-def test_varlen_backward_masked_not_read(cam, orc, P):
+def test_varlen_backward_masked_not_read(cam, orc, P, D):
     """Ragged lengths with zero-length and shorter-than-P sequences: masked
-    partials get exact zero gradients and their rows are never read."""
-    H, D = 4, 128
+    partials get exact zero gradients and their rows are never read (rows
+    under a wave, and rows of more than a wave)."""
+    H = 4
     lengths = [0, 1, 3, P - 1, 37, 5, 0, 64, 2 * P + 1, 11]
     cu = synth.cu_seqlens(lengths)
     T = int(cu[-1])
-    announce(f"varlen backward P={P} T={T}")
+    announce(f"varlen backward P={P} T={T} D={D}")
     po = synth.normal((P, T, H, D), seed=70 + P)
     pl = synth.partial_lse((P, T, H), seed=71 + P)
     mask = orc.causal_mask(cu, P)
@@ -133,7 +143,31 @@ def test_varlen_backward_masked_not_read(cam, orc, P):
     cu_d = torch.from_numpy(cu).cuda()
     d_po, d_pl = cam.lse_combine_backward(po.cuda(), pl.cuda(), go.cuda(), gl.cuda(), cu_seqlens=cu_d)
     torch.cuda.synchronize()
-    _check_backward(orc, po, pl, go, gl, d_po, d_pl, cu=cu, tag=f"varlen P={P}")
+    _check_backward(orc, po, pl, go, gl, d_po, d_pl, cu=cu, tag=f"varlen P={P} D={D}")
+
+
+def test_mla_shape_backward_full_size(cam, orc):
+    """The combine's gradient at the MLA decode shape (P = 8, T = 128, H = 128,
+    Dv = 512: rows of 1 KB, the row-stream form), with invalid statistics, an
+    upstream LSE gradient and the gradient written into a gapped partial
+    stack; every row against the oracle."""
+    P, T, H, D = 8, 128, 128, 512
+    announce("MLA-shape combine backward, every row")
+    po = synth.normal((P, T, H, D), seed=synth.BASE_SEED + 81)
+    pl = synth.partial_lse((P, T, H), seed=synth.BASE_SEED + 82)
+    rng = np.random.default_rng(synth.BASE_SEED + 83)
+    bad = rng.random((P, T, H)) < 0.01
+    pl[torch.from_numpy(bad)] = float("-inf")
+    po[torch.from_numpy(bad)] = float("nan")
+    go = synth.normal((T, H, D), seed=synth.BASE_SEED + 84)
+    gl = synth.normal((T, H), seed=synth.BASE_SEED + 85, dtype="fp32")
+    buf = torch.full((P * (T * H * D + 4096),), 7.0, dtype=torch.bfloat16, device="cuda")
+    d_po = buf.as_strided((P, T, H, D), (T * H * D + 4096, H * D, D, 1))
+    d_po, d_pl = cam.lse_combine_backward(po.cuda(), pl.cuda(), go.cuda(), gl.cuda(), d_part_out=d_po)
+    torch.cuda.synchronize()
+    gaps = buf.view(P, T * H * D + 4096)[:, T * H * D:]
+    assert torch.all(gaps == 7.0), "wrote into the gaps between partials"
+    _check_backward(orc, po, pl, go, gl, d_po, d_pl, tag="MLA shape")
 
 
 def test_thd_backward_full_size(cam, orc):
