@@ -338,13 +338,16 @@ constexpr int kVarlenTileVecs = kThreads * kVarlenVecs;
 #define CAM_NT_COPY 3
 #endif
 // gradient rows of >= 64 vectors by the LDS-free row-stream kernel (1) or the
-// tiled kernel with shuffle-reduced dot products (0), and the stream kernel's
-// tile order (1 XCD-aware)
+// tiled kernel with shuffle-reduced dot products (0); the stream kernel's tile
+// order (1 XCD-aware) and non-temporal policy (bit 0 loads, bit 1 stores)
 #ifndef CAM_COMBINE_BWD_STREAM
 #define CAM_COMBINE_BWD_STREAM 1
 #endif
 #ifndef CAM_XCD_COMBINE_BWD_STREAM
 #define CAM_XCD_COMBINE_BWD_STREAM 1
+#endif
+#ifndef CAM_NT_COMBINE_BWD_STREAM
+#define CAM_NT_COMBINE_BWD_STREAM 3
 #endif
 #ifndef CAM_NT_COMBINE_BWD
 #define CAM_NT_COMBINE_BWD 2

@@ -1235,7 +1235,7 @@ __global__ __launch_bounds__(kThreads) void k_combine_bwd_stream(CombineBwd a)
     typedef typename VecOf<W>::type V;
     constexpr int E = W / 2;
     constexpr int CH = kCombineBatchWave;
-    constexpr bool NTL = (CAM_NT_COMBINE_BWD & 1) != 0, NTS = (CAM_NT_COMBINE_BWD & 2) != 0;
+    constexpr bool NTL = (CAM_NT_COMBINE_BWD_STREAM & 1) != 0, NTS = (CAM_NT_COMBINE_BWD_STREAM & 2) != 0;
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t wpb = blockDim.x >> 6;
     const uint64_t blk = CAM_XCD_COMBINE_BWD_STREAM ? xcd_first(blockIdx.x, gridDim.x) : blockIdx.x;
