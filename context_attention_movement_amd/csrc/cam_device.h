@@ -70,6 +70,48 @@ __device__ __forceinline__ int32_t seq_of_token(const int32_t* cu, int32_t nseq,
     return lo;
 }
 
+// The same search done by a whole wave for one token (every lane passes the
+// same t, all 64 lanes active): each step the lanes probe 64 evenly spaced
+// entries of the bracket and a ballot keeps the last one at or before t, so a
+// table in global memory costs ceil(log64 n) dependent loads, not log2 n.
+__device__ __forceinline__ int32_t wave_seq_of_token(const int32_t* cu, int32_t nseq, uint32_t t)
+{
+    const int64_t lane = int64_t(threadIdx.x & 63u);
+    int64_t lo = 0, hi = nseq;
+    while (hi - lo > 1) {
+        const int64_t step = (hi - lo + 63) >> 6;
+        const int64_t i = lo + lane * step;
+        const bool le = i < hi && int64_t(cu[i]) <= int64_t(t);
+        const uint64_t m = __ballot(le);
+        if (!m)  // cu[lo] > t: a malformed table; stay in range
+            break;
+        lo += int64_t(63 - __builtin_clzll(m)) * step;
+        hi = hi < lo + step ? hi : lo + step;
+    }
+    return int32_t(lo);
+}
+
+// The search for a token known to lie in sequence b or later (cu[b] <= t):
+// gallop forward from b, then bisect -- one load when t is in sequence b,
+// which is the common case for the consecutive tokens of a tile.
+__device__ __forceinline__ int32_t seq_of_token_from(const int32_t* cu, int32_t nseq, int32_t b, uint32_t t)
+{
+    int64_t lo = b, span = 1;
+    while (lo + span < nseq && int64_t(cu[lo + span]) <= int64_t(t)) {
+        lo += span;
+        span <<= 1;
+    }
+    int64_t hi = lo + span < nseq ? lo + span : nseq;
+    while (hi - lo > 1) {
+        const int64_t mid = (lo + hi) >> 1;
+        if (int64_t(cu[mid]) <= int64_t(t))
+            lo = mid;
+        else
+            hi = mid;
+    }
+    return int32_t(lo);
+}
+
 
 // Keep a batch of independent loads together: no instruction is scheduled
 // across this point, so every load above it is issued before anything below

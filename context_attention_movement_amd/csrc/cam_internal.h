@@ -282,7 +282,7 @@ void note_launch(uint64_t workgroups, uint32_t threads, uint64_t lds_bytes);
 void clear_error();
 
 // cu_seqlens entries staged in LDS by the varlen kernels (larger tables are
-// searched in global memory).
+// searched in global memory, 64 entries per step by a whole wave).
 constexpr int32_t kCuCache = 1024;
 
 // Launch shape shared by all streaming kernels.

@@ -141,12 +141,12 @@ __device__ __forceinline__ uint16_t f32_to_half(float f)
     return uint16_t(f32_to_bf16_bits(f));
 }
 
-// Causal admission of KV piece p for the token t of a packed THD batch: the
-// piece must be non-empty and start at or before t's position in its sequence.
-__device__ __forceinline__ bool causal_piece_ok(const int32_t* cu, int32_t nseq, const FastDiv& divP,
-                                                uint32_t p, uint32_t t)
+// Causal admission of KV piece p for the token t of a packed THD batch (i:
+// t's sequence): the piece must be non-empty and start at or before t's
+// position in its sequence.
+__device__ __forceinline__ bool causal_piece_ok(const int32_t* cu, int32_t i, const FastDiv& divP, uint32_t p,
+                                                uint32_t t)
 {
-    const int32_t i = seq_of_token(cu, nseq, t);
     const int64_t c0 = cu[i];
     const int64_t L = int64_t(cu[i + 1]) - c0;
     const int64_t k = int64_t(t) - c0;
@@ -161,10 +161,9 @@ __device__ __forceinline__ bool causal_piece_ok(const int32_t* cu, int32_t nseq,
 // admitted for the token at position k of sequence i iff rank p holds a
 // position of sequence i at or before k, first[p][i] <= k (INT32_MAX when it
 // holds none of the sequence).
-__device__ __forceinline__ bool causal_span_ok(const int32_t* cu, int32_t nseq, const int32_t* first, uint32_t p,
-                                               uint32_t t)
+__device__ __forceinline__ bool causal_span_ok(const int32_t* cu, int32_t nseq, const int32_t* first, int32_t i,
+                                               uint32_t p, uint32_t t)
 {
-    const int32_t i = seq_of_token(cu, nseq, t);
     const int64_t c0 = cu[i];
     const int64_t k = int64_t(t) - c0;
     if (k < 0 || k >= int64_t(cu[i + 1]) - c0)
@@ -178,18 +177,32 @@ __device__ __forceinline__ bool causal_span_ok(const int32_t* cu, int32_t nseq, 
 enum Causal : int { kAll = 0, kPieces = 1, kPlan = 2 };
 
 template <int CZ, typename Rec>
-__device__ __forceinline__ bool admitted_partial(const Rec& a, const int32_t* cu, uint32_t p, uint32_t t)
+__device__ __forceinline__ bool admitted_partial(const Rec& a, const int32_t* cu, int32_t i, uint32_t p, uint32_t t)
 {
     if (CZ == kPlan)
-        return causal_span_ok(cu, a.nseq, a.first, p, t);
-    return causal_piece_ok(cu, a.nseq, a.div_P, p, t);
+        return causal_span_ok(cu, a.nseq, a.first, i, p, t);
+    return causal_piece_ok(cu, i, a.div_P, p, t);
+}
+
+// The sequence of token t in a tile's phase 1, called by every lane of the
+// wave: from the LDS copy of cu_seqlens when it is staged there; otherwise the
+// wave first finds the sequence of its first row's token in global memory with
+// 64-wide probes (every other lane's token is at or after it) and each lane
+// gallops from there.  w_live: the wave's first row w_row exists.
+template <typename Rec>
+__device__ __forceinline__ int32_t tile_token_seq(const Rec& a, const int32_t* cu_lds, bool cached, bool w_live,
+                                                  uint64_t w_row, bool live, uint32_t t)
+{
+    if (cached)
+        return live ? seq_of_token(cu_lds, a.nseq, t) : 0;
+    const int32_t hint = w_live ? wave_seq_of_token(a.cu, a.nseq, fdiv(uint32_t(w_row), a.div_H)) : 0;
+    return live ? seq_of_token_from(a.cu, a.nseq, hint, t) : 0;
 }
 
 // Rank-major (sequence-sharded) row of token t of a packed THD batch: the
 // row of the varlen relayout's sequence side for B = 1.
-__device__ __forceinline__ int64_t varlen_token_row(const int32_t* cu, const Combine& a, uint32_t t)
+__device__ __forceinline__ int64_t varlen_token_row(const int32_t* cu, const Combine& a, int32_t i, uint32_t t)
 {
-    const int32_t i = seq_of_token(cu, a.nseq, t);
     const uint32_t c0 = uint32_t(cu[i]);
     const uint32_t L = uint32_t(cu[i + 1]) - c0;
     const uint32_t k = t - c0;
@@ -361,13 +374,19 @@ __global__ __launch_bounds__(kThreads) CAM_COMBINE_OCC void k_combine(Combine a)
                 t = fdiv(uint32_t(row), a.div_H);
                 h = uint32_t(row) - t * a.H;
             }
+            int32_t seq = 0;  // the token's sequence (the causal rules and output mode 2)
+            if (CZ != kAll) {
+                const uint32_t wl = (base + (threadIdx.x & ~63u)) >> a.gp_log2;  // the wave's first row
+                seq = tile_token_seq(a, cu_lds, cached, wl < RB && row0 + wl < a.n_rows, row0 + wl, live, t);
+            }
             bool valid = false;
             float L = -__builtin_inff();
             if (live && sp < a.P) {
                 bool admitted = true;
                 if (CZ != kAll)
                     // the two calls differ only in the address space of the table
-                    admitted = cached ? admitted_partial<CZ>(a, cu_lds, sp, t) : admitted_partial<CZ>(a, a.cu, sp, t);
+                    admitted = cached ? admitted_partial<CZ>(a, cu_lds, seq, sp, t)
+                                      : admitted_partial<CZ>(a, a.cu, seq, sp, t);
                 if (admitted) {
                     L = a.pl[int64_t(sp) * a.pl_sp + int64_t(t) * a.pl_st + int64_t(h) * a.pl_sh];
                     valid = __builtin_isfinite(L);
@@ -403,7 +422,8 @@ __global__ __launch_bounds__(kThreads) CAM_COMBINE_OCC void k_combine(Combine a)
                             const uint32_t tq = fdiv(h, a.div_Hp);
                             g = int64_t(tq) * a.Hq + int64_t(t) * a.Hp + (h - tq * a.Hp);
                         } else {
-                            g = (cached ? varlen_token_row(cu_lds, a, t) : varlen_token_row(a.cu, a, t)) * a.H + h;
+                            g = (cached ? varlen_token_row(cu_lds, a, seq, t) : varlen_token_row(a.cu, a, seq, t)) *
+                                    a.H + h;
                         }
                         // a plan that places the token outside [0, T) skips the row
                         const bool in = g >= 0 && uint64_t(g) < a.n_rows;
@@ -666,12 +686,17 @@ __device__ __forceinline__ void stream_rows(const char* prow, int64_t sp_b, uint
 template <int CZ, typename Rec>
 __device__ __forceinline__ float row_stat(const Rec& a, uint64_t row, uint32_t lane)
 {
-    if (row >= a.n_rows || lane >= a.P)
+    if (row >= a.n_rows)  // wave-uniform
         return -__builtin_inff();
     const uint32_t t = fdiv(uint32_t(row), a.div_H);
     const uint32_t h = uint32_t(row) - t * a.H;
-    if (CZ != kAll && !admitted_partial<CZ>(a, a.cu, lane, t))
+    if (CZ != kAll) {
+        const int32_t seq = wave_seq_of_token(a.cu, a.nseq, t);  // one token per wave: the wave searches
+        if (lane >= a.P || !admitted_partial<CZ>(a, a.cu, seq, lane, t))
+            return -__builtin_inff();
+    } else if (lane >= a.P) {
         return -__builtin_inff();
+    }
     return a.pl[int64_t(lane) * a.pl_sp + int64_t(t) * a.pl_st + int64_t(h) * a.pl_sh];
 }
 
@@ -708,7 +733,7 @@ __global__ __launch_bounds__(kThreads) void k_combine_stream(Combine a)
                 const uint32_t tq = fdiv(h, a.div_Hp);
                 g = int64_t(tq) * a.Hq + int64_t(t) * a.Hp + (h - tq * a.Hp);
             } else {
-                g = varlen_token_row(a.cu, a, t) * a.H + h;
+                g = varlen_token_row(a.cu, a, wave_seq_of_token(a.cu, a.nseq, t), t) * a.H + h;
             }
             const bool in = g >= 0 && uint64_t(g) < a.n_rows;
             o_off = in ? g * int64_t(a.o_row_b) : -1;
@@ -978,12 +1003,18 @@ __global__ __launch_bounds__(kThreads) void k_combine_bwd(CombineBwd a)
                 t = fdiv(uint32_t(row), a.div_H);
                 h = uint32_t(row) - t * a.H;
             }
+            int32_t seq = 0;  // the token's sequence (the causal rules)
+            if (CZ != kAll) {
+                const uint32_t wl = (base + (threadIdx.x & ~63u)) >> a.gp_log2;  // the wave's first row
+                seq = tile_token_seq(a, cu_lds, cached, wl < RB && row0 + wl < a.n_rows, row0 + wl, live, t);
+            }
             bool valid = false;
             float L = -__builtin_inff();
             if (live && sp < a.P) {
                 bool admitted = true;
                 if (CZ != kAll)
-                    admitted = cached ? admitted_partial<CZ>(a, cu_lds, sp, t) : admitted_partial<CZ>(a, a.cu, sp, t);
+                    admitted = cached ? admitted_partial<CZ>(a, cu_lds, seq, sp, t)
+                                      : admitted_partial<CZ>(a, a.cu, seq, sp, t);
                 if (admitted) {
                     L = a.pl[int64_t(sp) * a.pl_sp + int64_t(t) * a.pl_st + int64_t(h) * a.pl_sh];
                     valid = __builtin_isfinite(L);

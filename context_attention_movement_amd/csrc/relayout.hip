@@ -74,12 +74,12 @@ __global__ __launch_bounds__(kThreads) void k_dense_relayout(DenseRelayout a)
     }
 }
 
-// Sequence-side vector offset of token t's row for destination head block r
-// of plane b, or -1 if the plan does not place t inside the buffer.
-__device__ __forceinline__ int64_t varlen_seq_row(const VarlenRelayout& a, const int32_t* cu, uint32_t t,
+// Sequence-side vector offset of token t's row (i: t's sequence) for
+// destination head block r of plane b, or -1 if the plan does not place t
+// inside the buffer.
+__device__ __forceinline__ int64_t varlen_seq_row(const VarlenRelayout& a, const int32_t* cu, int32_t i, uint32_t t,
                                                   uint32_t r, uint32_t b)
 {
-    const int32_t i = seq_of_token(cu, a.nseq, t);
     const int64_t c0 = cu[i];
     const int64_t L = int64_t(cu[i + 1]) - c0;
     const int64_t k = int64_t(t) - c0;
@@ -98,11 +98,11 @@ __device__ __forceinline__ int64_t varlen_seq_row(const VarlenRelayout& a, const
     return row * int64_t(a.Pc) + int64_t(r) * a.c;
 }
 
-// The same for a THD layout plan: cu holds the spans' first tokens.
-__device__ __forceinline__ int64_t span_seq_row(const VarlenRelayout& a, const int32_t* cu, uint32_t t,
+// The same for a THD layout plan: cu holds the spans' first tokens (s: t's
+// span).
+__device__ __forceinline__ int64_t span_seq_row(const VarlenRelayout& a, const int32_t* cu, int32_t s, uint32_t t,
                                                 uint32_t r, uint32_t b)
 {
-    const int32_t s = seq_of_token(cu, a.nseq, t);
     const int64_t c0 = cu[s];
     const int64_t k = int64_t(t) - c0;
     if (k < 0 || k >= int64_t(cu[s + 1]) - c0)
@@ -122,10 +122,10 @@ __device__ __forceinline__ int64_t span_seq_row(const VarlenRelayout& a, const i
 }
 
 template <bool SPANS>
-__device__ __forceinline__ int64_t seq_row(const VarlenRelayout& a, const int32_t* cu, uint32_t t, uint32_t r,
-                                           uint32_t b)
+__device__ __forceinline__ int64_t seq_row(const VarlenRelayout& a, const int32_t* cu, int32_t i, uint32_t t,
+                                           uint32_t r, uint32_t b)
 {
-    return SPANS ? span_seq_row(a, cu, t, r, b) : varlen_seq_row(a, cu, t, r, b);
+    return SPANS ? span_seq_row(a, cu, i, t, r, b) : varlen_seq_row(a, cu, i, t, r, b);
 }
 
 template <int W, bool S2H, bool GUARD, int NTP>
@@ -186,13 +186,29 @@ __global__ __launch_bounds__(kThreads) void k_varlen_relayout(VarlenRelayout a)
         const uint32_t nrows = fdiv(ve - 1, a.div_c) - row0 + 1;
         __syncthreads();  // the previous tile's readers are done with row_off
         bool rows_ok = true;
-        for (uint32_t i = threadIdx.x; i < nrows; i += kThreads) {
-            // the two calls differ only in the address space of the table,
-            // so each compiles to plain LDS or global loads
-            const int64_t off = cached ? seq_row<SPANS>(a, cu_lds, row0 + i, r, b)
-                                       : seq_row<SPANS>(a, a.cu, row0 + i, r, b);
-            row_off[i] = off;
-            rows_ok = rows_ok && off >= 0;
+        for (uint32_t i0 = 0; i0 < nrows; i0 += kThreads) {
+            const uint32_t i = i0 + threadIdx.x;
+            const bool live = i < nrows;
+            const uint32_t t = row0 + i;
+            // the row's sequence: from the LDS table, or else the wave finds
+            // its first row's sequence in global memory with 64-wide probes
+            // and each lane gallops from there
+            int32_t sq;
+            if (cached) {
+                sq = live ? seq_of_token(cu_lds, a.nseq, t) : 0;
+            } else {
+                const uint32_t w0 = i0 + (threadIdx.x & ~63u);
+                const int32_t hint = w0 < nrows ? wave_seq_of_token(a.cu, a.nseq, row0 + w0) : 0;
+                sq = live ? seq_of_token_from(a.cu, a.nseq, hint, t) : 0;
+            }
+            if (live) {
+                // the two calls differ only in the address space of the table,
+                // so each compiles to plain LDS or global loads
+                const int64_t off = cached ? seq_row<SPANS>(a, cu_lds, sq, t, r, b)
+                                           : seq_row<SPANS>(a, a.cu, sq, t, r, b);
+                row_off[i] = off;
+                rows_ok = rows_ok && off >= 0;
+            }
         }
         // full tile whose every row the plan places inside the buffer: no guards
         const bool fast = __syncthreads_and(rows_ok && ve - vb == uint32_t(kVarlenTileVecs));

@@ -1,6 +1,6 @@
 """Packed batches with more sequences (or planned spans) than the kernels
 stage in LDS (1024 cu_seqlens entries): the tables are then searched in
-global memory.  Varlen relayout, causal combine (256-byte and 1 KB rows),
+global memory (64-wide by a wave, then a gallop per lane).  Varlen relayout, causal combine (256-byte and 1 KB rows),
 the combine written to sequence shards, the combine gradient and the
 planned relayout, each against the oracle."""
 
