@@ -507,6 +507,16 @@ cam_status combine(const char* op, const CombineIn& c, void* stream)
     const uint32_t groups = a.threads >> a.g_log2;
     if (rows < groups)
         rows = groups;
+    if (!wave) {
+        // many partials: the first phase gives every (row, partial) a lane, so
+        // a tile takes (rows * pow2(P)) / threads dependent rounds of LSE
+        // loads; widen the workgroup, then shorten the tile, to cap them
+        const auto rounds = [&] { return (uint64_t(rows) << a.gp_log2) / a.threads; };
+        while (rounds() > CAM_COMBINE_STATS_ROUNDS && a.threads < kThreads)
+            a.threads *= 2;
+        while (rounds() > CAM_COMBINE_STATS_ROUNDS && rows > 1)
+            rows /= 2;
+    }
     a.rows_per_tile = rows;
     a.n_tiles = (uint64_t(n_rows) + rows - 1) / rows;
     a.cu = c.cu;
@@ -643,8 +653,13 @@ cam_status combine_backward(const char* op, const CombineBwdIn& c, void* stream)
     // cross-lane shuffles
     {
         const uint32_t g = (kCombineBwdVpl == 2 && g_full > 0 && g_full < 6) ? g_full - 1 : g_full;
-        const uint32_t threads = std::min<uint32_t>(kThreads, std::max<uint32_t>(64u, rows0 << g));
-        const uint32_t rows = std::max(rows0, threads >> g);
+        uint32_t threads = std::min<uint32_t>(kThreads, std::max<uint32_t>(64u, rows0 << g));
+        uint32_t rows = std::max(rows0, threads >> g);
+        // many partials: cap the first phase's rounds as the forward does
+        while ((uint64_t(rows) << a.gp_log2) / threads > CAM_COMBINE_STATS_ROUNDS && threads < kThreads)
+            threads *= 2;
+        while ((uint64_t(rows) << a.gp_log2) / threads > CAM_COMBINE_STATS_ROUNDS && rows > 1)
+            rows /= 2;
         const uint64_t lds = uint64_t(rows) * a.P * (4 + 8 + 4 * (uint64_t(1) << g)) + uint64_t(rows) * (8 + 4 + 4) +
                              (c.cu && c.nseq < kCuCache ? uint64_t(c.nseq + 1) * 4 : 0) + 16;
         a.compact = g_full < 6 && lds <= 65536;

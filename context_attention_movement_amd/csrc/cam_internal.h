@@ -370,6 +370,11 @@ constexpr int kVarlenTileVecs = kThreads * kVarlenVecs;
 #define CAM_PROJ_VEC_OUT 1
 #endif
 // Combine gradient tiling: rows per tile for rows of >= 512 bytes and shorter.
+// rounds of the tiled combines' first phase (one lane per (row, partial)) a
+// tile may take: workgroups widen, then tiles shorten, for many partials
+#ifndef CAM_COMBINE_STATS_ROUNDS
+#define CAM_COMBINE_STATS_ROUNDS 4
+#endif
 #ifndef CAM_COMBINE_BWD_ROWS_WIDE
 #define CAM_COMBINE_BWD_ROWS_WIDE 8
 #endif
