@@ -146,6 +146,27 @@ def test_varlen_backward_masked_not_read(cam, orc, P, D):
     _check_backward(orc, po, pl, go, gl, d_po, d_pl, cu=cu, tag=f"varlen P={P} D={D}")
 
 
+def test_backward_many_short_rows(cam, orc):
+    """Rows of 16 bytes, more than 2^22 of them (6.3 million rows over 2
+    partials): invalid statistics and an upstream LSE gradient; every row of
+    both gradients against the oracle."""
+    P, T, H, D = 2, (1 << 21) + 37, 3, 8
+    announce(f"combine backward, {T * H} short rows")
+    po = synth.normal((P, T, H, D), seed=synth.BASE_SEED + 91)
+    pl = synth.partial_lse((P, T, H), seed=synth.BASE_SEED + 92)
+    rng = np.random.default_rng(synth.BASE_SEED + 93)
+    bad = torch.from_numpy(rng.random((P, T, H)) < 0.02)
+    pl[bad] = float("-inf")
+    po[bad] = float("nan")
+    go = synth.normal((T, H, D), seed=synth.BASE_SEED + 94)
+    gl = synth.normal((T, H), seed=synth.BASE_SEED + 95, dtype="fp32")
+    d_po = torch.full((P, T, H, D), 7.0, dtype=torch.bfloat16, device="cuda")
+    d_pl = torch.full((P, T, H), 7.0, dtype=torch.float32, device="cuda")
+    cam.lse_combine_backward(po.cuda(), pl.cuda(), go.cuda(), gl.cuda(), d_part_out=d_po, d_part_lse=d_pl)
+    torch.cuda.synchronize()
+    _check_backward(orc, po, pl, go, gl, d_po, d_pl, tag="many short rows")
+
+
 def test_mla_shape_backward_full_size(cam, orc):
     """The combine's gradient at the MLA decode shape (P = 8, T = 128, H = 128,
     Dv = 512: rows of 1 KB, the row-stream form), with invalid statistics, an
