@@ -516,11 +516,13 @@ def _cpu_work_items(w):
     return items
 
 
-def cpu_baseline(w, max_threads: int = 16):
+def cpu_baseline(w, max_threads: int = 16, keep: dict | None = None):
     """The oracle as it stands, timed on the host cores over the whole step's
     workload (every operation at full size): once on one core, then with the
     same independent calls spread over N threads (ctypes releases the GIL
-    during each oracle call).  The median of 3 runs is taken for each leg."""
+    during each oracle call).  The median of 3 runs is taken for each leg.
+    `keep`, if given, receives each call's result (label -> oracle output)
+    from the last threaded run: the parity reference of this run."""
     from concurrent.futures import ThreadPoolExecutor
 
     items = _cpu_work_items(w)
@@ -537,8 +539,11 @@ def cpu_baseline(w, max_threads: int = 16):
         t0 = time.perf_counter()
         # costliest first so that the pool's tail is short
         with ThreadPoolExecutor(max_workers=n_threads) as ex:
-            for f in [ex.submit(fn) for _, _, fn in sorted(items, key=lambda x: -x[1])]:
-                f.result()
+            futs = [(label, ex.submit(fn)) for label, _, fn in sorted(items, key=lambda x: -x[1])]
+            for label, f in futs:
+                r = f.result()
+                if keep is not None:
+                    keep[label] = r
         return time.perf_counter() - t0
 
     t1 = serial()
@@ -561,6 +566,104 @@ def cpu_baseline(w, max_threads: int = 16):
         "cpu": _cpu_model(),
         "affinity_cores": len(os.sched_getaffinity(0)),
     }
+
+
+OUT_ROW_RTOL = 8e-3   # combined payload: per row max|gpu - oracle| / max|oracle|
+LSE_ATOL = 1e-5       # fp32 LSE, absolute
+
+
+def _rows_rel(got_bits, want_bits, D, dt="bf16"):
+    """Worst per-row relative error max|g - o| / max|o| of two payload bit
+    arrays, in windows of rows; rows whose reference is all zero must be
+    exactly zero.  Returns (worst, bad_zero_rows, nan_count)."""
+    import numpy as np
+    import oracle
+
+    g = got_bits.reshape(-1, D)
+    o = want_bits.reshape(-1, D)
+    worst, bad, nan = 0.0, 0, 0
+    step = max(1, (1 << 23) // D)
+    for a in range(0, g.shape[0], step):
+        gd = oracle.half_bits_to_double(g[a:a + step], dt)
+        od = oracle.half_bits_to_double(o[a:a + step], dt)
+        nan += int(np.isnan(gd).sum())
+        num = np.max(np.abs(gd - od), axis=-1)
+        den = np.max(np.abs(od), axis=-1)
+        zero = den == 0
+        bad += int(np.count_nonzero(num[zero]))
+        if (~zero).any():
+            worst = max(worst, float(np.max(num[~zero] / den[~zero])))
+    return worst, bad, nan
+
+
+def _lse_diff(got, want):
+    """(max |got - want| over entries finite in the oracle, entries whose
+    finiteness differs, NaN count) of two fp32 LSE arrays."""
+    import numpy as np
+
+    got = np.asarray(got, dtype=np.float64).reshape(-1)
+    want = np.asarray(want, dtype=np.float64).reshape(-1)
+    fin = np.isfinite(want)
+    mism = int(np.count_nonzero(fin & ~np.isfinite(got))) + int(np.count_nonzero(~fin & (got != want)))
+    diff = float(np.max(np.abs(got[fin] - want[fin]))) if fin.any() else 0.0
+    return diff, mism, int(np.isnan(got).sum())
+
+
+def oracle_parity(w, ref):
+    """Every step operation run once more on the GPU (buffer set 0) and its
+    output compared, element by element at full size, with the oracle's
+    output for the same inputs (`ref`, from the cpu_baseline leg): bit-exact
+    for the relayouts and the packed payload; LSE within 1e-5; combined rows
+    within 8e-3 relative."""
+    import numpy as np
+    import oracle
+
+    torch = w.torch
+    for _, _, fn in w.ops(k=0):
+        fn()
+    torch.cuda.synchronize()
+
+    def bits(t):
+        return t.detach().contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
+
+    res = {}
+
+    def exact(label, gpu):
+        want = ref[label]
+        n = int(np.count_nonzero(bits(gpu).reshape(-1) != np.asarray(want).reshape(-1)))
+        res[label] = {"check": "bit-exact", "elements": int(np.asarray(want).size), "mismatches": n, "pass": n == 0}
+
+    exact("video P=4 QKV seq->head", w.v_qkv_out)
+    exact("video P=4 O head->seq", w.v_o_sets[0][1])
+    exact("THD QKV varlen seq->head", w.t_qkv_out)
+    exact("THD O varlen head->seq", w.t_o_out)
+    ms = w.m_sets[0]
+    P, T, H, Dv = w.mP, w.mT, w.mH, w.mDv
+    Og, Lg = oracle.packed_regions(ms["packed_out"].cpu().numpy(), P, T, H, Dv, 1)
+    Oo, Lo = oracle.packed_regions(np.asarray(ref["MLA pack"]), P, T, H, Dv, 1)
+    nO = int(np.count_nonzero(Og != Oo))
+    dL, mL, nanL = _lse_diff(Lg, Lo)
+    res["MLA pack"] = {"check": "O-region bit-exact, L-region within 1e-5 with the same -inf entries",
+                       "o_mismatches": nO, "lse_max_abs_diff": dL, "lse_nonfinite_mismatches": mL,
+                       "pass": nO == 0 and dL <= LSE_ATOL and mL == 0 and nanL == 0}
+
+    def combined(label, out, lse, D, want_out, want_lse):
+        rel, bad, nan = _rows_rel(bits(out), np.asarray(want_out), D)
+        dL, mL, nanL = _lse_diff(lse.cpu().numpy(), want_lse)
+        res[label] = {"check": "rows within 8e-3 relative, LSE within 1e-5", "rows": int(np.asarray(want_out).size // D),
+                      "worst_row_rel": rel, "lse_max_abs_diff": dL,
+                      "pass": rel <= OUT_ROW_RTOL and bad == 0 and nan == 0 and dL <= LSE_ATOL and mL == 0
+                      and nanL == 0}
+
+    mo, ml = ref["MLA combine"]
+    combined("MLA combine", ms["comb"], ms["lse"], Dv, mo, ml)
+    wins = sorted((k for k in ref if k.startswith("THD causal combine [")),
+                  key=lambda k: int(k.split("[")[1].split(",")[0]))
+    to = np.concatenate([np.asarray(ref[k][0]).reshape(-1) for k in wins])
+    tl = np.concatenate([np.asarray(ref[k][1]).reshape(-1) for k in wins])
+    combined("THD causal combine", w.t_comb, w.t_comb_lse, w.tD, to, tl)
+    return {"reference": "the oracle's outputs from the cpu_baseline leg, on the same inputs, every element",
+            "ops": res, "all_pass": all(r["pass"] for r in res.values())}
 
 
 def _cpu_model():
@@ -1049,7 +1152,10 @@ def main():
                   "operation alone, each block between two HIP events: the median block (us_per_call_p95: its "
                   "95th percentile); ops[*].in_step_*: HIP events around the operation inside the steps",
     }
-    result["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(w, args.cpu_threads)
+    ref = {}
+    result["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(w, args.cpu_threads, keep=ref)
+    result["parity"] = oracle_parity(w, ref) if ref else None
+    del ref
     # the gated figures and the per-operation table last, so that the end of
     # the line carries them
     result["gates"] = {n: {"us_per_call": op_table[n]["us_per_call"],
