@@ -19,6 +19,9 @@ than 15 GB of other traffic in between), so no input is served from the
 Prints ONE JSON line.  `value` is the step's algorithmic bytes (each input
 read once, each output written once, invalid or causally masked partials not
 read) divided by the step time.  Per-operation figures are under "ops".
+The CPU leg (skipped with --no-cpu-baseline) times the oracle over the same
+step ("cpu_baseline") and then compares every element of the GPU's outputs
+with the oracle's ("parity").
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
     python bench.py --summarize-rocprof TRACE FETCH WRITE BENCH_JSON --summary-out F --command TEXT
@@ -522,7 +525,8 @@ def cpu_baseline(w, max_threads: int = 16, keep: dict | None = None):
     same independent calls spread over N threads (ctypes releases the GIL
     during each oracle call).  The median of 3 runs is taken for each leg.
     `keep`, if given, receives each call's result (label -> oracle output)
-    from the last threaded run: the parity reference of this run."""
+    from the last threaded run: the parity reference of this run (see
+    cpu_leg)."""
     from concurrent.futures import ThreadPoolExecutor
 
     items = _cpu_work_items(w)
@@ -607,6 +611,15 @@ def _lse_diff(got, want):
     mism = int(np.count_nonzero(fin & ~np.isfinite(got))) + int(np.count_nonzero(~fin & (got != want)))
     diff = float(np.max(np.abs(got[fin] - want[fin]))) if fin.any() else 0.0
     return diff, mism, int(np.isnan(got).sum())
+
+
+def cpu_leg(w, max_threads: int = 16):
+    """The CPU leg of the benchmark: the oracle timed over the whole step
+    (cpu_baseline), then the GPU's outputs checked against the oracle's
+    outputs of those same calls (oracle_parity).  Returns (baseline, parity)."""
+    ref = {}
+    baseline = cpu_baseline(w, max_threads, keep=ref)
+    return baseline, oracle_parity(w, ref)
 
 
 def oracle_parity(w, ref):
@@ -1152,10 +1165,7 @@ def main():
                   "operation alone, each block between two HIP events: the median block (us_per_call_p95: its "
                   "95th percentile); ops[*].in_step_*: HIP events around the operation inside the steps",
     }
-    ref = {}
-    result["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(w, args.cpu_threads, keep=ref)
-    result["parity"] = oracle_parity(w, ref) if ref else None
-    del ref
+    result["cpu_baseline"], result["parity"] = (None, None) if args.no_cpu_baseline else cpu_leg(w, args.cpu_threads)
     # the gated figures and the per-operation table last, so that the end of
     # the line carries them
     result["gates"] = {n: {"us_per_call": op_table[n]["us_per_call"],
