@@ -151,9 +151,6 @@ uint32_t log2u(uint32_t x)
 }
 
 constexpr uint64_t kU32Limit = (uint64_t(1) << 31);  // vector-index headroom inside one slab
-// largest output (bytes) written through a buffer resource: its byte offsets
-// and the resource's record count are 32-bit
-constexpr uint64_t kBufStoreLimit = 0xFFFFFFFFull;
 
 uint32_t tiles(uint64_t vecs, uint64_t per_tile) { return uint32_t((vecs + per_tile - 1) / per_tile); }
 
@@ -213,7 +210,6 @@ cam_status dense_relayout(const void* in, void* out, int64_t P, int64_t B, int64
         return set_error(CAM_ERR_UNSUPPORTED, "%s: more than 2^32 tiles", op);
     a.n_tiles = uint32_t(n_tiles);
     a.seq_to_head = seq_to_head;
-    a.buf_st = CAM_BUF_STORE_DENSE && uint64_t(bytes) <= kBufStoreLimit;
     return launch_dense_relayout(a, stream);
 }
 
@@ -1246,7 +1242,7 @@ cam_status cam_copy(const void* src, void* dst, int64_t bytes, void* stream)
         return set_error(CAM_ERR_ALIGNMENT, "cam_copy: 16-byte aligned pointers and size required");
     if (overlaps(src, bytes, dst, bytes))
         return set_error(CAM_ERR_OVERLAP, "cam_copy: src and dst overlap");
-    Copy a{src, dst, uint64_t(bytes) / 16, CAM_BUF_STORE_COPY && uint64_t(bytes) <= kBufStoreLimit};
+    Copy a{src, dst, uint64_t(bytes) / 16};
     return launch_copy(a, stream);
 }
 

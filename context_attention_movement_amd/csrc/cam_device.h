@@ -155,31 +155,6 @@ __device__ __forceinline__ void st(void* base, uint64_t vec_index, typename VecO
     st_at<W, NT>(static_cast<char*>(base) + vec_index * W, v);
 }
 
-// A store through a buffer resource over [base, base + 4 GiB): `base` is
-// wave-uniform (a kernel argument), `off` the lane's byte offset from it.
-// The access carries the system-scope bit (sc1), a write-through policy that
-// global stores cannot request; on MI355X it streams the dense relayouts'
-// writes about 2% faster than non-temporal global stores, and it is slower for
-// the combines (so only the dense relayouts and the copy use it).  The
-// resource's word 3 selects 32-bit raw buffer accesses; the hardware drops a
-// store at or past 4 GiB, which the host rules out by only choosing this path
-// for outputs below 4 GiB.
-constexpr uint32_t kBufRsrcWord3 = 0x00020000u;
-constexpr int kBufStoreSc1 = 16;
-template <int W>
-__device__ __forceinline__ void st_buf(void* base, uint32_t off, typename VecOf<W>::type v)
-{
-    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(base, 0, 0xFFFFFFFFu, kBufRsrcWord3);
-    if constexpr (W == 16)
-        __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kBufStoreSc1);
-    else if constexpr (W == 8)
-        __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, kBufStoreSc1);
-    else if constexpr (W == 4)
-        __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, kBufStoreSc1);
-    else
-        __builtin_amdgcn_raw_buffer_store_b16(v, r, off, 0, kBufStoreSc1);
-}
-
 // bf16 <-> fp32.  bf16 is the upper half of an fp32 word; narrowing rounds to
 // nearest, ties to even, and keeps NaN a (quiet) NaN.
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }

@@ -61,7 +61,6 @@ struct DenseRelayout {
     uint32_t n_tiles;      // P*B*P*tiles_per_slab
     int width;             // W in bytes: 16, 8, 4 or 2
     bool seq_to_head;
-    uint32_t buf_st;       // 1: the output is under 4 GiB, stores go through a buffer resource (st_buf)
 };
 
 // Varlen relayout.  A plane is (r, b); the head side of plane (r, b) is rows
@@ -242,7 +241,6 @@ struct Copy {
     const void* src;
     void* dst;
     uint64_t n_vecs;        // 16-byte vectors
-    uint32_t buf_st;        // as DenseRelayout::buf_st
 };
 
 // LDS-staged seq->head relayout (an ablation measured against the direct
@@ -481,15 +479,6 @@ constexpr int kCombineBatchWave = CAM_COMBINE_BATCH_WAVE;
 #endif
 #ifndef CAM_XCD_COMBINE_NARROW
 #define CAM_XCD_COMBINE_NARROW 0
-#endif
-// Dense relayouts and the copy: stores through a buffer resource with the
-// write-through (system-scope) policy when the output is under 4 GiB (1), or
-// global stores with the non-temporal policy above (0); measured on MI355X.
-#ifndef CAM_BUF_STORE_DENSE
-#define CAM_BUF_STORE_DENSE 1
-#endif
-#ifndef CAM_BUF_STORE_COPY
-#define CAM_BUF_STORE_COPY 1
 #endif
 #ifndef CAM_XCD_COPY
 #define CAM_XCD_COPY 1

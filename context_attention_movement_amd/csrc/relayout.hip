@@ -46,12 +46,8 @@ __device__ __forceinline__ void dense_tile(const DenseRelayout& a, uint64_t head
 #pragma unroll
     for (int u = 0; u < kDenseVecs; ++u) {
         const uint32_t v = v0 + uint32_t(u * kThreads);
-        if (!GUARD || v < a.slab_vecs) {
-            if (a.buf_st)  // wave-uniform
-                st_buf<W>(a.dst, uint32_t(dst_off[u] * W), x[u]);
-            else
-                st<W, (NTP & 2) != 0>(a.dst, dst_off[u], x[u]);
-        }
+        if (!GUARD || v < a.slab_vecs)
+            st<W, (NTP & 2) != 0>(a.dst, dst_off[u], x[u]);
     }
 }
 
@@ -239,12 +235,8 @@ __device__ __forceinline__ void copy_tile(const Copy& a, uint64_t v0)
 #pragma unroll
     for (int u = 0; u < kCopyVecs; ++u) {
         const uint64_t v = v0 + uint64_t(u * kThreads);
-        if (!GUARD || v < a.n_vecs) {
-            if (a.buf_st)  // wave-uniform
-                st_buf<16>(a.dst, uint32_t(v * 16), x[u]);
-            else
-                st<16, (CAM_NT_COPY & 2) != 0>(a.dst, v, x[u]);
-        }
+        if (!GUARD || v < a.n_vecs)
+            st<16, (CAM_NT_COPY & 2) != 0>(a.dst, v, x[u]);
     }
 }
 
