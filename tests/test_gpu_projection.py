@@ -57,6 +57,35 @@ def test_projection(cam, orc, case):
     _check(orc, to_host_bits(out), synth.bits(x), synth.bits(w), P, B, H, D, dt, str(case))
 
 
+def _random_cases(n, seed):
+    """Seeded shapes inside the ABI's limits: K a multiple of 64, B*H*D a
+    multiple of 256, H divisible by P; S ragged against the 256-row tile."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        P = int(rng.choice([1, 2, 4, 8]))
+        B = int(rng.integers(1, 4))
+        H = P * int(rng.integers(1, 5))
+        D = int(rng.choice([8, 16, 32, 64, 128]))
+        if (B * H * D) % 256:
+            continue
+        S = P * int(rng.integers(1, 160))
+        K = 64 * int(rng.integers(1, 7))
+        out.append((S, K, P, B, H, D, "bf16" if len(out) % 3 else "fp16"))
+    return out
+
+
+@pytest.mark.parametrize("case", _random_cases(10, 20260913), ids=lambda c: "S{}K{}P{}B{}H{}D{}{}".format(*c))
+def test_projection_random_shapes(cam, orc, case):
+    S, K, P, B, H, D, dt = case
+    announce(f"projection random shape {case}")
+    x = synth.normal((S, K), seed=S * 7 + K, dtype=dt)
+    w = synth.normal((B * H * D, K), seed=S * 7 + K + 1, std=0.05, dtype=dt)
+    out = cam.qkv_projection_head_sharded(x.cuda(), w.cuda(), P, B, H, D)
+    torch.cuda.synchronize()
+    _check(orc, to_host_bits(out), synth.bits(x), synth.bits(w), P, B, H, D, dt, str(case))
+
+
 def test_projection_video_shape_sampled_rows(cam, orc):
     """Video DiT P = 4: S = 32760 (127 full row tiles and a ragged one),
     K = 3072, Q/K/V of 24 heads x 128.  Every output column of 632 token rows:
